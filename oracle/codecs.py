@@ -1,0 +1,172 @@
+"""Closed-form decoders for the number formats the routed MoE layer reads, in fp64.
+
+TEST INFRASTRUCTURE: part of the CPU oracle (see oracle/__init__.py for who may use it).
+
+The expert-offloading pages ask for the experts to be computed on their native
+block-quantized bytes, with no bf16 copy of the weights (tinyserve README, opening
+paragraph and "How it works" item 2; "What we tried and ruled out", last row).
+They name the formats (MXFP4; GGUF Q8_0 in "Supported models" / "Formats") but do
+not define them, so the definitions below are the public ones:
+  * E2M1 (OCP Microscaling Formats v1.0): sign bit, 2 exponent bits (bias 1),
+    1 mantissa bit, no inf/NaN; exponent 0 is subnormal (value m * 1/2).
+  * E8M0 (same spec): an unsigned power-of-two scale 2^(b-127); b = 255 is NaN.
+  * MXFP4 block: 32 E2M1 codes sharing one E8M0 scale.
+  * Q8_0 block (GGUF): 32 two's-complement int8 codes sharing one fp16 scale d.
+  * IEEE binary16 and bfloat16 (the upper 16 bits of an IEEE binary32).
+Every function returns exact fp64 values; all of these formats embed exactly in fp64.
+"""
+from __future__ import annotations
+
+import math
+import numpy as np
+
+# ---------------------------------------------------------------------------- scalars
+
+
+def e2m1_value(code: int) -> float:
+    """Value of a 4-bit E2M1 code, bits s e1 e0 m (s is the top bit)."""
+    s = (code >> 3) & 1
+    e = (code >> 1) & 3
+    m = code & 1
+    mag = m * 0.5 if e == 0 else math.ldexp(1.0 + m / 2.0, e - 1)
+    return -mag if s else mag   # code 8 gives -0.0
+
+
+def e8m0_value(b: int) -> float:
+    """Value of an E8M0 scale byte: 2^(b - 127), NaN for 0xFF."""
+    if b == 255:
+        return math.nan
+    return math.ldexp(1.0, b - 127)
+
+
+def fp16_value(bits: int) -> float:
+    """Value of an IEEE binary16 bit pattern."""
+    s = (bits >> 15) & 1
+    e = (bits >> 10) & 0x1F
+    f = bits & 0x3FF
+    if e == 0:
+        mag = math.ldexp(f, -24)                 # subnormal: f * 2^-14 * 2^-10
+    elif e == 31:
+        mag = math.inf if f == 0 else math.nan
+    else:
+        mag = math.ldexp(1024 + f, e - 25)       # (1 + f/1024) * 2^(e-15)
+    return -mag if s else mag
+
+
+def bf16_value(bits: int) -> float:
+    """Value of a bfloat16 bit pattern: the binary32 whose upper half it is."""
+    s = (bits >> 15) & 1
+    e = (bits >> 7) & 0xFF
+    f = bits & 0x7F
+    if e == 0:
+        mag = math.ldexp(f, -133)                # f * 2^-126 * 2^-7
+    elif e == 255:
+        mag = math.inf if f == 0 else math.nan
+    else:
+        mag = math.ldexp(128 + f, e - 134)       # (1 + f/128) * 2^(e-127)
+    return -mag if s else mag
+
+
+# ----------------------------------------------------------------------------- arrays
+
+_E2M1_TABLE = np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
+_E8M0_TABLE = np.array([e8m0_value(b) for b in range(256)], dtype=np.float64)
+
+
+def e2m1_decode(codes: np.ndarray) -> np.ndarray:
+    return _E2M1_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+def e8m0_decode(b: np.ndarray) -> np.ndarray:
+    return _E8M0_TABLE[np.asarray(b, dtype=np.uint8)]
+
+
+def fp16_decode(bits: np.ndarray) -> np.ndarray:
+    bits = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    s = (bits >> 15) & 1
+    e = (bits >> 10) & 0x1F
+    f = bits & 0x3FF
+    mag = np.where(e == 0, np.ldexp(f.astype(np.float64), -24),
+                   np.ldexp((1024 + f).astype(np.float64), (e - 25).astype(np.int64)))
+    mag = np.where(e == 31, np.where(f == 0, np.inf, np.nan), mag)
+    return np.where(s == 1, -mag, mag)
+
+
+def bf16_decode(bits: np.ndarray) -> np.ndarray:
+    bits = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    s = (bits >> 15) & 1
+    e = (bits >> 7) & 0xFF
+    f = bits & 0x7F
+    mag = np.where(e == 0, np.ldexp(f.astype(np.float64), -133),
+                   np.ldexp((128 + f).astype(np.float64), (e - 134).astype(np.int64)))
+    mag = np.where(e == 255, np.where(f == 0, np.inf, np.nan), mag)
+    return np.where(s == 1, -mag, mag)
+
+
+def bf16_round(a: np.ndarray) -> np.ndarray:
+    """Round fp64 values to the nearest bfloat16 value, ties to even, in one step.
+
+    Returns the rounded values as fp64 (exact). Normal range: 8 significant bits;
+    below 2^-126 the spacing is fixed at 2^-133; values that round past the largest
+    finite bf16 (just under 2^128) become +-inf.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    out = np.empty_like(a)
+    mag = np.abs(a)
+    fin = np.isfinite(a)
+    _, ex = np.frexp(mag)                    # mag = m * 2^ex, m in [0.5, 1)
+    normal = fin & (mag >= 2.0 ** -126)
+    # normal: keep 8 significant bits -> units of 2^(ex-8)
+    q = np.rint(np.ldexp(mag, 8 - ex))       # exact scaling; rint is round-half-even
+    r_norm = np.ldexp(q, ex - 8)
+    sub = fin & ~normal
+    r_sub = np.rint(np.ldexp(mag, 133)) * 2.0 ** -133
+    r = np.where(normal, r_norm, np.where(sub, r_sub, mag))
+    big = 2.0 ** 127 * (2.0 - 2.0 ** -7)     # largest finite bf16
+    r = np.where(fin & (r > big), np.inf, r)
+    out[...] = np.copysign(r, a)              # keeps the sign of -0
+    out[np.isnan(a)] = np.nan
+    return out
+
+
+def bf16_bits(v: np.ndarray) -> np.ndarray:
+    """Bit patterns of fp64 values that are already exactly bf16 (e.g. bf16_round's output)."""
+    u = np.asarray(v, dtype=np.float64).astype(np.float32).view(np.uint32)
+    return (u >> 16).astype(np.uint16)
+
+
+# ------------------------------------------------------------------ block dequantizers
+
+
+def dequant_mxfp4(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """MXFP4 matrix [rows, K/2] codes + [rows, K/32] E8M0 scales -> fp64 [rows, K].
+
+    Element 2j of a row is the low nibble of byte j, element 2j+1 the high nibble.
+    Weight (r, i) = E2M1(code[r, i]) * 2^(scale[r, i // 32] - 127).
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    rows, half = codes.shape
+    K = 2 * half
+    vals = np.empty((rows, K), dtype=np.float64)
+    vals[:, 0::2] = e2m1_decode(codes & 0x0F)
+    vals[:, 1::2] = e2m1_decode(codes >> 4)
+    sc = e8m0_decode(scales)                        # [rows, K/32]
+    return vals * np.repeat(sc, 32, axis=1)
+
+
+def dequant_q8_0(q: np.ndarray, d: np.ndarray) -> np.ndarray:
+    """Q8_0 matrix [rows, K] int8 codes + [rows, K/32] fp16 scale bits -> fp64 [rows, K].
+
+    Weight (r, i) = fp16(d[r, i // 32]) * q[r, i].
+    """
+    q = np.asarray(q, dtype=np.int8).astype(np.float64)
+    sc = fp16_decode(d)
+    return q * np.repeat(sc, 32, axis=1)
+
+
+def dequant(fmt: str, codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    if fmt == "mxfp4":
+        return dequant_mxfp4(codes, scales)
+    if fmt == "q8_0":
+        return dequant_q8_0(codes, scales)
+    raise ValueError(f"unknown block format {fmt!r}")

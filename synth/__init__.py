@@ -1,0 +1,198 @@
+"""Seeded synthetic inputs for the routed MoE FFN layer.
+
+This module only draws random numbers and stores them in the bit formats the
+layer consumes (bf16 activations and router weights, MXFP4 or Q8_0 expert
+blocks, an int32 expert->slot map, an optional fp32 router bias). It holds none
+of the layer's arithmetic: no routing, no decoding of the block formats, no
+matrix products. It is shared by the CPU oracle's tests, the GPU parity tests
+and the benchmark, so both sides see the same bytes.
+
+Workload shapes follow the models that the expert-offloading pages run:
+GPT-OSS-20B (24 layers x 32 experts, top-4; tinyserve README, "Performance"),
+Mixtral 8x7B and a 30B-A3B Qwen MoE (tinyserve README, "Supported models").
+Hidden and intermediate sizes, the value distributions and the Zipf load skew
+are this project's synthetic stand-ins for those models' real weights, which
+are not used.
+
+Layout of what is generated ("canonical" layout, indexed by pool slot):
+  x       uint16 [T, H]        bf16 bit patterns, ~N(0, 1) rounded to nearest even
+  wr      uint16 [E, H]        bf16 bit patterns, ~N(0, 1/H)
+  bias    float32 [E] or None  b_e = -s * ln(r_e), r a seeded permutation of 1..E
+  slot_map int32 [E]           expert e lives in pool slot slot_map[e]
+  MXFP4:  *_q uint8 [S, rows, K/2]  two E2M1 codes per byte, element 2j in the low nibble
+          *_s uint8 [S, rows, K/32] E8M0 scale bytes
+  Q8_0:   *_q int8  [S, rows, K]    two's-complement codes
+          *_s uint16 [S, rows, K/32] fp16 bit patterns of the block scale d
+  gate/up: rows = I, K = H;  down: rows = H, K = I.
+"""
+from __future__ import annotations
+
+import dataclasses
+import numpy as np
+
+__all__ = ["CONFIGS", "Config", "Layer", "make_layer", "make_x", "redraw_x_row",
+           "make_router", "make_bias", "make_slot_map", "make_expert", "config"]
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    name: str
+    T: int
+    H: int
+    I: int
+    E: int
+    k: int
+    fmt: str            # "mxfp4" or "q8_0"
+    zipf_s: float | None
+    slot: str           # "identity" or "perm"
+    seed: int
+    layers: int         # independent layers run back to back when timing
+
+    @property
+    def n_pairs(self) -> int:
+        return self.T * self.k
+
+
+# The five workloads, with T variants as separate entries.
+CONFIGS: dict[str, Config] = {c.name: c for c in [
+    # tiny single layer
+    Config("tiny", 64, 256, 512, 8, 2, "mxfp4", None, "identity", 101, 1),
+    # GPT-OSS-20B-shaped decode
+    Config("gptoss_decode_t1", 1, 2880, 2880, 32, 4, "mxfp4", None, "perm", 202, 24),
+    Config("gptoss_decode_t4", 4, 2880, 2880, 32, 4, "mxfp4", None, "perm", 202, 24),
+    # GPT-OSS-20B-shaped prefill with a Zipf(1.1) expert load
+    Config("gptoss_prefill", 16384, 2880, 2880, 32, 4, "mxfp4", 1.1, "perm", 303, 1),
+    # Mixtral-8x7B-shaped layer in Q8_0
+    Config("mixtral_q8_decode", 1, 4096, 14336, 8, 2, "q8_0", None, "perm", 404, 8),
+    Config("mixtral_q8_prefill", 4096, 4096, 14336, 8, 2, "q8_0", None, "perm", 404, 1),
+    # Qwen3-30B-A3B-shaped fine-grained layer with a Zipf(1.2) expert load
+    Config("qwen_a3b_decode", 1, 2048, 768, 128, 8, "mxfp4", 1.2, "perm", 505, 64),
+    Config("qwen_a3b_prefill", 8192, 2048, 768, 128, 8, "mxfp4", 1.2, "perm", 505, 1),
+]}
+
+
+def config(name: str, **overrides) -> Config:
+    """A named workload, optionally with fields replaced (e.g. a smaller T)."""
+    return dataclasses.replace(CONFIGS[name], **overrides)
+
+
+# --------------------------------------------------------------------------------------
+# storage-format encoders for the generator (input preparation only)
+# --------------------------------------------------------------------------------------
+
+def _f64_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Store fp64 draws as bf16 bit patterns: fp64 -> fp32 (nearest) -> bf16 (nearest even).
+
+    The stored bits are the ground truth for every consumer; how they were reached
+    only shapes the input distribution.
+    """
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def _f64_to_fp16_bits(a: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float16).view(np.uint16)
+
+
+def _rng(*key: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(list(key))))
+
+
+# stream tags
+_X, _ROUTER, _EXPERT, _ZIPF, _SLOT, _REDRAW = 1, 2, 3, 4, 5, 7
+
+
+def make_x(cfg: Config, layer: int = 0, T: int | None = None) -> np.ndarray:
+    """Activations: bf16 bits [T, H], ~N(0, 1). Row t does not depend on T."""
+    T = cfg.T if T is None else T
+    g = _rng(cfg.seed, _X, layer)
+    return _f64_to_bf16_bits(g.standard_normal((T, cfg.H)))
+
+
+def redraw_x_row(cfg: Config, layer: int, t: int, attempt: int) -> np.ndarray:
+    """A replacement activation row for token t, from a seed derived from (t, attempt)."""
+    g = _rng(cfg.seed, _REDRAW, layer, t, attempt)
+    return _f64_to_bf16_bits(g.standard_normal(cfg.H))
+
+
+def make_router(cfg: Config, layer: int = 0) -> np.ndarray:
+    """Router weights: bf16 bits [E, H], ~N(0, 1/H)."""
+    g = _rng(cfg.seed, _ROUTER, layer)
+    return _f64_to_bf16_bits(g.standard_normal((cfg.E, cfg.H)) / np.sqrt(cfg.H))
+
+
+def make_bias(cfg: Config) -> np.ndarray | None:
+    """Per-expert router offset giving a Zipf(s) prior over experts, or None.
+
+    b_e = -s * ln(r_e) with r a seeded permutation of 1..E, so exp(b_e) = r_e^-s.
+    """
+    if cfg.zipf_s is None:
+        return None
+    g = _rng(cfg.seed, _ZIPF)
+    r = g.permutation(cfg.E) + 1
+    return (-cfg.zipf_s * np.log(r.astype(np.float64))).astype(np.float32)
+
+
+def make_slot_map(cfg: Config, layer: int = 0) -> np.ndarray:
+    if cfg.slot == "identity":
+        return np.arange(cfg.E, dtype=np.int32)
+    g = _rng(cfg.seed, _SLOT, layer)
+    return g.permutation(cfg.E).astype(np.int32)
+
+
+def _mxfp4_matrix(g: np.random.Generator, rows: int, K: int):
+    codes = g.integers(0, 256, size=(rows, K // 2), dtype=np.uint8)       # 16 codes equally likely
+    scales = g.integers(120, 123, size=(rows, K // 32), dtype=np.uint8)   # exponents -7, -6, -5
+    return codes, scales
+
+
+def _q8_0_matrix(g: np.random.Generator, rows: int, K: int):
+    q = g.integers(-127, 128, size=(rows, K), dtype=np.int8)
+    d = _f64_to_fp16_bits(g.uniform(1e-3, 4e-3, size=(rows, K // 32)))
+    return q, d
+
+
+def make_expert(cfg: Config, layer: int, e: int) -> dict[str, np.ndarray]:
+    """Weights of logical expert e of one layer (canonical layout, no slot axis)."""
+    g = _rng(cfg.seed, _EXPERT, layer, e)
+    mk = _mxfp4_matrix if cfg.fmt == "mxfp4" else _q8_0_matrix
+    gq, gs = mk(g, cfg.I, cfg.H)
+    uq, us = mk(g, cfg.I, cfg.H)
+    dq, ds = mk(g, cfg.H, cfg.I)
+    return dict(gate_q=gq, gate_s=gs, up_q=uq, up_s=us, down_q=dq, down_s=ds)
+
+
+@dataclasses.dataclass
+class Layer:
+    cfg: Config
+    x: np.ndarray
+    wr: np.ndarray
+    bias: np.ndarray | None
+    slot_map: np.ndarray
+    gate_q: np.ndarray
+    gate_s: np.ndarray
+    up_q: np.ndarray
+    up_s: np.ndarray
+    down_q: np.ndarray
+    down_s: np.ndarray
+
+    @property
+    def planes(self) -> dict[str, np.ndarray]:
+        return {n: getattr(self, n) for n in
+                ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s")}
+
+
+def make_layer(cfg: Config, layer: int = 0, T: int | None = None) -> Layer:
+    """One whole layer: inputs, router, and a pool with expert e stored at slot_map[e]."""
+    slot_map = make_slot_map(cfg, layer)
+    planes: dict[str, np.ndarray] = {}
+    for e in range(cfg.E):
+        w = make_expert(cfg, layer, e)
+        s = int(slot_map[e])
+        for n, a in w.items():
+            if n not in planes:
+                planes[n] = np.empty((cfg.E,) + a.shape, dtype=a.dtype)
+            planes[n][s] = a
+    return Layer(cfg, make_x(cfg, layer, T), make_router(cfg, layer), make_bias(cfg),
+                 slot_map, **planes)

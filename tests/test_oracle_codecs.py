@@ -1,0 +1,164 @@
+"""Pins for the oracle's number-format decoders (CPU only).
+
+Each check compares the oracle's closed-form decoder with something independent of
+it: a value table transcribed from the format's published specification (E2M1), a
+library routine (math.ldexp for E8M0, numpy.float16 for binary16, torch's
+float32 -> bfloat16 conversion for rounding), or constructed midpoints.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import codecs
+
+
+def _load_e2m1_table(golden_dir):
+    vals = {}
+    with open(os.path.join(golden_dir, "e2m1_table.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            c, v = line.split()
+            vals[int(c)] = float(v)
+    return vals
+
+
+def test_e2m1_exhaustive_against_spec_table(golden_dir):
+    table = _load_e2m1_table(golden_dir)
+    assert sorted(table) == list(range(16))
+    for c in range(16):
+        got = codecs.e2m1_value(c)
+        assert got == table[c], c
+        assert math.copysign(1.0, got) == math.copysign(1.0, table[c]), c  # -0 for code 8
+    arr = codecs.e2m1_decode(np.arange(16, dtype=np.uint8))
+    assert np.array_equal(arr, np.array([table[c] for c in range(16)]))
+    assert np.signbit(arr[8])
+
+
+def test_e8m0_all_codes_against_ldexp():
+    for b in range(255):
+        assert codecs.e8m0_value(b) == math.ldexp(1.0, b - 127)
+    assert math.isnan(codecs.e8m0_value(255))
+    arr = codecs.e8m0_decode(np.arange(256, dtype=np.uint8))
+    assert np.array_equal(arr[:255], np.ldexp(1.0, np.arange(255) - 127))
+
+
+def test_fp16_all_65536_codes_against_numpy():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = codecs.fp16_decode(bits)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+    # scalar form agrees with the array form
+    for b in (0x0000, 0x0001, 0x03FF, 0x0400, 0x3C00, 0x7BFF, 0x7C00, 0x8001, 0xFBFF):
+        assert codecs.fp16_value(b) == got[b]
+
+
+def test_bf16_decode_all_codes_against_float32_upper_half():
+    bits = np.arange(65536, dtype=np.uint32)
+    ref = (bits << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+    got = codecs.bf16_decode(bits.astype(np.uint16))
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    for b in (0x0001, 0x007F, 0x0080, 0x3F80, 0x7F7F, 0x7F80, 0xBF80):
+        assert codecs.bf16_value(b) == got[b]
+
+
+def test_bf16_round_trip_identity_on_all_finite_codes():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = codecs.bf16_decode(bits)
+    fin = np.isfinite(v)
+    r = codecs.bf16_round(v[fin])
+    assert np.array_equal(r, v[fin])
+    b = codecs.bf16_bits(r)
+    # -0 and +0 both round-trip to themselves
+    assert np.array_equal(b, bits[fin])
+
+
+def test_bf16_round_constructed_midpoints_tie_to_even():
+    one = 1.0
+    ulp = 2.0 ** -7                       # bf16 spacing in [1, 2)
+    # exactly halfway between 1 and 1+ulp: 1 has an even mantissa -> stays 1
+    assert codecs.bf16_round(np.array([one + ulp / 2]))[0] == one
+    # halfway between 1+ulp (odd) and 1+2ulp (even) -> goes up
+    assert codecs.bf16_round(np.array([one + 1.5 * ulp]))[0] == one + 2 * ulp
+    # a hair above/below the midpoint decides by distance
+    assert codecs.bf16_round(np.array([one + ulp / 2 + 2.0 ** -40]))[0] == one + ulp
+    assert codecs.bf16_round(np.array([one + 1.5 * ulp - 2.0 ** -40]))[0] == one + ulp
+    # negative side mirrors
+    assert codecs.bf16_round(np.array([-(one + 1.5 * ulp)]))[0] == -(one + 2 * ulp)
+    # carry into the next binade
+    assert codecs.bf16_round(np.array([2.0 - ulp / 4]))[0] == 2.0
+    # subnormal spacing 2^-133, tie to even
+    s = 2.0 ** -133
+    assert codecs.bf16_round(np.array([2.5 * s]))[0] == 2 * s
+    assert codecs.bf16_round(np.array([3.5 * s]))[0] == 4 * s
+    # overflow
+    big = 2.0 ** 127 * (2.0 - 2.0 ** -7)
+    assert codecs.bf16_round(np.array([big]))[0] == big
+    mid = 2.0 ** 128 - 2.0 ** 119            # halfway from big to 2^128; big is odd -> up
+    assert codecs.bf16_round(np.array([mid]))[0] == np.inf
+    assert codecs.bf16_round(np.array([-mid]))[0] == -np.inf
+    assert codecs.bf16_round(np.array([mid - 2.0 ** 80]))[0] == big
+
+
+def test_bf16_round_matches_torch_on_float32_inputs():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(5)
+    # fp32 inputs are exact in fp64, so torch's single fp32 -> bf16 RNE step and the
+    # oracle's fp64 -> bf16 step must agree bit for bit.
+    u = rng.integers(0, 2 ** 32, size=200_000, dtype=np.uint64).astype(np.uint32)
+    f = u.view(np.float32)
+    f = f[np.isfinite(f)]
+    # also every exact midpoint pattern (low half 0x8000) and neighbours
+    hi = rng.integers(0, 2 ** 16, size=20_000, dtype=np.uint64).astype(np.uint32)
+    mids = np.concatenate([(hi << 16) | 0x8000, (hi << 16) | 0x7FFF, (hi << 16) | 0x8001])
+    fm = mids.astype(np.uint32).view(np.float32)
+    f = np.concatenate([f, fm[np.isfinite(fm)]])
+    ref = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = codecs.bf16_bits(codecs.bf16_round(f.astype(np.float64)))
+    assert np.array_equal(got, ref)
+
+
+def test_mxfp4_nibble_order_fixture(golden_dir):
+    with open(os.path.join(golden_dir, "mxfp4_nibble_order.txt")) as f:
+        rows = [l.split() for l in f if l.strip() and not l.startswith("#")]
+    d = {r[0]: r[1:] for r in rows}
+    codes = np.array([int(b, 16) for b in d["bytes"]], dtype=np.uint8)[None, :]
+    want = np.array([float(v) for v in d["values"]])
+    got = codecs.dequant_mxfp4(codes, np.array([[127]], dtype=np.uint8))[0]
+    assert np.array_equal(got, want)
+    assert np.array_equal(np.signbit(got), np.signbit(want))
+
+
+def test_mxfp4_block_scale_applies_per_32_elements(golden_dir):
+    table = _load_e2m1_table(golden_dir)
+    rng = np.random.default_rng(1)
+    rows, K = 3, 96
+    codes = rng.integers(0, 256, size=(rows, K // 2), dtype=np.uint8)
+    scales = rng.integers(100, 150, size=(rows, K // 32), dtype=np.uint8)
+    got = codecs.dequant_mxfp4(codes, scales)
+    for r in range(rows):
+        for i in range(K):
+            byte = int(codes[r, i // 2])
+            c = (byte >> 4) if (i % 2) else (byte & 0xF)
+            want = table[c] * math.ldexp(1.0, int(scales[r, i // 32]) - 127)
+            assert got[r, i] == want
+
+
+def test_q8_0_block_scale_applies_per_32_elements():
+    rng = np.random.default_rng(2)
+    rows, K = 3, 96
+    q = rng.integers(-128, 128, size=(rows, K), dtype=np.int8)
+    d = rng.uniform(-1, 1, size=(rows, K // 32)).astype(np.float16).view(np.uint16)
+    got = codecs.dequant_q8_0(q, d)
+    dv = d.view(np.float16).astype(np.float64)
+    for r in range(rows):
+        for i in range(K):
+            assert got[r, i] == float(q[r, i]) * dv[r, i // 32]
