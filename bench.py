@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Throughput of the routed MoE FFN layer on one MI355X.
+
+One step = one pass of the whole layer (route, bucket, gate/up + SwiGLU, down, combine)
+over every layer of the workload, on synthetic seeded inputs already resident in HBM.
+The default workload is the GPT-OSS-20B-shaped decode: T = 1 token through 24 independent
+layers (H = I = 2880, E = 32, top-4, MXFP4 experts in a 32-slot pool behind a permuted slot
+map). Other workloads are selectable with --workload (see synth.CONFIGS).
+
+Output: one JSON line with
+  value          MoE-layer tokens/s = T * layers * steps / elapsed
+  roofline       the dominant kernel (the gate/up pass: 2/3 of the weight bytes) timed with
+                 HIP events on its own stream over the timed region; decode is priced in
+                 algorithmic HBM bytes (the selected experts' gate+up code and scale bytes),
+                 prefill in useful MFMA flops (4 * T*k * H * I)
+  cpu_baseline   the fp64 CPU oracle timed on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+METRIC = "MoE-layer tokens/s; decode HBM GB/s and prefill MFMA % of peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gptoss_decode_t1")
+    ap.add_argument("--layers", type=int, default=None, help="override the workload's layer count")
+    ap.add_argument("--mode", choices=("graph", "eager"), default="graph")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="time budget of the CPU-oracle baseline sample (0 disables it)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "this layer is measured on a single MI355X; multi-GPU sharding is not built.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import quantized_routed_expert_gemv_amd as qm
+
+    cfg = synth.CONFIGS[args.workload]
+    n_layers = args.layers or cfg.layers
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] {cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} "
+          f"{cfg.fmt} x {n_layers} layers", file=sys.stderr, flush=True)
+
+    # ---- inputs, resident in HBM before timing
+    layers = []
+    host_keep = []          # a few layers kept on the host for the CPU baseline
+    for l in range(n_layers):
+        L = synth.make_layer(cfg, l)
+        pool = qm.Pool.from_canonical(cfg.fmt, cfg.H, cfg.I, L.planes, device=dev)
+        x = torch.from_numpy(L.x.view(np.int16)).to(dev).view(torch.bfloat16)
+        wr = torch.from_numpy(L.wr.view(np.int16)).to(dev).view(torch.bfloat16)
+        bias = None if L.bias is None else torch.from_numpy(L.bias).to(dev)
+        sm = torch.from_numpy(L.slot_map).to(dev)
+        layers.append((pool, x, wr, bias, sm))
+        if l < 4:
+            host_keep.append(L)
+        del L
+        torch.cuda.synchronize()
+    print("[bench] inputs resident", file=sys.stderr, flush=True)
+
+    T, k, E, H, I = cfg.T, cfg.k, cfg.E, cfg.H, cfg.I
+    ws = qm.Workspace(T, H, I, E, k, dev)
+    im = ws.intermediates()
+    scratch = ws.scratch()
+    outs = [torch.empty((T, H), dtype=torch.float32, device=dev) for _ in range(n_layers)]
+    stream = torch.cuda.Stream(device=dev)
+    prefill = T > 16
+
+    def step(ev=None):
+        for li, (pool, x, wr, bias, sm) in enumerate(layers):
+            qm.route(x, wr, bias, k, ids=im["ids"], w=im["w"], scratch=scratch, stream=stream)
+            qm.bucket(im["ids"], E, im["counts"], im["offsets"], im["perm"], im["inv_perm"],
+                      scratch=scratch, stream=stream)
+            if ev is not None:
+                ev[li][0].record(stream)
+            qm.expert_gate_up(pool, sm, x, k, im["offsets"], im["perm"], h=im["h"], stream=stream)
+            if ev is not None:
+                ev[li][1].record(stream)
+            qm.expert_down(pool, sm, T, k, im["offsets"], im["h"], y=im["y"], stream=stream)
+            qm.combine(im["y"], im["inv_perm"], im["w"], out=outs[li], stream=stream)
+
+    def make_events(external):
+        return [(torch.cuda.Event(enable_timing=True, external=external),
+                 torch.cuda.Event(enable_timing=True, external=external))
+                for _ in range(n_layers)]
+
+    mode = args.mode
+    graph = None
+    ev = None
+    with torch.cuda.stream(stream):
+        step()                          # first call: kernels load, caches warm
+        stream.synchronize()
+        if mode == "graph":
+            try:
+                ev = make_events(True)
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph, stream=stream):
+                    step(ev)
+                graph.replay()
+                stream.synchronize()
+                ev[0][0].elapsed_time(ev[0][1])
+            except Exception as exc:     # graph capture of timing events not available
+                print(f"[bench] graph mode unavailable ({exc}); timing eagerly", file=sys.stderr)
+                mode, graph = "eager", None
+        if mode == "eager":
+            ev = make_events(False)
+
+        def run_step():
+            if graph is not None:
+                graph.replay()
+            else:
+                step(ev)
+
+        for _ in range(args.warmup):
+            run_step()
+        stream.synchronize()
+        torch.cuda.synchronize()
+
+        # ---- timed region
+        kern_ms = []
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            run_step()
+            stream.synchronize()
+            kern_ms.extend(a.elapsed_time(b) for a, b in ev)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+
+    elapsed = t1 - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = T * n_layers * args.steps / elapsed
+
+    # ---- roofline of the gate/up kernel
+    ids_last = im["ids"].cpu().numpy()
+    kern_avg_s = float(np.mean(kern_ms)) * 1e-3
+    if prefill:
+        flops = 4.0 * T * k * H * I          # gate and up: 2 flops per weight per pair, twice
+        achieved = flops / kern_avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "gate/up grouped GEMM (k_ggemm)", "work_per_launch": flops}
+    else:
+        bpw = 17.0 / 32.0 if cfg.fmt == "mxfp4" else 34.0 / 32.0
+        # distinct experts per layer: recomputed from each layer's routing on the device
+        n_distinct = []
+        for li, (pool, x, wr, bias, sm) in enumerate(layers):
+            ids_l, _ = qm.route(x, wr, bias, k)
+            n_distinct.append(len(np.unique(ids_l.cpu().numpy())))
+        bytes_per_launch = float(np.mean(n_distinct)) * 2 * I * H * bpw
+        achieved = bytes_per_launch / kern_avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "gate/up GEMV (k_gemv)", "work_per_launch": bytes_per_launch}
+    roof["avg_launch_us"] = round(kern_avg_s * 1e6, 3)
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": T, "H": H, "I": I, "E": E, "k": k, "fmt": cfg.fmt,
+                   "layers": n_layers, "mode": mode},
+        "roofline": roof,
+    }
+
+    # ---- CPU baseline: the oracle on a bounded sample of the same workload
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(cfg, host_keep, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(cfg, host_layers, budget_s):
+    import numpy as np
+    from oracle import moe as omoe
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    T, k = cfg.T, cfg.k
+    t0 = time.perf_counter()
+    tokens = 0
+    layers_done = 0
+    sample_T = T
+    while time.perf_counter() - t0 < budget_s and layers_done < len(host_layers):
+        L = host_layers[layers_done]
+        x = L.x
+        if T > 64:                           # prefill: a bounded token sample
+            sample_T = 64
+            x = L.x[:sample_T]
+        omoe.layer(L.planes, cfg.fmt, L.slot_map, L.wr, L.bias, x, k)
+        tokens += x.shape[0]
+        layers_done += 1
+    dt = time.perf_counter() - t0
+    sample = (f"{layers_done} layer(s) x {sample_T} token(s) of {cfg.name}, whole layer "
+              "(route, bucket, dequantize selected experts, FFN, combine) in fp64")
+    return {"value": round(tokens / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 2)}
+
+
+if __name__ == "__main__":
+    main()

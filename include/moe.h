@@ -1,0 +1,219 @@
+/*
+ * moe.h -- C ABI of the routed Mixture-of-Experts FFN layer on block-quantized experts,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The layer is the GPU work under the expert-offloading systems described in
+ *   [T]  "tinyserve -- MoE Expert Offloading for Consumer GPUs" (README), and
+ *   [L]  llama.cpp discussion "Experiment: fixed GPU expert working set with Native CPU
+ *        miss execution for Qwen sparse MoE".
+ * It has five stages, each one entry point below, plus one fused call:
+ *   moe_route       router GEMV, top-k, softmax over the chosen k     ([L] original post:
+ *                   the router stays on the GPU; [T] "Performance": top_k = 4)
+ *   moe_bucket      group the (token, choice) pairs by expert          ([T] "How it works" 6)
+ *   moe_expert_ffn  gate / up / SwiGLU / down on the experts' native block-quantized bytes,
+ *                   reached through an expert -> slot map into a resident pool
+ *                   ([T] "How it works" 2 and 3; [L] original post: fixed packed GPU pool;
+ *                   [L] "Formal gate results": mapping rewrite -> grouped quantized matmul)
+ *   moe_combine     weighted merge of the k expert outputs per token  ([L] original post)
+ *   moe_layer       all of the above on one stream
+ *
+ * Conventions for every call:
+ *   - All data pointers are DEVICE pointers owned by the caller, 16-byte aligned unless
+ *     said otherwise. The library never allocates, frees or synchronises: every call only
+ *     enqueues kernels on `stream` (a hipStream_t; NULL = the default stream) and returns.
+ *     The fused call issues no host<->device traffic, so it can be captured in a HIP graph.
+ *   - bf16 values are passed as uint16_t bit patterns. Logits, gate weights, the expert
+ *     outputs y and the layer output are fp32. The hidden activation h (after SwiGLU) is the
+ *     one bf16 rounding point inside the layer (round to nearest even).
+ *   - Argument errors are detected on the host before anything is enqueued and return
+ *     MOE_ERR_INVALID_ARG; moe_last_error() then holds a description (thread-local).
+ *     A failed launch returns MOE_ERR_HIP with the HIP error text.
+ *   - Limits: 1 <= k <= 8, k <= E <= 256, H and I multiples of 32, T >= 0. T = 0 enqueues
+ *     nothing and returns MOE_OK, except moe_bucket, which then writes all-zero counts and
+ *     offsets.
+ *
+ * Notation: T tokens, H hidden size, I expert intermediate size, E experts, k choices per
+ * token, S pool slots. A pair is p = t*k + j, the j-th choice of token t.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,
+  MOE_ERR_UNSUPPORTED = 2,
+  MOE_ERR_HIP = 3
+} moe_status;
+
+/* Block formats of the expert weights.
+ * MOE_W_MXFP4: blocks of 32 E2M1 codes (4 bits each) sharing one E8M0 scale byte;
+ *              weight = E2M1(code) * 2^(scale - 127). Scale bytes 1..254 are supported.
+ * MOE_W_Q8_0:  blocks of 32 int8 codes sharing one fp16 scale d; weight = d * q.      */
+typedef enum { MOE_W_MXFP4 = 1, MOE_W_Q8_0 = 2 } moe_wfmt;
+
+/* Which expert-FFN schedule to use. AUTO picks the GEMV schedule for T <= 16 and the
+ * grouped MFMA GEMM otherwise. Both give results within the same tolerance; they are not
+ * bitwise equal to each other. */
+typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_GROUPED = 2 } moe_path;
+
+/*
+ * Resident expert pool ([T] "How it works" 3: a GPU slot map in front of cached experts;
+ * [L] original post: a fixed subset of packed experts materialised in a GPU pool).
+ *
+ * Three matrices per slot: gate [I x H], up [I x H], down [H x I] (rows x K, the
+ * reduction dimension K is contiguous within a block). Each matrix has a code plane and a
+ * scale plane, stored in the library's TILED layout (produced by moe_pool_pack):
+ *   nb = K / 32 blocks per row; a row group is 16 consecutive rows;
+ *   unit(r, b) = ((r / 16) * nb + b) * 16 + (r % 16)
+ *   MXFP4 codes : 16 bytes at unit(r,b) * 16; byte j holds element 2j of the block in its
+ *                 low nibble and element 2j+1 in its high nibble
+ *   MXFP4 scales: 1 byte at unit(r,b)
+ *   Q8_0  codes : 32 bytes at unit(r,b) * 32, element i of the block at byte i
+ *   Q8_0  scales: fp16 at byte unit(r,b) * 2
+ * so the 16 rows of a row group are interleaved block by block: one 64-lane 16-byte load
+ * reads 16 rows x 4 MXFP4 blocks (or 16 rows x 2 Q8_0 blocks) from one contiguous KiB.
+ * Slot s of a plane starts at s * (bytes per matrix); rows of a matrix must be a multiple
+ * of 16 (always true, since H and I are multiples of 32).
+ */
+typedef struct {
+  int32_t fmt;      /* moe_wfmt */
+  int32_t n_slots;  /* S >= 1 */
+  int32_t H, I;
+  const void* gate_q; const void* gate_s;
+  const void* up_q;   const void* up_s;
+  const void* down_q; const void* down_s;
+} moe_pool;
+
+/* Bytes of one matrix's code plane / scale plane for one slot. */
+size_t moe_plane_bytes(int32_t fmt, int32_t rows, int32_t K, int32_t scales);
+
+/*
+ * moe_pool_pack -- convert n_mats matrices [rows x K] from the CANONICAL layout into the
+ * tiled pool layout above (device to device, on `stream`). This is the "mapping" step
+ * a loader runs when an expert lands in a slot; it is not on the per-token path.
+ * Canonical layout (row-major, per matrix):
+ *   MXFP4: codes u8 [rows][K/2] (element 2j in the low nibble of byte j),
+ *          scales u8 [rows][K/32]
+ *   Q8_0 : codes i8 [rows][K], scales fp16 [rows][K/32]
+ * src and dst must not overlap. Returns MOE_ERR_INVALID_ARG for rows % 16 != 0 or
+ * K % 32 != 0, MOE_ERR_UNSUPPORTED for an unknown fmt.
+ */
+moe_status moe_pool_pack(int32_t fmt, int32_t n_mats, int32_t rows, int32_t K,
+                         const void* src_q, const void* src_s, void* dst_q, void* dst_s,
+                         void* stream);
+
+/*
+ * moe_route -- router GEMV + top-k + softmax over the chosen k.
+ *   x        bf16 [T][H] activations
+ *   w_router bf16 [E][H] router weights
+ *   bias     fp32 [E] added to every token's logits, or NULL
+ *   topk_ids int32 [T][k] (out): for each token the k largest logits
+ *            L[t,e] = sum_h x[t,h] * w_router[e,h] + bias[e], in descending order; equal
+ *            logits go to the lower expert index
+ *   topk_w   fp32 [T][k] (out): w[t,j] = exp(L_j - L_0) / sum_{i<k} exp(L_i - L_0)
+ *   scratch  device memory of at least moe_route_scratch_bytes(T, H, E) bytes, or NULL
+ *            when that function returns 0. Logits are accumulated in fp32 from exact
+ *            bf16 products.
+ */
+size_t moe_route_scratch_bytes(int32_t T, int32_t H, int32_t E);
+moe_status moe_route(const uint16_t* x, const uint16_t* w_router, const float* bias,
+                     int32_t T, int32_t H, int32_t E, int32_t k,
+                     int32_t* topk_ids, float* topk_w,
+                     void* scratch, size_t scratch_bytes, void* stream);
+
+/*
+ * moe_bucket -- stable counting sort of the T*k pairs by expert ([T] "How it works" 6:
+ * tokens grouped by expert so each expert is loaded once).
+ *   topk_ids int32 [T*k], every value in [0, E) (values outside are a caller error and
+ *            give unspecified buckets, never an out-of-bounds access)
+ *   counts   int32 [E]   (out) pairs per expert
+ *   offsets  int32 [E+1] (out) exclusive prefix sum of counts; offsets[E] = T*k
+ *   perm     int32 [T*k] (out) perm[pos] = p, pairs of one expert in ascending p
+ *   inv_perm int32 [T*k] (out) inv_perm[p] = pos
+ *   scratch  at least moe_bucket_scratch_bytes(T, k, E) bytes (may be NULL if that is 0)
+ * Bit-exact and deterministic: no ordering decision depends on atomics.
+ */
+size_t moe_bucket_scratch_bytes(int32_t T, int32_t k, int32_t E);
+moe_status moe_bucket(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
+                      int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                      void* scratch, size_t scratch_bytes, void* stream);
+
+/*
+ * moe_expert_ffn -- for every bucket position pos of expert e (offsets[e] <= pos <
+ * offsets[e+1]), with token t = perm[pos] / k and slot s = slot_map[e]:
+ *   g = W_gate[s] x[t],  u = W_up[s] x[t]              (fp32 accumulation)
+ *   h[pos] = bf16_RNE(silu(g) * u),  silu(z) = z / (1 + exp(-z))
+ *   y[pos] = W_down[s] h[pos]                          (fp32)
+ *   x  bf16 [T][H];  h bf16 [T*k][I] (out);  y fp32 [T*k][H] (out)
+ *   offsets/perm as produced by moe_bucket for the same T, k, E.
+ *   err_flags uint32 (nullable): if slot_map[e] is outside [0, n_slots), that expert's h
+ *   and y rows are written as zeros and bit 0 of *err_flags is set (atomic OR); nothing
+ *   traps.
+ *   path: moe_path.
+ */
+moe_status moe_expert_ffn(const moe_pool* pool, const int32_t* slot_map, int32_t E,
+                          const uint16_t* x, int32_t T, int32_t k,
+                          const int32_t* offsets, const int32_t* perm,
+                          uint16_t* h, float* y, uint32_t* err_flags, int32_t path,
+                          void* stream);
+
+/*
+ * The two halves of moe_expert_ffn, for callers that schedule them separately (the pages'
+ * per-expert forward is "gate, up, down"; here gate and up share one pass):
+ *   moe_expert_gate_up  writes h only (same arguments and meaning as moe_expert_ffn)
+ *   moe_expert_down     y[pos] = W_down[slot_map[e]] h[pos] for every bucket position
+ * Calling gate_up then down with the same path equals moe_expert_ffn.
+ */
+moe_status moe_expert_gate_up(const moe_pool* pool, const int32_t* slot_map, int32_t E,
+                              const uint16_t* x, int32_t T, int32_t k,
+                              const int32_t* offsets, const int32_t* perm, uint16_t* h,
+                              uint32_t* err_flags, int32_t path, void* stream);
+moe_status moe_expert_down(const moe_pool* pool, const int32_t* slot_map, int32_t E,
+                           int32_t T, int32_t k, const int32_t* offsets, const uint16_t* h,
+                           float* y, uint32_t* err_flags, int32_t path, void* stream);
+
+/*
+ * moe_combine -- out[t,:] = sum_{j<k} topk_w[t,j] * y[inv_perm[t*k+j], :], summed in
+ * increasing j, fp32. y fp32 [T*k][H], out fp32 [T][H].
+ */
+moe_status moe_combine(const float* y, const int32_t* inv_perm, const float* topk_w,
+                       int32_t T, int32_t k, int32_t H, float* out, void* stream);
+
+/*
+ * Workspace of the fused call: byte offsets (from the workspace base) of every
+ * intermediate, so a caller can read them back. All offsets are 256-byte aligned.
+ */
+typedef struct {
+  size_t total;
+  size_t topk_ids, topk_w, counts, offsets, perm, inv_perm, h, y, scratch;
+} moe_ws_layout;
+
+moe_status moe_layer_workspace(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                               moe_ws_layout* out);
+
+/*
+ * moe_layer -- route, bucket, expert FFN and combine for T tokens, enqueued on one stream.
+ * out fp32 [T][H]. workspace: at least moe_layer_workspace(...).total bytes, 256-byte
+ * aligned; its contents on entry do not matter. Results equal calling the four stages in
+ * order with the same path.
+ */
+moe_status moe_layer(const moe_pool* pool, const int32_t* slot_map,
+                     const uint16_t* w_router, const float* bias, const uint16_t* x,
+                     int32_t T, int32_t E, int32_t k, float* out,
+                     void* workspace, size_t workspace_bytes, uint32_t* err_flags,
+                     int32_t path, void* stream);
+
+const char* moe_status_string(moe_status s);
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,370 @@
+// C ABI of the routed MoE FFN layer (declared in include/moe.h): argument checking,
+// workspace layout and dispatch to the kernels. No call allocates, frees or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/moe.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+moe_status ok() {
+  g_err[0] = 0;
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return ok();
+  return fail(MOE_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define CHECK_PTR(p)                                                                 \
+  do {                                                                               \
+    if ((p) == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s is NULL", #p);          \
+    if (!aligned16(p)) return fail(MOE_ERR_INVALID_ARG, "%s is not 16-byte aligned", #p); \
+  } while (0)
+
+moe_status check_shape(int32_t T, int32_t H, int32_t E, int32_t k) {
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T = %d < 0", T);
+  if (H <= 0 || H % 32) return fail(MOE_ERR_INVALID_ARG, "H = %d is not a positive multiple of 32", H);
+  if (E < 1 || E > moe::kMaxE) return fail(MOE_ERR_INVALID_ARG, "E = %d outside [1, %d]", E, moe::kMaxE);
+  if (k < 1 || k > moe::kMaxK) return fail(MOE_ERR_INVALID_ARG, "k = %d outside [1, %d]", k, moe::kMaxK);
+  if (k > E) return fail(MOE_ERR_INVALID_ARG, "k = %d > E = %d", k, E);
+  if ((int64_t)T * k > 0x3FFFFFFF) return fail(MOE_ERR_INVALID_ARG, "T*k too large");
+  return MOE_OK;
+}
+
+moe_status check_pool(const moe_pool* pool) {
+  if (pool == nullptr) return fail(MOE_ERR_INVALID_ARG, "pool is NULL");
+  if (pool->fmt != MOE_W_MXFP4 && pool->fmt != MOE_W_Q8_0)
+    return fail(MOE_ERR_UNSUPPORTED, "unknown weight format %d", pool->fmt);
+  if (pool->n_slots < 1) return fail(MOE_ERR_INVALID_ARG, "n_slots = %d < 1", pool->n_slots);
+  if (pool->H <= 0 || pool->H % 32) return fail(MOE_ERR_INVALID_ARG, "pool H = %d", pool->H);
+  if (pool->I <= 0 || pool->I % 32) return fail(MOE_ERR_INVALID_ARG, "pool I = %d", pool->I);
+  CHECK_PTR(pool->gate_q);
+  CHECK_PTR(pool->up_q);
+  CHECK_PTR(pool->down_q);
+  CHECK_PTR(pool->gate_s);
+  CHECK_PTR(pool->up_s);
+  CHECK_PTR(pool->down_s);
+  return MOE_OK;
+}
+
+size_t plane_bytes(int fmt, int64_t rows, int64_t K, bool scales) {
+  const int64_t nb = K / 32;
+  if (scales) return (size_t)(rows * nb * moe::scale_bytes_per_block(fmt));
+  return (size_t)(rows * nb * moe::code_bytes_per_block(fmt));
+}
+
+void pool_views(const moe_pool* p, moe::PoolView* g, moe::PoolView* u, moe::PoolView* d) {
+  const int fmt = p->fmt;
+  const int64_t gq = plane_bytes(fmt, p->I, p->H, false), gs = plane_bytes(fmt, p->I, p->H, true);
+  const int64_t dq = plane_bytes(fmt, p->H, p->I, false), ds = plane_bytes(fmt, p->H, p->I, true);
+  *g = {(const uint8_t*)p->gate_q, (const uint8_t*)p->gate_s, gq, gs};
+  *u = {(const uint8_t*)p->up_q, (const uint8_t*)p->up_s, gq, gs};
+  *d = {(const uint8_t*)p->down_q, (const uint8_t*)p->down_s, dq, ds};
+}
+
+size_t route_scratch(int32_t T, int32_t H, int32_t E) {
+  const int ks = moe::route_ksplit(T, H);
+  return ks > 1 ? (size_t)ks * T * E * sizeof(float) : 0;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+bool use_gemv(int32_t path, int32_t T) {
+  return path == MOE_PATH_GEMV || (path == MOE_PATH_AUTO && T <= 16);
+}
+
+moe_status gate_up_dispatch(const moe_pool* pool, const int32_t* slot_map, int32_t E,
+                            const uint16_t* x, int32_t T, int32_t k, const int32_t* offsets,
+                            const int32_t* perm, uint16_t* h, uint32_t* err, int32_t path,
+                            hipStream_t stream) {
+  moe::PoolView g, u, d;
+  pool_views(pool, &g, &u, &d);
+  if (use_gemv(path, T))
+    return hip_status(moe::launch_gate_up_gemv(pool->fmt, g, u, slot_map, pool->n_slots, E, x, T,
+                                               k, pool->H, pool->I, offsets, perm, h, err, stream),
+                      "gate/up (GEMV)");
+  return hip_status(moe::launch_gate_up_grouped(pool->fmt, g, u, slot_map, pool->n_slots, E, x, T,
+                                                k, pool->H, pool->I, offsets, perm, h, err, stream),
+                    "gate/up (grouped GEMM)");
+}
+
+moe_status down_dispatch(const moe_pool* pool, const int32_t* slot_map, int32_t E, int32_t T,
+                         int32_t k, const int32_t* offsets, const uint16_t* h, float* y,
+                         uint32_t* err, int32_t path, hipStream_t stream) {
+  moe::PoolView g, u, d;
+  pool_views(pool, &g, &u, &d);
+  if (use_gemv(path, T))
+    return hip_status(moe::launch_down_gemv(pool->fmt, d, slot_map, pool->n_slots, E, T, k,
+                                            pool->H, pool->I, offsets, h, y, err, stream),
+                      "down (GEMV)");
+  return hip_status(moe::launch_down_grouped(pool->fmt, d, slot_map, pool->n_slots, E, T, k,
+                                             pool->H, pool->I, offsets, h, y, err, stream),
+                    "down (grouped GEMM)");
+}
+
+moe_status ffn_dispatch(const moe_pool* pool, const int32_t* slot_map, int32_t E,
+                        const uint16_t* x, int32_t T, int32_t k, const int32_t* offsets,
+                        const int32_t* perm, uint16_t* h, float* y, uint32_t* err,
+                        int32_t path, hipStream_t stream) {
+  moe_status s = gate_up_dispatch(pool, slot_map, E, x, T, k, offsets, perm, h, err, path, stream);
+  if (s != MOE_OK) return s;
+  return down_dispatch(pool, slot_map, E, T, k, offsets, h, y, err, path, stream);
+}
+
+// Shared argument checks of the expert-FFN entry points.
+moe_status check_ffn_args(const moe_pool* pool, const int32_t* slot_map, int32_t E, int32_t T,
+                          int32_t k, const int32_t* offsets, uint32_t* err_flags, int32_t path) {
+  moe_status s = check_pool(pool);
+  if (s != MOE_OK) return s;
+  s = check_shape(T, pool->H, E, k);
+  if (s != MOE_OK) return s;
+  if (path < MOE_PATH_AUTO || path > MOE_PATH_GROUPED)
+    return fail(MOE_ERR_INVALID_ARG, "path = %d", path);
+  if (T == 0) return MOE_OK;
+  CHECK_PTR(slot_map);
+  CHECK_PTR(offsets);
+  if (err_flags != nullptr && ((uintptr_t)err_flags & 3))
+    return fail(MOE_ERR_INVALID_ARG, "err_flags misaligned");
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "unknown moe_status";
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+size_t moe_plane_bytes(int32_t fmt, int32_t rows, int32_t K, int32_t scales) {
+  if ((fmt != MOE_W_MXFP4 && fmt != MOE_W_Q8_0) || rows < 0 || K < 0) return 0;
+  return plane_bytes(fmt, rows, K, scales != 0);
+}
+
+moe_status moe_pool_pack(int32_t fmt, int32_t n_mats, int32_t rows, int32_t K,
+                         const void* src_q, const void* src_s, void* dst_q, void* dst_s,
+                         void* stream) {
+  if (fmt != MOE_W_MXFP4 && fmt != MOE_W_Q8_0)
+    return fail(MOE_ERR_UNSUPPORTED, "unknown weight format %d", fmt);
+  if (n_mats < 0 || rows < 0 || K < 0) return fail(MOE_ERR_INVALID_ARG, "negative size");
+  if (rows % 16) return fail(MOE_ERR_INVALID_ARG, "rows = %d is not a multiple of 16", rows);
+  if (K % 32) return fail(MOE_ERR_INVALID_ARG, "K = %d is not a multiple of 32", K);
+  if (n_mats == 0 || rows == 0 || K == 0) return ok();
+  CHECK_PTR(src_q);
+  CHECK_PTR(dst_q);
+  if (src_s == nullptr || dst_s == nullptr) return fail(MOE_ERR_INVALID_ARG, "scale plane is NULL");
+  if (fmt == MOE_W_Q8_0 && (((uintptr_t)src_s | (uintptr_t)dst_s) & 1))
+    return fail(MOE_ERR_INVALID_ARG, "fp16 scale plane is not 2-byte aligned");
+  return hip_status(moe::launch_pack(fmt, n_mats, rows, K, src_q, src_s, dst_q, dst_s,
+                                     (hipStream_t)stream),
+                    "pool pack");
+}
+
+size_t moe_route_scratch_bytes(int32_t T, int32_t H, int32_t E) {
+  if (T <= 0 || H <= 0 || E <= 0) return 0;
+  return route_scratch(T, H, E);
+}
+
+moe_status moe_route(const uint16_t* x, const uint16_t* w_router, const float* bias, int32_t T,
+                     int32_t H, int32_t E, int32_t k, int32_t* topk_ids, float* topk_w,
+                     void* scratch, size_t scratch_bytes, void* stream) {
+  moe_status s = check_shape(T, H, E, k);
+  if (s != MOE_OK) return s;
+  if (T == 0) return ok();
+  CHECK_PTR(x);
+  CHECK_PTR(w_router);
+  CHECK_PTR(topk_ids);
+  CHECK_PTR(topk_w);
+  if (bias != nullptr && ((uintptr_t)bias & 3)) return fail(MOE_ERR_INVALID_ARG, "bias misaligned");
+  const size_t need = route_scratch(T, H, E);
+  if (need) {
+    CHECK_PTR(scratch);
+    if (scratch_bytes < need)
+      return fail(MOE_ERR_INVALID_ARG, "route scratch %zu bytes < %zu needed", scratch_bytes, need);
+  }
+  return hip_status(moe::launch_route(x, w_router, bias, T, H, E, k, topk_ids, topk_w,
+                                      (float*)scratch, (hipStream_t)stream),
+                    "route");
+}
+
+size_t moe_bucket_scratch_bytes(int32_t T, int32_t k, int32_t E) {
+  if (T <= 0 || k <= 0 || E <= 0) return 0;
+  return moe::bucket_scratch_bytes(T * k, E);
+}
+
+moe_status moe_bucket(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t* counts,
+                      int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* scratch,
+                      size_t scratch_bytes, void* stream) {
+  moe_status s = check_shape(T, 32, E, k);
+  if (s != MOE_OK) return s;
+  CHECK_PTR(counts);
+  CHECK_PTR(offsets);
+  if (T == 0)   // empty input: one small kernel still writes all-zero counts and offsets
+    return hip_status(moe::launch_bucket(nullptr, 0, E, counts, offsets, nullptr, nullptr,
+                                         nullptr, (hipStream_t)stream),
+                      "bucket");
+  CHECK_PTR(topk_ids);
+  CHECK_PTR(perm);
+  CHECK_PTR(inv_perm);
+  const size_t need = moe::bucket_scratch_bytes(T * k, E);
+  if (need) {
+    CHECK_PTR(scratch);
+    if (scratch_bytes < need)
+      return fail(MOE_ERR_INVALID_ARG, "bucket scratch %zu bytes < %zu needed", scratch_bytes, need);
+  }
+  return hip_status(moe::launch_bucket(topk_ids, T * k, E, counts, offsets, perm, inv_perm,
+                                       scratch, (hipStream_t)stream),
+                    "bucket");
+}
+
+moe_status moe_expert_ffn(const moe_pool* pool, const int32_t* slot_map, int32_t E,
+                          const uint16_t* x, int32_t T, int32_t k, const int32_t* offsets,
+                          const int32_t* perm, uint16_t* h, float* y, uint32_t* err_flags,
+                          int32_t path, void* stream) {
+  moe_status s = check_ffn_args(pool, slot_map, E, T, k, offsets, err_flags, path);
+  if (s != MOE_OK || T == 0) return s == MOE_OK ? ok() : s;
+  CHECK_PTR(x);
+  CHECK_PTR(perm);
+  CHECK_PTR(h);
+  CHECK_PTR(y);
+  return ffn_dispatch(pool, slot_map, E, x, T, k, offsets, perm, h, y, err_flags, path,
+                      (hipStream_t)stream);
+}
+
+moe_status moe_expert_gate_up(const moe_pool* pool, const int32_t* slot_map, int32_t E,
+                              const uint16_t* x, int32_t T, int32_t k, const int32_t* offsets,
+                              const int32_t* perm, uint16_t* h, uint32_t* err_flags,
+                              int32_t path, void* stream) {
+  moe_status s = check_ffn_args(pool, slot_map, E, T, k, offsets, err_flags, path);
+  if (s != MOE_OK || T == 0) return s == MOE_OK ? ok() : s;
+  CHECK_PTR(x);
+  CHECK_PTR(perm);
+  CHECK_PTR(h);
+  return gate_up_dispatch(pool, slot_map, E, x, T, k, offsets, perm, h, err_flags, path,
+                          (hipStream_t)stream);
+}
+
+moe_status moe_expert_down(const moe_pool* pool, const int32_t* slot_map, int32_t E, int32_t T,
+                           int32_t k, const int32_t* offsets, const uint16_t* h, float* y,
+                           uint32_t* err_flags, int32_t path, void* stream) {
+  moe_status s = check_ffn_args(pool, slot_map, E, T, k, offsets, err_flags, path);
+  if (s != MOE_OK || T == 0) return s == MOE_OK ? ok() : s;
+  CHECK_PTR(h);
+  CHECK_PTR(y);
+  return down_dispatch(pool, slot_map, E, T, k, offsets, h, y, err_flags, path,
+                       (hipStream_t)stream);
+}
+
+moe_status moe_combine(const float* y, const int32_t* inv_perm, const float* topk_w, int32_t T,
+                       int32_t k, int32_t H, float* out, void* stream) {
+  moe_status s = check_shape(T, H, moe::kMaxE, k);
+  if (s != MOE_OK) return s;
+  if (T == 0) return ok();
+  CHECK_PTR(y);
+  CHECK_PTR(inv_perm);
+  CHECK_PTR(topk_w);
+  CHECK_PTR(out);
+  return hip_status(moe::launch_combine(y, inv_perm, topk_w, T, k, H, out, (hipStream_t)stream),
+                    "combine");
+}
+
+moe_status moe_layer_workspace(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                               moe_ws_layout* out) {
+  if (out == nullptr) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
+  moe_status s = check_shape(T, H, E, k);
+  if (s != MOE_OK) return s;
+  if (I <= 0 || I % 32) return fail(MOE_ERR_INVALID_ARG, "I = %d", I);
+  const size_t n = (size_t)T * k;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  out->topk_ids = take(n * 4);
+  out->topk_w = take(n * 4);
+  out->counts = take((size_t)E * 4);
+  out->offsets = take((size_t)(E + 1) * 4);
+  out->perm = take(n * 4);
+  out->inv_perm = take(n * 4);
+  out->h = take(n * I * 2);
+  out->y = take(n * H * 4);
+  const size_t rs = T > 0 ? route_scratch(T, H, E) : 0;
+  const size_t bs = T > 0 ? moe::bucket_scratch_bytes((int)n, E) : 0;
+  out->scratch = take(rs > bs ? rs : bs);
+  out->total = off;
+  return ok();
+}
+
+moe_status moe_layer(const moe_pool* pool, const int32_t* slot_map, const uint16_t* w_router,
+                     const float* bias, const uint16_t* x, int32_t T, int32_t E, int32_t k,
+                     float* out, void* workspace, size_t workspace_bytes, uint32_t* err_flags,
+                     int32_t path, void* stream) {
+  moe_status s = check_pool(pool);
+  if (s != MOE_OK) return s;
+  s = check_shape(T, pool->H, E, k);
+  if (s != MOE_OK) return s;
+  if (path < MOE_PATH_AUTO || path > MOE_PATH_GROUPED)
+    return fail(MOE_ERR_INVALID_ARG, "path = %d", path);
+  if (T == 0) return ok();
+  CHECK_PTR(slot_map);
+  CHECK_PTR(w_router);
+  CHECK_PTR(x);
+  CHECK_PTR(out);
+  if (bias != nullptr && ((uintptr_t)bias & 3)) return fail(MOE_ERR_INVALID_ARG, "bias misaligned");
+  if (workspace == nullptr || ((uintptr_t)workspace & 255))
+    return fail(MOE_ERR_INVALID_ARG, "workspace is NULL or not 256-byte aligned");
+  if (err_flags != nullptr && ((uintptr_t)err_flags & 3))
+    return fail(MOE_ERR_INVALID_ARG, "err_flags misaligned");
+  moe_ws_layout L;
+  s = moe_layer_workspace(T, pool->H, pool->I, E, k, &L);
+  if (s != MOE_OK) return s;
+  if (workspace_bytes < L.total)
+    return fail(MOE_ERR_INVALID_ARG, "workspace %zu bytes < %zu needed", workspace_bytes, L.total);
+  char* ws = (char*)workspace;
+  int32_t* ids = (int32_t*)(ws + L.topk_ids);
+  float* w = (float*)(ws + L.topk_w);
+  int32_t* counts = (int32_t*)(ws + L.counts);
+  int32_t* offsets = (int32_t*)(ws + L.offsets);
+  int32_t* perm = (int32_t*)(ws + L.perm);
+  int32_t* inv_perm = (int32_t*)(ws + L.inv_perm);
+  uint16_t* h = (uint16_t*)(ws + L.h);
+  float* y = (float*)(ws + L.y);
+  void* scratch = ws + L.scratch;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = moe::launch_route(x, w_router, bias, T, pool->H, E, k, ids, w, (float*)scratch, st);
+  if (e != hipSuccess) return hip_status(e, "route");
+  e = moe::launch_bucket(ids, T * k, E, counts, offsets, perm, inv_perm, scratch, st);
+  if (e != hipSuccess) return hip_status(e, "bucket");
+  s = ffn_dispatch(pool, slot_map, E, x, T, k, offsets, perm, h, y, err_flags, path, st);
+  if (s != MOE_OK) return s;
+  return hip_status(moe::launch_combine(y, inv_perm, w, T, k, pool->H, out, st), "combine");
+}
+
+}  // extern "C"

@@ -1,0 +1,40 @@
+// Weighted merge of each token's k expert outputs: the "merges the weighted outputs" step
+// of the llama.cpp discussion's original post.
+//   out[t, :] = sum_{j<k} w[t, j] * y[inv_perm[t*k + j], :]   (fp32, increasing j)
+// Pure streaming: each thread owns 4 consecutive columns of one token and reads the k
+// source rows with 16-byte loads.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+namespace {
+
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
+                                                 const int32_t* __restrict__ inv_perm,
+                                                 const float* __restrict__ w, int T, int k,
+                                                 int H, float* __restrict__ out) {
+  const int t = blockIdx.y;
+  const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (c >= H) return;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < k; ++j) {
+    const float wj = w[(int64_t)t * k + j];
+    const int pos = inv_perm[(int64_t)t * k + j];
+    const f32x4 v = *(const f32x4*)(y + (int64_t)pos * H + c);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = fmaf(wj, v[q], acc[q]);
+  }
+  *(f32x4*)(out + (int64_t)t * H + c) = acc;
+}
+
+}  // namespace
+
+hipError_t launch_combine(const float* y, const int32_t* inv_perm, const float* w, int T, int k,
+                          int H, float* out, hipStream_t stream) {
+  dim3 grid((H / 4 + 255) / 256, T);
+  hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, stream, y, inv_perm, w, T, k, H, out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,116 @@
+// Device helpers shared by the layer's kernels (gfx950 / CDNA4, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
+
+constexpr int kWave = 64;
+constexpr int kBlock = 32;      // elements per quantization block (MXFP4 and Q8_0)
+constexpr int kRowGroup = 16;   // rows interleaved per tile in the pool layout
+constexpr int kMaxK = 8;        // largest supported top-k
+constexpr int kMaxE = 256;      // largest supported expert count
+
+enum Fmt : int { kMXFP4 = 1, kQ8_0 = 2 };
+
+// ---------------------------------------------------------------- scalar conversions
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float(uint32_t(v) << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+// fp16 bits -> fp32 (exact).
+__device__ __forceinline__ float fp16_to_f32(uint16_t v) {
+  return (float)__builtin_bit_cast(_Float16, v);
+}
+
+// E8M0 scale byte -> fp32 2^(b-127), exact for b in [1, 254].
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b) { return __uint_as_float(b << 23); }
+
+// Two E2M1 codes in byte `sel` of `src` -> two bf16 values times `scale` (a power of two):
+// element 0 from the low nibble, element 1 from the high nibble. One gfx950 instruction.
+template <int sel>
+__device__ __forceinline__ bf16x2 fp4x2_to_bf16x2(uint32_t src, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, scale, sel);
+}
+
+// 8 E2M1 codes (one dword, element 0 in the low nibble of byte 0) -> 8 bf16, scaled.
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t v, float scale) {
+  bf16x2 a = fp4x2_to_bf16x2<0>(v, scale);
+  bf16x2 b = fp4x2_to_bf16x2<1>(v, scale);
+  bf16x2 c = fp4x2_to_bf16x2<2>(v, scale);
+  bf16x2 d = fp4x2_to_bf16x2<3>(v, scale);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// 4 int8 codes (one dword) -> 4 fp32 (exact).
+__device__ __forceinline__ void i8x4_to_f32(uint32_t v, float* o) {
+  o[0] = float(int32_t(v << 24) >> 24);
+  o[1] = float(int32_t(v << 16) >> 24);
+  o[2] = float(int32_t(v << 8) >> 24);
+  o[3] = float(int32_t(v) >> 24);
+}
+
+// 2 fp32 holding bf16-exact values -> packed bf16x2 (truncation is exact here).
+__device__ __forceinline__ uint32_t pack_bf16x2_exact(float lo, float hi) {
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+}
+
+// 8 int8 codes (two dwords) -> 8 bf16 (exact: |q| <= 128 has at most 8 significant bits).
+__device__ __forceinline__ bf16x8 i8x8_to_bf16x8(uint32_t v0, uint32_t v1) {
+  float f[8];
+  i8x4_to_f32(v0, f);
+  i8x4_to_f32(v1, f + 4);
+  u32x4 p = {pack_bf16x2_exact(f[0], f[1]), pack_bf16x2_exact(f[2], f[3]),
+             pack_bf16x2_exact(f[4], f[5]), pack_bf16x2_exact(f[6], f[7])};
+  return __builtin_bit_cast(bf16x8, p);
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), acc, false);
+}
+__device__ __forceinline__ float dot2_bf16(bf16x2 a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(a, __builtin_bit_cast(bf16x2, b), acc, false);
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g / (1.0f + __expf(-g)) * u;
+}
+
+// ------------------------------------------------------------------ wave reductions
+
+__device__ __forceinline__ float wave_xor(float v, int mask) { return __shfl_xor(v, mask, kWave); }
+
+// ------------------------------------------------------------------ pool layout
+
+// Index of the 16-byte (MXFP4) / 32-byte (Q8_0) unit of row r, block b, in a matrix
+// with nb blocks per row (see the tiled layout in include/moe.h).
+__device__ __forceinline__ int64_t pool_unit(int r, int b, int nb) {
+  return (int64_t(r >> 4) * nb + b) * kRowGroup + (r & 15);
+}
+
+__host__ __device__ constexpr int64_t code_bytes_per_block(int fmt) { return fmt == kMXFP4 ? 16 : 32; }
+__host__ __device__ constexpr int64_t scale_bytes_per_block(int fmt) { return fmt == kMXFP4 ? 1 : 2; }
+
+struct PoolView {
+  const uint8_t* q;   // code plane, slot 0
+  const uint8_t* s;   // scale plane, slot 0
+  int64_t q_slot;     // bytes per slot in the code plane
+  int64_t s_slot;     // bytes per slot in the scale plane
+};
+
+}  // namespace moe

@@ -1,0 +1,44 @@
+// Host-side launchers of the layer's kernels (internal to the library; the public
+// interface is include/moe.h). Every launcher only enqueues on `stream`.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace moe {
+
+int route_ksplit(int T, int H);
+hipError_t launch_route(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H,
+                        int E, int k, int32_t* ids, float* w, float* partial,
+                        hipStream_t stream);
+
+size_t bucket_scratch_bytes(int n, int E);
+hipError_t launch_bucket(const int32_t* ids, int n, int E, int32_t* counts, int32_t* offsets,
+                         int32_t* perm, int32_t* inv_perm, void* scratch, hipStream_t stream);
+
+hipError_t launch_gate_up_gemv(int fmt, const PoolView& gate, const PoolView& up,
+                               const int32_t* slot_map, int n_slots, int E, const uint16_t* x,
+                               int T, int k, int H, int I, const int32_t* offsets,
+                               const int32_t* perm, uint16_t* h, uint32_t* err,
+                               hipStream_t stream);
+hipError_t launch_down_gemv(int fmt, const PoolView& down, const int32_t* slot_map, int n_slots,
+                            int E, int T, int k, int H, int I, const int32_t* offsets,
+                            const uint16_t* h, float* y, uint32_t* err, hipStream_t stream);
+hipError_t launch_gate_up_grouped(int fmt, const PoolView& gate, const PoolView& up,
+                                  const int32_t* slot_map, int n_slots, int E, const uint16_t* x,
+                                  int T, int k, int H, int I, const int32_t* offsets,
+                                  const int32_t* perm, uint16_t* h, uint32_t* err,
+                                  hipStream_t stream);
+hipError_t launch_down_grouped(int fmt, const PoolView& down, const int32_t* slot_map,
+                               int n_slots, int E, int T, int k, int H, int I,
+                               const int32_t* offsets, const uint16_t* h, float* y,
+                               uint32_t* err, hipStream_t stream);
+
+hipError_t launch_combine(const float* y, const int32_t* inv_perm, const float* w, int T, int k,
+                          int H, float* out, hipStream_t stream);
+
+hipError_t launch_pack(int fmt, int n_mats, int rows, int K, const void* sq, const void* ss,
+                       void* dq, void* ds, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,52 @@
+// Canonical row-major block planes -> the pool's tiled layout (16 rows interleaved block
+// by block). This is the per-slot "mapping" a loader runs when an expert lands in the
+// resident pool (tinyserve README, "How it works" item 3; llama.cpp discussion, "Formal
+// gate results": mapping rewrite before the grouped matmul). Pure data movement.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+namespace {
+
+template <int FMT>
+__global__ __launch_bounds__(256) void k_pack(int64_t n_units, int rows, int nb,
+                                              const uint8_t* __restrict__ sq,
+                                              const uint8_t* __restrict__ ss,
+                                              uint8_t* __restrict__ dq, uint8_t* __restrict__ ds) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // canonical (mat, row, block)
+  if (i >= n_units) return;
+  const int64_t per_mat = (int64_t)rows * nb;
+  const int64_t mat = i / per_mat;
+  const int64_t rem = i % per_mat;
+  const int r = (int)(rem / nb), b = (int)(rem % nb);
+  const int64_t u = mat * per_mat + pool_unit(r, b, nb);
+  if constexpr (FMT == kMXFP4) {
+    *(u32x4*)(dq + u * 16) = *(const u32x4*)(sq + i * 16);
+    ds[u] = ss[i];
+  } else {
+    *(u32x4*)(dq + u * 32) = *(const u32x4*)(sq + i * 32);
+    *(u32x4*)(dq + u * 32 + 16) = *(const u32x4*)(sq + i * 32 + 16);
+    ((uint16_t*)ds)[u] = ((const uint16_t*)ss)[i];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pack(int fmt, int n_mats, int rows, int K, const void* sq, const void* ss,
+                       void* dq, void* ds, hipStream_t stream) {
+  const int nb = K / 32;
+  const int64_t n = (int64_t)n_mats * rows * nb;
+  const int64_t blocks = (n + 255) / 256;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (fmt == kMXFP4)
+    hipLaunchKernelGGL(k_pack<kMXFP4>, dim3((unsigned)blocks), dim3(256), 0, stream, n, rows, nb,
+                       (const uint8_t*)sq, (const uint8_t*)ss, (uint8_t*)dq, (uint8_t*)ds);
+  else
+    hipLaunchKernelGGL(k_pack<kQ8_0>, dim3((unsigned)blocks), dim3(256), 0, stream, n, rows, nb,
+                       (const uint8_t*)sq, (const uint8_t*)ss, (uint8_t*)dq, (uint8_t*)ds);
+  return hipGetLastError();
+}
+
+}  // namespace moe

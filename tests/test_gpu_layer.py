@@ -1,0 +1,189 @@
+"""GPU parity of the fused layer (moe_layer) against the CPU oracle, through the C ABI.
+
+Small workloads are checked on every token; the full-size prefill workloads are checked
+bit-exactly on routing and bucketing for every token, and numerically on a stratified
+sample (every token of experts with < 16 tokens, tile-boundary rows, 512 seeded tokens),
+in the launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import codecs, moe as omoe
+
+from parity import (W_ABS, _ulp_bf16, assert_close_rows, check_h, h_bits, h_slack, make_case,
+                    to_device)
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+import quantized_routed_expert_gemv_amd as qm  # noqa: E402
+
+
+def _sample_tokens(ids, E, n_uniform=512, seed=0):
+    T, k = ids.shape
+    counts = np.bincount(ids.ravel(), minlength=E)
+    rng = np.random.default_rng(seed)
+    toks = set(rng.choice(T, size=min(n_uniform, T), replace=False).tolist())
+    small = np.nonzero((counts > 0) & (counts < 16))[0]
+    for e in range(E):
+        ts = np.nonzero((ids == e).any(axis=1))[0]
+        if ts.size == 0:
+            continue
+        if e in small:
+            toks.update(ts.tolist())
+        else:
+            toks.update([int(ts[0]), int(ts[-1])])
+    return np.array(sorted(toks), dtype=np.int64)
+
+
+def run_layer(cfg, path=qm.PATH_AUTO, layer=0, sample=False):
+    L = make_case(cfg, layer)
+    k, E, T = cfg.k, cfg.E, cfg.T
+    pool, x, wr, bias, sm = to_device(L)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out, ws = qm.layer(pool, sm, wr, bias, x, k, err_flags=err, path=path)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    got = {n: t.cpu() for n, t in ws.intermediates().items()}
+    out = out.cpu().numpy()
+
+    ids, w, _ = omoe.route(L.x, L.wr, L.bias, k)
+    counts, offsets, perm, inv = omoe.bucket(ids, E)
+    assert np.array_equal(got["ids"].numpy(), ids)
+    assert np.abs(got["w"].numpy() - w).max() <= W_ABS
+    for n, ref in (("counts", counts), ("offsets", offsets), ("perm", perm), ("inv_perm", inv)):
+        assert np.array_equal(got[n].numpy(), ref), n
+
+    toks = _sample_tokens(ids, E) if sample else np.arange(T)
+    positions = np.sort(inv.reshape(T, k)[toks].ravel())
+    hb = got["h"].view(torch.int16).numpy().view(np.uint16)
+    _, _, a_ref = omoe.expert_ffn(L.planes, cfg.fmt, L.slot_map, L.x, k, offsets, perm, positions)
+    a = a_ref[positions]
+    off = np.abs(codecs.bf16_decode(hb[positions]) - a) >= _ulp_bf16(a)
+    slack = np.zeros_like(a)
+    rows = np.nonzero(off.any(axis=1))[0]
+    if rows.size:
+        slack[rows] = h_slack(L.planes, cfg.fmt, L.slot_map, L.x, k, offsets, perm,
+                              positions[rows], a_ref)
+    frac = check_h(hb[positions], a, slack)
+    y_gh = omoe.down_proj(L.planes, cfg.fmt, L.slot_map, hb, offsets, positions)
+    ry, ey = assert_close_rows(got["y"].numpy()[positions], y_gh[positions], "y")
+    out_ref = omoe.combine(y_gh, inv, w, T, k, tokens=toks)
+    ro, eo = assert_close_rows(out[toks], out_ref[toks], "out")
+    # end to end against the pure oracle (its own h) -- reported, judged on the L2 bound
+    y_pure = omoe.down_proj(L.planes, cfg.fmt, L.slot_map,
+                            codecs.bf16_bits(codecs.bf16_round(a_ref)), offsets, positions)
+    out_pure = omoe.combine(y_pure, inv, w, T, k, tokens=toks)
+    from parity import rel_l2_rows
+    rp = rel_l2_rows(out[toks], out_pure[toks]).max()
+    print(f"  {cfg.name} T={T}: h mismatch {frac:.2e}; y L2 {ry:.2e} elem {ey:.2e}; "
+          f"out L2 {ro:.2e} elem {eo:.2e}; vs pure oracle L2 {rp:.2e}", flush=True)
+    assert rp <= 2e-3
+    return L, out, got
+
+
+SMALL = [("tiny", qm.PATH_AUTO), ("tiny", qm.PATH_GEMV), ("gptoss_decode_t1", qm.PATH_AUTO),
+         ("gptoss_decode_t4", qm.PATH_AUTO), ("gptoss_decode_t4", qm.PATH_GROUPED),
+         ("mixtral_q8_decode", qm.PATH_AUTO), ("qwen_a3b_decode", qm.PATH_AUTO)]
+
+
+@pytest.mark.parametrize("name,path", SMALL)
+def test_layer_parity_small(name, path):
+    print(f"layer {name} path={path}", flush=True)
+    run_layer(synth.CONFIGS[name], path)
+
+
+def test_layer_parity_decode_last_of_24_layers():
+    print("layer gptoss_decode_t1 layer 23", flush=True)
+    run_layer(synth.CONFIGS["gptoss_decode_t1"], layer=23)
+
+
+@pytest.mark.parametrize("name", ["gptoss_prefill", "qwen_a3b_prefill", "mixtral_q8_prefill"])
+def test_layer_parity_full_size_prefill(name):
+    print(f"layer {name} (full size, sampled)", flush=True)
+    run_layer(synth.CONFIGS[name], sample=True)
+
+
+@pytest.mark.parametrize("T", [2, 17, 130, 257])
+def test_layer_ragged_tails(T):
+    print(f"layer tiny T={T}", flush=True)
+    run_layer(synth.config("tiny", T=T))
+
+
+def test_layer_dense_and_full_mixture_special_cases():
+    for cfg in (synth.Config("dense1", 40, 256, 512, 1, 1, "mxfp4", None, "identity", 21, 1),
+                synth.Config("allk", 24, 256, 512, 8, 8, "q8_0", 1.1, "perm", 22, 1),
+                synth.Config("q8tiny", 70, 256, 512, 8, 2, "q8_0", None, "perm", 23, 1)):
+        print(f"layer {cfg.name}", flush=True)
+        run_layer(cfg)
+
+
+def test_layer_empty_input_is_a_no_op():
+    cfg = synth.config("tiny", T=0)
+    L = synth.make_layer(cfg)
+    pool, x, wr, bias, sm = to_device(L)
+    out, _ = qm.layer(pool, sm, wr, None, x, cfg.k)
+    torch.cuda.synchronize()
+    assert out.shape == (0, cfg.H)
+
+
+def test_slot_map_permutation_invariance_bit_exact():
+    cfg = synth.CONFIGS["qwen_a3b_decode"]
+    cfg = synth.config("qwen_a3b_decode", T=8)
+    L = make_case(cfg)
+    pool, x, wr, bias, sm = to_device(L)
+    rng = np.random.default_rng(7)
+    sigma = rng.permutation(cfg.E)
+    planes2 = {}
+    for n, a in L.planes.items():
+        b = np.empty_like(a)
+        b[sigma] = a
+        planes2[n] = b
+    pool2 = qm.Pool.from_canonical(cfg.fmt, cfg.H, cfg.I, planes2)
+    sm2 = torch.from_numpy(sigma[L.slot_map].astype(np.int32)).cuda()
+    for path in (qm.PATH_GEMV, qm.PATH_GROUPED):
+        o1, _ = qm.layer(pool, sm, wr, bias, x, cfg.k, path=path)
+        o2, _ = qm.layer(pool2, sm2, wr, bias, x, cfg.k, path=path)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("name", ["gptoss_decode_t4", "tiny"])
+def test_layer_repeat_runs_are_bit_identical(name):
+    cfg = synth.CONFIGS[name]
+    L = make_case(cfg)
+    pool, x, wr, bias, sm = to_device(L)
+    ref, ws = qm.layer(pool, sm, wr, bias, x, cfg.k)
+    ref = ref.clone()
+    for _ in range(3):
+        o, _ = qm.layer(pool, sm, wr, bias, x, cfg.k, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref)
+
+
+def test_layer_in_a_hip_graph_matches_eager():
+    cfg = synth.CONFIGS["gptoss_decode_t1"]
+    L = make_case(cfg)
+    pool, x, wr, bias, sm = to_device(L)
+    ws = qm.Workspace(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k)
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device="cuda")
+    eager, _ = qm.layer(pool, sm, wr, bias, x, cfg.k, workspace=ws)
+    eager = eager.clone()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        qm.layer(pool, sm, wr, bias, x, cfg.k, out=out, workspace=ws, stream=s)   # warm up
+        s.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            qm.layer(pool, sm, wr, bias, x, cfg.k, out=out, workspace=ws, stream=s)
+    for i in range(4):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i}"
+        # eager work between replays
+        o2, _ = qm.layer(pool, sm, wr, bias, x, cfg.k)
+        torch.cuda.synchronize()
+        assert torch.equal(o2, eager)
