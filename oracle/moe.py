@@ -109,14 +109,12 @@ def _slot_weights(planes, fmt, slot, name):
 
 
 def expert_ffn(planes: dict, fmt: str, slot_map, x_bits, k: int, offsets, perm,
-               positions=None, h_override=None):
+               positions=None):
     """Gate/up/SwiGLU/down for the bucketed pairs.
 
     planes: the pool in canonical layout, indexed by slot (see synth).
     positions: bucket positions to compute (default: all). Results for other positions
-    are left as NaN so a partial evaluation cannot be mistaken for a full one.
-    h_override: bf16 bits [T*k, I]; when given, y is computed from these h rows instead
-    of the oracle's own (used to judge a down projection at another party's h).
+    are left as NaN (h as 0) so a partial evaluation cannot be mistaken for a full one.
     Returns (h_bits uint16 [T*k, I], y fp64 [T*k, H], a fp64 [T*k, I]) where a is the
     pre-rounding silu(g)*u.
     """
@@ -125,33 +123,54 @@ def expert_ffn(planes: dict, fmt: str, slot_map, x_bits, k: int, offsets, perm,
     n = perm.size
     E = offsets.size - 1
     I = planes["gate_q"].shape[1]
-    H = planes["down_q"].shape[1]
-    want = np.zeros(n, dtype=bool)
-    want[np.arange(n) if positions is None else np.asarray(positions, dtype=np.int64)] = True
+    want = _wanted(n, positions)
     x_all = codecs.bf16_decode(x_bits)
     h_bits = np.zeros((n, I), dtype=np.uint16)
     a = np.full((n, I), np.nan)
-    y = np.full((n, H), np.nan)
     for e in range(E):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         pos = np.arange(lo, hi)[want[lo:hi]]
         if pos.size == 0:
             continue
         slot = int(slot_map[e])
-        toks = perm[pos] // k
-        xe = x_all[toks]                                    # [n_e, H]
+        xe = x_all[perm[pos] // k]                          # [n_e, H]
         Wg = _slot_weights(planes, fmt, slot, "gate")       # [I, H]
-        Wu = _slot_weights(planes, fmt, slot, "up")
         g = xe @ Wg.T
+        del Wg
+        Wu = _slot_weights(planes, fmt, slot, "up")
         u = xe @ Wu.T
-        del Wg, Wu
+        del Wu
         a[pos] = silu(g) * u
         h_bits[pos] = codecs.bf16_bits(codecs.bf16_round(a[pos]))
-        hb = h_bits[pos] if h_override is None else np.asarray(h_override)[pos]
-        Wd = _slot_weights(planes, fmt, slot, "down")       # [H, I]
-        y[pos] = codecs.bf16_decode(hb) @ Wd.T
-        del Wd
+    y = down_proj(planes, fmt, slot_map, h_bits, offsets, positions)
     return h_bits, y, a
+
+
+def down_proj(planes: dict, fmt: str, slot_map, h_bits, offsets, positions=None):
+    """y[pos] = W_down[slot_map[e]] h[pos] in fp64 for the bucketed rows of h (bf16 bits).
+
+    Used on the oracle's own h, and to judge a down projection at another party's h.
+    """
+    offsets = np.asarray(offsets, dtype=np.int64)
+    n = int(offsets[-1])
+    E = offsets.size - 1
+    H = planes["down_q"].shape[1]
+    want = _wanted(n, positions)
+    y = np.full((n, H), np.nan)
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        pos = np.arange(lo, hi)[want[lo:hi]]
+        if pos.size == 0:
+            continue
+        Wd = _slot_weights(planes, fmt, int(slot_map[e]), "down")   # [H, I]
+        y[pos] = codecs.bf16_decode(np.asarray(h_bits)[pos]) @ Wd.T
+    return y
+
+
+def _wanted(n, positions):
+    want = np.zeros(n, dtype=bool)
+    want[np.arange(n) if positions is None else np.asarray(positions, dtype=np.int64)] = True
+    return want
 
 
 # ---------------------------------------------------------------------------- combine
