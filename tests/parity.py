@@ -42,7 +42,9 @@ def margin_fixed_x(cfg: synth.Config, layer: int = 0, T: int | None = None,
 
     def bad_rows(xx):
         L = omoe.router_logits(xx, wr, bias)
-        s = -np.sort(-L, axis=1)[:, :cfg.k + 1]
+        s = -np.sort(-L, axis=1)[:, :min(cfg.k + 1, cfg.E)]
+        if s.shape[1] < 2:                   # E = 1: nothing to order
+            return np.zeros(0, dtype=np.int64)
         gaps = s[:, :-1] - s[:, 1:]
         return np.nonzero(gaps.min(axis=1) <= MARGIN)[0]
 
@@ -183,3 +185,22 @@ def sample_positions(offsets, n_uniform=512, seed=0, tile=128):
     if n:
         pos.update(rng.choice(n, size=min(n_uniform, n), replace=False).tolist())
     return np.array(sorted(pos), dtype=np.int64)
+
+
+def sample_tokens(ids, E, n_uniform=512, seed=0):
+    """Tokens to check at large sizes: all tokens of experts with < 16 tokens, the first
+    and last token of every other expert, plus a seeded uniform sample."""
+    T, k = ids.shape
+    counts = np.bincount(ids.ravel(), minlength=E)
+    rng = np.random.default_rng(seed)
+    toks = set(rng.choice(T, size=min(n_uniform, T), replace=False).tolist())
+    small = np.nonzero((counts > 0) & (counts < 16))[0]
+    for e in range(E):
+        ts = np.nonzero((ids == e).any(axis=1))[0]
+        if ts.size == 0:
+            continue
+        if e in small:
+            toks.update(ts.tolist())
+        else:
+            toks.update([int(ts[0]), int(ts[-1])])
+    return np.array(sorted(toks), dtype=np.int64)

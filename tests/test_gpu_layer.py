@@ -11,31 +11,14 @@ import pytest
 import synth
 from oracle import codecs, moe as omoe
 
-from parity import (W_ABS, _ulp_bf16, assert_close_rows, check_h, h_bits, h_slack, make_case,
-                    to_device)
+from parity import (W_ABS, _ulp_bf16, assert_close_rows, check_h, h_slack, make_case,
+                    rel_l2_rows, sample_tokens, to_device)
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 if not torch.cuda.is_available():
     pytest.skip("needs a GPU", allow_module_level=True)
 import quantized_routed_expert_gemv_amd as qm  # noqa: E402
-
-
-def _sample_tokens(ids, E, n_uniform=512, seed=0):
-    T, k = ids.shape
-    counts = np.bincount(ids.ravel(), minlength=E)
-    rng = np.random.default_rng(seed)
-    toks = set(rng.choice(T, size=min(n_uniform, T), replace=False).tolist())
-    small = np.nonzero((counts > 0) & (counts < 16))[0]
-    for e in range(E):
-        ts = np.nonzero((ids == e).any(axis=1))[0]
-        if ts.size == 0:
-            continue
-        if e in small:
-            toks.update(ts.tolist())
-        else:
-            toks.update([int(ts[0]), int(ts[-1])])
-    return np.array(sorted(toks), dtype=np.int64)
 
 
 def run_layer(cfg, path=qm.PATH_AUTO, layer=0, sample=False):
@@ -56,7 +39,7 @@ def run_layer(cfg, path=qm.PATH_AUTO, layer=0, sample=False):
     for n, ref in (("counts", counts), ("offsets", offsets), ("perm", perm), ("inv_perm", inv)):
         assert np.array_equal(got[n].numpy(), ref), n
 
-    toks = _sample_tokens(ids, E) if sample else np.arange(T)
+    toks = sample_tokens(ids, E) if sample else np.arange(T)
     positions = np.sort(inv.reshape(T, k)[toks].ravel())
     hb = got["h"].view(torch.int16).numpy().view(np.uint16)
     _, _, a_ref = omoe.expert_ffn(L.planes, cfg.fmt, L.slot_map, L.x, k, offsets, perm, positions)
@@ -76,7 +59,6 @@ def run_layer(cfg, path=qm.PATH_AUTO, layer=0, sample=False):
     y_pure = omoe.down_proj(L.planes, cfg.fmt, L.slot_map,
                             codecs.bf16_bits(codecs.bf16_round(a_ref)), offsets, positions)
     out_pure = omoe.combine(y_pure, inv, w, T, k, tokens=toks)
-    from parity import rel_l2_rows
     rp = rel_l2_rows(out[toks], out_pure[toks]).max()
     print(f"  {cfg.name} T={T}: h mismatch {frac:.2e}; y L2 {ry:.2e} elem {ey:.2e}; "
           f"out L2 {ro:.2e} elem {eo:.2e}; vs pure oracle L2 {rp:.2e}", flush=True)
