@@ -35,7 +35,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gptoss_decode_t1")
     ap.add_argument("--layers", type=int, default=None, help="override the workload's layer count")
-    ap.add_argument("--mode", choices=("graph", "eager"), default="graph")
+    ap.add_argument("--mode", choices=("graph", "eager"), default="graph",
+                    help="graph: the step's layer calls are captured once into a HIP graph "
+                         "and replayed; eager: every layer call is launched from the host")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the CPU-oracle baseline sample (0 disables it)")
     return ap.parse_args()
@@ -82,78 +84,69 @@ def main():
 
     T, k, E, H, I = cfg.T, cfg.k, cfg.E, cfg.H, cfg.I
     ws = qm.Workspace(T, H, I, E, k, dev)
-    im = ws.intermediates()
-    scratch = ws.scratch()
     outs = [torch.empty((T, H), dtype=torch.float32, device=dev) for _ in range(n_layers)]
     stream = torch.cuda.Stream(device=dev)
     prefill = T > 16
+    # timing events around each layer's gate/up launch (recorded by moe_layer_timed on the
+    # stream the kernel runs on); created without the system-scope fence that a default
+    # event adds on record, which would flush caches between the layer's kernels
+    hip = HipEvents()
+    ev = [(hip.create(), hip.create()) for _ in range(n_layers)]
+    timed_calls = [qm.LayerCall(pool, sm, wr, bias, x, k, outs[li], ws, stream=stream,
+                                events=ev[li])
+                   for li, (pool, x, wr, bias, sm) in enumerate(layers)]
+    plain_calls = [qm.LayerCall(pool, sm, wr, bias, x, k, outs[li], ws, stream=stream)
+                   for li, (pool, x, wr, bias, sm) in enumerate(layers)]
 
-    def step(ev=None):
-        for li, (pool, x, wr, bias, sm) in enumerate(layers):
-            qm.route(x, wr, bias, k, ids=im["ids"], w=im["w"], scratch=scratch, stream=stream)
-            qm.bucket(im["ids"], E, im["counts"], im["offsets"], im["perm"], im["inv_perm"],
-                      scratch=scratch, stream=stream)
-            if ev is not None:
-                ev[li][0].record(stream)
-            qm.expert_gate_up(pool, sm, x, k, im["offsets"], im["perm"], h=im["h"], stream=stream)
-            if ev is not None:
-                ev[li][1].record(stream)
-            qm.expert_down(pool, sm, T, k, im["offsets"], im["h"], y=im["y"], stream=stream)
-            qm.combine(im["y"], im["inv_perm"], im["w"], out=outs[li], stream=stream)
+    def run(calls):
+        for c in calls:
+            c()
 
-    def make_events(external):
-        return [(torch.cuda.Event(enable_timing=True, external=external),
-                 torch.cuda.Event(enable_timing=True, external=external))
-                for _ in range(n_layers)]
+    def eager_pass(steps):
+        """`steps` steps launched from the host, gate/up events read after each step."""
+        ms = []
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            run(timed_calls)
+            stream.synchronize()
+            ms.extend(hip.elapsed_ms(a, b) for a, b in ev)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, ms
 
     mode = args.mode
-    graph = None
-    ev = None
-    with torch.cuda.stream(stream):
-        step()                          # first call: kernels load, caches warm
-        stream.synchronize()
-        if mode == "graph":
-            try:
-                ev = make_events(True)
-                graph = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(graph, stream=stream):
-                    step(ev)
-                graph.replay()
-                stream.synchronize()
-                ev[0][0].elapsed_time(ev[0][1])
-            except Exception as exc:     # graph capture of timing events not available
-                print(f"[bench] graph mode unavailable ({exc}); timing eagerly", file=sys.stderr)
-                mode, graph = "eager", None
-        if mode == "eager":
-            ev = make_events(False)
+    run(plain_calls)                       # load the kernels (and warm caches) once
+    stream.synchronize()
+    graph = hip.capture(stream.cuda_stream, lambda: run(plain_calls)) if mode == "graph" else None
+    for _ in range(args.warmup):
+        if graph is not None:
+            hip.launch(graph, stream.cuda_stream)
+        else:
+            run(timed_calls)
+    stream.synchronize()
+    torch.cuda.synchronize()
 
-        def run_step():
-            if graph is not None:
-                graph.replay()
-            else:
-                step(ev)
-
-        for _ in range(args.warmup):
-            run_step()
-        stream.synchronize()
-        torch.cuda.synchronize()
-
-        # ---- timed region
-        kern_ms = []
+    # ---- timed region: K steps
+    if graph is not None:
+        # the step as it is meant to run: one graph of every layer's launches, replayed
         t0 = time.perf_counter()
         for _ in range(args.steps):
-            run_step()
-            stream.synchronize()
-            kern_ms.extend(a.elapsed_time(b) for a, b in ev)
+            hip.launch(graph, stream.cuda_stream)
+        stream.synchronize()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
+        # ROCm's runtime here refuses event nodes inside a captured graph, so the dominant
+        # kernel is timed on an eager pass of the same K steps right after
+        eager_s, kern_ms = eager_pass(args.steps)
+    else:
+        t0 = time.perf_counter()
+        eager_s, kern_ms = eager_pass(args.steps)
+        t1 = t0 + eager_s
 
     elapsed = t1 - t0
     ms_per_step = elapsed * 1e3 / args.steps
     value = T * n_layers * args.steps / elapsed
 
     # ---- roofline of the gate/up kernel
-    ids_last = im["ids"].cpu().numpy()
     kern_avg_s = float(np.mean(kern_ms)) * 1e-3
     if prefill:
         flops = 4.0 * T * k * H * I          # gate and up: 2 flops per weight per pair, twice
@@ -174,6 +167,8 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                 "kernel": "gate/up GEMV (k_gemv)", "work_per_launch": bytes_per_launch}
     roof["avg_launch_us"] = round(kern_avg_s * 1e6, 3)
+    roof["method"] = ("HIP events recorded on the kernel's stream around every gate/up launch "
+                      f"of {args.steps} eager steps ({len(kern_ms)} launches)")
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -181,14 +176,89 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": T, "H": H, "I": I, "E": E, "k": k, "fmt": cfg.fmt,
-                   "layers": n_layers, "mode": mode},
+                   "layers": n_layers,
+                   "launch": ("one HIP graph of the step's moe_layer calls" if mode == "graph"
+                              else "moe_layer per layer, eager")},
         "roofline": roof,
     }
+    if graph is not None:
+        result["eager_ms_per_step"] = round(eager_s * 1e3 / args.steps, 4)
 
     # ---- CPU baseline: the oracle on a bounded sample of the same workload
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(cfg, host_keep, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime that torch already loaded."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        # bind to the HIP runtime this process already uses (torch's and the library's):
+        # loading another copy by name would give events that runtime does not know
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    path = line.split()[-1]
+                    break
+        if path is None:
+            raise RuntimeError("no HIP runtime is loaded in this process")
+        self.lib = ctypes.CDLL(path)
+        self.lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.made = []
+
+    def create(self) -> int:
+        h = self.ct.c_void_p()
+        st = self.lib.hipEventCreateWithFlags(self.ct.byref(h), self.DISABLE_SYSTEM_FENCE)
+        if st != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({st})")
+        self.made.append(h.value)
+        return h.value
+
+    def capture(self, stream: int, fn):
+        """Capture fn()'s launches on `stream` into an instantiated HIP graph."""
+        ct, lib = self.ct, self.lib
+        lib.hipStreamBeginCapture.argtypes = [ct.c_void_p, ct.c_int]
+        lib.hipStreamEndCapture.argtypes = [ct.c_void_p, ct.POINTER(ct.c_void_p)]
+        lib.hipGraphInstantiate.argtypes = [ct.POINTER(ct.c_void_p), ct.c_void_p, ct.c_void_p,
+                                            ct.c_char_p, ct.c_size_t]
+        GLOBAL = 0
+        st = lib.hipStreamBeginCapture(ct.c_void_p(stream), GLOBAL)
+        if st != 0:
+            raise RuntimeError(f"hipStreamBeginCapture failed ({st})")
+        try:
+            fn()
+        finally:
+            g = ct.c_void_p()
+            st = lib.hipStreamEndCapture(ct.c_void_p(stream), ct.byref(g))
+        if st != 0:
+            raise RuntimeError(f"hipStreamEndCapture failed ({st})")
+        ge = ct.c_void_p()
+        st = lib.hipGraphInstantiate(ct.byref(ge), g, None, None, 0)
+        if st != 0:
+            raise RuntimeError(f"hipGraphInstantiate failed ({st})")
+        self.graphs = getattr(self, "graphs", []) + [(g, ge)]
+        return ge.value
+
+    def launch(self, graph_exec: int, stream: int):
+        self.lib.hipGraphLaunch.argtypes = [self.ct.c_void_p, self.ct.c_void_p]
+        st = self.lib.hipGraphLaunch(self.ct.c_void_p(graph_exec), self.ct.c_void_p(stream))
+        if st != 0:
+            raise RuntimeError(f"hipGraphLaunch failed ({st})")
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = self.ct.c_float()
+        st = self.lib.hipEventElapsedTime(self.ct.byref(ms), self.ct.c_void_p(a), self.ct.c_void_p(b))
+        if st != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({st})")
+        return ms.value
 
 
 def cpu_baseline(cfg, host_layers, budget_s):
@@ -204,8 +274,8 @@ def cpu_baseline(cfg, host_layers, budget_s):
     tokens = 0
     layers_done = 0
     sample_T = T
-    while time.perf_counter() - t0 < budget_s and layers_done < len(host_layers):
-        L = host_layers[layers_done]
+    while time.perf_counter() - t0 < budget_s and layers_done < 4 * len(host_layers):
+        L = host_layers[layers_done % len(host_layers)]
         x = L.x
         if T > 64:                           # prefill: a bounded token sample
             sample_T = 64
@@ -214,7 +284,7 @@ def cpu_baseline(cfg, host_layers, budget_s):
         tokens += x.shape[0]
         layers_done += 1
     dt = time.perf_counter() - t0
-    sample = (f"{layers_done} layer(s) x {sample_T} token(s) of {cfg.name}, whole layer "
+    sample = (f"{layers_done} layer call(s) x {sample_T} token(s) of {cfg.name}, whole layer "
               "(route, bucket, dequantize selected experts, FFN, combine) in fp64")
     return {"value": round(tokens / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": sample, "seconds": round(dt, 2)}

@@ -193,6 +193,7 @@ moe_status moe_combine(const float* y, const int32_t* inv_perm, const float* top
 typedef struct {
   size_t total;
   size_t topk_ids, topk_w, counts, offsets, perm, inv_perm, h, y, scratch;
+  size_t act;   /* int32 list of the active experts, written for small batches */
 } moe_ws_layout;
 
 moe_status moe_layer_workspace(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k,
@@ -201,14 +202,33 @@ moe_status moe_layer_workspace(int32_t T, int32_t H, int32_t I, int32_t E, int32
 /*
  * moe_layer -- route, bucket, expert FFN and combine for T tokens, enqueued on one stream.
  * out fp32 [T][H]. workspace: at least moe_layer_workspace(...).total bytes, 256-byte
- * aligned; its contents on entry do not matter. Results equal calling the four stages in
- * order with the same path.
+ * aligned; its contents on entry do not matter. Calls that share a workspace must not
+ * overlap in time. Small batches take shorter launch sequences: for T <= 16 and E <= 128
+ * one single-workgroup kernel routes, takes the top-k, bucket-sorts the pairs and lists
+ * the active experts; on the GEMV path with T*k <= 8 one kernel does the down projection
+ * and the combine (each workgroup owns 16 output columns across all active experts, so no
+ * atomics are involved). Results equal calling the stage entry points in order with the
+ * same path.
  */
 moe_status moe_layer(const moe_pool* pool, const int32_t* slot_map,
                      const uint16_t* w_router, const float* bias, const uint16_t* x,
                      int32_t T, int32_t E, int32_t k, float* out,
                      void* workspace, size_t workspace_bytes, uint32_t* err_flags,
                      int32_t path, void* stream);
+
+/*
+ * moe_layer_timed -- moe_layer, plus hipEventRecord of two caller-owned events (hipEvent_t,
+ * NULL to skip) on `stream` immediately before and after the gate/up launch, so a caller
+ * can time the layer's dominant kernel without a profiler. While `stream` is being captured
+ * into a HIP graph the records are made with hipEventRecordExternal, so they become event
+ * nodes of the graph and every replay re-records them. Same results as moe_layer.
+ */
+moe_status moe_layer_timed(const moe_pool* pool, const int32_t* slot_map,
+                           const uint16_t* w_router, const float* bias, const uint16_t* x,
+                           int32_t T, int32_t E, int32_t k, float* out,
+                           void* workspace, size_t workspace_bytes, uint32_t* err_flags,
+                           int32_t path, void* stream, void* ev_gate_up_begin,
+                           void* ev_gate_up_end);
 
 const char* moe_status_string(moe_status s);
 const char* moe_last_error(void);

@@ -49,7 +49,7 @@ class PoolStruct(ctypes.Structure):
 
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, _sz) for n in ("total", "topk_ids", "topk_w", "counts", "offsets", "perm",
-                                   "inv_perm", "h", "y", "scratch")]
+                                   "inv_perm", "h", "y", "scratch", "act")]
 
 
 def _sig(name, res, *args):
@@ -75,13 +75,16 @@ _combine = _sig("moe_combine", _i32, _p, _p, _p, _i32, _i32, _i32, _p, _p)
 _ws = _sig("moe_layer_workspace", _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(WsLayout))
 _layer = _sig("moe_layer", _i32, ctypes.POINTER(PoolStruct), _p, _p, _p, _p, _i32, _i32, _i32,
               _p, _p, _sz, _p, _i32, _p)
+_layer_timed = _sig("moe_layer_timed", _i32, ctypes.POINTER(PoolStruct), _p, _p, _p, _p, _i32,
+                    _i32, _i32, _p, _p, _sz, _p, _i32, _p, _p, _p)
 _status_string = _sig("moe_status_string", ctypes.c_char_p, _i32)
 _last_error = _sig("moe_last_error", ctypes.c_char_p)
 
 EXPORTED = ("moe_plane_bytes", "moe_pool_pack", "moe_route_scratch_bytes", "moe_route",
             "moe_bucket_scratch_bytes", "moe_bucket", "moe_expert_ffn", "moe_expert_gate_up",
             "moe_expert_down", "moe_combine",
-            "moe_layer_workspace", "moe_layer", "moe_status_string", "moe_last_error")
+            "moe_layer_workspace", "moe_layer", "moe_layer_timed", "moe_status_string",
+            "moe_last_error")
 
 
 def _check(status: int):
@@ -263,6 +266,21 @@ def combine(y, inv_perm, w, out=None, stream=None):
     return out
 
 
+def _event_handles(events):
+    """Raw hipEvent_t handles of a (begin, end) pair: ints (handles) or torch.cuda.Event.
+    torch creates its underlying event on first record, so such events are recorded once
+    (on the current stream) first."""
+    hs = []
+    for ev in events:
+        if isinstance(ev, int):
+            hs.append(ctypes.c_void_p(ev))
+            continue
+        if ev.cuda_event == 0:
+            ev.record()
+        hs.append(ctypes.c_void_p(ev.cuda_event))
+    return tuple(hs)
+
+
 def layer_workspace(T: int, H: int, I: int, E: int, k: int) -> WsLayout:
     L = WsLayout()
     _check(_ws(T, H, I, E, k, ctypes.byref(L)))
@@ -286,8 +304,8 @@ class Workspace:
         return self.buf[off:off + nbytes].view(dtype).view(shape)
 
     def scratch(self):
-        n = self.layout.total - self.layout.scratch
-        return self.buf[self.layout.scratch:self.layout.total] if n > 0 else None
+        n = self.layout.act - self.layout.scratch
+        return self.buf[self.layout.scratch:self.layout.act] if n > 0 else None
 
     def intermediates(self):
         T, k, E, H, I = self.T, self.k, self.E, self.H, self.I
@@ -302,8 +320,11 @@ class Workspace:
 
 
 def layer(pool: Pool, slot_map, w_router, bias, x, k: int, out=None, workspace=None,
-          err_flags=None, path=PATH_AUTO, stream=None):
-    """The fused layer: x bf16 [T, H] -> out fp32 [T, H]. Returns (out, workspace)."""
+          err_flags=None, path=PATH_AUTO, stream=None, events=None):
+    """The fused layer: x bf16 [T, H] -> out fp32 [T, H]. Returns (out, workspace).
+
+    events: optional (begin, end) pair of timing events recorded on the stream around the
+    gate/up launch (moe_layer_timed)."""
     T, H = x.shape
     E = w_router.shape[0]
     _need(x, torch.bfloat16, (T, pool.H), "x")
@@ -315,7 +336,43 @@ def layer(pool: Pool, slot_map, w_router, bias, x, k: int, out=None, workspace=N
         out = torch.empty((T, H), dtype=torch.float32, device=x.device)
     if workspace is None:
         workspace = Workspace(T, pool.H, pool.I, E, k, x.device)
-    _check(_layer(ctypes.byref(pool.struct), _ptr(slot_map), _ptr(w_router), _ptr(bias), _ptr(x),
-                  T, E, k, _ptr(out), _ptr(workspace.buf), workspace.buf.numel(), _ptr(err_flags),
-                  path, _stream(stream)))
+    args = (ctypes.byref(pool.struct), _ptr(slot_map), _ptr(w_router), _ptr(bias), _ptr(x),
+            T, E, k, _ptr(out), _ptr(workspace.buf), workspace.buf.numel(), _ptr(err_flags),
+            path, _stream(stream))
+    if events is None:
+        _check(_layer(*args))
+    else:   # (begin, end) torch.cuda.Event pair recorded around the gate/up launch
+        _check(_layer_timed(*args, *_event_handles(events)))
     return out, workspace
+
+
+class LayerCall:
+    """A moe_layer (or moe_layer_timed) call with its arguments marshalled once.
+
+    For loops that launch the same layer many times: calling the object enqueues the layer
+    on `stream` with no per-call argument conversion. The tensors must stay alive.
+    """
+
+    def __init__(self, pool: Pool, slot_map, w_router, bias, x, k: int, out, workspace,
+                 err_flags=None, path=PATH_AUTO, stream=None, events=None):
+        T = x.shape[0]
+        E = w_router.shape[0]
+        _need(x, torch.bfloat16, (T, pool.H), "x")
+        _need(w_router, torch.bfloat16, (E, pool.H), "w_router")
+        _need(slot_map, torch.int32, (E,), "slot_map")
+        _need(out, torch.float32, (T, pool.H), "out")
+        self._keep = (pool, slot_map, w_router, bias, x, out, workspace, err_flags, events)
+        args = (ctypes.byref(pool.struct), _ptr(slot_map), _ptr(w_router), _ptr(bias), _ptr(x),
+                T, E, k, _ptr(out), _ptr(workspace.buf), workspace.buf.numel(), _ptr(err_flags),
+                path, _stream(stream))
+        if events is None:
+            self._fn, self._args = _layer, args
+        else:
+            self._fn = _layer_timed
+            self._args = args + _event_handles(events)
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != 0:
+            _check(st)
+

@@ -33,6 +33,10 @@ moe_status hip_status(hipError_t e, const char* where) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Launch errors are read back with hipGetLastError; drop any error an earlier, unrelated
+// HIP call left behind so it is not reported as this call's failure.
+void clear_stale_error() { (void)hipGetLastError(); }
+
 #define CHECK_PTR(p)                                                                 \
   do {                                                                               \
     if ((p) == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s is NULL", #p);          \
@@ -81,6 +85,7 @@ void pool_views(const moe_pool* p, moe::PoolView* g, moe::PoolView* u, moe::Pool
 }
 
 size_t route_scratch(int32_t T, int32_t H, int32_t E) {
+  if (moe::route_small_ok(T, E)) return 0;   // one workgroup, no partials
   const int ks = moe::route_ksplit(T, H);
   return ks > 1 ? (size_t)ks * T * E * sizeof(float) : 0;
 }
@@ -94,12 +99,14 @@ bool use_gemv(int32_t path, int32_t T) {
 moe_status gate_up_dispatch(const moe_pool* pool, const int32_t* slot_map, int32_t E,
                             const uint16_t* x, int32_t T, int32_t k, const int32_t* offsets,
                             const int32_t* perm, uint16_t* h, uint32_t* err, int32_t path,
-                            hipStream_t stream) {
+                            hipStream_t stream, const int32_t* act = nullptr) {
+  clear_stale_error();
   moe::PoolView g, u, d;
   pool_views(pool, &g, &u, &d);
   if (use_gemv(path, T))
     return hip_status(moe::launch_gate_up_gemv(pool->fmt, g, u, slot_map, pool->n_slots, E, x, T,
-                                               k, pool->H, pool->I, offsets, perm, h, err, stream),
+                                               k, pool->H, pool->I, offsets, perm, h, err, act,
+                                               stream),
                       "gate/up (GEMV)");
   return hip_status(moe::launch_gate_up_grouped(pool->fmt, g, u, slot_map, pool->n_slots, E, x, T,
                                                 k, pool->H, pool->I, offsets, perm, h, err, stream),
@@ -109,6 +116,7 @@ moe_status gate_up_dispatch(const moe_pool* pool, const int32_t* slot_map, int32
 moe_status down_dispatch(const moe_pool* pool, const int32_t* slot_map, int32_t E, int32_t T,
                          int32_t k, const int32_t* offsets, const uint16_t* h, float* y,
                          uint32_t* err, int32_t path, hipStream_t stream) {
+  clear_stale_error();
   moe::PoolView g, u, d;
   pool_views(pool, &g, &u, &d);
   if (use_gemv(path, T))
@@ -181,6 +189,7 @@ moe_status moe_pool_pack(int32_t fmt, int32_t n_mats, int32_t rows, int32_t K,
   if (src_s == nullptr || dst_s == nullptr) return fail(MOE_ERR_INVALID_ARG, "scale plane is NULL");
   if (fmt == MOE_W_Q8_0 && (((uintptr_t)src_s | (uintptr_t)dst_s) & 1))
     return fail(MOE_ERR_INVALID_ARG, "fp16 scale plane is not 2-byte aligned");
+  clear_stale_error();
   return hip_status(moe::launch_pack(fmt, n_mats, rows, K, src_q, src_s, dst_q, dst_s,
                                      (hipStream_t)stream),
                     "pool pack");
@@ -208,6 +217,7 @@ moe_status moe_route(const uint16_t* x, const uint16_t* w_router, const float* b
     if (scratch_bytes < need)
       return fail(MOE_ERR_INVALID_ARG, "route scratch %zu bytes < %zu needed", scratch_bytes, need);
   }
+  clear_stale_error();
   return hip_status(moe::launch_route(x, w_router, bias, T, H, E, k, topk_ids, topk_w,
                                       (float*)scratch, (hipStream_t)stream),
                     "route");
@@ -225,6 +235,7 @@ moe_status moe_bucket(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, 
   if (s != MOE_OK) return s;
   CHECK_PTR(counts);
   CHECK_PTR(offsets);
+  clear_stale_error();
   if (T == 0)   // empty input: one small kernel still writes all-zero counts and offsets
     return hip_status(moe::launch_bucket(nullptr, 0, E, counts, offsets, nullptr, nullptr,
                                          nullptr, (hipStream_t)stream),
@@ -290,6 +301,7 @@ moe_status moe_combine(const float* y, const int32_t* inv_perm, const float* top
   CHECK_PTR(inv_perm);
   CHECK_PTR(topk_w);
   CHECK_PTR(out);
+  clear_stale_error();
   return hip_status(moe::launch_combine(y, inv_perm, topk_w, T, k, H, out, (hipStream_t)stream),
                     "combine");
 }
@@ -318,14 +330,28 @@ moe_status moe_layer_workspace(int32_t T, int32_t H, int32_t I, int32_t E, int32
   const size_t rs = T > 0 ? route_scratch(T, H, E) : 0;
   const size_t bs = T > 0 ? moe::bucket_scratch_bytes((int)n, E) : 0;
   out->scratch = take(rs > bs ? rs : bs);
+  out->act = take((size_t)moe::act_ints(E) * sizeof(int32_t));
   out->total = off;
   return ok();
 }
 
-moe_status moe_layer(const moe_pool* pool, const int32_t* slot_map, const uint16_t* w_router,
-                     const float* bias, const uint16_t* x, int32_t T, int32_t E, int32_t k,
-                     float* out, void* workspace, size_t workspace_bytes, uint32_t* err_flags,
-                     int32_t path, void* stream) {
+// Record a timing event; inside a stream capture it becomes an event-record node of the
+// graph (so replays can still be timed).
+static moe_status record_event(hipEvent_t ev, hipStream_t st) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(st, &cs);
+  if (e != hipSuccess) return hip_status(e, "event record: stream capture query");
+  if (cs == hipStreamCaptureStatusActive)
+    return hip_status(hipEventRecordWithFlags(ev, st, hipEventRecordExternal),
+                      "event record (external, in capture)");
+  return hip_status(hipEventRecord(ev, st), "event record");
+}
+
+static moe_status layer_impl(const moe_pool* pool, const int32_t* slot_map,
+                             const uint16_t* w_router, const float* bias, const uint16_t* x,
+                             int32_t T, int32_t E, int32_t k, float* out, void* workspace,
+                             size_t workspace_bytes, uint32_t* err_flags, int32_t path,
+                             void* stream, void* ev_begin, void* ev_end) {
   moe_status s = check_pool(pool);
   if (s != MOE_OK) return s;
   s = check_shape(T, pool->H, E, k);
@@ -357,14 +383,70 @@ moe_status moe_layer(const moe_pool* pool, const int32_t* slot_map, const uint16
   uint16_t* h = (uint16_t*)(ws + L.h);
   float* y = (float*)(ws + L.y);
   void* scratch = ws + L.scratch;
+  int32_t* act = (int32_t*)(ws + L.act);
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = moe::launch_route(x, w_router, bias, T, pool->H, E, k, ids, w, (float*)scratch, st);
-  if (e != hipSuccess) return hip_status(e, "route");
-  e = moe::launch_bucket(ids, T * k, E, counts, offsets, perm, inv_perm, scratch, st);
-  if (e != hipSuccess) return hip_status(e, "bucket");
-  s = ffn_dispatch(pool, slot_map, E, x, T, k, offsets, perm, h, y, err_flags, path, st);
+  hipError_t e;
+  bool have_act = false;
+  clear_stale_error();
+  // route + bucket: for small batches the split router is finished (top-k and counting
+  // sort) by one single-workgroup kernel; otherwise router, then the counting sort
+  if (moe::route_small_ok(T, E)) {
+    // one workgroup: router, top-k, counting sort and the active-expert list
+    e = moe::launch_route_small(x, w_router, bias, T, pool->H, E, k, slot_map, ids, w, counts,
+                                offsets, perm, inv_perm, act, st);
+    if (e != hipSuccess) return hip_status(e, "route+bucket");
+    have_act = true;
+  } else if (moe::route_bucket_fusable(T, E)) {
+    e = moe::launch_route_bucket_small(x, w_router, bias, T, pool->H, E, k, (float*)scratch, ids,
+                                       w, counts, offsets, perm, inv_perm, st);
+    if (e != hipSuccess) return hip_status(e, "route+bucket");
+  } else {
+    e = moe::launch_route(x, w_router, bias, T, pool->H, E, k, ids, w, (float*)scratch, st);
+    if (e != hipSuccess) return hip_status(e, "route");
+    e = moe::launch_bucket(ids, T * k, E, counts, offsets, perm, inv_perm, scratch, st);
+    if (e != hipSuccess) return hip_status(e, "bucket");
+  }
+  if (ev_begin != nullptr) {
+    s = record_event((hipEvent_t)ev_begin, st);
+    if (s != MOE_OK) return s;
+  }
+  s = gate_up_dispatch(pool, slot_map, E, x, T, k, offsets, perm, h, err_flags, path, st,
+                       have_act ? act : nullptr);
   if (s != MOE_OK) return s;
+  if (ev_end != nullptr) {
+    s = record_event((hipEvent_t)ev_end, st);
+    if (s != MOE_OK) return s;
+  }
+  if (have_act && use_gemv(path, T) && moe::down_combine_small_ok(T, k, E, pool->I)) {
+    clear_stale_error();
+    moe::PoolView g, u, d;
+    pool_views(pool, &g, &u, &d);
+    return hip_status(moe::launch_down_combine_small(pool->fmt, d, pool->n_slots, E, T, k, pool->H,
+                                                     pool->I, act, h, inv_perm, w, y, out,
+                                                     err_flags, st),
+                      "down+combine");
+  }
+  s = down_dispatch(pool, slot_map, E, T, k, offsets, h, y, err_flags, path, st);
+  if (s != MOE_OK) return s;
+  clear_stale_error();
   return hip_status(moe::launch_combine(y, inv_perm, w, T, k, pool->H, out, st), "combine");
+}
+
+moe_status moe_layer(const moe_pool* pool, const int32_t* slot_map, const uint16_t* w_router,
+                     const float* bias, const uint16_t* x, int32_t T, int32_t E, int32_t k,
+                     float* out, void* workspace, size_t workspace_bytes, uint32_t* err_flags,
+                     int32_t path, void* stream) {
+  return layer_impl(pool, slot_map, w_router, bias, x, T, E, k, out, workspace, workspace_bytes,
+                    err_flags, path, stream, nullptr, nullptr);
+}
+
+moe_status moe_layer_timed(const moe_pool* pool, const int32_t* slot_map,
+                           const uint16_t* w_router, const float* bias, const uint16_t* x,
+                           int32_t T, int32_t E, int32_t k, float* out, void* workspace,
+                           size_t workspace_bytes, uint32_t* err_flags, int32_t path,
+                           void* stream, void* ev_gate_up_begin, void* ev_gate_up_end) {
+  return layer_impl(pool, slot_map, w_router, bias, x, T, E, k, out, workspace, workspace_bytes,
+                    err_flags, path, stream, ev_gate_up_begin, ev_gate_up_end);
 }
 
 }  // extern "C"

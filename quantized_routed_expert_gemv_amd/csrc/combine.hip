@@ -17,14 +17,25 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
   const int t = blockIdx.y;
   const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (c >= H) return;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const float wj = w[(int64_t)t * k + j];
-    const int pos = inv_perm[(int64_t)t * k + j];
-    const f32x4 v = *(const f32x4*)(y + (int64_t)pos * H + c);
+  // every load is issued before the first one is consumed (k <= kMaxK)
+  int pos[kMaxK];
+  float wj[kMaxK];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc[q] = fmaf(wj, v[q], acc[q]);
+  for (int j = 0; j < kMaxK; ++j) {
+    const int jj = j < k ? j : 0;
+    pos[j] = inv_perm[(int64_t)t * k + jj];
+    wj[j] = w[(int64_t)t * k + jj];
   }
+  f32x4 v[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) v[j] = *(const f32x4*)(y + (int64_t)pos[j] * H + c);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j)
+    if (j < k) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = fmaf(wj[j], v[j][q], acc[q]);
+    }
   *(f32x4*)(out + (int64_t)t * H + c) = acc;
 }
 

@@ -106,6 +106,11 @@ __device__ __forceinline__ int64_t pool_unit(int r, int b, int nb) {
 __host__ __device__ constexpr int64_t code_bytes_per_block(int fmt) { return fmt == kMXFP4 ? 16 : 32; }
 __host__ __device__ constexpr int64_t scale_bytes_per_block(int fmt) { return fmt == kMXFP4 ? 1 : 2; }
 
+// Active-expert list written by the small-batch router (see route.hip): act[0] = count,
+// then kActStride int32 per active expert.
+constexpr int kActStride = 8;
+__host__ __device__ constexpr int act_ints(int E) { return 1 + kActStride * E; }
+
 struct PoolView {
   const uint8_t* q;   // code plane, slot 0
   const uint8_t* s;   // scale plane, slot 0

@@ -4,11 +4,14 @@
 // on the quantized bytes, with no bf16 copy of the weights (tinyserve README, "How it
 // works" item 2, and "What we tried and ruled out": full dequantization at load). With
 // few tokens per expert the work is a stream of the selected experts' bytes from HBM, so
-// the kernel is built around that stream:
-//   * one workgroup = one 16-row group of one active expert; its 4 waves split the
-//     reduction dimension K;
+// the kernel is built around keeping that stream in flight:
+//   * one workgroup = one 16-row group of one active expert; its 4 waves split K;
 //   * in the pool's tiled layout one 64-lane 16-byte load is one contiguous KiB holding
 //     16 rows x 4 MXFP4 blocks (or 16 rows x 2 Q8_0 blocks): every HBM line is used once;
+//   * each wave issues the loads of up to 8 such chunks per matrix before it consumes any,
+//     so at the workloads' sizes a workgroup has its whole share of the expert in flight
+//     after one round trip; the activations for the same K range are staged in LDS once
+//     per workgroup and read back as broadcasts;
 //   * codes are widened in registers (gfx950 v_cvt_scalef32_pk_bf16_fp4 for MXFP4, exact
 //     int8 -> bf16 for Q8_0) and reduced with v_dot2_f32_bf16 into fp32;
 //   * partial sums meet through xor-shuffles and a fixed-order LDS sum over the 4 waves,
@@ -16,6 +19,7 @@
 // Gate and up are read in the same pass and SwiGLU is applied before h is written
 // (rounded once to bf16); the down projection writes fp32 y.
 #include "common.hpp"
+#include "bucket_dev.hpp"
 #include "kernels.hpp"
 
 namespace moe {
@@ -24,57 +28,62 @@ namespace {
 
 constexpr int kGThreads = 256;
 constexpr int kGWaves = kGThreads / kWave;
-constexpr int kUnroll = 2;     // chunks in flight per wave per iteration
+constexpr int kU = 8;          // chunks per wave per batch (all loads issued first)
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
+// Expert weights are streamed once per call: nontemporal loads keep them from displacing
+// the activations and small tables in the caches (and stream measurably faster).
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load((const u32x4*)p);
+}
 
 // Find the j-th expert (in expert order) with a non-empty bucket; -1 if there are fewer.
-// Every lane of the calling wave gets the result.
-__device__ int find_active_expert(const int32_t* __restrict__ offsets, int E, int j) {
+// *n_active receives the number of non-empty buckets. Every lane of the wave gets both.
+__device__ int find_active_expert(const int32_t* __restrict__ offsets, int E, int j,
+                                  int* n_active) {
   const int lane = threadIdx.x & (kWave - 1);
+  int found = -1, total = 0;
   for (int base = 0; base < E; base += kWave) {
     const int e = base + lane;
     const bool ne = e < E && offsets[e + 1] > offsets[e];
     const uint64_t bal = __ballot(ne);
     const int cnt = __popcll(bal);
-    if (j < cnt) {
+    if (found < 0 && j >= total && j < total + cnt) {
       const uint64_t below = lane ? (~0ull >> (kWave - lane)) : 0ull;
-      const bool mine = ne && __popcll(bal & below) == j;
+      const bool mine = ne && __popcll(bal & below) == j - total;
       const uint64_t hit = __ballot(mine);
-      return base + __ffsll((unsigned long long)hit) - 1;
+      found = base + __ffsll((unsigned long long)hit) - 1;
     }
-    j -= cnt;
+    total += cnt;
   }
-  return -1;
+  *n_active = total;
+  return found;
 }
 
-// Per-lane share of one chunk for one matrix: the lane's row, the lane's block (MXFP4:
-// 32 codes; Q8_0: 16 codes = half a block), converted once and dotted with each token.
-template <int FMT>
+// One lane's share of one chunk of one matrix (16 bytes of codes and the block scale).
+// Loads are issued unconditionally (from a valid address when the chunk lies past the end
+// of the row) and masked when consumed: a guarded load would make the compiler wait for it
+// before issuing the next one.
 struct Chunk {
   u32x4 q;
   uint32_t s;
+  bool ok;
 };
 
 template <int FMT>
-__device__ __forceinline__ void load_chunk(Chunk<FMT>& c, const uint8_t* q, const uint8_t* s,
-                                           bool ok) {
-  if (ok) {
-    c.q = ld16(q);
-    if constexpr (FMT == kMXFP4) c.s = *s;
-    else c.s = *(const uint16_t*)s;
-  } else {
-    c.q = u32x4{0, 0, 0, 0};
-    c.s = 0;
-  }
+__device__ __forceinline__ void load_chunk(Chunk& c, const uint8_t* q, const uint8_t* s, bool ok) {
+  c.q = ld16_stream(q);
+  if constexpr (FMT == kMXFP4) c.s = __builtin_nontemporal_load(s);
+  else c.s = __builtin_nontemporal_load((const uint16_t*)s);
+  c.ok = ok;
 }
 
 // Weights of the chunk as bf16 pairs (MXFP4: 16 pairs, scale folded in; Q8_0: 8 pairs,
 // scale applied later to the fp32 partial).
 template <int FMT>
-__device__ __forceinline__ void widen(const Chunk<FMT>& c, bf16x2* w) {
+__device__ __forceinline__ void widen(const Chunk& c, bf16x2* w) {
   if constexpr (FMT == kMXFP4) {
-    const float sc = e8m0_to_f32(c.s);
+    const float sc = c.ok ? e8m0_to_f32(c.s) : 0.f;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       w[4 * d + 0] = fp4x2_to_bf16x2<0>(c.q[d], sc);
@@ -104,41 +113,64 @@ __device__ __forceinline__ float dot_chunk(const bf16x2* w, const uint32_t* xv, 
     float part = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) part = dot2_bf16(w[i], xv[i], part);
-    return fmaf(fp16_to_f32((uint16_t)s), part, acc);
+    return fmaf(fp16_to_f32((uint16_t)s), part, acc);   // s is 0 for masked chunks
   }
 }
 
-// Geometry of the lane within a 1 KiB chunk of the tiled layout.
+// Geometry of a lane within a 1 KiB chunk of the tiled layout.
+//   MXFP4: unit = 16 B = one block of one row; lane l -> row l%16, block 4c + l/16
+//   Q8_0 : unit = 32 B = one block of one row; lane l -> row (l/2)%16, block 2c + l/32,
+//          half l%2 of the block
 template <int FMT>
 struct LaneMap {
-  // MXFP4: unit = 16 B = one block of one row; lane l -> row l%16, block 4c + l/16
-  // Q8_0 : unit = 32 B = one block of one row; lane l -> row (l/2)%16, block 2c + l/32,
-  //        half l%2 of the block
   static constexpr int kBlocksPerChunk = FMT == kMXFP4 ? 4 : 2;
-  static constexpr int kXWords = FMT == kMXFP4 ? 16 : 8;     // u32 of x per lane per chunk
+  static constexpr int kKPerChunk = 32 * kBlocksPerChunk;     // K elements per chunk
+  static constexpr int kXWords = FMT == kMXFP4 ? 16 : 8;      // u32 of x per lane per chunk
   __device__ static int row(int lane) { return FMT == kMXFP4 ? (lane & 15) : ((lane >> 1) & 15); }
   __device__ static int blk(int lane) { return FMT == kMXFP4 ? (lane >> 4) : (lane >> 5); }
-  __device__ static int xoff(int lane) { return FMT == kMXFP4 ? 0 : (lane & 1) * 16; }
+  // K offset of the lane's codes inside its chunk
+  __device__ static int koff(int lane) {
+    return FMT == kMXFP4 ? (lane >> 4) * 32 : (lane >> 5) * 32 + (lane & 1) * 16;
+  }
 };
 
-template <int FMT, bool GATED, int NT>
+template <int FMT, bool GATED, bool ACT, int NT>
 __global__ __launch_bounds__(kGThreads) void k_gemv(
     const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as, int64_t a_qslot,
     int64_t a_sslot, const uint8_t* __restrict__ bq, const uint8_t* __restrict__ bs,
     const int32_t* __restrict__ slot_map, int n_slots, int E,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm, int k,
     const uint16_t* __restrict__ src, int K, int rows, uint16_t* __restrict__ h_out,
-    float* __restrict__ y_out, uint32_t* __restrict__ err_flags) {
+    float* __restrict__ y_out, uint32_t* __restrict__ err_flags, const int32_t* __restrict__ act) {
   using LM = LaneMap<FMT>;
   constexpr int kM = GATED ? 2 : 1;
+  constexpr int kSlice = kGWaves * kU * LM::kKPerChunk;   // K elements staged per batch
+  __shared__ __attribute__((aligned(16))) uint16_t xs[NT][kSlice];
   __shared__ float red[kGWaves][NT][kM][16];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int rg = blockIdx.x;
-  const int e = find_active_expert(offsets, E, blockIdx.y);
-  if (e < 0) return;
-  const int lo = offsets[e], hi = offsets[e + 1];
-  const int slot = slot_map[e];
+  int e, lo, hi, slot;
+  int atok[4] = {0, 0, 0, 0};
+  if constexpr (ACT) {
+    // the small-batch router's active list: one round trip for expert, slot, range, tokens
+    const int32_t* a = act + 1 + kActStride * blockIdx.y;
+    const int n_act = act[0];
+    e = a[0];
+    slot = a[1];
+    lo = a[2];
+    hi = a[3];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) atok[i] = a[4 + i];
+    if ((int)blockIdx.y >= n_act) return;
+  } else {
+    int n_active;
+    e = find_active_expert(offsets, E, blockIdx.y, &n_active);
+    if (e < 0) return;
+    lo = offsets[e];
+    hi = offsets[e + 1];
+    slot = slot_map[e];
+  }
   const int r0 = rg * 16;
   if (slot < 0 || slot >= n_slots) {
     for (int i = threadIdx.x; i < (hi - lo) * 16; i += kGThreads) {
@@ -147,130 +179,364 @@ __global__ __launch_bounds__(kGThreads) void k_gemv(
       else y_out[(int64_t)pos * rows + r] = 0.f;
     }
     if (threadIdx.x == 0 && err_flags) atomicOr(err_flags, 1u);
-    return;
-  }
-  const int nb = K / 32;
-  const int nc = (nb + LM::kBlocksPerChunk - 1) / LM::kBlocksPerChunk;
-  const int64_t cb = code_bytes_per_block(FMT), sb = scale_bytes_per_block(FMT);
-  // start of this row group in the code / scale planes, plus the lane's 16-byte slot
-  const int64_t unit0 = (int64_t)rg * nb * 16;
-  const uint8_t* qa = aq + slot * a_qslot + unit0 * cb + lane * 16;
-  const uint8_t* qb = GATED ? bq + slot * a_qslot + unit0 * cb + lane * 16 : nullptr;
-  const int lane_unit = FMT == kMXFP4 ? lane : (lane >> 1);
-  const uint8_t* sa = as + slot * a_sslot + (unit0 + lane_unit) * sb;
-  const uint8_t* sbp = GATED ? bs + slot * a_sslot + (unit0 + lane_unit) * sb : nullptr;
-  const int lblk = LM::blk(lane);
+  } else {
+    const int nb = K / 32;
+    const int nc = (nb + LM::kBlocksPerChunk - 1) / LM::kBlocksPerChunk;
+    constexpr int64_t cb = code_bytes_per_block(FMT), sb = scale_bytes_per_block(FMT);
+    const int64_t unit0 = (int64_t)rg * nb * 16;
+    const uint8_t* qa = aq + slot * a_qslot + unit0 * cb + lane * 16;
+    const uint8_t* qb = GATED ? bq + slot * a_qslot + unit0 * cb + lane * 16 : nullptr;
+    const int lane_unit = FMT == kMXFP4 ? lane : (lane >> 1);
+    const uint8_t* sa = as + slot * a_sslot + (unit0 + lane_unit) * sb;
+    const uint8_t* sbp = GATED ? bs + slot * a_sslot + (unit0 + lane_unit) * sb : nullptr;
+    const int lblk = LM::blk(lane);
+    const int koff = LM::koff(lane);
 
-  for (int c0 = lo; c0 < hi; c0 += NT) {
-    const uint16_t* xr[NT];
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      const int pos = min(c0 + i, hi - 1);
-      const int64_t row = GATED ? (int64_t)(perm[pos] / k) : (int64_t)pos;
-      xr[i] = src + row * K + LM::xoff(lane);
-    }
-    float acc[kM][NT];
-#pragma unroll
-    for (int m = 0; m < kM; ++m)
-#pragma unroll
-      for (int i = 0; i < NT; ++i) acc[m][i] = 0.f;
-
-    for (int c = wave; c < nc; c += kGWaves * kUnroll) {
-      Chunk<FMT> ca[kUnroll], cbk[kUnroll];
-      uint32_t xv[kUnroll][NT][LM::kXWords];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int cc = c + u * kGWaves;
-        const int b = cc * LM::kBlocksPerChunk + lblk;
-        const bool ok = cc < nc && b < nb;
-        const int64_t qoff = (int64_t)cc * 1024;
-        const int64_t soff = (int64_t)cc * (FMT == kMXFP4 ? 64 : 64);
-        load_chunk<FMT>(ca[u], qa + qoff, sa + soff, ok);
-        if constexpr (GATED) load_chunk<FMT>(cbk[u], qb + qoff, sbp + soff, ok);
-#pragma unroll
-        for (int i = 0; i < NT; ++i) {
-#pragma unroll
-          for (int w4 = 0; w4 < LM::kXWords / 4; ++w4) {
-            u32x4 v = ok ? ld16(xr[i] + b * 32 + w4 * 8) : u32x4{0, 0, 0, 0};
-            xv[u][i][4 * w4 + 0] = v[0];
-            xv[u][i][4 * w4 + 1] = v[1];
-            xv[u][i][4 * w4 + 2] = v[2];
-            xv[u][i][4 * w4 + 3] = v[3];
-          }
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        bf16x2 w[16];
-        widen<FMT>(ca[u], w);
-#pragma unroll
-        for (int i = 0; i < NT; ++i) acc[0][i] = dot_chunk<FMT>(w, xv[u][i], ca[u].s, acc[0][i]);
-        if constexpr (GATED) {
-          widen<FMT>(cbk[u], w);
-#pragma unroll
-          for (int i = 0; i < NT; ++i)
-            acc[kM - 1][i] = dot_chunk<FMT>(w, xv[u][i], cbk[u].s, acc[kM - 1][i]);
-        }
-      }
-    }
-    // lanes that share a row: MXFP4 {l, l^16, l^32, l^48}; Q8_0 {l, l^1, l^32, l^33}
-#pragma unroll
-    for (int m = 0; m < kM; ++m)
+    for (int c0 = lo; c0 < hi; c0 += NT) {
+      // activation row of each token of this chunk (clamped to a valid row past the end)
+      const uint16_t* xrow[NT];
 #pragma unroll
       for (int i = 0; i < NT; ++i) {
-        float v = acc[m][i];
-        if constexpr (FMT == kMXFP4) {
-          v += wave_xor(v, 16);
-          v += wave_xor(v, 32);
-        } else {
-          v += wave_xor(v, 1);
-          v += wave_xor(v, 32);
+        const int pos = min(c0 + i, hi - 1);
+        int64_t row = pos;
+        if constexpr (GATED) {
+          // first chunk of the bucket: tokens come with the active list (past the bucket's
+          // end, any valid row: those results are never stored)
+          if (ACT && i < 4 && c0 == lo) row = c0 + i < hi ? atok[i & 3] : atok[0];
+          else row = perm[pos] / k;
         }
-        acc[m][i] = v;
+        xrow[i] = src + row * K;
       }
-    const bool writer = FMT == kMXFP4 ? (lane < 16) : (lane < 32 && (lane & 1) == 0);
-    if (writer) {
-      const int r = LM::row(lane);
+      float acc[kM][NT];
 #pragma unroll
       for (int m = 0; m < kM; ++m)
 #pragma unroll
-        for (int i = 0; i < NT; ++i) red[wave][i][m][r] = acc[m][i];
-    }
-    __syncthreads();
-    if (threadIdx.x < NT * 16) {
-      const int i = threadIdx.x / 16, r = threadIdx.x % 16;
-      const int pos = c0 + i;
-      if (pos < hi) {
-        float v[kM];
+        for (int i = 0; i < NT; ++i) acc[m][i] = 0.f;
+
+      for (int cbase = 0; cbase < nc; cbase += kGWaves * kU) {
+        // 1. the batch's K range of every token's activation row (L2-resident): loads first,
+        //    LDS writes after the weight loads are issued
+        constexpr int kPieces = NT * (kSlice / 8) / kGThreads;   // 16-byte pieces per thread
+        const int k0 = cbase * LM::kKPerChunk;
+        u32x4 xp[kPieces];
+        bool xok[kPieces];
 #pragma unroll
-        for (int m = 0; m < kM; ++m) {
-          float sum = red[0][i][m][r];
-#pragma unroll
-          for (int q = 1; q < kGWaves; ++q) sum += red[q][i][m][r];
-          v[m] = sum;
+        for (int it = 0; it < kPieces; ++it) {
+          const int idx = threadIdx.x + it * kGThreads;
+          const int i = idx / (kSlice / 8), q = idx % (kSlice / 8);
+          const int kk = k0 + q * 8;
+          xok[it] = c0 + i < hi && kk < K;
+          xp[it] = ld16(xrow[i] + (xok[it] ? kk : 0));
         }
-        if constexpr (GATED) h_out[(int64_t)pos * rows + r0 + r] = f32_to_bf16_rne(silu_mul(v[0], v[1]));
-        else y_out[(int64_t)pos * rows + r0 + r] = v[0];
+        // 2. this wave's weight chunks of the batch, all in flight at once
+        Chunk ca[kU], cbk[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int c = cbase + wave + kGWaves * u;
+          const int b = c * LM::kBlocksPerChunk + lblk;
+          const bool ok = c < nc && b < nb;
+          const int cs = ok ? c : 0;      // chunk 0 of the row group always exists
+          load_chunk<FMT>(ca[u], qa + (int64_t)cs * 1024, sa + (int64_t)cs * 64, ok);
+          if constexpr (GATED) load_chunk<FMT>(cbk[u], qb + (int64_t)cs * 1024, sbp + (int64_t)cs * 64, ok);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // keep the whole batch of loads ahead of its use
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < kPieces; ++it) {
+          const int idx = threadIdx.x + it * kGThreads;
+          const int i = idx / (kSlice / 8), q = idx % (kSlice / 8);
+          *(u32x4*)&xs[i][q * 8] = xok[it] ? xp[it] : u32x4{0, 0, 0, 0};
+        }
+        __syncthreads();
+        // 3. consume (chunks past the end of the row carry a zero scale and add nothing)
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int c = cbase + wave + kGWaves * u;
+          const int xo = (c - cbase) * LM::kKPerChunk + koff;
+          bf16x2 w[16];
+          uint32_t xv[LM::kXWords];
+          widen<FMT>(ca[u], w);
+#pragma unroll
+          for (int i = 0; i < NT; ++i) {
+#pragma unroll
+            for (int q = 0; q < LM::kXWords / 4; ++q) {
+              const u32x4 v = *(const u32x4*)&xs[i][xo + q * 8];
+              xv[4 * q + 0] = v[0];
+              xv[4 * q + 1] = v[1];
+              xv[4 * q + 2] = v[2];
+              xv[4 * q + 3] = v[3];
+            }
+            acc[0][i] = dot_chunk<FMT>(w, xv, ca[u].ok ? ca[u].s : 0u, acc[0][i]);
+          }
+          if constexpr (GATED) {
+            widen<FMT>(cbk[u], w);
+#pragma unroll
+            for (int i = 0; i < NT; ++i) {
+#pragma unroll
+              for (int q = 0; q < LM::kXWords / 4; ++q) {
+                const u32x4 v = *(const u32x4*)&xs[i][xo + q * 8];
+                xv[4 * q + 0] = v[0];
+                xv[4 * q + 1] = v[1];
+                xv[4 * q + 2] = v[2];
+                xv[4 * q + 3] = v[3];
+              }
+              acc[kM - 1][i] = dot_chunk<FMT>(w, xv, cbk[u].ok ? cbk[u].s : 0u, acc[kM - 1][i]);
+            }
+          }
+        }
       }
+      // lanes that share a row: MXFP4 {l, l^16, l^32, l^48}; Q8_0 {l, l^1, l^32, l^33}
+#pragma unroll
+      for (int m = 0; m < kM; ++m)
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+          float v = acc[m][i];
+          if constexpr (FMT == kMXFP4) {
+            v += wave_xor(v, 16);
+            v += wave_xor(v, 32);
+          } else {
+            v += wave_xor(v, 1);
+            v += wave_xor(v, 32);
+          }
+          acc[m][i] = v;
+        }
+      const bool writer = FMT == kMXFP4 ? (lane < 16) : (lane < 32 && (lane & 1) == 0);
+      if (writer) {
+        const int r = LM::row(lane);
+#pragma unroll
+        for (int m = 0; m < kM; ++m)
+#pragma unroll
+          for (int i = 0; i < NT; ++i) red[wave][i][m][r] = acc[m][i];
+      }
+      __syncthreads();
+      if (threadIdx.x < NT * 16) {
+        const int i = threadIdx.x / 16, r = threadIdx.x % 16;
+        const int pos = c0 + i;
+        if (pos < hi) {
+          float v[kM];
+#pragma unroll
+          for (int m = 0; m < kM; ++m) {
+            float sum = red[0][i][m][r];
+#pragma unroll
+            for (int q = 1; q < kGWaves; ++q) sum += red[q][i][m][r];
+            v[m] = sum;
+          }
+          if constexpr (GATED) h_out[(int64_t)pos * rows + r0 + r] = f32_to_bf16_rne(silu_mul(v[0], v[1]));
+          else y_out[(int64_t)pos * rows + r0 + r] = v[0];
+        }
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
 }
 
-template <int FMT, bool GATED>
+// Down projection (and, with COMBINE, the combine) for a small batch (T*k <= 8 pairs) in
+// one launch, with no atomics: a workgroup owns 16 output columns (one row group of the
+// down matrices) for every active expert and every token. Its 8 waves split the (expert,
+// chunk) work, each with all of its chunk loads in flight; the h rows of all pairs sit in
+// LDS. Per pair and column the wave partials are summed in increasing wave order and
+// written to y; COMBINE then merges them per token in increasing j exactly like the
+// stand-alone combine kernel. The active experts come from the small-batch router's list
+// (act) or, when act is NULL, from offsets and slot_map.
+constexpr int kDCWaves = 8;
+constexpr int kDCMaxPairs = 8;
+constexpr int kDCMaxH = 57344 / 2;   // bf16 elements of h staged in LDS (pairs x I)
+constexpr int kDCU = 12;             // chunks per wave per load batch
+
+template <int FMT, bool COMBINE>
+__global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
+    const uint8_t* __restrict__ dq, const uint8_t* __restrict__ ds, int64_t qslot,
+    int64_t sslot, int n_slots, int E, const int32_t* __restrict__ act,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ slot_map,
+    const uint16_t* __restrict__ h, int T, int k, int H, int I, const int32_t* __restrict__ inv_perm,
+    const float* __restrict__ topk_w, float* __restrict__ y, float* __restrict__ out,
+    uint32_t* __restrict__ err_flags) {
+  using LM = LaneMap<FMT>;
+  constexpr int NTH = kDCWaves * kWave;
+  __shared__ __attribute__((aligned(16))) uint16_t hs[kDCMaxH];
+  __shared__ float red[kDCWaves][kDCMaxPairs][16];
+  __shared__ float yl[kDCMaxPairs][16];
+  __shared__ int actl[1 + kActStride * kDCMaxPairs];
+  __shared__ int tmp[kDCWaves];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int rg = blockIdx.x;
+  const int r0 = rg * 16;
+  const int np = T * k;
+  // 1. active list and all h rows (independent loads, issued together)
+  const int na_ints = 1 + kActStride * min(min(np, E), kDCMaxPairs);   // entries that exist
+  int av = 0, olo = 0, ohi = 0, osl = 0;
+  if (act != nullptr) {
+    av = act[min((int)threadIdx.x, na_ints - 1)];
+  } else {
+    const int ec = threadIdx.x < E ? threadIdx.x : 0;
+    olo = offsets[ec];
+    ohi = offsets[ec + 1];
+    osl = slot_map[ec];
+  }
+  constexpr int kHPieces = kDCMaxH / 8 / NTH;    // 16-byte pieces per thread (upper bound)
+  const int hp = np * I / 8;                     // pieces actually present
+  u32x4 hv[kHPieces];
+#pragma unroll
+  for (int r = 0; r < kHPieces; ++r)
+    hv[r] = *(const u32x4*)(h + (int64_t)min((int)threadIdx.x + r * NTH, hp - 1) * 8);
+  if (act != nullptr) {
+    if (threadIdx.x < na_ints) actl[threadIdx.x] = av;
+  } else {
+    const bool ne = (int)threadIdx.x < E && ohi > olo;
+    int total;
+    const int rank = bucket_dev::block_exclusive_scan<kDCWaves * kWave>(ne ? 1 : 0, tmp, &total);
+    if (ne && rank < kDCMaxPairs) {
+      int* a = &actl[1 + kActStride * rank];
+      a[0] = threadIdx.x;
+      a[1] = osl;
+      a[2] = olo;
+      a[3] = ohi;
+    }
+    if (threadIdx.x == 0) actl[0] = total;
+  }
+#pragma unroll
+  for (int r = 0; r < kHPieces; ++r) {
+    const int i = threadIdx.x + r * NTH;
+    if (i < hp) *(u32x4*)&hs[i * 8] = hv[r];
+  }
+  __syncthreads();
+  const int n_act = actl[0];
+  // 2. wave -> (active expert j, its q-th share of the chunks)
+  const int per = kDCWaves / n_act;              // waves per expert (n_act <= 8)
+  const int j = wave % n_act;
+  const int q = wave / n_act;
+  const bool busy = q < per;
+  const int* ent = &actl[1 + kActStride * j];
+  const int slot = ent[1], lo = ent[2], hi = ent[3];
+  const bool valid = slot >= 0 && slot < n_slots;
+  const int nb = I / 32;
+  const int nc = (nb + LM::kBlocksPerChunk - 1) / LM::kBlocksPerChunk;
+  constexpr int64_t cb = code_bytes_per_block(FMT), sb = scale_bytes_per_block(FMT);
+  const int64_t unit0 = (int64_t)rg * nb * 16;
+  const int lane_unit = FMT == kMXFP4 ? lane : (lane >> 1);
+  const int sl = valid ? slot : 0;
+  const uint8_t* qa = dq + sl * qslot + unit0 * cb + lane * 16;
+  const uint8_t* sa = ds + sl * sslot + (unit0 + lane_unit) * sb;
+  const int lblk = LM::blk(lane);
+  const int koff = LM::koff(lane);
+  float acc[kDCMaxPairs];
+#pragma unroll
+  for (int p = 0; p < kDCMaxPairs; ++p) acc[p] = 0.f;
+  if (busy && valid) {
+    for (int cbase = q; cbase < nc; cbase += per * kDCU) {
+      Chunk ch[kDCU];
+#pragma unroll
+      for (int u = 0; u < kDCU; ++u) {
+        const int c = cbase + u * per;
+        const int b = c * LM::kBlocksPerChunk + lblk;
+        const bool ok = c < nc && b < nb;
+        const int cs = ok ? c : 0;
+        load_chunk<FMT>(ch[u], qa + (int64_t)cs * 1024, sa + (int64_t)cs * 64, ok);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < kDCU; ++u) {
+        const int c = cbase + u * per;
+        const int kx = ch[u].ok ? c * LM::kKPerChunk + koff : 0;   // masked lanes: any valid row part
+        bf16x2 w[16];
+        uint32_t xv[LM::kXWords];
+        widen<FMT>(ch[u], w);
+#pragma unroll
+        for (int p = 0; p < kDCMaxPairs; ++p) {
+          if (lo + p < hi) {
+            const uint16_t* hrow = &hs[(lo + p) * I + kx];
+#pragma unroll
+            for (int qq = 0; qq < LM::kXWords / 4; ++qq) {
+              const u32x4 v = *(const u32x4*)(hrow + qq * 8);
+              xv[4 * qq + 0] = v[0];
+              xv[4 * qq + 1] = v[1];
+              xv[4 * qq + 2] = v[2];
+              xv[4 * qq + 3] = v[3];
+            }
+            acc[p] = dot_chunk<FMT>(w, xv, ch[u].ok ? ch[u].s : 0u, acc[p]);
+          }
+        }
+      }
+    }
+  }
+  // 3. rows of the wave's partials, then fixed-order sums over the waves of each expert
+#pragma unroll
+  for (int p = 0; p < kDCMaxPairs; ++p) {
+    float v = acc[p];
+    if constexpr (FMT == kMXFP4) {
+      v += wave_xor(v, 16);
+      v += wave_xor(v, 32);
+    } else {
+      v += wave_xor(v, 1);
+      v += wave_xor(v, 32);
+    }
+    acc[p] = v;
+  }
+  const bool writer = FMT == kMXFP4 ? (lane < 16) : (lane < 32 && (lane & 1) == 0);
+  if (writer) {
+    const int r = LM::row(lane);
+#pragma unroll
+    for (int p = 0; p < kDCMaxPairs; ++p) red[wave][p][r] = acc[p];
+  }
+  __syncthreads();
+  if (threadIdx.x < np * 16) {
+    const int pos = threadIdx.x / 16, r = threadIdx.x % 16;
+    // the expert owning this bucket position, and its waves j, j + n_act, ...
+    int jj = 0;
+    for (int t = 0; t < n_act; ++t)
+      if (pos >= actl[1 + kActStride * t + 2] && pos < actl[1 + kActStride * t + 3]) jj = t;
+    const int plo = actl[1 + kActStride * jj + 2];
+    const int ps = actl[1 + kActStride * jj + 1];
+    float sum = 0.f;
+    if (ps >= 0 && ps < n_slots) {
+      sum = red[jj][pos - plo][r];
+      for (int ww = jj + n_act; ww < per * n_act; ww += n_act) sum += red[ww][pos - plo][r];
+    }
+    yl[pos][r] = sum;
+    y[(int64_t)pos * H + r0 + r] = sum;
+  }
+  if (!valid && busy && q == 0 && lane == 0 && err_flags) atomicOr(err_flags, 1u);
+  if constexpr (!COMBINE) return;
+  __syncthreads();
+  // 4. combine, in increasing j, as k_combine does
+  if (threadIdx.x < T * 16) {
+    const int t = threadIdx.x / 16, r = threadIdx.x % 16;
+    float a = 0.f;
+    for (int jj = 0; jj < k; ++jj) {
+      const int p = t * k + jj;
+      a = fmaf(topk_w[p], yl[inv_perm[p]][r], a);
+    }
+    out[(int64_t)t * H + r0 + r] = a;
+  }
+}
+
+int gemv_nt(int fmt, int T) {
+  if (T <= 1) return 1;
+  if (T <= 2) return 2;
+  if (T <= 4 || fmt == kMXFP4) return 4;
+  return 8;
+}
+
+template <int FMT, bool GATED, bool ACT>
 hipError_t launch_gemv_t(const PoolView& a, const PoolView& b, const int32_t* slot_map,
                          int n_slots, int E, const int32_t* offsets, const int32_t* perm,
                          int T, int k, const uint16_t* src, int K, int rows, uint16_t* h,
-                         float* y, uint32_t* err, hipStream_t stream) {
+                         float* y, uint32_t* err, const int32_t* act, hipStream_t stream) {
   const int n_act = min(E, T * k);
   dim3 grid(rows / 16, n_act);
-#define MOE_GEMV_CASE(N)                                                                     \
-  hipLaunchKernelGGL((k_gemv<FMT, GATED, N>), grid, dim3(kGThreads), 0, stream, a.q, a.s,    \
-                     a.q_slot, a.s_slot, b.q, b.s, slot_map, n_slots, E, offsets, perm, k,   \
-                     src, K, rows, h, y, err)
-  if (T <= 1) MOE_GEMV_CASE(1);
-  else if (T <= 2) MOE_GEMV_CASE(2);
-  else MOE_GEMV_CASE(4);
+#define MOE_GEMV_CASE(N)                                                                        \
+  hipLaunchKernelGGL((k_gemv<FMT, GATED, ACT, N>), grid, dim3(kGThreads), 0, stream, a.q, a.s,  \
+                     a.q_slot, a.s_slot, b.q, b.s, slot_map, n_slots, E, offsets, perm, k,      \
+                     src, K, rows, h, y, err, act)
+  switch (gemv_nt(FMT, T)) {
+    case 1: MOE_GEMV_CASE(1); break;
+    case 2: MOE_GEMV_CASE(2); break;
+    case 4: MOE_GEMV_CASE(4); break;
+    default:
+      if constexpr (FMT == kQ8_0) MOE_GEMV_CASE(8);
+      break;
+  }
 #undef MOE_GEMV_CASE
   return hipGetLastError();
 }
@@ -281,22 +547,63 @@ hipError_t launch_gate_up_gemv(int fmt, const PoolView& gate, const PoolView& up
                                const int32_t* slot_map, int n_slots, int E, const uint16_t* x,
                                int T, int k, int H, int I, const int32_t* offsets,
                                const int32_t* perm, uint16_t* h, uint32_t* err,
-                               hipStream_t stream) {
+                               const int32_t* act, hipStream_t stream) {
+  if (act != nullptr) {
+    if (fmt == kMXFP4)
+      return launch_gemv_t<kMXFP4, true, true>(gate, up, slot_map, n_slots, E, offsets, perm, T, k,
+                                               x, H, I, h, nullptr, err, act, stream);
+    return launch_gemv_t<kQ8_0, true, true>(gate, up, slot_map, n_slots, E, offsets, perm, T, k, x,
+                                            H, I, h, nullptr, err, act, stream);
+  }
   if (fmt == kMXFP4)
-    return launch_gemv_t<kMXFP4, true>(gate, up, slot_map, n_slots, E, offsets, perm, T, k, x, H,
-                                       I, h, nullptr, err, stream);
-  return launch_gemv_t<kQ8_0, true>(gate, up, slot_map, n_slots, E, offsets, perm, T, k, x, H, I,
-                                    h, nullptr, err, stream);
+    return launch_gemv_t<kMXFP4, true, false>(gate, up, slot_map, n_slots, E, offsets, perm, T, k,
+                                              x, H, I, h, nullptr, err, nullptr, stream);
+  return launch_gemv_t<kQ8_0, true, false>(gate, up, slot_map, n_slots, E, offsets, perm, T, k, x,
+                                           H, I, h, nullptr, err, nullptr, stream);
 }
 
 hipError_t launch_down_gemv(int fmt, const PoolView& down, const int32_t* slot_map, int n_slots,
                             int E, int T, int k, int H, int I, const int32_t* offsets,
                             const uint16_t* h, float* y, uint32_t* err, hipStream_t stream) {
+  if (down_combine_small_ok(T, k, E, I)) {   // the fused layer's kernel, without the combine
+    dim3 grid(H / 16);
+    if (fmt == kMXFP4)
+      hipLaunchKernelGGL((k_down_small<kMXFP4, false>), grid, dim3(kDCWaves * kWave), 0, stream,
+                         down.q, down.s, down.q_slot, down.s_slot, n_slots, E, nullptr, offsets,
+                         slot_map, h, T, k, H, I, nullptr, nullptr, y, nullptr, err);
+    else
+      hipLaunchKernelGGL((k_down_small<kQ8_0, false>), grid, dim3(kDCWaves * kWave), 0, stream,
+                         down.q, down.s, down.q_slot, down.s_slot, n_slots, E, nullptr, offsets,
+                         slot_map, h, T, k, H, I, nullptr, nullptr, y, nullptr, err);
+    return hipGetLastError();
+  }
   if (fmt == kMXFP4)
-    return launch_gemv_t<kMXFP4, false>(down, down, slot_map, n_slots, E, offsets, nullptr, T, k,
-                                        h, I, H, nullptr, y, err, stream);
-  return launch_gemv_t<kQ8_0, false>(down, down, slot_map, n_slots, E, offsets, nullptr, T, k, h,
-                                     I, H, nullptr, y, err, stream);
+    return launch_gemv_t<kMXFP4, false, false>(down, down, slot_map, n_slots, E, offsets, nullptr,
+                                               T, k, h, I, H, nullptr, y, err, nullptr, stream);
+  return launch_gemv_t<kQ8_0, false, false>(down, down, slot_map, n_slots, E, offsets, nullptr, T,
+                                            k, h, I, H, nullptr, y, err, nullptr, stream);
+}
+
+bool down_combine_small_ok(int T, int k, int E, int I) {
+  const int np = T * k;
+  return np >= 1 && np <= kDCMaxPairs && (int64_t)np * I <= kDCMaxH && min(E, np) <= kDCWaves;
+}
+
+hipError_t launch_down_combine_small(int fmt, const PoolView& down, int n_slots, int E, int T,
+                                     int k, int H, int I, const int32_t* act, const uint16_t* h,
+                                     const int32_t* inv_perm, const float* topk_w, float* y,
+                                     float* out, uint32_t* err, hipStream_t stream) {
+  if (!down_combine_small_ok(T, k, E, I)) return hipErrorInvalidValue;
+  dim3 grid(H / 16);
+  if (fmt == kMXFP4)
+    hipLaunchKernelGGL((k_down_small<kMXFP4, true>), grid, dim3(kDCWaves * kWave), 0, stream,
+                       down.q, down.s, down.q_slot, down.s_slot, n_slots, E, act, nullptr,
+                       nullptr, h, T, k, H, I, inv_perm, topk_w, y, out, err);
+  else
+    hipLaunchKernelGGL((k_down_small<kQ8_0, true>), grid, dim3(kDCWaves * kWave), 0, stream,
+                       down.q, down.s, down.q_slot, down.s_slot, n_slots, E, act, nullptr,
+                       nullptr, h, T, k, H, I, inv_perm, topk_w, y, out, err);
+  return hipGetLastError();
 }
 
 }  // namespace moe

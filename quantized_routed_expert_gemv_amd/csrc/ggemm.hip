@@ -75,33 +75,39 @@ template <>
 struct BFrag<kMXFP4> {
   u32x4 q;        // 32 codes of one block of one row
   uint32_t s;     // its E8M0 scale
+  bool ok;
 };
 template <>
 struct BFrag<kQ8_0> {
   u32x2 q[4];     // 8 codes from each of the step's 4 blocks
   uint32_t s[4];  // fp16 scale bits of each block
+  uint32_t okm;   // bit j: block j exists
 };
 
 // Load the lane's B share of step c for the row group rg (MXFP4: block 4c + lane/16 of row
-// lane%16; Q8_0: codes 8*(lane/16).. of blocks 4c..4c+3 of row lane%16).
+// lane%16; Q8_0: codes 8*(lane/16).. of blocks 4c..4c+3 of row lane%16). Loads are issued
+// unconditionally (from the matrix base when out of range) and masked when consumed, so
+// none of them waits for another.
 template <int FMT>
 __device__ __forceinline__ void load_b(BFrag<FMT>& f, const uint8_t* q, const uint8_t* s,
                                        int rg, int nb, int c, bool row_ok) {
   const int lane = threadIdx.x & (kWave - 1);
   if constexpr (FMT == kMXFP4) {
     const int b = 4 * c + (lane >> 4);
-    const bool ok = row_ok && b < nb;
-    const int64_t unit = ((int64_t)rg * nb + b) * 16 + (lane & 15);
-    f.q = ok ? ldg16(q + unit * 16) : u32x4{0, 0, 0, 0};
-    f.s = ok ? (uint32_t)s[unit] : 0u;
+    f.ok = row_ok && b < nb;
+    const int64_t unit = f.ok ? ((int64_t)rg * nb + b) * 16 + (lane & 15) : 0;
+    f.q = ldg16(q + unit * 16);
+    f.s = s[unit];
   } else {
+    f.okm = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int b = 4 * c + j;
       const bool ok = row_ok && b < nb;
-      const int64_t unit = ((int64_t)rg * nb + b) * 16 + (lane & 15);
-      f.q[j] = ok ? ldg8(q + unit * 32 + 8 * (lane >> 4)) : u32x2{0, 0};
-      f.s[j] = ok ? (uint32_t)(*(const uint16_t*)(s + unit * 2)) : 0u;
+      f.okm |= (uint32_t)ok << j;
+      const int64_t unit = ok ? ((int64_t)rg * nb + b) * 16 + (lane & 15) : 0;
+      f.q[j] = ldg8(q + unit * 32 + 8 * (lane >> 4));
+      f.s[j] = *(const uint16_t*)(s + unit * 2);
     }
   }
 }
@@ -147,18 +153,27 @@ __global__ __launch_bounds__(kTThreads) void k_ggemm(
   const int piece = threadIdx.x & 15;
   const int rbase = threadIdx.x >> 4;
   int64_t arow[8];
+  int prow[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)   // all perm loads first (clamped to the tile's first row)
+    prow[j] = GATED ? perm[min(m0 + rbase + 16 * j, mend - 1)] : 0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int pos = m0 + rbase + 16 * j;
-    if (pos < mend) arow[j] = GATED ? (int64_t)(perm[pos] / k) * K : (int64_t)pos * K;
+    if (pos < mend) arow[j] = GATED ? (int64_t)(prow[j] / k) * K : (int64_t)pos * K;
     else arow[j] = -1;
   }
   u32x4 areg[8];
+  uint32_t aok = 0;   // bit j: areg[j] holds real data (else it is stored as zeros)
   auto load_a = [&](int c) {
     const int kk = c * kBK + piece * 8;
+    aok = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      areg[j] = (arow[j] >= 0 && kk < K) ? ldg16(src + arow[j] + kk) : u32x4{0, 0, 0, 0};
+    for (int j = 0; j < 8; ++j) {
+      const bool ok = arow[j] >= 0 && kk < K;
+      aok |= (uint32_t)ok << j;
+      areg[j] = ldg16(src + (ok ? arow[j] + kk : 0));
+    }
   };
 
   // ---- B: 4 n-fragments per wave
@@ -203,7 +218,8 @@ __global__ __launch_bounds__(kTThreads) void k_ggemm(
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      *(u32x4*)(lds_a + (rbase + 16 * j) * kLdsStride + piece * 16) = areg[j];
+      *(u32x4*)(lds_a + (rbase + 16 * j) * kLdsStride + piece * 16) =
+          ((aok >> j) & 1) ? areg[j] : u32x4{0, 0, 0, 0};
     __syncthreads();
     if (c + 1 < nsteps) {
       load_a(c + 1);
@@ -215,7 +231,8 @@ __global__ __launch_bounds__(kTThreads) void k_ggemm(
       for (int i = 0; i < 4; ++i) {
         bf16x8 bv[4];
 #pragma unroll
-        for (int f = 0; f < 4; ++f) bv[f] = fp4x8_to_bf16x8(bcur[f].q[i], e8m0_to_f32(bcur[f].s));
+        for (int f = 0; f < 4; ++f)
+          bv[f] = fp4x8_to_bf16x8(bcur[f].q[i], bcur[f].ok ? e8m0_to_f32(bcur[f].s) : 0.f);
 #pragma unroll
         for (int mf = 0; mf < 4; ++mf) {
           const int row = 64 * wm + 16 * mf + mrow;
@@ -235,7 +252,7 @@ __global__ __launch_bounds__(kTThreads) void k_ggemm(
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
           bv[f] = i8x8_to_bf16x8(bcur[f].q[j][0], bcur[f].q[j][1]);
-          ds[f] = fp16_to_f32((uint16_t)bcur[f].s[j]);
+          ds[f] = ((bcur[f].okm >> j) & 1) ? fp16_to_f32((uint16_t)bcur[f].s[j]) : 0.f;
         }
 #pragma unroll
         for (int mf = 0; mf < 4; ++mf) {

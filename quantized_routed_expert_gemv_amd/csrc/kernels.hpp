@@ -12,19 +12,43 @@ int route_ksplit(int T, int H);
 hipError_t launch_route(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H,
                         int E, int k, int32_t* ids, float* w, float* partial,
                         hipStream_t stream);
+// Route + bucket for T <= 16 (route_bucket_fusable): the split router, then one
+// single-workgroup kernel that finishes the top-k and bucket-sorts the pairs.
+bool route_bucket_fusable(int T, int E);
+hipError_t launch_route_bucket_small(const uint16_t* x, const uint16_t* wr, const float* bias,
+                                     int T, int H, int E, int k, float* partial, int32_t* ids,
+                                     float* w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                                     int32_t* inv_perm, hipStream_t stream);
+
+// Route, top-k and bucket for T <= 16, E <= 128 in one single-workgroup launch, which also
+// writes the active-expert list act (1 + 4 * E int32; format in route.hip).
+bool route_small_ok(int T, int E);
+hipError_t launch_route_small(const uint16_t* x, const uint16_t* wr, const float* bias, int T,
+                              int H, int E, int k, const int32_t* slot_map, int32_t* ids,
+                              float* w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                              int32_t* inv_perm, int32_t* act, hipStream_t stream);
 
 size_t bucket_scratch_bytes(int n, int E);
 hipError_t launch_bucket(const int32_t* ids, int n, int E, int32_t* counts, int32_t* offsets,
                          int32_t* perm, int32_t* inv_perm, void* scratch, hipStream_t stream);
 
+// act: the small-batch router's active-expert list, or NULL (then the kernel derives the
+// active experts from offsets and slot_map).
 hipError_t launch_gate_up_gemv(int fmt, const PoolView& gate, const PoolView& up,
                                const int32_t* slot_map, int n_slots, int E, const uint16_t* x,
                                int T, int k, int H, int I, const int32_t* offsets,
                                const int32_t* perm, uint16_t* h, uint32_t* err,
-                               hipStream_t stream);
+                               const int32_t* act, hipStream_t stream);
 hipError_t launch_down_gemv(int fmt, const PoolView& down, const int32_t* slot_map, int n_slots,
                             int E, int T, int k, int H, int I, const int32_t* offsets,
                             const uint16_t* h, float* y, uint32_t* err, hipStream_t stream);
+// Down projection + combine in one launch for T*k <= 8 (down_combine_small_ok); needs the
+// small-batch router's active-expert list.
+bool down_combine_small_ok(int T, int k, int E, int I);
+hipError_t launch_down_combine_small(int fmt, const PoolView& down, int n_slots, int E, int T,
+                                     int k, int H, int I, const int32_t* act, const uint16_t* h,
+                                     const int32_t* inv_perm, const float* topk_w, float* y,
+                                     float* out, uint32_t* err, hipStream_t stream);
 hipError_t launch_gate_up_grouped(int fmt, const PoolView& gate, const PoolView& up,
                                   const int32_t* slot_map, int n_slots, int E, const uint16_t* x,
                                   int T, int k, int H, int I, const int32_t* offsets,

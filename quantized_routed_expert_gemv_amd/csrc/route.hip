@@ -9,8 +9,13 @@
 // accumulate in fp32. A workgroup owns 16 tokens and all E experts; its 4 waves split the
 // reduction dimension and their partial tiles are summed in LDS in a fixed order, so the
 // result is deterministic. For small T the reduction dimension is also split across
-// workgroups (grid.y) and a second kernel sums the partials in a fixed order.
+// workgroups (grid.y) and a second, single-workgroup kernel sums the partials in a fixed
+// order, takes the top-k and (in the fused layer) also bucket-sorts the pairs. A kernel
+// boundary, not an arrival counter, hands the partials over: on this chip a device-scope
+// release in every workgroup writes back the whole L2 of its XCD, which costs far more
+// than a launch.
 #include "common.hpp"
+#include "bucket_dev.hpp"
 #include "kernels.hpp"
 
 namespace moe {
@@ -19,50 +24,147 @@ namespace {
 
 constexpr int kRouteTok = 16;   // tokens per workgroup (one MFMA row tile)
 constexpr int kRouteWaves = 4;
+constexpr int kMaxSplit = 32;   // largest split of the reduction dimension across workgroups
 
 // Top-k of one token's E logits held in LDS, by one wave. Ties go to the lower index;
-// NaN counts as -inf. Writes ids and softmax weights over the chosen k.
+// NaN counts as -inf. Lane l holds the logits of experts l, l + 64, ...; each logit is
+// ranked against all E (broadcast from its lane with readlane):
+//   rank(e) = #{e' : L[e'] > L[e], or L[e'] == L[e] and e' < e},
+// and the experts of rank j < k are the choices, in order. The softmax over the chosen k is
+// z_j = exp(L_j - L_0), sum = z_0 + z_1 + ... (increasing j), w_j = z_j / sum.
+// zs: kMaxK floats of LDS private to the wave. Writes ids and weights (and, if ids_lds is
+// given, a copy of the ids).
 __device__ void wave_topk_softmax(const float* logit, int E, int k, int32_t* ids_out,
-                                  float* w_out) {
+                                  float* w_out, float* zs, int* ids_lds = nullptr) {
   const int lane = threadIdx.x & (kWave - 1);
-  float v[kMaxE / kWave];
+  constexpr int kPer = kMaxE / kWave;
+  const int n_slots = (E + kWave - 1) / kWave;        // wave-uniform
+  float v[kPer];
+  int rank[kPer];
 #pragma unroll
-  for (int i = 0; i < kMaxE / kWave; ++i) {
-    int e = lane + i * kWave;
-    float x = e < E ? logit[e] : -INFINITY;
+  for (int i = 0; i < kPer; ++i) {
+    const int e = lane + i * kWave;
+    const float x = e < E ? logit[e] : -INFINITY;
     v[i] = (x != x) ? -INFINITY : x;
+    rank[i] = 0;
   }
-  uint32_t taken = 0;   // bit i: v[i] already chosen
-  float chosen_v[kMaxK];
-  int chosen_e[kMaxK];
-  for (int j = 0; j < k; ++j) {
-    // best of this lane: largest value, lowest index among equals (indices grow with i)
-    float bv = -INFINITY;
-    int be = 0x7FFFFFFF;
 #pragma unroll
-    for (int i = 0; i < kMaxE / kWave; ++i) {
-      int e = lane + i * kWave;
-      bool ok = e < E && !((taken >> i) & 1u);
-      if (ok && (v[i] > bv || (v[i] == bv && e < be))) { bv = v[i]; be = e; }
-    }
-    // wave arg-max on the key (value desc, index asc)
+  for (int i2 = 0; i2 < kPer; ++i2) {
+    if (i2 >= n_slots) break;
+    const int lim = min(kWave, E - i2 * kWave);
+    for (int l = 0; l < lim; ++l) {
+      const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[i2]), l));
+      const int e2 = i2 * kWave + l;
 #pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) {
-      float ov = __shfl_xor(bv, m, kWave);
-      int oe = __shfl_xor(be, m, kWave);
-      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+      for (int i = 0; i < kPer; ++i) {
+        if (i >= n_slots) break;
+        const int e = lane + i * kWave;
+        rank[i] += (c > v[i] || (c == v[i] && e2 < e)) ? 1 : 0;
+      }
     }
-    chosen_v[j] = bv;
-    chosen_e[j] = be;
-    if ((be & (kWave - 1)) == lane) taken |= 1u << (be / kWave);
   }
-  if (lane == 0) {
-    float z[kMaxK];
-    float sum = 0.f;
-    for (int j = 0; j < k; ++j) { z[j] = expf(chosen_v[j] - chosen_v[0]); sum += z[j]; }
-    for (int j = 0; j < k; ++j) { ids_out[j] = chosen_e[j]; w_out[j] = z[j] / sum; }
+  // the chosen experts' logits, by rank, then the softmax terms in parallel
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = lane + i * kWave;
+    if (i < n_slots && e < E && rank[i] < k) {
+      ids_out[rank[i]] = e;
+      zs[rank[i]] = v[i];
+      if (ids_lds) ids_lds[rank[i]] = e;
+    }
   }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  const float l0 = zs[0];
+  const float z = lane < k ? expf(zs[lane < k ? lane : 0] - l0) : 0.f;
+  float sum = 0.f;
+  for (int j = 0; j < k; ++j) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), j));
+  if (lane < k) w_out[lane] = z / sum;
 }
+
+// Partial logits of tokens [t0, t0 + 16) over this workgroup's share (split z of nsplit) of
+// the reduction dimension, summed over the NW waves in a fixed order into red[0][token][e]
+// (red holds 4 wave slots: with 8 waves, wave w + 4 first adds its tile to wave w's).
+// Each wave issues the loads of RB 32-wide steps before the MFMAs that consume them; rows
+// past T or E are loaded from a valid row and zeroed when consumed.
+template <int NF, int NW, int RB>
+__device__ void router_tile(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+                            int T, int H, int E, int t0, int z, int nsplit,
+                            float (*red)[kRouteTok][NF * 16]) {
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int nsteps = H / 32;
+  const int s_begin = (int)((int64_t)nsteps * z / nsplit);
+  const int s_end = (int)((int64_t)nsteps * (z + 1) / nsplit);
+  const int row = lane & 15;        // token (A) / expert (B) within the 16-tile
+  const int kq = (lane >> 4) * 8;   // this lane's 8-element slice of the 32-step
+  const bool tok_ok = t0 + row < T;
+  const uint16_t* xr = x + (int64_t)(tok_ok ? t0 + row : 0) * H + kq;
+  const uint16_t* wrow[NF];
+  bool e_ok[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    e_ok[f] = f * 16 + row < E;
+    wrow[f] = wr + (int64_t)(e_ok[f] ? f * 16 + row : 0) * H + kq;
+  }
+  f32x4 acc[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const u32x4 zero = {0, 0, 0, 0};
+  for (int s0 = s_begin + wave; s0 < s_end; s0 += NW * RB) {
+    u32x4 a[RB], bq[RB][NF];
+    bool ok[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const int s = s0 + r * NW;
+      ok[r] = s < s_end;
+      const int ss = ok[r] ? s : s_begin;
+      a[r] = *(const u32x4*)(xr + ss * 32);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) bq[r][f] = *(const u32x4*)(wrow[f] + ss * 32);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const bf16x8 av = __builtin_bit_cast(bf16x8, (ok[r] && tok_ok) ? a[r] : zero);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, e_ok[f] ? bq[r][f] : zero);
+        acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[f], 0, 0, 0);
+      }
+    }
+  }
+  // lane holds D[token 4*(lane/16)+v][expert 16f + lane%16]
+  if (wave < 4) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[wave][4 * (lane >> 4) + v][f * 16 + row] = acc[f][v];
+  }
+  __syncthreads();
+  if (NW == 8 && wave >= 4) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[wave - 4][4 * (lane >> 4) + v][f * 16 + row] += acc[f][v];
+  }
+  if (NW == 8) __syncthreads();
+  for (int i = threadIdx.x; i < kRouteTok * NF * 16; i += NW * kWave) {
+    int tt = i / (NF * 16), e = i % (NF * 16);
+    float sum = red[0][tt][e];
+#pragma unroll
+    for (int q = 1; q < 4; ++q) sum += red[q][tt][e];
+    red[0][tt][e] = sum;
+  }
+  __syncthreads();
+}
+
+// Steps per load batch for NF expert tiles: as many as fit in about 144 VGPRs
+// (4 VGPRs per 16-byte operand, 1 + NF operands per step).
+template <int NF>
+constexpr int router_rb() { return 144 / (4 * (1 + NF)) > 0 ? 144 / (4 * (1 + NF)) : 1; }
 
 template <int NF>   // NF = ceil(E / 16) expert tiles
 __global__ __launch_bounds__(256) void k_router(const uint16_t* __restrict__ x,
@@ -72,51 +174,11 @@ __global__ __launch_bounds__(256) void k_router(const uint16_t* __restrict__ x,
                                                 int32_t* __restrict__ ids,
                                                 float* __restrict__ w) {
   __shared__ float red[kRouteWaves][kRouteTok][NF * 16];
-  const int lane = threadIdx.x & (kWave - 1);
+  __shared__ float zs[kRouteWaves][kMaxK];
   const int wave = threadIdx.x / kWave;
   const int t0 = blockIdx.x * kRouteTok;
-  const int nsteps = H / 32;
-  const int ksplit = gridDim.y;
-  const int s_begin = (int)((int64_t)nsteps * blockIdx.y / ksplit);
-  const int s_end = (int)((int64_t)nsteps * (blockIdx.y + 1) / ksplit);
-
-  const int row = lane & 15;        // token (A) / expert (B) within the 16-tile
-  const int kq = (lane >> 4) * 8;   // this lane's 8-element slice of the 32-step
-  const int tok = t0 + row;
-  const bool tok_ok = tok < T;
-  const uint16_t* xr = x + (int64_t)(tok_ok ? tok : 0) * H + kq;
-
-  f32x4 acc[NF];
-#pragma unroll
-  for (int f = 0; f < NF; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int s = s_begin + wave; s < s_end; s += kRouteWaves) {
-    u32x4 a = tok_ok ? *(const u32x4*)(xr + s * 32) : u32x4{0, 0, 0, 0};
-    bf16x8 av = __builtin_bit_cast(bf16x8, a);
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      int e = f * 16 + row;
-      u32x4 b = e < E ? *(const u32x4*)(wr + (int64_t)e * H + kq + s * 32) : u32x4{0, 0, 0, 0};
-      acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, b),
-                                                      acc[f], 0, 0, 0);
-    }
-  }
-  // lane holds D[token 4*(lane/16)+v][expert 16f + lane%16]
-#pragma unroll
-  for (int f = 0; f < NF; ++f)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) red[wave][4 * (lane >> 4) + v][f * 16 + row] = acc[f][v];
-  __syncthreads();
-  // fixed-order sum over waves
-  for (int i = threadIdx.x; i < kRouteTok * NF * 16; i += blockDim.x) {
-    int tt = i / (NF * 16), e = i % (NF * 16);
-    float sum = red[0][tt][e];
-#pragma unroll
-    for (int q = 1; q < kRouteWaves; ++q) sum += red[q][tt][e];
-    red[0][tt][e] = sum;
-  }
-  __syncthreads();
-  if (ksplit > 1) {
+  router_tile<NF, kRouteWaves, router_rb<NF>()>(x, wr, T, H, E, t0, blockIdx.y, gridDim.y, red);
+  if (gridDim.y > 1) {
     float* dst = partial + (int64_t)blockIdx.y * T * E;
     for (int i = threadIdx.x; i < kRouteTok * E; i += blockDim.x) {
       int tt = i / E, e = i % E;
@@ -134,58 +196,168 @@ __global__ __launch_bounds__(256) void k_router(const uint16_t* __restrict__ x,
   for (int tt = wave; tt < kRouteTok; tt += kRouteWaves) {
     if (t0 + tt >= T) break;
     wave_topk_softmax(&red[0][tt][0], E, k, ids + (int64_t)(t0 + tt) * k,
-                      w + (int64_t)(t0 + tt) * k);
+                      w + (int64_t)(t0 + tt) * k, zs[wave]);
   }
 }
 
-// Sum the split-K partial logits in a fixed order, add the bias, take top-k.
-__global__ __launch_bounds__(256) void k_router_finish(const float* __restrict__ partial,
-                                                       int ksplit, const float* __restrict__ bias,
-                                                       int T, int E, int k,
-                                                       int32_t* __restrict__ ids,
-                                                       float* __restrict__ w) {
-  __shared__ float lg[4][kMaxE];
+// Finish a split router for a small batch (T <= 16) in one workgroup: load every split's
+// partial logits (all loads issued before any is used), sum them in increasing split order,
+// add the bias, take top-k and softmax per token, and, with BUCKET, bucket-sort the pairs.
+// partial: [ksplit][T][E]; ksplit * T * E <= kFinishCap.
+constexpr int kFinishCap = 8192;
+template <bool BUCKET>
+__global__ __launch_bounds__(256) void k_router_finish(
+    const float* __restrict__ partial, int ksplit, const float* __restrict__ bias, int T, int E,
+    int k, int32_t* __restrict__ ids, float* __restrict__ w, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm) {
+  __shared__ float flat[kFinishCap];
+  __shared__ float lg[kRouteTok][kMaxE];
+  __shared__ int ids_l[kRouteTok * kMaxK];
+  __shared__ float zs[kRouteWaves][kMaxK];
+  __shared__ int lid[BUCKET ? kRouteTok * kMaxK : 1];
+  __shared__ int hist[BUCKET ? kMaxE : 1], run[BUCKET ? kMaxE : 1];
+  __shared__ int wcnt[BUCKET ? kRouteWaves : 1][kMaxE];
+  __shared__ int tmp[4];
   const int wave = threadIdx.x / kWave;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int t = blockIdx.x * 4 + wave;
-  if (t >= T) return;
-  for (int e = lane; e < E; e += kWave) {
-    float sum = partial[(int64_t)t * E + e];
-    for (int z = 1; z < ksplit; ++z) sum += partial[((int64_t)z * T + t) * E + e];
-    if (bias != nullptr) sum += bias[e];
-    lg[wave][e] = sum;
+  const int te = T * E;
+  const int n = ksplit * te;
+  constexpr int kBatch = 8;
+  for (int base = threadIdx.x; base < n; base += 256 * kBatch) {
+    float v[kBatch];
+#pragma unroll
+    for (int r = 0; r < kBatch; ++r) v[r] = partial[min(base + r * 256, n - 1)];
+#pragma unroll
+    for (int r = 0; r < kBatch; ++r)
+      if (base + r * 256 < n) flat[base + r * 256] = v[r];
   }
-  // the wave's own LDS row: lanes of one wave are in lock-step on wave64 hardware, but
-  // make the ordering explicit anyway
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  wave_topk_softmax(lg[wave], E, k, ids + (int64_t)t * k, w + (int64_t)t * k);
+  __syncthreads();
+  for (int i = threadIdx.x; i < te; i += 256) {
+    float sum = flat[i];
+    for (int z = 1; z < ksplit; ++z) sum += flat[z * te + i];
+    if (bias != nullptr) sum += bias[i % E];
+    lg[i / E][i % E] = sum;
+  }
+  __syncthreads();
+  for (int tt = wave; tt < T; tt += kRouteWaves)
+    wave_topk_softmax(lg[tt], E, k, ids + (int64_t)tt * k, w + (int64_t)tt * k, zs[wave],
+                      ids_l + tt * k);
+  if constexpr (BUCKET) {
+    __syncthreads();
+    bucket_dev::bucket_one_block<256>(ids_l, T * k, E, counts, offsets, perm, inv_perm, lid,
+                                      hist, run, wcnt, tmp);
+  }
+}
+
+// Route and bucket a small batch (T <= 16, E <= 128) in one workgroup of 8 waves: every
+// router load is in flight at once, then top-k and softmax per token, the counting sort of
+// the pairs, and the list of active experts the expert FFN reads:
+//   act[0] = number of non-empty buckets; for j < act[0], entry j at act[1 + 8j]:
+//   {expert e, slot_map[e], offsets[e], offsets[e + 1], token of the expert's first four
+//    pairs (-1 where it has fewer)}   (experts in increasing order).
+// Without BUCKET only ids and w are written (the stand-alone router for small batches, so
+// that it sums in exactly the same order as the fused layer does).
+constexpr int kSmallWaves = 8;
+template <int NF, bool BUCKET>
+__global__ __launch_bounds__(kSmallWaves * kWave) void k_route_small(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+    const float* __restrict__ bias, int T, int H, int E, int k,
+    const int32_t* __restrict__ slot_map, int32_t* __restrict__ ids, float* __restrict__ w,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+    int32_t* __restrict__ inv_perm, int32_t* __restrict__ act) {
+  constexpr int NTH = kSmallWaves * kWave;
+  __shared__ float red[4][kRouteTok][NF * 16];
+  __shared__ int ids_l[kRouteTok * kMaxK];
+  __shared__ int lid[kRouteTok * kMaxK];
+  __shared__ int perm_l[kRouteTok * kMaxK];
+  __shared__ float zs[kSmallWaves][kMaxK];
+  __shared__ int hist[kMaxE], run[kMaxE], wcnt[kSmallWaves][kMaxE], tmp[kSmallWaves];
+  const int wave = threadIdx.x / kWave;
+  const int tid = threadIdx.x;
+  // per-expert values needed at the end, loaded together with the router operands
+  const int ec = tid < E ? tid : 0;
+  const float bv = bias != nullptr ? bias[ec] : 0.f;
+  const int sv = BUCKET ? slot_map[ec] : 0;
+  router_tile<NF, kSmallWaves, router_rb<NF>()>(x, wr, T, H, E, 0, 0, 1, red);
+  if (bias != nullptr && tid < E)
+    for (int tt = 0; tt < T; ++tt) red[0][tt][tid] += bv;
+  __syncthreads();
+  for (int tt = wave; tt < T; tt += kSmallWaves)
+    wave_topk_softmax(&red[0][tt][0], E, k, ids + (int64_t)tt * k, w + (int64_t)tt * k,
+                      zs[wave], ids_l + tt * k);
+  if constexpr (!BUCKET) return;
+  __syncthreads();
+  bucket_dev::bucket_one_block<NTH>(ids_l, T * k, E, counts, offsets, perm, inv_perm, lid, hist,
+                                    run, wcnt, tmp, perm_l);
+  __syncthreads();
+  // after the counting sort: hist[e] = count, run[e] = offsets[e] + count
+  const bool ne = tid < E && hist[tid] > 0;
+  int total;
+  const int rank = bucket_dev::block_exclusive_scan<NTH>(ne ? 1 : 0, tmp, &total);
+  if (ne) {
+    int32_t* a = act + 1 + kActStride * rank;
+    const int lo = run[tid] - hist[tid], hi = run[tid];
+    a[0] = tid;
+    a[1] = sv;
+    a[2] = lo;
+    a[3] = hi;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[4 + i] = lo + i < hi ? perm_l[lo + i] / k : -1;
+  }
+  if (tid == 0) act[0] = total;
 }
 
 }  // namespace
 
 int route_ksplit(int T, int H) {
-  const int nsteps = H / 32;
-  if (T > 64) return 1;
-  int ks = nsteps / 4;
-  if (ks < 1) ks = 1;
-  if (ks > 32) ks = 32;
-  return ks;
+  if (T > kRouteTok) return 1;
+  int ks = (H / 32) / 4;
+  ks = min(ks, kMaxSplit);
+  ks = min(ks, kFinishCap / (T * kMaxE));
+  return max(ks, 1);
 }
 
-hipError_t launch_route(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H,
-                        int E, int k, int32_t* ids, float* w, float* partial,
-                        hipStream_t stream) {
+bool route_bucket_fusable(int T, int E) { return T >= 1 && T <= kRouteTok; }
+
+bool route_small_ok(int T, int E) { return T >= 1 && T <= kRouteTok && E <= 128; }
+
+hipError_t launch_route_small(const uint16_t* x, const uint16_t* wr, const float* bias, int T,
+                              int H, int E, int k, const int32_t* slot_map, int32_t* ids,
+                              float* w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                              int32_t* inv_perm, int32_t* act, hipStream_t stream) {
+  if (!route_small_ok(T, E)) return hipErrorInvalidValue;
+  const bool bucket = counts != nullptr;
+#define MOE_SMALL_CASE(N)                                                                       \
+  case N:                                                                                      \
+    if (bucket)                                                                                \
+      hipLaunchKernelGGL((k_route_small<N, true>), dim3(1), dim3(kSmallWaves * kWave), 0,       \
+                         stream, x, wr, bias, T, H, E, k, slot_map, ids, w, counts, offsets,    \
+                         perm, inv_perm, act);                                                  \
+    else                                                                                       \
+      hipLaunchKernelGGL((k_route_small<N, false>), dim3(1), dim3(kSmallWaves * kWave), 0,      \
+                         stream, x, wr, bias, T, H, E, k, slot_map, ids, w, counts, offsets,    \
+                         perm, inv_perm, act);                                                  \
+    break;
+  switch ((E + 15) / 16) {
+    MOE_SMALL_CASE(1) MOE_SMALL_CASE(2) MOE_SMALL_CASE(3) MOE_SMALL_CASE(4)
+    MOE_SMALL_CASE(5) MOE_SMALL_CASE(6) MOE_SMALL_CASE(7) MOE_SMALL_CASE(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef MOE_SMALL_CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_route_impl(const uint16_t* x, const uint16_t* wr, const float* bias, int T,
+                             int H, int E, int k, int32_t* ids, float* w, float* partial,
+                             int32_t* counts, int32_t* offsets, int32_t* perm,
+                             int32_t* inv_perm, bool bucket, hipStream_t stream) {
   const int ks = route_ksplit(T, H);
   dim3 grid((T + kRouteTok - 1) / kRouteTok, ks);
-  const int nf = (E + 15) / 16;
 #define MOE_ROUTER_CASE(N)                                                                  \
   case N:                                                                                  \
-    hipLaunchKernelGGL(k_router<N>, grid, dim3(256), 0, stream, x, wr, bias, T, H, E, k, \
+    hipLaunchKernelGGL(k_router<N>, grid, dim3(256), 0, stream, x, wr, bias, T, H, E, k,   \
                        partial, ids, w);                                                   \
     break;
-  switch (nf) {
+  switch ((E + 15) / 16) {
     MOE_ROUTER_CASE(1) MOE_ROUTER_CASE(2) MOE_ROUTER_CASE(3) MOE_ROUTER_CASE(4)
     MOE_ROUTER_CASE(5) MOE_ROUTER_CASE(6) MOE_ROUTER_CASE(7) MOE_ROUTER_CASE(8)
     MOE_ROUTER_CASE(9) MOE_ROUTER_CASE(10) MOE_ROUTER_CASE(11) MOE_ROUTER_CASE(12)
@@ -195,9 +367,37 @@ hipError_t launch_route(const uint16_t* x, const uint16_t* wr, const float* bias
 #undef MOE_ROUTER_CASE
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || ks == 1) return err;
-  hipLaunchKernelGGL(k_router_finish, dim3((T + 3) / 4), dim3(256), 0, stream, partial, ks,
-                     bias, T, E, k, ids, w);
+  if (bucket)
+    hipLaunchKernelGGL(k_router_finish<true>, dim3(1), dim3(256), 0, stream, partial, ks, bias,
+                       T, E, k, ids, w, counts, offsets, perm, inv_perm);
+  else
+    hipLaunchKernelGGL(k_router_finish<false>, dim3(1), dim3(256), 0, stream, partial, ks, bias,
+                       T, E, k, ids, w, nullptr, nullptr, nullptr, nullptr);
   return hipGetLastError();
+}
+
+hipError_t launch_route(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H,
+                        int E, int k, int32_t* ids, float* w, float* partial,
+                        hipStream_t stream) {
+  if (route_small_ok(T, E))   // same kernel, same summation order as the fused layer
+    return launch_route_small(x, wr, bias, T, H, E, k, nullptr, ids, w, nullptr, nullptr,
+                              nullptr, nullptr, nullptr, stream);
+  return launch_route_impl(x, wr, bias, T, H, E, k, ids, w, partial, nullptr, nullptr, nullptr,
+                           nullptr, false, stream);
+}
+
+hipError_t launch_route_bucket_small(const uint16_t* x, const uint16_t* wr, const float* bias,
+                                     int T, int H, int E, int k, float* partial, int32_t* ids,
+                                     float* w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                                     int32_t* inv_perm, hipStream_t stream) {
+  if (!route_bucket_fusable(T, E)) return hipErrorInvalidValue;
+  if (route_ksplit(T, H) == 1) {   // nothing to finish: router, then the counting sort
+    hipError_t e = launch_route(x, wr, bias, T, H, E, k, ids, w, partial, stream);
+    if (e != hipSuccess) return e;
+    return launch_bucket(ids, T * k, E, counts, offsets, perm, inv_perm, nullptr, stream);
+  }
+  return launch_route_impl(x, wr, bias, T, H, E, k, ids, w, partial, counts, offsets, perm,
+                           inv_perm, true, stream);
 }
 
 }  // namespace moe

@@ -53,7 +53,7 @@ class Pool(ctypes.Structure):
 
 class Ws(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("total", "topk_ids", "topk_w", "counts", "offsets",
-                                               "perm", "inv_perm", "h", "y", "scratch")]
+                                               "perm", "inv_perm", "h", "y", "scratch", "act")]
 
 
 def _setup(lib):
@@ -102,11 +102,13 @@ def test_route_argument_checks(lib):
     assert f(MISALIGNED, FAKE, None, 4, 64, 8, 2, FAKE, FAKE, None, 0, None) == INVALID
     # T = 0: nothing to do
     assert f(None, None, None, 0, 64, 8, 2, None, None, None, 0, None) == OK
-    # split-K scratch required for small T and missing
-    need = lib.moe_route_scratch_bytes(1, 2880, 32)
+    # small batches with E <= 128 are routed by one workgroup: no scratch
+    assert lib.moe_route_scratch_bytes(1, 2880, 32) == 0
+    # with more experts the reduction is split across workgroups: scratch required
+    need = lib.moe_route_scratch_bytes(1, 2880, 256)
     assert need > 0
-    assert f(FAKE, FAKE, None, 1, 2880, 32, 4, FAKE, FAKE, None, 0, None) == INVALID
-    assert f(FAKE, FAKE, None, 1, 2880, 32, 4, FAKE, FAKE, FAKE, need - 1, None) == INVALID
+    assert f(FAKE, FAKE, None, 1, 2880, 256, 4, FAKE, FAKE, None, 0, None) == INVALID
+    assert f(FAKE, FAKE, None, 1, 2880, 256, 4, FAKE, FAKE, FAKE, need - 1, None) == INVALID
 
 
 def test_bucket_argument_checks(lib):
@@ -155,7 +157,8 @@ def test_ffn_and_layer_argument_checks(lib):
     lib.moe_layer_workspace.argtypes = [ctypes.c_int32] * 5 + [ctypes.POINTER(Ws)]
     assert lib.moe_layer_workspace(3, 64, 32, 4, 2, ctypes.byref(ws)) == OK
     assert ws.total >= 3 * 2 * (32 * 2 + 64 * 4)
-    for name in ("topk_ids", "topk_w", "counts", "offsets", "perm", "inv_perm", "h", "y", "scratch"):
+    for name in ("topk_ids", "topk_w", "counts", "offsets", "perm", "inv_perm", "h", "y", "scratch",
+                 "act"):
         assert getattr(ws, name) % 256 == 0
     # workspace too small
     assert g(ctypes.byref(p), FAKE, FAKE, None, FAKE, 3, 4, 2, FAKE, FAKE, ws.total - 1, None, 0,
@@ -176,3 +179,18 @@ def test_pack_argument_checks(lib):
     assert f(3, 1, 32, 64, FAKE, FAKE, FAKE, FAKE, None) == UNSUPPORTED
     assert f(2, 1, 32, 64, FAKE, ctypes.c_void_p(0x10001), FAKE, FAKE, None) == INVALID
     assert f(1, 0, 32, 64, None, None, None, None, None) == OK
+
+
+def test_workspace_layout_struct_matches_library(lib):
+    """moe_layer_workspace writes exactly len(Ws._fields_) size_t values (no more)."""
+    SENT = 0xDEADBEEFCAFE
+    buf = (ctypes.c_size_t * 32)(*([SENT] * 32))
+    lib.moe_layer_workspace.argtypes = [ctypes.c_int32] * 5 + [ctypes.c_void_p]
+    assert lib.moe_layer_workspace(3, 64, 32, 4, 2, ctypes.cast(buf, ctypes.c_void_p)) == OK
+    n = len(Ws._fields_)
+    assert all(buf[i] != SENT for i in range(n))
+    assert all(buf[i] == SENT for i in range(n, 32))
+    pytest.importorskip("torch")
+    import quantized_routed_expert_gemv_amd as qm
+    assert [f[0] for f in qm.WsLayout._fields_] == [f[0] for f in Ws._fields_]
+

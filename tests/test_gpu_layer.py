@@ -169,3 +169,60 @@ def test_layer_in_a_hip_graph_matches_eager():
         o2, _ = qm.layer(pool, sm, wr, bias, x, cfg.k)
         torch.cuda.synchronize()
         assert torch.equal(o2, eager)
+
+
+def _stages(pool, sm, wr, bias, x, k, path):
+    ids, w = qm.route(x, wr, bias, k)
+    counts, offsets, perm, inv = qm.bucket(ids, wr.shape[0])
+    h, y = qm.expert_ffn(pool, sm, x, k, offsets, perm, path=path)
+    return qm.combine(y, inv, w), ids, w, perm, h, y
+
+
+@pytest.mark.parametrize("name,T,path", [("gptoss_decode_t4", 1, qm.PATH_GEMV),
+                                         ("gptoss_decode_t4", 4, qm.PATH_GEMV),
+                                         ("qwen_a3b_decode", 16, qm.PATH_GEMV),
+                                         ("mixtral_q8_decode", 3, qm.PATH_GEMV),
+                                         ("tiny", 12, qm.PATH_GROUPED),
+                                         ("tiny", 64, qm.PATH_AUTO)])
+def test_layer_equals_its_stages_bit_exact(name, T, path):
+    """The fused call (router finished and bucketed by one kernel) equals the stage calls."""
+    cfg = synth.config(name, T=T)
+    L = make_case(cfg)
+    pool, x, wr, bias, sm = to_device(L)
+    ref, ids, w, perm, h, y = _stages(pool, sm, wr, bias, x, cfg.k, path)
+    out, ws = qm.layer(pool, sm, wr, bias, x, cfg.k, path=path)
+    torch.cuda.synchronize()
+    im = ws.intermediates()
+    assert torch.equal(im["ids"], ids) and torch.equal(im["w"], w)
+    assert torch.equal(im["perm"], perm)
+    assert torch.equal(im["h"], h) and torch.equal(im["y"], y)
+    assert torch.equal(out, ref)
+
+
+def test_layer_timed_equals_layer_and_records_events():
+    cfg = synth.CONFIGS["gptoss_decode_t1"]
+    L = make_case(cfg)
+    pool, x, wr, bias, sm = to_device(L)
+    ref, ws = qm.layer(pool, sm, wr, bias, x, cfg.k)
+    ref = ref.clone()
+    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    out = torch.empty_like(ref)
+    call = qm.LayerCall(pool, sm, wr, bias, x, cfg.k, out, ws, events=ev)
+    for _ in range(3):
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+        assert ev[0].elapsed_time(ev[1]) > 0
+
+
+def test_workspace_reuse_across_batch_sizes():
+    """One workspace, sized for the largest T, serves smaller batches in turn."""
+    cfg = synth.config("qwen_a3b_decode", T=16)
+    L = make_case(cfg)
+    pool, x, wr, bias, sm = to_device(L)
+    ws = qm.Workspace(16, cfg.H, cfg.I, cfg.E, cfg.k)
+    for T in (16, 1, 5, 16, 2):
+        fresh, _ = qm.layer(pool, sm, wr, bias, x[:T].contiguous(), cfg.k)
+        got, _ = qm.layer(pool, sm, wr, bias, x[:T].contiguous(), cfg.k, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(got, fresh), T
