@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--mode", choices=("graph", "eager"), default="graph",
                     help="graph: the step's layer calls are captured once into a HIP graph "
                          "and replayed; eager: every layer call is launched from the host")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="time budget of the CPU-oracle baseline sample (0 disables it)")
     return ap.parse_args()
 
@@ -274,7 +274,7 @@ def cpu_baseline(cfg, host_layers, budget_s):
     tokens = 0
     layers_done = 0
     sample_T = T
-    while time.perf_counter() - t0 < budget_s and layers_done < 4 * len(host_layers):
+    while time.perf_counter() - t0 < budget_s and layers_done < 400:
         L = host_layers[layers_done % len(host_layers)]
         x = L.x
         if T > 64:                           # prefill: a bounded token sample
