@@ -85,6 +85,8 @@ void pool_views(const moe_pool* p, moe::PoolView* g, moe::PoolView* u, moe::Pool
 }
 
 size_t route_scratch(int32_t T, int32_t H, int32_t E) {
+  if (moe::route_fused_ok(T, H, E))          // split router, finished by a later kernel
+    return (size_t)moe::route_fused_split(H) * T * E * sizeof(float);
   if (moe::route_small_ok(T, E)) return 0;   // one workgroup, no partials
   const int ks = moe::route_ksplit(T, H);
   return ks > 1 ? (size_t)ks * T * E * sizeof(float) : 0;
@@ -335,6 +337,29 @@ moe_status moe_layer_workspace(int32_t T, int32_t H, int32_t I, int32_t E, int32
   return ok();
 }
 
+// Down projection and combine of the fused layer. With the small-batch active-expert list
+// (act != NULL) and few pairs, one kernel does both.
+static moe_status down_combine_tail(const moe_pool* pool, const int32_t* slot_map, int32_t E,
+                                    int32_t T, int32_t k, const int32_t* offsets,
+                                    const int32_t* act, const uint16_t* h,
+                                    const int32_t* inv_perm, const float* w, float* y,
+                                    float* out, uint32_t* err_flags, int32_t path,
+                                    hipStream_t st) {
+  if (act != nullptr && use_gemv(path, T) && moe::down_combine_small_ok(T, k, E, pool->I)) {
+    clear_stale_error();
+    moe::PoolView g, u, d;
+    pool_views(pool, &g, &u, &d);
+    return hip_status(moe::launch_down_combine_small(pool->fmt, d, pool->n_slots, E, T, k, pool->H,
+                                                     pool->I, act, h, inv_perm, w, y, out,
+                                                     err_flags, st),
+                      "down+combine");
+  }
+  moe_status s = down_dispatch(pool, slot_map, E, T, k, offsets, h, y, err_flags, path, st);
+  if (s != MOE_OK) return s;
+  clear_stale_error();
+  return hip_status(moe::launch_combine(y, inv_perm, w, T, k, pool->H, out, st), "combine");
+}
+
 // Record a timing event; inside a stream capture it becomes an event-record node of the
 // graph (so replays can still be timed).
 static moe_status record_event(hipEvent_t ev, hipStream_t st) {
@@ -390,7 +415,37 @@ static moe_status layer_impl(const moe_pool* pool, const int32_t* slot_map,
   clear_stale_error();
   // route + bucket: for small batches the split router is finished (top-k and counting
   // sort) by one single-workgroup kernel; otherwise router, then the counting sort
-  if (moe::route_small_ok(T, E)) {
+  const bool gemv = use_gemv(path, T);
+  if (moe::route_fused_ok(T, pool->H, E)) {
+    // router partials over slices of H; the gate/up GEMV finishes the routing itself (or,
+    // for the grouped path, one workgroup finishes it and bucket-sorts)
+    const int ns = moe::route_fused_split(pool->H);
+    e = moe::launch_router_partials(x, w_router, T, pool->H, E, ns, (float*)scratch, st);
+    if (e != hipSuccess) return hip_status(e, "router");
+    if (gemv) {
+      if (ev_begin != nullptr) {
+        s = record_event((hipEvent_t)ev_begin, st);
+        if (s != MOE_OK) return s;
+      }
+      moe::PoolView g, u, d;
+      pool_views(pool, &g, &u, &d);
+      const moe::RouteIn rin{(const float*)scratch, ns, bias, T, ids, w, counts, offsets, perm,
+                             inv_perm, act};
+      clear_stale_error();
+      e = moe::launch_gate_up_route(pool->fmt, g, u, slot_map, pool->n_slots, E, x, T, k,
+                                    pool->H, pool->I, rin, h, err_flags, st);
+      if (e != hipSuccess) return hip_status(e, "route + gate/up (GEMV)");
+      if (ev_end != nullptr) {
+        s = record_event((hipEvent_t)ev_end, st);
+        if (s != MOE_OK) return s;
+      }
+      return down_combine_tail(pool, slot_map, E, T, k, offsets, act, h, inv_perm, w, y, out,
+                               err_flags, path, st);
+    }
+    e = moe::launch_router_finish((const float*)scratch, ns, bias, T, E, k, ids, w, counts,
+                                  offsets, perm, inv_perm, st);
+    if (e != hipSuccess) return hip_status(e, "route+bucket");
+  } else if (moe::route_small_ok(T, E)) {
     // one workgroup: router, top-k, counting sort and the active-expert list
     e = moe::launch_route_small(x, w_router, bias, T, pool->H, E, k, slot_map, ids, w, counts,
                                 offsets, perm, inv_perm, act, st);
@@ -417,19 +472,8 @@ static moe_status layer_impl(const moe_pool* pool, const int32_t* slot_map,
     s = record_event((hipEvent_t)ev_end, st);
     if (s != MOE_OK) return s;
   }
-  if (have_act && use_gemv(path, T) && moe::down_combine_small_ok(T, k, E, pool->I)) {
-    clear_stale_error();
-    moe::PoolView g, u, d;
-    pool_views(pool, &g, &u, &d);
-    return hip_status(moe::launch_down_combine_small(pool->fmt, d, pool->n_slots, E, T, k, pool->H,
-                                                     pool->I, act, h, inv_perm, w, y, out,
-                                                     err_flags, st),
-                      "down+combine");
-  }
-  s = down_dispatch(pool, slot_map, E, T, k, offsets, h, y, err_flags, path, st);
-  if (s != MOE_OK) return s;
-  clear_stale_error();
-  return hip_status(moe::launch_combine(y, inv_perm, w, T, k, pool->H, out, st), "combine");
+  return down_combine_tail(pool, slot_map, E, T, k, offsets, have_act ? act : nullptr, h,
+                           inv_perm, w, y, out, err_flags, path, st);
 }
 
 moe_status moe_layer(const moe_pool* pool, const int32_t* slot_map, const uint16_t* w_router,

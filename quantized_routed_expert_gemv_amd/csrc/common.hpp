@@ -109,6 +109,29 @@ __host__ __device__ constexpr int64_t scale_bytes_per_block(int fmt) { return fm
 // Active-expert list written by the small-batch router (see route.hip): act[0] = count,
 // then kActStride int32 per active expert.
 constexpr int kActStride = 8;
+
+// A split router's partial logits handed to the kernel that finishes the routing (the
+// decode gate/up kernel), and where that kernel stores the routing it computes.
+//   partial [ns][T][E] fp32; ids, w [T][k]; counts [E]; offsets [E+1]; perm, inv_perm [T*k];
+//   act: the active-expert list (1 + kActStride * E int32).
+constexpr int kMaxRouteSplit = 32;   // most splits of the router's reduction dimension
+constexpr int kFuseMaxT = 4;         // most tokens a fused routing prologue handles
+constexpr int kFuseMaxTE = 256;      // most (token, expert) logits it handles
+constexpr int kFuseMaxPairs = kFuseMaxT * kMaxK;
+constexpr int kRouteMaxH = 4096;    // largest H whose activation rows it stages whole
+struct RouteIn {
+  const float* partial;
+  int ns;
+  const float* bias;
+  int T;
+  int32_t* ids;
+  float* w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* inv_perm;
+  int32_t* act;
+};
 __host__ __device__ constexpr int act_ints(int E) { return 1 + kActStride * E; }
 
 struct PoolView {

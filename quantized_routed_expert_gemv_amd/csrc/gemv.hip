@@ -21,6 +21,7 @@
 #include "common.hpp"
 #include "bucket_dev.hpp"
 #include "kernels.hpp"
+#include "topk_dev.hpp"
 
 namespace moe {
 
@@ -134,7 +135,12 @@ struct LaneMap {
   }
 };
 
-template <int FMT, bool GATED, bool ACT, int NT>
+// Where a workgroup learns its expert, bucket range and tokens:
+//   kSrcOffsets  bucket offsets (+ perm) from a previous stage
+//   kSrcAct      the small-batch router's active-expert list
+constexpr int kSrcOffsets = 0, kSrcAct = 1;
+
+template <int FMT, bool GATED, int SRC, int NT>
 __global__ __launch_bounds__(kGThreads) void k_gemv(
     const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as, int64_t a_qslot,
     int64_t a_sslot, const uint8_t* __restrict__ bq, const uint8_t* __restrict__ bs,
@@ -152,7 +158,7 @@ __global__ __launch_bounds__(kGThreads) void k_gemv(
   const int rg = blockIdx.x;
   int e, lo, hi, slot;
   int atok[4] = {0, 0, 0, 0};
-  if constexpr (ACT) {
+  if constexpr (SRC == kSrcAct) {
     // the small-batch router's active list: one round trip for expert, slot, range, tokens
     const int32_t* a = act + 1 + kActStride * blockIdx.y;
     const int n_act = act[0];
@@ -202,7 +208,7 @@ __global__ __launch_bounds__(kGThreads) void k_gemv(
         if constexpr (GATED) {
           // first chunk of the bucket: tokens come with the active list (past the bucket's
           // end, any valid row: those results are never stored)
-          if (ACT && i < 4 && c0 == lo) row = c0 + i < hi ? atok[i & 3] : atok[0];
+          if (SRC != kSrcOffsets && i < 4 && c0 == lo) row = c0 + i < hi ? atok[i & 3] : atok[0];
           else row = perm[pos] / k;
         }
         xrow[i] = src + row * K;
@@ -357,17 +363,27 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
   __shared__ float red[kDCWaves][kDCMaxPairs][16];
   __shared__ float yl[kDCMaxPairs][16];
   __shared__ int actl[1 + kActStride * kDCMaxPairs];
+  __shared__ float tw_l[kDCMaxPairs];
+  __shared__ int ip_l[kDCMaxPairs];
   __shared__ int tmp[kDCWaves];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int rg = blockIdx.x;
   const int r0 = rg * 16;
   const int np = T * k;
-  // 1. active list and all h rows (independent loads, issued together)
+  const int nb = I / 32;
+  const int nc = (nb + LM::kBlocksPerChunk - 1) / LM::kBlocksPerChunk;
+  constexpr int64_t cb = code_bytes_per_block(FMT), sb = scale_bytes_per_block(FMT);
+  const int64_t unit0 = (int64_t)rg * nb * 16;
+  const int lane_unit = FMT == kMXFP4 ? lane : (lane >> 1);
+  const int lblk = LM::blk(lane);
+  const int koff = LM::koff(lane);
+  // 1. one round trip: the active list (or the offsets), every h row, the gate weights and
+  //    the inverse permutation (independent loads, issued together)
   const int na_ints = 1 + kActStride * min(min(np, E), kDCMaxPairs);   // entries that exist
   int av = 0, olo = 0, ohi = 0, osl = 0;
   if (act != nullptr) {
-    av = act[min((int)threadIdx.x, na_ints - 1)];
+    av = act[min(lane, na_ints - 1)];   // every wave reads the list's first 64 ints itself
   } else {
     const int ec = threadIdx.x < E ? threadIdx.x : 0;
     olo = offsets[ec];
@@ -380,8 +396,46 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
 #pragma unroll
   for (int r = 0; r < kHPieces; ++r)
     hv[r] = *(const u32x4*)(h + (int64_t)min((int)threadIdx.x + r * NTH, hp - 1) * 8);
+  float twv = 0.f;
+  int ipv = 0;
+  if constexpr (COMBINE) {
+    const int pc = min((int)threadIdx.x, np - 1);
+    twv = topk_w[pc];
+    ipv = inv_perm[pc];
+  }
+  // 2. with the list in registers each wave knows its (expert j, share q) and issues its
+  //    first batch of weight loads before the h rows reach LDS
+  int n_act = 0, per = 1, j = 0, q = 0, slot = 0, lo = 0, hi = 0;
   if (act != nullptr) {
-    if (threadIdx.x < na_ints) actl[threadIdx.x] = av;
+    n_act = __builtin_amdgcn_readlane(av, 0);   // lane 0 holds act[0]
+    n_act = min(max(n_act, 1), kDCWaves);
+    per = kDCWaves / n_act;
+    j = wave % n_act;
+    q = wave / n_act;
+    slot = __builtin_amdgcn_readlane(av, 1 + kActStride * j + 1);
+    lo = __builtin_amdgcn_readlane(av, 1 + kActStride * j + 2);
+    hi = __builtin_amdgcn_readlane(av, 1 + kActStride * j + 3);
+  }
+  bool busy = q < per;
+  bool valid = slot >= 0 && slot < n_slots;
+  const uint8_t* qa = dq + (valid ? slot : 0) * qslot + unit0 * cb + lane * 16;
+  const uint8_t* sa = ds + (valid ? slot : 0) * sslot + (unit0 + lane_unit) * sb;
+  Chunk ch[kDCU];
+  auto load_batch = [&](int cbase) {
+#pragma unroll
+    for (int u = 0; u < kDCU; ++u) {
+      const int c = cbase + u * per;
+      const int b = c * LM::kBlocksPerChunk + lblk;
+      const bool ok = c < nc && b < nb;
+      const int cs = ok ? c : 0;
+      load_chunk<FMT>(ch[u], qa + (int64_t)cs * 1024, sa + (int64_t)cs * 64, ok);
+    }
+  };
+  if (act != nullptr && busy && valid) load_batch(q);
+  __builtin_amdgcn_sched_barrier(0);
+  // 3. h rows, list and combine inputs into LDS
+  if (act != nullptr) {
+    if (wave == 0 && lane < na_ints) actl[lane] = av;
   } else {
     const bool ne = (int)threadIdx.x < E && ohi > olo;
     int total;
@@ -395,46 +449,39 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
     }
     if (threadIdx.x == 0) actl[0] = total;
   }
+  if constexpr (COMBINE) {
+    if ((int)threadIdx.x < np) {
+      tw_l[threadIdx.x] = twv;
+      ip_l[threadIdx.x] = ipv;
+    }
+  }
 #pragma unroll
   for (int r = 0; r < kHPieces; ++r) {
     const int i = threadIdx.x + r * NTH;
     if (i < hp) *(u32x4*)&hs[i * 8] = hv[r];
   }
   __syncthreads();
-  const int n_act = actl[0];
-  // 2. wave -> (active expert j, its q-th share of the chunks)
-  const int per = kDCWaves / n_act;              // waves per expert (n_act <= 8)
-  const int j = wave % n_act;
-  const int q = wave / n_act;
-  const bool busy = q < per;
-  const int* ent = &actl[1 + kActStride * j];
-  const int slot = ent[1], lo = ent[2], hi = ent[3];
-  const bool valid = slot >= 0 && slot < n_slots;
-  const int nb = I / 32;
-  const int nc = (nb + LM::kBlocksPerChunk - 1) / LM::kBlocksPerChunk;
-  constexpr int64_t cb = code_bytes_per_block(FMT), sb = scale_bytes_per_block(FMT);
-  const int64_t unit0 = (int64_t)rg * nb * 16;
-  const int lane_unit = FMT == kMXFP4 ? lane : (lane >> 1);
-  const int sl = valid ? slot : 0;
-  const uint8_t* qa = dq + sl * qslot + unit0 * cb + lane * 16;
-  const uint8_t* sa = ds + sl * sslot + (unit0 + lane_unit) * sb;
-  const int lblk = LM::blk(lane);
-  const int koff = LM::koff(lane);
+  if (act == nullptr) {
+    n_act = actl[0];
+    per = kDCWaves / n_act;
+    j = wave % n_act;
+    q = wave / n_act;
+    const int* ent = &actl[1 + kActStride * j];
+    slot = ent[1];
+    lo = ent[2];
+    hi = ent[3];
+    busy = q < per;
+    valid = slot >= 0 && slot < n_slots;
+    qa = dq + (valid ? slot : 0) * qslot + unit0 * cb + lane * 16;
+    sa = ds + (valid ? slot : 0) * sslot + (unit0 + lane_unit) * sb;
+    if (busy && valid) load_batch(q);
+  }
+  // 4. consume each batch as it arrives, then load the next
   float acc[kDCMaxPairs];
 #pragma unroll
   for (int p = 0; p < kDCMaxPairs; ++p) acc[p] = 0.f;
   if (busy && valid) {
-    for (int cbase = q; cbase < nc; cbase += per * kDCU) {
-      Chunk ch[kDCU];
-#pragma unroll
-      for (int u = 0; u < kDCU; ++u) {
-        const int c = cbase + u * per;
-        const int b = c * LM::kBlocksPerChunk + lblk;
-        const bool ok = c < nc && b < nb;
-        const int cs = ok ? c : 0;
-        load_chunk<FMT>(ch[u], qa + (int64_t)cs * 1024, sa + (int64_t)cs * 64, ok);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+    for (int cbase = q;;) {
 #pragma unroll
       for (int u = 0; u < kDCU; ++u) {
         const int c = cbase + u * per;
@@ -458,9 +505,13 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
           }
         }
       }
+      cbase += per * kDCU;
+      if (cbase >= nc) break;
+      load_batch(cbase);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
-  // 3. rows of the wave's partials, then fixed-order sums over the waves of each expert
+  // 5. rows of the wave's partials, then fixed-order sums over the waves of each expert
 #pragma unroll
   for (int p = 0; p < kDCMaxPairs; ++p) {
     float v = acc[p];
@@ -499,15 +550,265 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
   if (!valid && busy && q == 0 && lane == 0 && err_flags) atomicOr(err_flags, 1u);
   if constexpr (!COMBINE) return;
   __syncthreads();
-  // 4. combine, in increasing j, as k_combine does
+  // 6. combine, in increasing j, as k_combine does
   if (threadIdx.x < T * 16) {
     const int t = threadIdx.x / 16, r = threadIdx.x % 16;
     float a = 0.f;
     for (int jj = 0; jj < k; ++jj) {
       const int p = t * k + jj;
-      a = fmaf(topk_w[p], yl[inv_perm[p]][r], a);
+      a = fmaf(tw_l[p], yl[ip_l[p]][r], a);
     }
     out[(int64_t)t * H + r0 + r] = a;
+  }
+}
+
+// Decode gate/up that first finishes a split router (1 <= T <= 4 tokens, H <= kRouteMaxH).
+//
+// The router's partial logits (one set per slice of H) come from the previous kernel.
+// Every workgroup finishes the routing itself from them -- sum in split order, top-k per
+// token, counting sort of the T*k pairs, list of active experts -- so no workgroup waits
+// for another; workgroup (0, 0) also stores the routing for the stages after this kernel.
+// Everything that does not depend on the routing (the partials, the slot map, the bias and
+// the tokens' activation rows) is loaded in one round trip at the start; then the expert's
+// gate and up rows of this row group are streamed and each chunk is consumed as it
+// arrives. Chunk order, per-lane accumulation and the reduction are those of k_gemv, so
+// the two give bit-identical h.
+template <int FMT, int NT>
+__global__ __launch_bounds__(kGThreads) void k_gate_up_routed(
+    const uint8_t* __restrict__ gq, const uint8_t* __restrict__ gsc,
+    const uint8_t* __restrict__ uq, const uint8_t* __restrict__ usc, int64_t qslot,
+    int64_t sslot, const int32_t* __restrict__ slot_map, int n_slots, int E, int k,
+    const uint16_t* __restrict__ x, int H, int I, uint16_t* __restrict__ h_out,
+    uint32_t* __restrict__ err_flags, RouteIn rin) {
+  using LM = LaneMap<FMT>;
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  __shared__ __attribute__((aligned(16))) uint16_t xs[NT * kRouteMaxH];
+  __shared__ float lg_l[kFuseMaxTE];
+  __shared__ int slot_l[kMaxE];
+  __shared__ TopkScratch tk_l[NT];
+  __shared__ int ids_l[kFuseMaxPairs];
+  __shared__ float w_l[kFuseMaxPairs];
+  __shared__ __attribute__((aligned(16))) int key_l[kFuseMaxPairs];
+  __shared__ int perm_l[kFuseMaxPairs], inv_l[kFuseMaxPairs], tokp_l[kFuseMaxPairs];
+  __shared__ unsigned long long hit_l[kMaxE / 64];
+  __shared__ int act_l[kFuseMaxPairs][kActStride];
+  __shared__ int nact_l;
+  __shared__ float red[kGWaves][NT][2][16];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int T = rin.T, TE = T * E, ns = rin.ns, n = T * k;
+
+  // 1. one round trip: partials of logit tid, slot and bias of expert tid, activation rows
+  const int ic = tid < TE ? tid : 0;
+  float v[kMaxRouteSplit];
+#pragma unroll
+  for (int z = 0; z < kMaxRouteSplit; ++z) v[z] = rin.partial[(int64_t)min(z, ns - 1) * TE + ic];
+  const int ec = tid < E ? tid : 0;
+  const int sm = slot_map[ec];
+  const float bz = rin.bias != nullptr ? rin.bias[ic % E] : 0.f;
+  constexpr int kXP = NT * kRouteMaxH / 8 / kGThreads;   // 16-byte pieces per thread
+  const int xp_n = T * H / 8;
+  u32x4 xv[kXP];
+#pragma unroll
+  for (int r = 0; r < kXP; ++r)
+    xv[r] = *(const u32x4*)(x + (int64_t)min(tid + r * kGThreads, xp_n - 1) * 8);
+  if (tid < kMaxE / 64) hit_l[tid] = 0ull;
+  if (tid < E) slot_l[tid] = sm;
+  if (tid < TE) lg_l[tid] = finish_logit(v, ns, bz);
+#pragma unroll
+  for (int r = 0; r < kXP; ++r) {
+    const int i = tid + r * kGThreads;
+    if (i < xp_n) *(u32x4*)&xs[i * 8] = xv[r];
+  }
+  __syncthreads();
+
+  // 2. top-k + softmax, wave t for token t
+  if (wave < T) wave_topk_softmax(&lg_l[wave * E], E, k, ids_l + wave * k, w_l + wave * k, tk_l[wave]);
+  __syncthreads();
+
+  // 3. counting sort of the n = T*k pairs by wave 0. Pair p (expert e_p) has the unique key
+  //    32*e_p + p; its bucket position is the number of smaller keys, its expert's range
+  //    [lo, hi) the numbers of keys below 32*e_p and below 32*(e_p + 1), and its expert's
+  //    index among the active ones the number of hit experts below e_p.
+  if (wave == 0) {
+    const bool has = lane < n;
+    const int ep = has ? ids_l[lane] : 0;
+    const int key = has ? ep * kFuseMaxPairs + lane : 0x7fffffff;
+    if (lane < kFuseMaxPairs) key_l[lane] = key;
+    if (has) atomicOr(&hit_l[ep >> 6], 1ull << (ep & 63));
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    const int klo = ep * kFuseMaxPairs, khi = klo + kFuseMaxPairs;
+    int pos = 0, lo = 0, hi = 0;
+    for (int q = 0; q < n; q += 4) {
+      const i32x4 kq = *(const i32x4*)&key_l[q];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        pos += kq[c] < key ? 1 : 0;
+        lo += kq[c] < klo ? 1 : 0;
+        hi += kq[c] < khi ? 1 : 0;
+      }
+    }
+    const int hw = ep >> 6;
+    int aidx = __popcll(hit_l[hw] & ((1ull << (ep & 63)) - 1ull));
+    int nact = 0;
+#pragma unroll
+    for (int w = 0; w < kMaxE / 64; ++w) {
+      const int c = __popcll(hit_l[w]);
+      nact += c;
+      aidx += w < hw ? c : 0;
+    }
+    if (has) {
+      perm_l[pos] = lane;
+      inv_l[lane] = pos;
+      tokp_l[pos] = lane / k;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    if (has && pos == lo) {   // the first pair of its expert writes the expert's entry
+      int* a = act_l[aidx];
+      a[0] = ep;
+      a[1] = slot_l[ep];
+      a[2] = lo;
+      a[3] = hi;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[4 + i] = lo + i < hi ? tokp_l[lo + i] : -1;
+    }
+    if (lane == 0) nact_l = nact;
+  }
+  __syncthreads();
+  const int na = nact_l;
+  if (blockIdx.x == 0 && blockIdx.y == 0) {   // publish the routing
+    if (tid < n) {
+      rin.ids[tid] = ids_l[tid];
+      rin.w[tid] = w_l[tid];
+      rin.perm[tid] = perm_l[tid];
+      rin.inv_perm[tid] = inv_l[tid];
+    }
+    if (tid <= E) {
+      int c = 0, o = 0;
+      for (int q = 0; q < n; ++q) {
+        const int eq = ids_l[q];
+        c += eq == tid ? 1 : 0;
+        o += eq < tid ? 1 : 0;
+      }
+      if (tid < E) rin.counts[tid] = c;
+      rin.offsets[tid] = o;
+    }
+    for (int i = tid; i < na * kActStride; i += kGThreads) rin.act[1 + i] = (&act_l[0][0])[i];
+    if (tid == 0) rin.act[0] = na;
+  }
+  const int j = blockIdx.y;
+  if (j >= na) return;
+  const int slot = act_l[j][1], lo = act_l[j][2], hi = act_l[j][3];
+  const int np = hi - lo;   // <= T <= NT
+  const int rg = blockIdx.x;
+  const int r0 = rg * 16;
+  if (slot < 0 || slot >= n_slots) {
+    for (int i = tid; i < np * 16; i += kGThreads)
+      h_out[(int64_t)(lo + i / 16) * I + r0 + i % 16] = 0;
+    if (tid == 0 && err_flags) atomicOr(err_flags, 1u);
+    return;
+  }
+
+  // 4. stream this row group of the expert's gate and up rows
+  const int nb = H / 32;
+  const int nc = (nb + LM::kBlocksPerChunk - 1) / LM::kBlocksPerChunk;
+  constexpr int64_t cb = code_bytes_per_block(FMT), sb = scale_bytes_per_block(FMT);
+  const int64_t unit0 = (int64_t)rg * nb * 16;
+  const int lane_unit = FMT == kMXFP4 ? lane : (lane >> 1);
+  const uint8_t* qa = gq + slot * qslot + unit0 * cb + lane * 16;
+  const uint8_t* qb = uq + slot * qslot + unit0 * cb + lane * 16;
+  const uint8_t* sa = gsc + slot * sslot + (unit0 + lane_unit) * sb;
+  const uint8_t* sbp = usc + slot * sslot + (unit0 + lane_unit) * sb;
+  const int lblk = LM::blk(lane);
+  const int koff = LM::koff(lane);
+  const uint16_t* xrow[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const int t = act_l[j][4 + (i < 4 ? i : 3)];
+    xrow[i] = &xs[(t >= 0 ? t : 0) * H];
+  }
+  float acc[2][NT];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int i = 0; i < NT; ++i) acc[m][i] = 0.f;
+  for (int cbase = 0; cbase < nc; cbase += kGWaves * kU) {
+    Chunk ca[kU], cbk[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int c = cbase + wave + kGWaves * u;
+      const int b = c * LM::kBlocksPerChunk + lblk;
+      const bool ok = c < nc && b < nb;
+      const int cs = ok ? c : 0;
+      load_chunk<FMT>(ca[u], qa + (int64_t)cs * 1024, sa + (int64_t)cs * 64, ok);
+      load_chunk<FMT>(cbk[u], qb + (int64_t)cs * 1024, sbp + (int64_t)cs * 64, ok);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // the whole batch in flight before any is used
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int c = cbase + wave + kGWaves * u;
+      const int xo = ca[u].ok ? c * LM::kKPerChunk + koff : 0;   // masked: any valid part
+      bf16x2 w[16];
+      uint32_t xw[LM::kXWords];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const Chunk& ch = m == 0 ? ca[u] : cbk[u];
+        widen<FMT>(ch, w);
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+#pragma unroll
+          for (int q = 0; q < LM::kXWords / 4; ++q) {
+            const u32x4 xq = *(const u32x4*)(xrow[i] + xo + q * 8);
+            xw[4 * q + 0] = xq[0];
+            xw[4 * q + 1] = xq[1];
+            xw[4 * q + 2] = xq[2];
+            xw[4 * q + 3] = xq[3];
+          }
+          acc[m][i] = dot_chunk<FMT>(w, xw, ch.ok ? ch.s : 0u, acc[m][i]);
+        }
+      }
+    }
+  }
+  // 5. lanes that share a row, then the 4 waves in a fixed order; SwiGLU; h in bf16
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      float a = acc[m][i];
+      if constexpr (FMT == kMXFP4) {
+        a += wave_xor(a, 16);
+        a += wave_xor(a, 32);
+      } else {
+        a += wave_xor(a, 1);
+        a += wave_xor(a, 32);
+      }
+      acc[m][i] = a;
+    }
+  const bool writer = FMT == kMXFP4 ? (lane < 16) : (lane < 32 && (lane & 1) == 0);
+  if (writer) {
+    const int r = LM::row(lane);
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int i = 0; i < NT; ++i) red[wave][i][m][r] = acc[m][i];
+  }
+  __syncthreads();
+  if (tid < NT * 16) {
+    const int i = tid / 16, r = tid % 16;
+    if (i < np) {
+      float g = red[0][i][0][r], u = red[0][i][1][r];
+#pragma unroll
+      for (int q = 1; q < kGWaves; ++q) {
+        g += red[q][i][0][r];
+        u += red[q][i][1][r];
+      }
+      h_out[(int64_t)(lo + i) * I + r0 + r] = f32_to_bf16_rne(silu_mul(g, u));
+    }
   }
 }
 
@@ -518,7 +819,7 @@ int gemv_nt(int fmt, int T) {
   return 8;
 }
 
-template <int FMT, bool GATED, bool ACT>
+template <int FMT, bool GATED, int SRC>
 hipError_t launch_gemv_t(const PoolView& a, const PoolView& b, const int32_t* slot_map,
                          int n_slots, int E, const int32_t* offsets, const int32_t* perm,
                          int T, int k, const uint16_t* src, int K, int rows, uint16_t* h,
@@ -526,7 +827,7 @@ hipError_t launch_gemv_t(const PoolView& a, const PoolView& b, const int32_t* sl
   const int n_act = min(E, T * k);
   dim3 grid(rows / 16, n_act);
 #define MOE_GEMV_CASE(N)                                                                        \
-  hipLaunchKernelGGL((k_gemv<FMT, GATED, ACT, N>), grid, dim3(kGThreads), 0, stream, a.q, a.s,  \
+  hipLaunchKernelGGL((k_gemv<FMT, GATED, SRC, N>), grid, dim3(kGThreads), 0, stream, a.q, a.s,  \
                      a.q_slot, a.s_slot, b.q, b.s, slot_map, n_slots, E, offsets, perm, k,      \
                      src, K, rows, h, y, err, act)
   switch (gemv_nt(FMT, T)) {
@@ -550,16 +851,45 @@ hipError_t launch_gate_up_gemv(int fmt, const PoolView& gate, const PoolView& up
                                const int32_t* act, hipStream_t stream) {
   if (act != nullptr) {
     if (fmt == kMXFP4)
-      return launch_gemv_t<kMXFP4, true, true>(gate, up, slot_map, n_slots, E, offsets, perm, T, k,
-                                               x, H, I, h, nullptr, err, act, stream);
-    return launch_gemv_t<kQ8_0, true, true>(gate, up, slot_map, n_slots, E, offsets, perm, T, k, x,
-                                            H, I, h, nullptr, err, act, stream);
+      return launch_gemv_t<kMXFP4, true, kSrcAct>(gate, up, slot_map, n_slots, E, offsets, perm,
+                                                  T, k, x, H, I, h, nullptr, err, act, stream);
+    return launch_gemv_t<kQ8_0, true, kSrcAct>(gate, up, slot_map, n_slots, E, offsets, perm, T,
+                                               k, x, H, I, h, nullptr, err, act, stream);
   }
   if (fmt == kMXFP4)
-    return launch_gemv_t<kMXFP4, true, false>(gate, up, slot_map, n_slots, E, offsets, perm, T, k,
-                                              x, H, I, h, nullptr, err, nullptr, stream);
-  return launch_gemv_t<kQ8_0, true, false>(gate, up, slot_map, n_slots, E, offsets, perm, T, k, x,
-                                           H, I, h, nullptr, err, nullptr, stream);
+    return launch_gemv_t<kMXFP4, true, kSrcOffsets>(gate, up, slot_map, n_slots, E, offsets, perm,
+                                                    T, k, x, H, I, h, nullptr, err, nullptr,
+                                                    stream);
+  return launch_gemv_t<kQ8_0, true, kSrcOffsets>(gate, up, slot_map, n_slots, E, offsets, perm, T,
+                                                 k, x, H, I, h, nullptr, err, nullptr,
+                                                 stream);
+}
+
+
+hipError_t launch_gate_up_route(int fmt, const PoolView& gate, const PoolView& up,
+                                const int32_t* slot_map, int n_slots, int E, const uint16_t* x,
+                                int T, int k, int H, int I, const RouteIn& rin, uint16_t* h,
+                                uint32_t* err, hipStream_t stream) {
+  if (!route_fused_ok(T, H, E) || rin.T != T || rin.ns != route_fused_split(H) ||
+      gate.q_slot != up.q_slot || gate.s_slot != up.s_slot)
+    return hipErrorInvalidValue;
+  dim3 grid(I / 16, min(E, T * k));
+#define MOE_ROUTED_CASE(F, N)                                                                 \
+  hipLaunchKernelGGL((k_gate_up_routed<F, N>), grid, dim3(kGThreads), 0, stream, gate.q,     \
+                     gate.s, up.q, up.s, gate.q_slot, gate.s_slot, slot_map, n_slots, E, k, x, \
+                     H, I, h, err, rin)
+  const int nt = gemv_nt(fmt, T);
+  if (fmt == kMXFP4) {
+    if (nt == 1) MOE_ROUTED_CASE(kMXFP4, 1);
+    else if (nt == 2) MOE_ROUTED_CASE(kMXFP4, 2);
+    else MOE_ROUTED_CASE(kMXFP4, 4);
+  } else {
+    if (nt == 1) MOE_ROUTED_CASE(kQ8_0, 1);
+    else if (nt == 2) MOE_ROUTED_CASE(kQ8_0, 2);
+    else MOE_ROUTED_CASE(kQ8_0, 4);
+  }
+#undef MOE_ROUTED_CASE
+  return hipGetLastError();
 }
 
 hipError_t launch_down_gemv(int fmt, const PoolView& down, const int32_t* slot_map, int n_slots,
@@ -578,10 +908,12 @@ hipError_t launch_down_gemv(int fmt, const PoolView& down, const int32_t* slot_m
     return hipGetLastError();
   }
   if (fmt == kMXFP4)
-    return launch_gemv_t<kMXFP4, false, false>(down, down, slot_map, n_slots, E, offsets, nullptr,
-                                               T, k, h, I, H, nullptr, y, err, nullptr, stream);
-  return launch_gemv_t<kQ8_0, false, false>(down, down, slot_map, n_slots, E, offsets, nullptr, T,
-                                            k, h, I, H, nullptr, y, err, nullptr, stream);
+    return launch_gemv_t<kMXFP4, false, kSrcOffsets>(down, down, slot_map, n_slots, E, offsets,
+                                                     nullptr, T, k, h, I, H, nullptr, y, err,
+                                                     nullptr, stream);
+  return launch_gemv_t<kQ8_0, false, kSrcOffsets>(down, down, slot_map, n_slots, E, offsets,
+                                                  nullptr, T, k, h, I, H, nullptr, y, err, nullptr,
+                                                  stream);
 }
 
 bool down_combine_small_ok(int T, int k, int E, int I) {

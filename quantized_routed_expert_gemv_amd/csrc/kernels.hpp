@@ -28,6 +28,20 @@ hipError_t launch_route_small(const uint16_t* x, const uint16_t* wr, const float
                               float* w, int32_t* counts, int32_t* offsets, int32_t* perm,
                               int32_t* inv_perm, int32_t* act, hipStream_t stream);
 
+// Decode routing split in two: the router's partial logits over route_fused_split(H)
+// slices of H (launch_router_partials), finished inside the gate/up kernel
+// (launch_gate_up_route). For 1 <= T <= 4, T*E <= 256 and at least 2 slices.
+bool route_fused_ok(int T, int H, int E);
+int route_fused_split(int H);
+hipError_t launch_router_partials(const uint16_t* x, const uint16_t* wr, int T, int H, int E,
+                                  int ns, float* partial, hipStream_t stream);
+// The partials finished by one workgroup (same order as the fused gate/up kernel), with
+// or without the counting sort.
+hipError_t launch_router_finish(const float* partial, int ns, const float* bias, int T, int E,
+                                int k, int32_t* ids, float* w, int32_t* counts,
+                                int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                                hipStream_t stream);
+
 size_t bucket_scratch_bytes(int n, int E);
 hipError_t launch_bucket(const int32_t* ids, int n, int E, int32_t* counts, int32_t* offsets,
                          int32_t* perm, int32_t* inv_perm, void* scratch, hipStream_t stream);
@@ -42,6 +56,12 @@ hipError_t launch_gate_up_gemv(int fmt, const PoolView& gate, const PoolView& up
 hipError_t launch_down_gemv(int fmt, const PoolView& down, const int32_t* slot_map, int n_slots,
                             int E, int T, int k, int H, int I, const int32_t* offsets,
                             const uint16_t* h, float* y, uint32_t* err, hipStream_t stream);
+// Gate/up GEMV that first finishes a split router (see RouteIn); every workgroup derives
+// its expert from the partials, workgroup (0, 0) stores the routing.
+hipError_t launch_gate_up_route(int fmt, const PoolView& gate, const PoolView& up,
+                                const int32_t* slot_map, int n_slots, int E, const uint16_t* x,
+                                int T, int k, int H, int I, const RouteIn& rin, uint16_t* h,
+                                uint32_t* err, hipStream_t stream);
 // Down projection + combine in one launch for T*k <= 8 (down_combine_small_ok); needs the
 // small-batch router's active-expert list.
 bool down_combine_small_ok(int T, int k, int E, int I);

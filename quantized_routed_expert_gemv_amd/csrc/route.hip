@@ -17,6 +17,7 @@
 #include "common.hpp"
 #include "bucket_dev.hpp"
 #include "kernels.hpp"
+#include "topk_dev.hpp"
 
 namespace moe {
 
@@ -24,64 +25,7 @@ namespace {
 
 constexpr int kRouteTok = 16;   // tokens per workgroup (one MFMA row tile)
 constexpr int kRouteWaves = 4;
-constexpr int kMaxSplit = 32;   // largest split of the reduction dimension across workgroups
-
-// Top-k of one token's E logits held in LDS, by one wave. Ties go to the lower index;
-// NaN counts as -inf. Lane l holds the logits of experts l, l + 64, ...; each logit is
-// ranked against all E (broadcast from its lane with readlane):
-//   rank(e) = #{e' : L[e'] > L[e], or L[e'] == L[e] and e' < e},
-// and the experts of rank j < k are the choices, in order. The softmax over the chosen k is
-// z_j = exp(L_j - L_0), sum = z_0 + z_1 + ... (increasing j), w_j = z_j / sum.
-// zs: kMaxK floats of LDS private to the wave. Writes ids and weights (and, if ids_lds is
-// given, a copy of the ids).
-__device__ void wave_topk_softmax(const float* logit, int E, int k, int32_t* ids_out,
-                                  float* w_out, float* zs, int* ids_lds = nullptr) {
-  const int lane = threadIdx.x & (kWave - 1);
-  constexpr int kPer = kMaxE / kWave;
-  const int n_slots = (E + kWave - 1) / kWave;        // wave-uniform
-  float v[kPer];
-  int rank[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int e = lane + i * kWave;
-    const float x = e < E ? logit[e] : -INFINITY;
-    v[i] = (x != x) ? -INFINITY : x;
-    rank[i] = 0;
-  }
-#pragma unroll
-  for (int i2 = 0; i2 < kPer; ++i2) {
-    if (i2 >= n_slots) break;
-    const int lim = min(kWave, E - i2 * kWave);
-    for (int l = 0; l < lim; ++l) {
-      const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[i2]), l));
-      const int e2 = i2 * kWave + l;
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        if (i >= n_slots) break;
-        const int e = lane + i * kWave;
-        rank[i] += (c > v[i] || (c == v[i] && e2 < e)) ? 1 : 0;
-      }
-    }
-  }
-  // the chosen experts' logits, by rank, then the softmax terms in parallel
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int e = lane + i * kWave;
-    if (i < n_slots && e < E && rank[i] < k) {
-      ids_out[rank[i]] = e;
-      zs[rank[i]] = v[i];
-      if (ids_lds) ids_lds[rank[i]] = e;
-    }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  const float l0 = zs[0];
-  const float z = lane < k ? expf(zs[lane < k ? lane : 0] - l0) : 0.f;
-  float sum = 0.f;
-  for (int j = 0; j < k; ++j) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), j));
-  if (lane < k) w_out[lane] = z / sum;
-}
+constexpr int kMaxSplit = kMaxRouteSplit;   // largest split of the reduction dimension
 
 // Partial logits of tokens [t0, t0 + 16) over this workgroup's share (split z of nsplit) of
 // the reduction dimension, summed over the NW waves in a fixed order into red[0][token][e]
@@ -174,7 +118,7 @@ __global__ __launch_bounds__(256) void k_router(const uint16_t* __restrict__ x,
                                                 int32_t* __restrict__ ids,
                                                 float* __restrict__ w) {
   __shared__ float red[kRouteWaves][kRouteTok][NF * 16];
-  __shared__ float zs[kRouteWaves][kMaxK];
+  __shared__ TopkScratch tks[kRouteWaves];
   const int wave = threadIdx.x / kWave;
   const int t0 = blockIdx.x * kRouteTok;
   router_tile<NF, kRouteWaves, router_rb<NF>()>(x, wr, T, H, E, t0, blockIdx.y, gridDim.y, red);
@@ -196,7 +140,7 @@ __global__ __launch_bounds__(256) void k_router(const uint16_t* __restrict__ x,
   for (int tt = wave; tt < kRouteTok; tt += kRouteWaves) {
     if (t0 + tt >= T) break;
     wave_topk_softmax(&red[0][tt][0], E, k, ids + (int64_t)(t0 + tt) * k,
-                      w + (int64_t)(t0 + tt) * k, zs[wave]);
+                      w + (int64_t)(t0 + tt) * k, tks[wave]);
   }
 }
 
@@ -213,7 +157,7 @@ __global__ __launch_bounds__(256) void k_router_finish(
   __shared__ float flat[kFinishCap];
   __shared__ float lg[kRouteTok][kMaxE];
   __shared__ int ids_l[kRouteTok * kMaxK];
-  __shared__ float zs[kRouteWaves][kMaxK];
+  __shared__ TopkScratch tks[kRouteWaves];
   __shared__ int lid[BUCKET ? kRouteTok * kMaxK : 1];
   __shared__ int hist[BUCKET ? kMaxE : 1], run[BUCKET ? kMaxE : 1];
   __shared__ int wcnt[BUCKET ? kRouteWaves : 1][kMaxE];
@@ -232,14 +176,14 @@ __global__ __launch_bounds__(256) void k_router_finish(
   }
   __syncthreads();
   for (int i = threadIdx.x; i < te; i += 256) {
-    float sum = flat[i];
-    for (int z = 1; z < ksplit; ++z) sum += flat[z * te + i];
-    if (bias != nullptr) sum += bias[i % E];
-    lg[i / E][i % E] = sum;
+    float v[kMaxSplit];
+#pragma unroll
+    for (int z = 0; z < kMaxSplit; ++z) v[z] = flat[min(z, ksplit - 1) * te + i];
+    lg[i / E][i % E] = finish_logit(v, ksplit, bias != nullptr ? bias[i % E] : 0.f);
   }
   __syncthreads();
   for (int tt = wave; tt < T; tt += kRouteWaves)
-    wave_topk_softmax(lg[tt], E, k, ids + (int64_t)tt * k, w + (int64_t)tt * k, zs[wave],
+    wave_topk_softmax(lg[tt], E, k, ids + (int64_t)tt * k, w + (int64_t)tt * k, tks[wave],
                       ids_l + tt * k);
   if constexpr (BUCKET) {
     __syncthreads();
@@ -269,7 +213,7 @@ __global__ __launch_bounds__(kSmallWaves * kWave) void k_route_small(
   __shared__ int ids_l[kRouteTok * kMaxK];
   __shared__ int lid[kRouteTok * kMaxK];
   __shared__ int perm_l[kRouteTok * kMaxK];
-  __shared__ float zs[kSmallWaves][kMaxK];
+  __shared__ TopkScratch tks[kSmallWaves];
   __shared__ int hist[kMaxE], run[kMaxE], wcnt[kSmallWaves][kMaxE], tmp[kSmallWaves];
   const int wave = threadIdx.x / kWave;
   const int tid = threadIdx.x;
@@ -283,7 +227,7 @@ __global__ __launch_bounds__(kSmallWaves * kWave) void k_route_small(
   __syncthreads();
   for (int tt = wave; tt < T; tt += kSmallWaves)
     wave_topk_softmax(&red[0][tt][0], E, k, ids + (int64_t)tt * k, w + (int64_t)tt * k,
-                      zs[wave], ids_l + tt * k);
+                      tks[wave], ids_l + tt * k);
   if constexpr (!BUCKET) return;
   __syncthreads();
   bucket_dev::bucket_one_block<NTH>(ids_l, T * k, E, counts, offsets, perm, inv_perm, lid, hist,
@@ -314,6 +258,48 @@ int route_ksplit(int T, int H) {
   ks = min(ks, kMaxSplit);
   ks = min(ks, kFinishCap / (T * kMaxE));
   return max(ks, 1);
+}
+
+int route_fused_split(int H) { return min(kMaxRouteSplit, max(1, (H / 32) / 2)); }
+
+bool route_fused_ok(int T, int H, int E) {
+  // T * k <= kFuseMaxPairs follows from T <= kFuseMaxT and k <= kMaxK
+  return T >= 1 && T <= kFuseMaxT && T * E <= kFuseMaxTE && H <= kRouteMaxH &&
+         route_fused_split(H) >= 2;
+}
+
+hipError_t launch_router_partials(const uint16_t* x, const uint16_t* wr, int T, int H, int E,
+                                  int ns, float* partial, hipStream_t stream) {
+  if (T < 1 || T > kRouteTok || ns < 2 || ns > kMaxSplit) return hipErrorInvalidValue;
+  dim3 grid(1, ns);
+#define MOE_PART_CASE(N)                                                                     \
+  case N:                                                                                   \
+    hipLaunchKernelGGL(k_router<N>, grid, dim3(256), 0, stream, x, wr, nullptr, T, H, E, 1, \
+                       partial, nullptr, nullptr);                                          \
+    break;
+  switch ((E + 15) / 16) {
+    MOE_PART_CASE(1) MOE_PART_CASE(2) MOE_PART_CASE(3) MOE_PART_CASE(4)
+    MOE_PART_CASE(5) MOE_PART_CASE(6) MOE_PART_CASE(7) MOE_PART_CASE(8)
+    MOE_PART_CASE(9) MOE_PART_CASE(10) MOE_PART_CASE(11) MOE_PART_CASE(12)
+    MOE_PART_CASE(13) MOE_PART_CASE(14) MOE_PART_CASE(15) MOE_PART_CASE(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef MOE_PART_CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_router_finish(const float* partial, int ns, const float* bias, int T, int E,
+                                int k, int32_t* ids, float* w, int32_t* counts,
+                                int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                                hipStream_t stream) {
+  if (T < 1 || T > kRouteTok || ns * T * E > kFinishCap) return hipErrorInvalidValue;
+  if (counts != nullptr)
+    hipLaunchKernelGGL(k_router_finish<true>, dim3(1), dim3(256), 0, stream, partial, ns, bias,
+                       T, E, k, ids, w, counts, offsets, perm, inv_perm);
+  else
+    hipLaunchKernelGGL(k_router_finish<false>, dim3(1), dim3(256), 0, stream, partial, ns, bias,
+                       T, E, k, ids, w, nullptr, nullptr, nullptr, nullptr);
+  return hipGetLastError();
 }
 
 bool route_bucket_fusable(int T, int E) { return T >= 1 && T <= kRouteTok; }
@@ -379,6 +365,13 @@ hipError_t launch_route_impl(const uint16_t* x, const uint16_t* wr, const float*
 hipError_t launch_route(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H,
                         int E, int k, int32_t* ids, float* w, float* partial,
                         hipStream_t stream) {
+  if (route_fused_ok(T, H, E)) {   // same partials, same finishing order as the fused layer
+    const int ns = route_fused_split(H);
+    hipError_t e = launch_router_partials(x, wr, T, H, E, ns, partial, stream);
+    if (e != hipSuccess) return e;
+    return launch_router_finish(partial, ns, bias, T, E, k, ids, w, nullptr, nullptr, nullptr,
+                                nullptr, stream);
+  }
   if (route_small_ok(T, E))   // same kernel, same summation order as the fused layer
     return launch_route_small(x, wr, bias, T, H, E, k, nullptr, ids, w, nullptr, nullptr,
                               nullptr, nullptr, nullptr, stream);

@@ -1,0 +1,105 @@
+// Per-token top-k + softmax over the chosen k, by one wave; shared by the router kernels
+// and by the decode gate/up kernel that finishes a split router itself.
+#pragma once
+#include "common.hpp"
+
+namespace moe {
+
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+
+// LDS scratch of one wave for wave_topk_softmax.
+struct TopkScratch {
+  __attribute__((aligned(16))) uint64_t keys[kMaxE];
+  float zs[kMaxK];
+};
+
+// Unsigned key that orders like the float: NaN counts as -inf and -0 as +0.
+__device__ __forceinline__ uint32_t order_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (x != x) u = 0xff800000u;        // -inf
+  if (u == 0x80000000u) u = 0u;       // -0 -> +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int SLOTS>
+__device__ void wave_topk_softmax_impl(const float* logit, int E, int k, int32_t* ids_out,
+                                       float* w_out, TopkScratch& sc, int* ids_lds) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int E4 = (E + 3) & ~3;
+  uint64_t key[SLOTS];
+  float val[SLOTS];
+  int rank[SLOTS];
+#pragma unroll
+  for (int i = 0; i < SLOTS; ++i) {
+    const int e = lane + i * kWave;
+    float x = e < E ? logit[e] : -INFINITY;
+    x = (x != x) ? -INFINITY : x;
+    val[i] = x;
+    key[i] = e < E ? (((uint64_t)order_key(x) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e)) : 0ull;
+    if (e < E4) sc.keys[e] = key[i];
+    rank[i] = 0;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  // every key against every key, four at a time as LDS broadcasts (padding keys are 0,
+  // below every real key)
+  for (int e2 = 0; e2 < E4; e2 += 4) {
+    const u64x2 a = *(const u64x2*)&sc.keys[e2];
+    const u64x2 b = *(const u64x2*)&sc.keys[e2 + 2];
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i)
+      rank[i] += (int)(a[0] > key[i]) + (int)(a[1] > key[i]) + (int)(b[0] > key[i]) +
+                 (int)(b[1] > key[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < SLOTS; ++i) {
+    const int e = lane + i * kWave;
+    if (e < E && rank[i] < k) {
+      ids_out[rank[i]] = e;
+      sc.zs[rank[i]] = val[i];
+      if (ids_lds) ids_lds[rank[i]] = e;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  const float l0 = sc.zs[0];
+  const float z = lane < k ? expf(sc.zs[lane < k ? lane : 0] - l0) : 0.f;
+  float sum = 0.f;
+  for (int j = 0; j < k; ++j) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), j));
+  if (lane < k) w_out[lane] = z / sum;
+}
+
+// Top-k of one token's E logits (LDS), by one wave. Ties go to the lower index; NaN counts
+// as -inf and -0 equals +0. Each logit gets the unique key (value order, then lower index
+// first) and its rank
+//   rank(e) = #{e' : L[e'] > L[e], or L[e'] == L[e] and e' < e}
+// is the number of keys above its own; the experts of rank j < k are the choices, in
+// order. The softmax over the chosen k is z_j = exp(L_j - L_0),
+// sum = z_0 + z_1 + ... (increasing j), w_j = z_j / sum.
+// sc: LDS scratch private to the wave. Writes ids and weights (and, if ids_lds is given, a
+// copy of the ids).
+__device__ inline void wave_topk_softmax(const float* logit, int E, int k, int32_t* ids_out,
+                                         float* w_out, TopkScratch& sc,
+                                         int* ids_lds = nullptr) {
+  if (E <= kWave) wave_topk_softmax_impl<1>(logit, E, k, ids_out, w_out, sc, ids_lds);
+  else if (E <= 2 * kWave) wave_topk_softmax_impl<2>(logit, E, k, ids_out, w_out, sc, ids_lds);
+  else wave_topk_softmax_impl<kMaxE / kWave>(logit, E, k, ids_out, w_out, sc, ids_lds);
+}
+
+// Logit of one (token, expert) from a split router's partials: the splits are added in
+// increasing split order, then the bias. Every kernel that finishes a split router uses
+// this order, so they all agree bit for bit.
+//   partial [ns][T*E] fp32, i = t*E + e.
+//   v[z] = partial of split z (z < ns <= MAXS).
+template <int MAXS>
+__device__ __forceinline__ float finish_logit(const float (&v)[MAXS], int ns, float bias) {
+  float sum = v[0];
+#pragma unroll
+  for (int z = 1; z < MAXS; ++z)
+    if (z < ns) sum += v[z];
+  return sum + bias;
+}
+
+}  // namespace moe

@@ -102,8 +102,12 @@ def test_route_argument_checks(lib):
     assert f(MISALIGNED, FAKE, None, 4, 64, 8, 2, FAKE, FAKE, None, 0, None) == INVALID
     # T = 0: nothing to do
     assert f(None, None, None, 0, 64, 8, 2, None, None, None, 0, None) == OK
-    # small batches with E <= 128 are routed by one workgroup: no scratch
-    assert lib.moe_route_scratch_bytes(1, 2880, 32) == 0
+    # up to 4 tokens: the reduction is split into min(32, H/64) slices whose partial
+    # logits [slices][T][E] fp32 live in the scratch
+    assert lib.moe_route_scratch_bytes(1, 2880, 32) == 32 * 1 * 32 * 4
+    assert lib.moe_route_scratch_bytes(4, 256, 8) == 4 * 4 * 8 * 4
+    # 5..16 tokens with E <= 128 are routed by one workgroup: no scratch
+    assert lib.moe_route_scratch_bytes(8, 2880, 32) == 0
     # with more experts the reduction is split across workgroups: scratch required
     need = lib.moe_route_scratch_bytes(1, 2880, 256)
     assert need > 0
