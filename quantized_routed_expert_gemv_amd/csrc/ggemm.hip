@@ -68,59 +68,29 @@ __device__ bool map_row_tile(const int32_t* __restrict__ offsets, int E, int mt,
   return sh[0] >= 0;
 }
 
+// B of one K step (4 blocks = 128 K) for the workgroup's 8 row groups (128 weight rows):
+// in the tiled pool layout each row group's step is one contiguous run of 64 units
+// (4 blocks x 16 rows), so the step is copied verbatim into LDS and a lane's MFMA operand
+// is unit `lane` (MXFP4) or units 16 j + lane % 16 (Q8_0) of its row group's run.
 template <int FMT>
-struct BFrag;   // one n-fragment's share of a K step, per lane
-
-template <>
-struct BFrag<kMXFP4> {
-  u32x4 q;        // 32 codes of one block of one row
-  uint32_t s;     // its E8M0 scale
-  bool ok;
+struct BStage {
+  static constexpr int kRunQ = 64 * code_bytes_per_block(FMT);   // code bytes per row group
+  static constexpr int kRunS = 64 * scale_bytes_per_block(FMT);  // scale bytes per row group
+  static constexpr int kQPieces = 8 * kRunQ / 16 / kTThreads;    // 16-byte code pieces/thread
 };
-template <>
-struct BFrag<kQ8_0> {
-  u32x2 q[4];     // 8 codes from each of the step's 4 blocks
-  uint32_t s[4];  // fp16 scale bits of each block
-  uint32_t okm;   // bit j: block j exists
-};
-
-// Load the lane's B share of step c for the row group rg (MXFP4: block 4c + lane/16 of row
-// lane%16; Q8_0: codes 8*(lane/16).. of blocks 4c..4c+3 of row lane%16). Loads are issued
-// unconditionally (from the matrix base when out of range) and masked when consumed, so
-// none of them waits for another.
-template <int FMT>
-__device__ __forceinline__ void load_b(BFrag<FMT>& f, const uint8_t* q, const uint8_t* s,
-                                       int rg, int nb, int c, bool row_ok) {
-  const int lane = threadIdx.x & (kWave - 1);
-  if constexpr (FMT == kMXFP4) {
-    const int b = 4 * c + (lane >> 4);
-    f.ok = row_ok && b < nb;
-    const int64_t unit = f.ok ? ((int64_t)rg * nb + b) * 16 + (lane & 15) : 0;
-    f.q = ldg16(q + unit * 16);
-    f.s = s[unit];
-  } else {
-    f.okm = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int b = 4 * c + j;
-      const bool ok = row_ok && b < nb;
-      f.okm |= (uint32_t)ok << j;
-      const int64_t unit = ok ? ((int64_t)rg * nb + b) * 16 + (lane & 15) : 0;
-      f.q[j] = ldg8(q + unit * 32 + 8 * (lane >> 4));
-      f.s[j] = *(const uint16_t*)(s + unit * 2);
-    }
-  }
-}
 
 template <int FMT, bool GATED>
-__global__ __launch_bounds__(kTThreads) void k_ggemm(
+__global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
     const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as, int64_t qslot,
     int64_t sslot, const uint8_t* __restrict__ bq, const uint8_t* __restrict__ bs,
     const int32_t* __restrict__ slot_map, int n_slots, int E,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm, int k,
     const uint16_t* __restrict__ src, int K, int N, int n_ntiles,
     uint16_t* __restrict__ h_out, float* __restrict__ y_out, uint32_t* __restrict__ err_flags) {
+  using BS = BStage<FMT>;
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[kBM * kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_bq[8 * BS::kRunQ];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_bs[8 * BS::kRunS];
   __shared__ int tmp4[4];
   __shared__ int sh[2];
   const int lane = threadIdx.x & (kWave - 1);
@@ -149,58 +119,108 @@ __global__ __launch_bounds__(kTThreads) void k_ggemm(
   const int nb = K / 32;
   const int nsteps = (K + kBK - 1) / kBK;
 
-  // ---- A staging: thread handles 16-byte piece (tid % 16) of rows tid/16 + 16 j
+  // ---- A staging: thread handles 16-byte piece (tid % 16) of rows tid/16 + 16 j. Rows
+  // past the tile's end repeat its last row: their results are never stored. Only the
+  // last K step (past K) is masked to zeros, so that nothing but zeros meets the masked B.
   const int piece = threadIdx.x & 15;
   const int rbase = threadIdx.x >> 4;
-  int64_t arow[8];
-  int prow[8];
+  uint32_t arow[8];   // element offset of the thread's piece in each of its 8 rows
+  {
+    int prow[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j)   // all perm loads first (clamped to the tile's first row)
-    prow[j] = GATED ? perm[min(m0 + rbase + 16 * j, mend - 1)] : 0;
+    for (int j = 0; j < 8; ++j)   // all perm loads first
+      prow[j] = GATED ? perm[min(m0 + rbase + 16 * j, mend - 1)] : min(m0 + rbase + 16 * j, mend - 1);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int pos = m0 + rbase + 16 * j;
-    if (pos < mend) arow[j] = GATED ? (int64_t)(prow[j] / k) * K : (int64_t)pos * K;
-    else arow[j] = -1;
+    for (int j = 0; j < 8; ++j)
+      arow[j] = (uint32_t)(GATED ? prow[j] / k : prow[j]) * (uint32_t)K + piece * 8;
   }
   u32x4 areg[8];
-  uint32_t aok = 0;   // bit j: areg[j] holds real data (else it is stored as zeros)
   auto load_a = [&](int c) {
-    const int kk = c * kBK + piece * 8;
-    aok = 0;
+    const int kk = c * kBK;
+    if (kk + kBK <= K) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bool ok = arow[j] >= 0 && kk < K;
-      aok |= (uint32_t)ok << j;
-      areg[j] = ldg16(src + (ok ? arow[j] + kk : 0));
+      for (int j = 0; j < 8; ++j) areg[j] = ldg16(src + arow[j] + kk);
+    } else {
+      const bool ok = kk + piece * 8 < K;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const u32x4 v = ldg16(src + arow[j] + (ok ? kk : 0));
+        areg[j] = ok ? v : u32x4{0, 0, 0, 0};
+      }
     }
   };
 
-  // ---- B: 4 n-fragments per wave
+  // ---- B staging: local row group g (0..7) of the tile. GATED: g < 4 -> gate rows
+  // n0/16 + g, g >= 4 -> up rows n0/16 + g - 4; else rows n0/16 + g. A row group past N
+  // reads group 0 (its columns are never stored). Thread t copies code pieces
+  // t + 256 p of the 8 runs and, for t < 8 * kRunS / 4, one dword of scales.
   const uint8_t* q0 = aq + (int64_t)slot * qslot;
   const uint8_t* s0 = as + (int64_t)slot * sslot;
   const uint8_t* q1 = GATED ? bq + (int64_t)slot * qslot : q0;
   const uint8_t* s1 = GATED ? bs + (int64_t)slot * sslot : s0;
-  int frg[4];
-  bool fok[4];
-  const uint8_t* fq[4];
-  const uint8_t* fs[4];
+  auto group_base = [&](int g, const uint8_t** qb, const uint8_t** sb) {
+    const int rg = GATED ? n0 / 16 + (g & 3) : n0 / 16 + g;
+    const int rgc = rg * 16 < N ? rg : 0;
+    const int64_t u0 = (int64_t)rgc * nb * 16;   // first unit of the row group
+    *qb = (GATED && g >= 4 ? q1 : q0) + u0 * code_bytes_per_block(FMT);
+    *sb = (GATED && g >= 4 ? s1 : s0) + u0 * scale_bytes_per_block(FMT);
+  };
+  const uint8_t* bqp[BS::kQPieces];
+  int bq_blk[BS::kQPieces];   // block of the step that the piece lies in
+#pragma unroll
+  for (int p = 0; p < BS::kQPieces; ++p) {
+    const int off = (threadIdx.x + kTThreads * p) * 16;   // byte in the 8 runs
+    const int g = off / BS::kRunQ;
+    const uint8_t* qb;
+    const uint8_t* sb;
+    group_base(g, &qb, &sb);
+    bqp[p] = qb + (off % BS::kRunQ);
+    bq_blk[p] = (off % BS::kRunQ) / (16 * code_bytes_per_block(FMT));
+  }
+  constexpr int kSDwords = 8 * BS::kRunS / 4;
+  const bool s_thread = threadIdx.x < kSDwords;
+  const uint8_t* bsp;
+  int bs_blk;
+  {
+    const int off = (s_thread ? threadIdx.x : 0) * 4;
+    const int g = off / BS::kRunS;
+    const uint8_t* qb;
+    const uint8_t* sb;
+    group_base(g, &qb, &sb);
+    bsp = sb + (off % BS::kRunS);
+    bs_blk = (off % BS::kRunS) / (16 * scale_bytes_per_block(FMT));
+  }
+  u32x4 breg[BS::kQPieces];
+  uint32_t sreg = 0;
+  auto load_b = [&](int c) {
+    // a step's run starts 4 blocks (64 units) after the previous one's; pieces of blocks
+    // past the end of the row re-read step 0 (masked when consumed)
+#pragma unroll
+    for (int p = 0; p < BS::kQPieces; ++p) {
+      const int cs = 4 * c + bq_blk[p] < nb ? c : 0;
+      breg[p] = ldg16(bqp[p] + (int64_t)cs * BS::kRunQ);
+    }
+    if (s_thread) {
+      const int cs = 4 * c + bs_blk < nb ? c : 0;
+      sreg = *(const uint32_t*)(bsp + (int64_t)cs * BS::kRunS);
+    }
+  };
+
+  // ---- this wave's 4 n-fragments: local row group and column validity
+  int fg[4];
+  bool fcol[4];
 #pragma unroll
   for (int f = 0; f < 4; ++f) {
     int col0;
     if (GATED) {
       col0 = n0 + 32 * wn + 16 * (f & 1);
-      fq[f] = f < 2 ? q0 : q1;
-      fs[f] = f < 2 ? s0 : s1;
+      fg[f] = (f < 2 ? 0 : 4) + 2 * wn + (f & 1);
     } else {
       col0 = n0 + 64 * wn + 16 * f;
-      fq[f] = q0;
-      fs[f] = s0;
+      fg[f] = 4 * wn + f;
     }
-    frg[f] = col0 / 16;
-    fok[f] = col0 < N;
+    fcol[f] = col0 < N;
   }
-  BFrag<FMT> bcur[4], bnext[4];
 
   f32x4 acc[4][4];
 #pragma unroll
@@ -209,71 +229,85 @@ __global__ __launch_bounds__(kTThreads) void k_ggemm(
     for (int f = 0; f < 4; ++f) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   load_a(0);
-#pragma unroll
-  for (int f = 0; f < 4; ++f) load_b<FMT>(bcur[f], fq[f], fs[f], frg[f], nb, 0, fok[f]);
-
-  const int g = lane >> 4;
+  load_b(0);
+  const int g4 = lane >> 4;
   const int mrow = lane & 15;
   for (int c = 0; c < nsteps; ++c) {
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      *(u32x4*)(lds_a + (rbase + 16 * j) * kLdsStride + piece * 16) =
-          ((aok >> j) & 1) ? areg[j] : u32x4{0, 0, 0, 0};
+      *(u32x4*)(lds_a + (rbase + 16 * j) * kLdsStride + piece * 16) = areg[j];
+#pragma unroll
+    for (int p = 0; p < BS::kQPieces; ++p)
+      *(u32x4*)(lds_bq + (threadIdx.x + kTThreads * p) * 16) = breg[p];
+    if (s_thread) *(uint32_t*)(lds_bs + threadIdx.x * 4) = sreg;
     __syncthreads();
     if (c + 1 < nsteps) {
       load_a(c + 1);
-#pragma unroll
-      for (int f = 0; f < 4; ++f) load_b<FMT>(bnext[f], fq[f], fs[f], frg[f], nb, c + 1, fok[f]);
+      load_b(c + 1);
     }
     if constexpr (FMT == kMXFP4) {
+      // lane's operand: unit `lane` of its row group's run = block 4c + lane/16 of row lane%16
+      u32x4 bqv[4];
+      float bsc[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        bqv[f] = *(const u32x4*)(lds_bq + fg[f] * BS::kRunQ + lane * 16);
+        const bool ok = fcol[f] && 4 * c + g4 < nb;
+        bsc[f] = ok ? e8m0_to_f32(lds_bs[fg[f] * BS::kRunS + lane]) : 0.f;
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         bf16x8 bv[4];
 #pragma unroll
-        for (int f = 0; f < 4; ++f)
-          bv[f] = fp4x8_to_bf16x8(bcur[f].q[i], bcur[f].ok ? e8m0_to_f32(bcur[f].s) : 0.f);
+        for (int f = 0; f < 4; ++f) bv[f] = fp4x8_to_bf16x8(bqv[f][i], bsc[f]);
 #pragma unroll
         for (int mf = 0; mf < 4; ++mf) {
           const int row = 64 * wm + 16 * mf + mrow;
           const bf16x8 av =
-              __builtin_bit_cast(bf16x8, *(const u32x4*)(lds_a + row * kLdsStride + (32 * g + 8 * i) * 2));
+              __builtin_bit_cast(bf16x8, *(const u32x4*)(lds_a + row * kLdsStride + (32 * g4 + 8 * i) * 2));
 #pragma unroll
           for (int f = 0; f < 4; ++f)
             acc[mf][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[f], acc[mf][f], 0, 0, 0);
         }
       }
     } else {
-      // one MFMA per 32-wide block; lane supplies K = 32 j + 8 g .. + 7 of block j
-#pragma unroll
+      // one MFMA per 32-wide block; lane supplies K = 32 j + 8 g .. + 7 of block j, i.e.
+      // bytes 8 g .. of unit 16 j + lane%16 of its row group's run
+#pragma unroll 1
       for (int j = 0; j < 4; ++j) {
         bf16x8 bv[4];
         float ds[4];
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
-          bv[f] = i8x8_to_bf16x8(bcur[f].q[j][0], bcur[f].q[j][1]);
-          ds[f] = ((bcur[f].okm >> j) & 1) ? fp16_to_f32((uint16_t)bcur[f].s[j]) : 0.f;
+          const int unit = 16 * j + mrow;
+          const u32x2 q = *(const u32x2*)(lds_bq + fg[f] * BS::kRunQ + unit * 32 + 8 * g4);
+          bv[f] = i8x8_to_bf16x8(q[0], q[1]);
+          const bool ok = fcol[f] && 4 * c + j < nb;
+          ds[f] = ok ? fp16_to_f32(*(const uint16_t*)(lds_bs + fg[f] * BS::kRunS + unit * 2)) : 0.f;
         }
 #pragma unroll
         for (int mf = 0; mf < 4; ++mf) {
           const int row = 64 * wm + 16 * mf + mrow;
           const bf16x8 av =
-              __builtin_bit_cast(bf16x8, *(const u32x4*)(lds_a + row * kLdsStride + (32 * j + 8 * g) * 2));
+              __builtin_bit_cast(bf16x8, *(const u32x4*)(lds_a + row * kLdsStride + (32 * j + 8 * g4) * 2));
+          f32x4 t[4];
 #pragma unroll
-          for (int f = 0; f < 4; ++f) {
-            f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[f], f32x4{0.f, 0.f, 0.f, 0.f},
-                                                              0, 0, 0);
+          for (int f = 0; f < 4; ++f)
+            t[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[f], f32x4{0.f, 0.f, 0.f, 0.f}, 0,
+                                                           0, 0);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[mf][f][v] = fmaf(ds[f], t[v], acc[mf][f][v]);
-          }
+          for (int f = 0; f < 4; ++f)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[mf][f][v] = fmaf(ds[f], t[f][v], acc[mf][f][v]);
+          __builtin_amdgcn_sched_barrier(0);   // keep at most 4 products live
         }
       }
     }
-#pragma unroll
-    for (int f = 0; f < 4; ++f) bcur[f] = bnext[f];
   }
 
   // ---- epilogue: lane holds D[row 4*(lane/16) + v][col lane%16] of each 16x16 tile
+  const int g = g4;
 #pragma unroll
   for (int mf = 0; mf < 4; ++mf) {
 #pragma unroll

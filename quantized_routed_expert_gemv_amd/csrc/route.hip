@@ -40,8 +40,11 @@ __device__ void router_tile(const uint16_t* __restrict__ x, const uint16_t* __re
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int nsteps = H / 32;
-  const int s_begin = (int)((int64_t)nsteps * z / nsplit);
-  const int s_end = (int)((int64_t)nsteps * (z + 1) / nsplit);
+  // splits cover whole pairs of 32-wide steps, so no 128-byte line of a row is split
+  // between two workgroups (which may sit on different XCDs and both fetch it)
+  const int npairs = (nsteps + 1) / 2;
+  const int s_begin = 2 * (int)((int64_t)npairs * z / nsplit);
+  const int s_end = min(nsteps, 2 * (int)((int64_t)npairs * (z + 1) / nsplit));
   const int row = lane & 15;        // token (A) / expert (B) within the 16-tile
   const int kq = (lane >> 4) * 8;   // this lane's 8-element slice of the 32-step
   const bool tok_ok = t0 + row < T;
