@@ -688,15 +688,15 @@ __global__ __launch_bounds__(kGThreads) void k_gate_up_routed(
       rin.perm[tid] = perm_l[tid];
       rin.inv_perm[tid] = inv_l[tid];
     }
-    if (tid <= E) {
+    for (int e = tid; e <= E; e += kGThreads) {   // E + 1 offsets (E may equal the block)
       int c = 0, o = 0;
       for (int q = 0; q < n; ++q) {
         const int eq = ids_l[q];
-        c += eq == tid ? 1 : 0;
-        o += eq < tid ? 1 : 0;
+        c += eq == e ? 1 : 0;
+        o += eq < e ? 1 : 0;
       }
-      if (tid < E) rin.counts[tid] = c;
-      rin.offsets[tid] = o;
+      if (e < E) rin.counts[e] = c;
+      rin.offsets[e] = o;
     }
     for (int i = tid; i < na * kActStride; i += kGThreads) rin.act[1 + i] = (&act_l[0][0])[i];
     if (tid == 0) rin.act[0] = na;

@@ -253,8 +253,10 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
         bqv[f] = *(const u32x4*)(lds_bq + fg[f] * BS::kRunQ + lane * 16);
-        const bool ok = fcol[f] && 4 * c + g4 < nb;
-        bsc[f] = ok ? e8m0_to_f32(lds_bs[fg[f] * BS::kRunS + lane]) : 0.f;
+        // read unconditionally, mask arithmetically (a conditional read becomes a branch)
+        const uint32_t sb = lds_bs[fg[f] * BS::kRunS + lane];
+        const uint32_t keep = (fcol[f] && 4 * c + g4 < nb) ? 0xffffffffu : 0u;
+        bsc[f] = __uint_as_float((sb << 23) & keep);   // E8M0 -> 2^(b-127), or +0
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -283,8 +285,9 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
           const int unit = 16 * j + mrow;
           const u32x2 q = *(const u32x2*)(lds_bq + fg[f] * BS::kRunQ + unit * 32 + 8 * g4);
           bv[f] = i8x8_to_bf16x8(q[0], q[1]);
-          const bool ok = fcol[f] && 4 * c + j < nb;
-          ds[f] = ok ? fp16_to_f32(*(const uint16_t*)(lds_bs + fg[f] * BS::kRunS + unit * 2)) : 0.f;
+          const uint32_t db = *(const uint16_t*)(lds_bs + fg[f] * BS::kRunS + unit * 2);
+          const uint32_t keep = (fcol[f] && 4 * c + j < nb) ? 0xffffu : 0u;
+          ds[f] = fp16_to_f32((uint16_t)(db & keep));   // fp16 +0 when masked
         }
 #pragma unroll
         for (int mf = 0; mf < 4; ++mf) {

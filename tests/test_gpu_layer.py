@@ -102,6 +102,57 @@ def test_layer_dense_and_full_mixture_special_cases():
         run_layer(cfg)
 
 
+@pytest.mark.parametrize("cfg", [
+    # 256 experts: four logits per lane in the top-k; 8 experts chosen
+    synth.Config("e256_t1", 1, 256, 512, 256, 8, "mxfp4", 1.2, "perm", 31, 1),
+    # 4 tokens x 8 choices = 32 pairs, 64 experts (256 logits): the fused decode limits
+    synth.Config("e64_t4_k8", 4, 512, 256, 64, 8, "mxfp4", 1.1, "perm", 32, 1),
+    # 3 tokens (a partly used 4-token pass), Q8_0
+    synth.Config("q8_t3", 3, 256, 512, 16, 3, "q8_0", None, "perm", 33, 1),
+    # 2 tokens sharing experts (8 experts, 6 choices each)
+    synth.Config("shared_t2", 2, 256, 256, 8, 6, "mxfp4", None, "perm", 34, 1),
+])
+def test_layer_decode_routing_edge_cases(cfg):
+    """Shapes at the edges of the decode path that finishes the routing in the gate/up
+    kernel (up to 4 tokens, up to 256 (token, expert) logits, up to 32 pairs)."""
+    print(f"layer {cfg.name}", flush=True)
+    run_layer(cfg)
+
+
+def test_layer_decode_invalid_slot_sets_flag_and_zeroes():
+    """A slot outside the pool: the flag is set and that expert adds nothing."""
+    cfg = synth.config("gptoss_decode_t4", T=2, H=256, I=512)
+    L = make_case(cfg)
+    ids, w, _ = omoe.route(L.x, L.wr, L.bias, cfg.k)
+    pool, x, wr, bias, sm = to_device(L)
+    bad_e = int(ids[0, 0])
+    sm_bad = sm.clone()
+    sm_bad[bad_e] = cfg.E + 5
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out, ws = qm.layer(pool, sm_bad, wr, bias, x, cfg.k, err_flags=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & 1
+    im = {n: t.cpu() for n, t in ws.intermediates().items()}
+    counts, offsets, perm, inv = omoe.bucket(ids, cfg.E)
+    lo, hi = offsets[bad_e], offsets[bad_e + 1]
+    assert torch.all(im["h"][lo:hi].float() == 0) and torch.all(im["y"][lo:hi] == 0)
+    # every other pair is as in the valid layer, and out is their weighted sum
+    ref, ws2 = qm.layer(pool, sm, wr, bias, x, cfg.k)
+    torch.cuda.synchronize()
+    y_ok = ws2.intermediates()["y"].cpu().numpy()
+    keep = np.ones(perm.size, dtype=bool)
+    keep[lo:hi] = False
+    assert np.array_equal(im["y"].numpy()[keep], y_ok[keep])
+    y0 = y_ok.copy()
+    y0[~keep] = 0.0
+    wg = im["w"].numpy()
+    exp = np.zeros((cfg.T, cfg.H), dtype=np.float64)
+    for t in range(cfg.T):
+        for j in range(cfg.k):
+            exp[t] += np.float64(wg[t, j]) * y0[inv[t * cfg.k + j]]
+    assert np.allclose(out.cpu().numpy(), exp, rtol=1e-5, atol=1e-5)
+
+
 def test_layer_empty_input_is_a_no_op():
     cfg = synth.config("tiny", T=0)
     L = synth.make_layer(cfg)
