@@ -166,6 +166,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                 "kernel": "gate/up GEMV (k_gemv)", "work_per_launch": bytes_per_launch}
+    roof["traffic"] = measured_traffic(cfg.name)
     roof["avg_launch_us"] = round(kern_avg_s * 1e6, 3)
     roof["method"] = ("HIP events recorded on the kernel's stream around every gate/up launch "
                       f"of {args.steps} eager steps ({len(kern_ms)} launches)")
@@ -188,6 +189,41 @@ def main():
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(cfg, host_keep, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def library_sources_digest() -> str:
+    """SHA-256 over the library's sources (kernels and the C ABI), in name order."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    files = [os.path.join(root, "include", "moe.h")]
+    csrc = os.path.join(root, "quantized_routed_expert_gemv_amd", "csrc")
+    files += sorted(os.path.join(csrc, f) for f in os.listdir(csrc))
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel, from the rocprofv3 FETCH_SIZE and
+    WRITE_SIZE summary in profiles/ (each counter scaled by its reading on a copy of known
+    size), or None when there is none for this workload or the kernels have changed since
+    the counters were taken."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        "hbm_traffic_gate_up.md")
+    if not os.path.exists(path):
+        return None
+    digest = library_sources_digest()
+    with open(path) as fh:
+        for line in fh:
+            if not line.startswith("traffic:"):
+                continue
+            kv = dict(item.split("=", 1) for item in line.split()[1:])
+            if kv.get("workload") == workload and kv.get("sources") == digest:
+                return int(kv["bytes"])
+    return None
 
 
 class HipEvents:

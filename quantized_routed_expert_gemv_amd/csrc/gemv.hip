@@ -663,7 +663,7 @@ __global__ __launch_bounds__(kGThreads) void k_gate_up_routed(
     if (has) {
       perm_l[pos] = lane;
       inv_l[lane] = pos;
-      tokp_l[pos] = lane / k;
+      tokp_l[pos] = (lane >= k ? 1 : 0) + (lane >= 2 * k ? 1 : 0) + (lane >= 3 * k ? 1 : 0);  // lane / k, T <= 4
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();

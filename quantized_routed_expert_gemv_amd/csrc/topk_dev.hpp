@@ -36,21 +36,31 @@ __device__ void wave_topk_softmax_impl(const float* logit, int E, int k, int32_t
     x = (x != x) ? -INFINITY : x;
     val[i] = x;
     key[i] = e < E ? (((uint64_t)order_key(x) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e)) : 0ull;
-    if (e < E4) sc.keys[e] = key[i];
+    if (SLOTS == 1 || e < E4) sc.keys[e] = key[i];   // one slot: all 64 keys written
     rank[i] = 0;
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  // every key against every key, four at a time as LDS broadcasts (padding keys are 0,
-  // below every real key)
-  for (int e2 = 0; e2 < E4; e2 += 4) {
-    const u64x2 a = *(const u64x2*)&sc.keys[e2];
-    const u64x2 b = *(const u64x2*)&sc.keys[e2 + 2];
+  // every key against every key, as LDS broadcasts (padding keys are 0, below every real
+  // key)
+  if constexpr (SLOTS == 1) {
+    // all 64 slots hold a key: read them in one batch, no loop-carried LDS latency
+    u64x2 kv[kWave / 2];
 #pragma unroll
-    for (int i = 0; i < SLOTS; ++i)
-      rank[i] += (int)(a[0] > key[i]) + (int)(a[1] > key[i]) + (int)(b[0] > key[i]) +
-                 (int)(b[1] > key[i]);
+    for (int q = 0; q < kWave / 2; ++q) kv[q] = *(const u64x2*)&sc.keys[2 * q];
+#pragma unroll
+    for (int q = 0; q < kWave / 2; ++q)
+      rank[0] += (int)(kv[q][0] > key[0]) + (int)(kv[q][1] > key[0]);
+  } else {
+    for (int e2 = 0; e2 < E4; e2 += 4) {
+      const u64x2 a = *(const u64x2*)&sc.keys[e2];
+      const u64x2 b = *(const u64x2*)&sc.keys[e2 + 2];
+#pragma unroll
+      for (int i = 0; i < SLOTS; ++i)
+        rank[i] += (int)(a[0] > key[i]) + (int)(a[1] > key[i]) + (int)(b[0] > key[i]) +
+                   (int)(b[1] > key[i]);
+    }
   }
 #pragma unroll
   for (int i = 0; i < SLOTS; ++i) {
