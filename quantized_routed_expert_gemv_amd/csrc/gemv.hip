@@ -30,6 +30,7 @@ namespace {
 constexpr int kGThreads = 256;
 constexpr int kGWaves = kGThreads / kWave;
 constexpr int kU = 8;          // chunks per wave per batch (all loads issued first)
+constexpr int kRoutedMaxWG = 1024;   // workgroups of the routed gate/up kernel (4 per CU)
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
 // Expert weights are streamed once per call: nontemporal loads keep them from displacing
@@ -567,14 +568,15 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
 // The router's partial logits (one set per slice of H) come from the previous kernel.
 // Every workgroup finishes the routing itself from them -- sum in split order, top-k per
 // token, counting sort of the T*k pairs, list of active experts -- so no workgroup waits
-// for another; workgroup (0, 0) also stores the routing for the stages after this kernel.
+// for another; workgroup 0 also stores the routing for the stages after this kernel. Each
+// workgroup then serves units (row group, active expert) blockIdx.x, + gridDim.x, ...
 // Everything that does not depend on the routing (the partials, the slot map, the bias and
 // the tokens' activation rows) is loaded in one round trip at the start; then the expert's
 // gate and up rows of this row group are streamed and each chunk is consumed as it
 // arrives. Chunk order, per-lane accumulation and the reduction are those of k_gemv, so
 // the two give bit-identical h.
 template <int FMT, int NT>
-__global__ __launch_bounds__(kGThreads) void k_gate_up_routed(
+__global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
     const uint8_t* __restrict__ gq, const uint8_t* __restrict__ gsc,
     const uint8_t* __restrict__ uq, const uint8_t* __restrict__ usc, int64_t qslot,
     int64_t sslot, const int32_t* __restrict__ slot_map, int n_slots, int E, int k,
@@ -681,7 +683,7 @@ __global__ __launch_bounds__(kGThreads) void k_gate_up_routed(
   }
   __syncthreads();
   const int na = nact_l;
-  if (blockIdx.x == 0 && blockIdx.y == 0) {   // publish the routing
+  if (blockIdx.x == 0) {   // publish the routing
     if (tid < n) {
       rin.ids[tid] = ids_l[tid];
       rin.w[tid] = w_l[tid];
@@ -701,114 +703,121 @@ __global__ __launch_bounds__(kGThreads) void k_gate_up_routed(
     for (int i = tid; i < na * kActStride; i += kGThreads) rin.act[1 + i] = (&act_l[0][0])[i];
     if (tid == 0) rin.act[0] = na;
   }
-  const int j = blockIdx.y;
-  if (j >= na) return;
-  const int slot = act_l[j][1], lo = act_l[j][2], hi = act_l[j][3];
-  const int np = hi - lo;   // <= T <= NT
-  const int rg = blockIdx.x;
-  const int r0 = rg * 16;
-  if (slot < 0 || slot >= n_slots) {
-    for (int i = tid; i < np * 16; i += kGThreads)
-      h_out[(int64_t)(lo + i / 16) * I + r0 + i % 16] = 0;
-    if (tid == 0 && err_flags) atomicOr(err_flags, 1u);
-    return;
-  }
-
-  // 4. stream this row group of the expert's gate and up rows
+  // 4. the workgroup's units u = blockIdx.x, + gridDim.x, ...: unit u is row group
+  //    u % n_rg of active expert u / n_rg (the routing above is paid once per workgroup)
+  const int n_rg = I / 16;
   const int nb = H / 32;
   const int nc = (nb + LM::kBlocksPerChunk - 1) / LM::kBlocksPerChunk;
   constexpr int64_t cb = code_bytes_per_block(FMT), sb = scale_bytes_per_block(FMT);
-  const int64_t unit0 = (int64_t)rg * nb * 16;
   const int lane_unit = FMT == kMXFP4 ? lane : (lane >> 1);
-  const uint8_t* qa = gq + slot * qslot + unit0 * cb + lane * 16;
-  const uint8_t* qb = uq + slot * qslot + unit0 * cb + lane * 16;
-  const uint8_t* sa = gsc + slot * sslot + (unit0 + lane_unit) * sb;
-  const uint8_t* sbp = usc + slot * sslot + (unit0 + lane_unit) * sb;
   const int lblk = LM::blk(lane);
   const int koff = LM::koff(lane);
-  const uint16_t* xrow[NT];
-#pragma unroll
-  for (int i = 0; i < NT; ++i) {
-    const int t = act_l[j][4 + (i < 4 ? i : 3)];
-    xrow[i] = &xs[(t >= 0 ? t : 0) * H];
-  }
-  float acc[2][NT];
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int i = 0; i < NT; ++i) acc[m][i] = 0.f;
-  for (int cbase = 0; cbase < nc; cbase += kGWaves * kU) {
-    Chunk ca[kU], cbk[kU];
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int c = cbase + wave + kGWaves * u;
-      const int b = c * LM::kBlocksPerChunk + lblk;
-      const bool ok = c < nc && b < nb;
-      const int cs = ok ? c : 0;
-      load_chunk<FMT>(ca[u], qa + (int64_t)cs * 1024, sa + (int64_t)cs * 64, ok);
-      load_chunk<FMT>(cbk[u], qb + (int64_t)cs * 1024, sbp + (int64_t)cs * 64, ok);
+  for (int unit = blockIdx.x;; unit += gridDim.x) {
+    const int j = unit / n_rg;
+    if (j >= na) break;
+    const int rg = unit % n_rg;
+    const int slot = act_l[j][1], lo = act_l[j][2], hi = act_l[j][3];
+    const int np = hi - lo;   // <= T <= NT
+    const int r0 = rg * 16;
+    if (slot < 0 || slot >= n_slots) {
+      for (int i = tid; i < np * 16; i += kGThreads)
+        h_out[(int64_t)(lo + i / 16) * I + r0 + i % 16] = 0;
+      if (tid == 0 && err_flags) atomicOr(err_flags, 1u);
+      continue;
     }
-    __builtin_amdgcn_sched_barrier(0);   // the whole batch in flight before any is used
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int c = cbase + wave + kGWaves * u;
-      const int xo = ca[u].ok ? c * LM::kKPerChunk + koff : 0;   // masked: any valid part
-      bf16x2 w[16];
-      uint32_t xw[LM::kXWords];
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const Chunk& ch = m == 0 ? ca[u] : cbk[u];
-        widen<FMT>(ch, w);
-#pragma unroll
-        for (int i = 0; i < NT; ++i) {
-#pragma unroll
-          for (int q = 0; q < LM::kXWords / 4; ++q) {
-            const u32x4 xq = *(const u32x4*)(xrow[i] + xo + q * 8);
-            xw[4 * q + 0] = xq[0];
-            xw[4 * q + 1] = xq[1];
-            xw[4 * q + 2] = xq[2];
-            xw[4 * q + 3] = xq[3];
-          }
-          acc[m][i] = dot_chunk<FMT>(w, xw, ch.ok ? ch.s : 0u, acc[m][i]);
-        }
-      }
-    }
-  }
-  // 5. lanes that share a row, then the 4 waves in a fixed order; SwiGLU; h in bf16
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
+    // stream this row group of the expert's gate and up rows
+    const int64_t unit0 = (int64_t)rg * nb * 16;
+    const uint8_t* qa = gq + slot * qslot + unit0 * cb + lane * 16;
+    const uint8_t* qb = uq + slot * qslot + unit0 * cb + lane * 16;
+    const uint8_t* sa = gsc + slot * sslot + (unit0 + lane_unit) * sb;
+    const uint8_t* sbp = usc + slot * sslot + (unit0 + lane_unit) * sb;
+    const uint16_t* xrow[NT];
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
-      float a = acc[m][i];
-      if constexpr (FMT == kMXFP4) {
-        a += wave_xor(a, 16);
-        a += wave_xor(a, 32);
-      } else {
-        a += wave_xor(a, 1);
-        a += wave_xor(a, 32);
-      }
-      acc[m][i] = a;
+      const int t = act_l[j][4 + (i < 4 ? i : 3)];
+      xrow[i] = &xs[(t >= 0 ? t : 0) * H];
     }
-  const bool writer = FMT == kMXFP4 ? (lane < 16) : (lane < 32 && (lane & 1) == 0);
-  if (writer) {
-    const int r = LM::row(lane);
+    float acc[2][NT];
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int i = 0; i < NT; ++i) red[wave][i][m][r] = acc[m][i];
-  }
-  __syncthreads();
-  if (tid < NT * 16) {
-    const int i = tid / 16, r = tid % 16;
-    if (i < np) {
-      float g = red[0][i][0][r], u = red[0][i][1][r];
+      for (int i = 0; i < NT; ++i) acc[m][i] = 0.f;
+    constexpr int kRU = NT >= 4 ? 6 : kU;   // chunks per wave per batch (fewer live
+                                            // registers with 4 tokens)
+    for (int cbase = 0; cbase < nc; cbase += kGWaves * kRU) {
+      Chunk ca[kRU], cbk[kRU];
 #pragma unroll
-      for (int q = 1; q < kGWaves; ++q) {
-        g += red[q][i][0][r];
-        u += red[q][i][1][r];
+      for (int u = 0; u < kRU; ++u) {
+        const int c = cbase + wave + kGWaves * u;
+        const int b = c * LM::kBlocksPerChunk + lblk;
+        const bool ok = c < nc && b < nb;
+        const int cs = ok ? c : 0;
+        load_chunk<FMT>(ca[u], qa + (int64_t)cs * 1024, sa + (int64_t)cs * 64, ok);
+        load_chunk<FMT>(cbk[u], qb + (int64_t)cs * 1024, sbp + (int64_t)cs * 64, ok);
       }
-      h_out[(int64_t)(lo + i) * I + r0 + r] = f32_to_bf16_rne(silu_mul(g, u));
+      __builtin_amdgcn_sched_barrier(0);   // the whole batch in flight before any is used
+#pragma unroll
+      for (int u = 0; u < kRU; ++u) {
+        const int c = cbase + wave + kGWaves * u;
+        const int xo = ca[u].ok ? c * LM::kKPerChunk + koff : 0;   // masked: any valid part
+        bf16x2 w[16];
+        uint32_t xw[LM::kXWords];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const Chunk& ch = m == 0 ? ca[u] : cbk[u];
+          widen<FMT>(ch, w);
+#pragma unroll
+          for (int i = 0; i < NT; ++i) {
+#pragma unroll
+            for (int q = 0; q < LM::kXWords / 4; ++q) {
+              const u32x4 xq = *(const u32x4*)(xrow[i] + xo + q * 8);
+              xw[4 * q + 0] = xq[0];
+              xw[4 * q + 1] = xq[1];
+              xw[4 * q + 2] = xq[2];
+              xw[4 * q + 3] = xq[3];
+            }
+            acc[m][i] = dot_chunk<FMT>(w, xw, ch.ok ? ch.s : 0u, acc[m][i]);
+          }
+        }
+      }
     }
+    // 5. lanes that share a row, then the 4 waves in a fixed order; SwiGLU; h in bf16
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        float a = acc[m][i];
+        if constexpr (FMT == kMXFP4) {
+          a += wave_xor(a, 16);
+          a += wave_xor(a, 32);
+        } else {
+          a += wave_xor(a, 1);
+          a += wave_xor(a, 32);
+        }
+        acc[m][i] = a;
+      }
+    const bool writer = FMT == kMXFP4 ? (lane < 16) : (lane < 32 && (lane & 1) == 0);
+    if (writer) {
+      const int r = LM::row(lane);
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int i = 0; i < NT; ++i) red[wave][i][m][r] = acc[m][i];
+    }
+    __syncthreads();
+    if (tid < NT * 16) {
+      const int i = tid / 16, r = tid % 16;
+      if (i < np) {
+        float g = red[0][i][0][r], u = red[0][i][1][r];
+#pragma unroll
+        for (int q = 1; q < kGWaves; ++q) {
+          g += red[q][i][0][r];
+          u += red[q][i][1][r];
+        }
+        h_out[(int64_t)(lo + i) * I + r0 + r] = f32_to_bf16_rne(silu_mul(g, u));
+      }
+    }
+    __syncthreads();   // red is rewritten by the next unit
   }
 }
 
@@ -873,7 +882,8 @@ hipError_t launch_gate_up_route(int fmt, const PoolView& gate, const PoolView& u
   if (!route_fused_ok(T, H, E) || rin.T != T || rin.ns != route_fused_split(H) ||
       gate.q_slot != up.q_slot || gate.s_slot != up.s_slot)
     return hipErrorInvalidValue;
-  dim3 grid(I / 16, min(E, T * k));
+  const int n_units = (I / 16) * min(E, T * k);
+  dim3 grid(min(n_units, kRoutedMaxWG));
 #define MOE_ROUTED_CASE(F, N)                                                                 \
   hipLaunchKernelGGL((k_gate_up_routed<F, N>), grid, dim3(kGThreads), 0, stream, gate.q,     \
                      gate.s, up.q, up.s, gate.q_slot, gate.s_slot, slot_map, n_slots, E, k, x, \

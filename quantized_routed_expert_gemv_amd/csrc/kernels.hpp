@@ -57,7 +57,7 @@ hipError_t launch_down_gemv(int fmt, const PoolView& down, const int32_t* slot_m
                             int E, int T, int k, int H, int I, const int32_t* offsets,
                             const uint16_t* h, float* y, uint32_t* err, hipStream_t stream);
 // Gate/up GEMV that first finishes a split router (see RouteIn); every workgroup derives
-// its expert from the partials, workgroup (0, 0) stores the routing.
+// its expert from the partials, workgroup 0 stores the routing.
 hipError_t launch_gate_up_route(int fmt, const PoolView& gate, const PoolView& up,
                                 const int32_t* slot_map, int n_slots, int E, const uint16_t* x,
                                 int T, int k, int H, int I, const RouteIn& rin, uint16_t* h,
