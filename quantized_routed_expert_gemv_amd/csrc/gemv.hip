@@ -414,8 +414,8 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
     j = wave % n_act;
     q = wave / n_act;
     slot = __builtin_amdgcn_readlane(av, 1 + kActStride * j + 1);
-    lo = __builtin_amdgcn_readlane(av, 1 + kActStride * j + 2);
-    hi = __builtin_amdgcn_readlane(av, 1 + kActStride * j + 3);
+    lo = min(max(__builtin_amdgcn_readlane(av, 1 + kActStride * j + 2), 0), np);
+    hi = min(max(__builtin_amdgcn_readlane(av, 1 + kActStride * j + 3), lo), np);
   }
   bool busy = q < per;
   bool valid = slot >= 0 && slot < n_slots;
@@ -595,6 +595,7 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
   __shared__ unsigned long long hit_l[kMaxE / 64];
   __shared__ int act_l[kFuseMaxPairs][kActStride];
   __shared__ int nact_l;
+  __shared__ int rank_l[kWave];
   __shared__ float red[kGWaves][NT][2][16];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -616,6 +617,7 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
   for (int r = 0; r < kXP; ++r)
     xv[r] = *(const u32x4*)(x + (int64_t)min(tid + r * kGThreads, xp_n - 1) * 8);
   if (tid < kMaxE / 64) hit_l[tid] = 0ull;
+  if (tid < kWave) rank_l[tid] = 0;
   if (tid < E) slot_l[tid] = sm;
   if (tid < TE) lg_l[tid] = finish_logit(v, ns, bz);
 #pragma unroll
@@ -625,61 +627,123 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
   }
   __syncthreads();
 
-  // 2. top-k + softmax, wave t for token t
-  if (wave < T) wave_topk_softmax(&lg_l[wave * E], E, k, ids_l + wave * k, w_l + wave * k, tk_l[wave]);
-  __syncthreads();
+  // steps 2 and 3 for any T (used unless the one-token path below applies)
+  auto route_general = [&]() {
+    // 2. top-k + softmax, wave t for token t
+    if (wave < T) wave_topk_softmax(&lg_l[wave * E], E, k, ids_l + wave * k, w_l + wave * k, tk_l[wave]);
+    __syncthreads();
 
-  // 3. counting sort of the n = T*k pairs by wave 0. Pair p (expert e_p) has the unique key
-  //    32*e_p + p; its bucket position is the number of smaller keys, its expert's range
-  //    [lo, hi) the numbers of keys below 32*e_p and below 32*(e_p + 1), and its expert's
-  //    index among the active ones the number of hit experts below e_p.
-  if (wave == 0) {
-    const bool has = lane < n;
-    const int ep = has ? ids_l[lane] : 0;
-    const int key = has ? ep * kFuseMaxPairs + lane : 0x7fffffff;
-    if (lane < kFuseMaxPairs) key_l[lane] = key;
-    if (has) atomicOr(&hit_l[ep >> 6], 1ull << (ep & 63));
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    const int klo = ep * kFuseMaxPairs, khi = klo + kFuseMaxPairs;
-    int pos = 0, lo = 0, hi = 0;
-    for (int q = 0; q < n; q += 4) {
-      const i32x4 kq = *(const i32x4*)&key_l[q];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        pos += kq[c] < key ? 1 : 0;
-        lo += kq[c] < klo ? 1 : 0;
-        hi += kq[c] < khi ? 1 : 0;
+    // 3. counting sort of the n = T*k pairs by wave 0. Pair p (expert e_p) has the unique key
+    //    32*e_p + p; its bucket position is the number of smaller keys, its expert's range
+    //    [lo, hi) the numbers of keys below 32*e_p and below 32*(e_p + 1), and its expert's
+    //    index among the active ones the number of hit experts below e_p.
+    if (wave == 0) {
+      const bool has = lane < n;
+      const int ep = has ? ids_l[lane] : 0;
+      const int key = has ? ep * kFuseMaxPairs + lane : 0x7fffffff;
+      if (lane < kFuseMaxPairs) key_l[lane] = key;
+      if (has) atomicOr(&hit_l[ep >> 6], 1ull << (ep & 63));
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      const int klo = ep * kFuseMaxPairs, khi = klo + kFuseMaxPairs;
+      int pos = 0, lo = 0, hi = 0;
+      for (int q = 0; q < n; q += 4) {
+        const i32x4 kq = *(const i32x4*)&key_l[q];
+  #pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          pos += kq[c] < key ? 1 : 0;
+          lo += kq[c] < klo ? 1 : 0;
+          hi += kq[c] < khi ? 1 : 0;
+        }
       }
+      const int hw = ep >> 6;
+      int aidx = __popcll(hit_l[hw] & ((1ull << (ep & 63)) - 1ull));
+      int nact = 0;
+  #pragma unroll
+      for (int w = 0; w < kMaxE / 64; ++w) {
+        const int c = __popcll(hit_l[w]);
+        nact += c;
+        aidx += w < hw ? c : 0;
+      }
+      if (has) {
+        perm_l[pos] = lane;
+        inv_l[lane] = pos;
+        tokp_l[pos] = (lane >= k ? 1 : 0) + (lane >= 2 * k ? 1 : 0) + (lane >= 3 * k ? 1 : 0);  // lane / k, T <= 4
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      if (has && pos == lo) {   // the first pair of its expert writes the expert's entry
+        int* a = act_l[aidx];
+        a[0] = ep;
+        a[1] = slot_l[ep];
+        a[2] = lo;
+        a[3] = hi;
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) a[4 + i] = lo + i < hi ? tokp_l[lo + i] : -1;
+      }
+      if (lane == 0) nact_l = nact;
     }
-    const int hw = ep >> 6;
-    int aidx = __popcll(hit_l[hw] & ((1ull << (ep & 63)) - 1ull));
-    int nact = 0;
-#pragma unroll
-    for (int w = 0; w < kMaxE / 64; ++w) {
-      const int c = __popcll(hit_l[w]);
-      nact += c;
-      aidx += w < hw ? c : 0;
+  };
+  if constexpr (NT == 1) {   // NT == 1 means T == 1
+    if (E <= kWave) {
+      // 2'. one token, at most 64 experts: every wave holds all E keys (lane e) and counts,
+      //     for each, the keys above it among its quarter of the experts (broadcast with
+      //     readlane); the four counts meet in rank_l. Same keys and ranks as
+      //     wave_topk_softmax, so the same choices and order.
+      float v = lane < E ? lg_l[lane] : -INFINITY;
+      v = (v != v) ? -INFINITY : v;
+      const uint64_t key = lane < E ? topk_key(v, lane) : 0ull;
+      const uint32_t key_hi = (uint32_t)(key >> 32), key_lo = (uint32_t)key;
+      constexpr int kPerWave = kWave / kGWaves;
+      int r = 0;
+  #pragma unroll
+      for (int q = 0; q < kPerWave; ++q) {
+        const int c = wave * kPerWave + q;
+        // readlane returns a signed int: widen each half as unsigned
+        const uint64_t kc =
+            ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)key_hi, c) << 32) |
+            (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)key_lo, c);
+        r += kc > key ? 1 : 0;
+      }
+      atomicAdd(&rank_l[lane], r);
+      __syncthreads();
+      if (wave == 0) {
+        const int rank = rank_l[lane];
+        if (lane < E && rank < k) {
+          ids_l[rank] = lane;
+          tk_l[0].zs[rank] = v;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        wave_softmax_chosen(tk_l[0].zs, k, w_l);
+        // 3'. the k pairs of the one token (distinct experts): pair j goes to position
+        //     #{j' : e_j' < e_j}, and is its expert's only pair
+        const int ej = lane < k ? ids_l[lane] : 0x7fffffff;
+        int pos = 0;
+        for (int q = 0; q < k; ++q) pos += __builtin_amdgcn_readlane(ej, q) < ej ? 1 : 0;
+        if (lane < k) {
+          perm_l[pos] = lane;
+          inv_l[lane] = pos;
+          int* a = act_l[pos];
+          a[0] = ej;
+          a[1] = slot_l[ej];
+          a[2] = pos;
+          a[3] = pos + 1;
+          a[4] = 0;
+          a[5] = -1;
+          a[6] = -1;
+          a[7] = -1;
+        }
+        if (lane == 0) nact_l = k;
+      }
+    } else {
+      route_general();
     }
-    if (has) {
-      perm_l[pos] = lane;
-      inv_l[lane] = pos;
-      tokp_l[pos] = (lane >= k ? 1 : 0) + (lane >= 2 * k ? 1 : 0) + (lane >= 3 * k ? 1 : 0);  // lane / k, T <= 4
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    if (has && pos == lo) {   // the first pair of its expert writes the expert's entry
-      int* a = act_l[aidx];
-      a[0] = ep;
-      a[1] = slot_l[ep];
-      a[2] = lo;
-      a[3] = hi;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[4 + i] = lo + i < hi ? tokp_l[lo + i] : -1;
-    }
-    if (lane == 0) nact_l = nact;
+  } else {
+    route_general();
   }
   __syncthreads();
   const int na = nact_l;
@@ -716,8 +780,11 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
     const int j = unit / n_rg;
     if (j >= na) break;
     const int rg = unit % n_rg;
-    const int slot = act_l[j][1], lo = act_l[j][2], hi = act_l[j][3];
-    const int np = hi - lo;   // <= T <= NT
+    const int slot = act_l[j][1];
+    // the bucket range as the routing above wrote it, kept inside [0, n) and to at most NT
+    // pairs whatever it holds, so that no store below can leave h
+    const int lo = min(max(act_l[j][2], 0), n);
+    const int np = min(max(act_l[j][3] - lo, 0), min(NT, n - lo));
     const int r0 = rg * 16;
     if (slot < 0 || slot >= n_slots) {
       for (int i = tid; i < np * 16; i += kGThreads)

@@ -21,6 +21,22 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Softmax over the k chosen logits zs[0..k) (LDS, in rank order), by one wave:
+// z_j = exp(L_j - L_0), sum = z_0 + z_1 + ... (increasing j), w_j = z_j / sum.
+__device__ __forceinline__ void wave_softmax_chosen(const float* zs, int k, float* w_out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const float l0 = zs[0];
+  const float z = lane < k ? expf(zs[lane < k ? lane : 0] - l0) : 0.f;
+  float sum = 0.f;
+  for (int j = 0; j < k; ++j) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), j));
+  if (lane < k) w_out[lane] = z / sum;
+}
+
+// The key of expert e with logit x: order_key(x) above, then the lower index first.
+__device__ __forceinline__ uint64_t topk_key(float x, int e) {
+  return ((uint64_t)order_key(x) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
+}
+
 template <int SLOTS>
 __device__ void wave_topk_softmax_impl(const float* logit, int E, int k, int32_t* ids_out,
                                        float* w_out, TopkScratch& sc, int* ids_lds) {
@@ -35,7 +51,7 @@ __device__ void wave_topk_softmax_impl(const float* logit, int E, int k, int32_t
     float x = e < E ? logit[e] : -INFINITY;
     x = (x != x) ? -INFINITY : x;
     val[i] = x;
-    key[i] = e < E ? (((uint64_t)order_key(x) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e)) : 0ull;
+    key[i] = e < E ? topk_key(x, e) : 0ull;
     if (SLOTS == 1 || e < E4) sc.keys[e] = key[i];   // one slot: all 64 keys written
     rank[i] = 0;
   }
@@ -74,11 +90,7 @@ __device__ void wave_topk_softmax_impl(const float* logit, int E, int k, int32_t
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  const float l0 = sc.zs[0];
-  const float z = lane < k ? expf(sc.zs[lane < k ? lane : 0] - l0) : 0.f;
-  float sum = 0.f;
-  for (int j = 0; j < k; ++j) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), j));
-  if (lane < k) w_out[lane] = z / sum;
+  wave_softmax_chosen(sc.zs, k, w_out);
 }
 
 // Top-k of one token's E logits (LDS), by one wave. Ties go to the lower index; NaN counts
