@@ -20,6 +20,9 @@ of that structure:
   bucket   pairs p = t*k + j grouped by expert, ascending p inside each expert
   expert   g = Wg x, u = Wu x, h = bf16_RNE(silu(g) * u), y = Wd h, silu(z) = z / (1 + e^-z)
   combine  out[t] = sum_{j<k} w[t,j] * y[pair (t, j)]
+  misses   an expert whose slot is SLOT_MISS is not resident: its pairs are listed (in bucket
+           order) for computation elsewhere, the resident pairs are combined, and the
+           missed pairs' outputs are merged afterwards, per token in j order
 All arithmetic is fp64; the one rounding is h to bf16, taken directly from fp64.
 """
 from __future__ import annotations
@@ -105,6 +108,8 @@ def silu(z: np.ndarray) -> np.ndarray:
 
 
 def _slot_weights(planes, fmt, slot, name):
+    if slot < 0:
+        raise ValueError(f"slot {slot}: a non-resident expert has no weights in the pool")
     return codecs.dequant(fmt, planes[name + "_q"][slot], planes[name + "_s"][slot])
 
 
@@ -206,3 +211,69 @@ def layer(planes: dict, fmt: str, slot_map, wr_bits, bias, x_bits, k: int):
     out = combine(y, inv_perm, w, T, k)
     return dict(logits=L, ids=ids, w=w, counts=counts, offsets=offsets, perm=perm,
                 inv_perm=inv_perm, a=a, h=h, y=y, out=out)
+
+
+# -------------------------------------------------------------- resident hits and misses
+#
+# llama.cpp discussion "fixed GPU expert working set with Native CPU miss execution",
+# original post: the selected expert IDs are split into resident hits, served from the GPU
+# pool, and misses, computed elsewhere; the weighted outputs are then merged. The same post
+# proposes public hit/miss counters.
+
+SLOT_MISS = -1
+
+
+def miss_list(slot_map, offsets, perm):
+    """The pairs routed to non-resident experts (slot_map[e] == SLOT_MISS).
+
+    Returns (miss_pos, miss_of_pair, counters):
+      miss_pos      int32 [n_miss]: their bucket positions, increasing (expert by expert)
+      miss_of_pair  int32 [T*k]: for pair p = t*k + j, its index in miss_pos, or -1
+      counters      int32 [4]: resident pairs, missed pairs, resident experts with pairs,
+                    non-resident experts with pairs
+    """
+    offsets = np.asarray(offsets, dtype=np.int64)
+    perm = np.asarray(perm, dtype=np.int64)
+    E = offsets.size - 1
+    n = perm.size
+    miss_pos = []
+    hit_e = miss_e = 0
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        if int(slot_map[e]) == SLOT_MISS:
+            miss_pos.extend(range(lo, hi))
+            miss_e += 1
+        else:
+            hit_e += 1
+    miss_pos = np.array(miss_pos, dtype=np.int32)
+    miss_of_pair = np.full(n, -1, dtype=np.int32)
+    for i, pos in enumerate(miss_pos):
+        miss_of_pair[perm[pos]] = i
+    counters = np.array([n - miss_pos.size, miss_pos.size, hit_e, miss_e], dtype=np.int32)
+    return miss_pos, miss_of_pair, counters
+
+
+def combine_hits(y: np.ndarray, inv_perm, w: np.ndarray, T: int, k: int, miss_of_pair):
+    """out[t] = sum over the resident pairs j of w[t,j] * y[inv_perm[t*k + j]], j order."""
+    inv_perm = np.asarray(inv_perm, dtype=np.int64)
+    out = np.zeros((T, y.shape[1]))
+    for t in range(T):
+        for j in range(k):
+            p = t * k + j
+            if miss_of_pair[p] < 0:
+                out[t] = out[t] + float(w[t, j]) * y[inv_perm[p]]
+    return out
+
+
+def merge_misses(out: np.ndarray, y_miss: np.ndarray, miss_of_pair, w: np.ndarray, T: int,
+                 k: int):
+    """out[t] + sum over the missed pairs j (in j order) of w[t,j] * y_miss[miss_of_pair[p]]."""
+    res = np.array(out, dtype=np.float64, copy=True)
+    for t in range(T):
+        for j in range(k):
+            m = int(miss_of_pair[t * k + j])
+            if m >= 0:
+                res[t] = res[t] + float(w[t, j]) * y_miss[m]
+    return res

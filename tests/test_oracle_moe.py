@@ -239,3 +239,78 @@ def test_zipf_bias_skews_the_load():
     # the expert with the largest prior (r = 1, bias 0) is the busiest
     assert int(np.argmax(counts)) == int(np.argmax(bias))
     assert counts.max() > 4 * np.median(counts)
+
+
+# ----------------------------------------------------------- resident hits and misses
+
+def _routing(T, k, E, seed):
+    rng = np.random.default_rng(seed)
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    return ids
+
+
+def test_miss_list_with_no_misses_and_with_every_expert_missing():
+    T, k, E = 13, 3, 9
+    ids = _routing(T, k, E, 1)
+    counts, offsets, perm, inv = moe.bucket(ids, E)
+    nonempty = int((counts > 0).sum())
+    pos, mop, cnt = moe.miss_list(np.arange(E), offsets, perm)
+    assert pos.size == 0 and np.all(mop == -1)
+    assert cnt.tolist() == [T * k, 0, nonempty, 0]
+    pos, mop, cnt = moe.miss_list(np.full(E, moe.SLOT_MISS), offsets, perm)
+    assert np.array_equal(pos, np.arange(T * k))
+    assert np.array_equal(mop, inv)          # every pair's index is its bucket position
+    assert cnt.tolist() == [0, T * k, 0, nonempty]
+
+
+@pytest.mark.parametrize("seed", [2, 3, 4])
+def test_miss_list_matches_brute_force(seed):
+    T, k, E = 37, 4, 16
+    ids = _routing(T, k, E, seed)
+    rng = np.random.default_rng(seed + 100)
+    slot_map = rng.permutation(E).astype(np.int32)
+    slot_map[rng.choice(E, size=5, replace=False)] = moe.SLOT_MISS
+    counts, offsets, perm, inv = moe.bucket(ids, E)
+    pos, mop, cnt = moe.miss_list(slot_map, offsets, perm)
+    missed_pairs = [p for p in range(T * k) if slot_map[ids.flat[p]] == moe.SLOT_MISS]
+    assert sorted(inv[p] for p in missed_pairs) == pos.tolist()
+    for p in range(T * k):
+        if p in missed_pairs:
+            assert pos[mop[p]] == inv[p]
+        else:
+            assert mop[p] == -1
+    used = set(ids.flat)
+    assert cnt.tolist() == [T * k - len(missed_pairs), len(missed_pairs),
+                            sum(1 for e in used if slot_map[e] != moe.SLOT_MISS),
+                            sum(1 for e in used if slot_map[e] == moe.SLOT_MISS)]
+
+
+def test_resident_combine_plus_merged_misses_is_the_full_combine():
+    T, k, E, H = 21, 3, 8, 17
+    ids = _routing(T, k, E, 5)
+    rng = np.random.default_rng(6)
+    w = rng.random((T, k))
+    counts, offsets, perm, inv = moe.bucket(ids, E)
+    y = rng.standard_normal((T * k, H))
+    slot_map = np.arange(E, dtype=np.int32)
+    slot_map[[1, 4, 6]] = moe.SLOT_MISS
+    pos, mop, _ = moe.miss_list(slot_map, offsets, perm)
+    part = moe.combine_hits(y, inv, w, T, k, mop)
+    merged = moe.merge_misses(part, y[pos], mop, w, T, k)
+    full = moe.combine(y, inv, w, T, k)
+    assert np.allclose(merged, full, rtol=1e-13, atol=1e-13)
+    # and the resident part alone is the mixture with the missed terms dropped
+    y0 = y.copy()
+    y0[pos] = 0.0
+    assert np.allclose(part, moe.combine(y0, inv, w, T, k), rtol=1e-13, atol=1e-13)
+
+
+def test_oracle_refuses_a_non_resident_slot():
+    cfg = synth.config("tiny", T=4)
+    L = synth.make_layer(cfg)
+    ids, _, _ = moe.route(L.x, L.wr, None, cfg.k)
+    counts, offsets, perm, _ = moe.bucket(ids, cfg.E)
+    sm = L.slot_map.copy()
+    sm[int(ids[0, 0])] = moe.SLOT_MISS
+    with pytest.raises(ValueError):
+        moe.expert_ffn(L.planes, cfg.fmt, sm, L.x, cfg.k, offsets, perm)
