@@ -153,9 +153,11 @@ moe_status moe_bucket(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
  *   y[pos] = W_down[s] h[pos]                          (fp32)
  *   x  bf16 [T][H];  h bf16 [T*k][I] (out);  y fp32 [T*k][H] (out)
  *   offsets/perm as produced by moe_bucket for the same T, k, E.
- *   err_flags uint32 (nullable): if slot_map[e] is outside [0, n_slots), that expert's h
- *   and y rows are written as zeros and bit 0 of *err_flags is set (atomic OR); nothing
- *   traps.
+ *   slot_map[e] == MOE_SLOT_MISS marks a non-resident expert: its h and y rows are written
+ *   as zeros and no flag is raised (see moe_miss_list / moe_merge_misses).
+ *   err_flags uint32 (nullable): if slot_map[e] is any other value outside [0, n_slots),
+ *   that expert's h and y rows are written as zeros and bit 0 of *err_flags is set
+ *   (atomic OR); nothing traps.
  *   path: moe_path.
  */
 moe_status moe_expert_ffn(const moe_pool* pool, const int32_t* slot_map, int32_t E,
@@ -185,6 +187,36 @@ moe_status moe_expert_down(const moe_pool* pool, const int32_t* slot_map, int32_
  */
 moe_status moe_combine(const float* y, const int32_t* inv_perm, const float* topk_w,
                        int32_t T, int32_t k, int32_t H, float* out, void* stream);
+
+/*
+ * Resident hits and misses ([L] original post: the selected experts are split into
+ * resident hits, served from the GPU pool, and misses computed elsewhere; the weighted
+ * outputs are then merged; the same post proposes hit/miss counters).
+ *
+ * A slot_map entry MOE_SLOT_MISS marks an expert that is not in the pool. The expert FFN
+ * writes zeros for its pairs and the combine therefore sums the resident pairs only.
+ *
+ * moe_miss_list -- the pairs routed to non-resident experts.
+ *   slot_map int32 [E]; offsets int32 [E+1], perm int32 [T*k] as from moe_bucket
+ *   miss_pos     int32 [T*k] (out): the missed pairs' bucket positions, increasing, in
+ *                its first n_miss entries (the rest is left untouched)
+ *   miss_of_pair int32 [T*k] (out): for pair p = t*k + j, its index into miss_pos, or -1
+ *   counters     int32 [4] (out): resident pairs, missed pairs (n_miss), resident experts
+ *                with pairs, non-resident experts with pairs
+ *   A caller gathers x rows perm[miss_pos[i]] / k, computes those pairs' expert outputs
+ *   y_miss[i] elsewhere, and adds them with moe_merge_misses.
+ *
+ * moe_merge_misses -- out[t,:] += topk_w[t,j] * y_miss[miss_of_pair[t*k+j], :] for every
+ *   missed pair of token t, in increasing j (fp32, fused multiply-add).
+ *   out fp32 [T][H] (in/out); y_miss fp32 [n_miss][H]; miss_of_pair and topk_w as above.
+ */
+#define MOE_SLOT_MISS (-1)
+moe_status moe_miss_list(const int32_t* slot_map, int32_t E, const int32_t* offsets,
+                         const int32_t* perm, int32_t T, int32_t k, int32_t* miss_pos,
+                         int32_t* miss_of_pair, int32_t* counters, void* stream);
+moe_status moe_merge_misses(float* out, const float* y_miss, const int32_t* miss_of_pair,
+                            const float* topk_w, int32_t T, int32_t k, int32_t H,
+                            void* stream);
 
 /*
  * Workspace of the fused call: byte offsets (from the workspace base) of every

@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MXFP4, Q8_0 = 1, 2
 PATH_AUTO, PATH_GEMV, PATH_GROUPED = 0, 1, 2
+SLOT_MISS = -1      # slot_map value of an expert that is not in the pool (MOE_SLOT_MISS)
 _FMT = {"mxfp4": MXFP4, "q8_0": Q8_0}
 
 
@@ -72,6 +73,8 @@ _gate_up = _sig("moe_expert_gate_up", _i32, ctypes.POINTER(PoolStruct), _p, _i32
 _down = _sig("moe_expert_down", _i32, ctypes.POINTER(PoolStruct), _p, _i32, _i32, _i32, _p, _p,
              _p, _p, _i32, _p)
 _combine = _sig("moe_combine", _i32, _p, _p, _p, _i32, _i32, _i32, _p, _p)
+_miss_list = _sig("moe_miss_list", _i32, _p, _i32, _p, _p, _i32, _i32, _p, _p, _p, _p)
+_merge_misses = _sig("moe_merge_misses", _i32, _p, _p, _p, _p, _i32, _i32, _i32, _p)
 _ws = _sig("moe_layer_workspace", _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(WsLayout))
 _layer = _sig("moe_layer", _i32, ctypes.POINTER(PoolStruct), _p, _p, _p, _p, _i32, _i32, _i32,
               _p, _p, _sz, _p, _i32, _p)
@@ -82,7 +85,7 @@ _last_error = _sig("moe_last_error", ctypes.c_char_p)
 
 EXPORTED = ("moe_plane_bytes", "moe_pool_pack", "moe_route_scratch_bytes", "moe_route",
             "moe_bucket_scratch_bytes", "moe_bucket", "moe_expert_ffn", "moe_expert_gate_up",
-            "moe_expert_down", "moe_combine",
+            "moe_expert_down", "moe_combine", "moe_miss_list", "moe_merge_misses",
             "moe_layer_workspace", "moe_layer", "moe_layer_timed", "moe_status_string",
             "moe_last_error")
 
@@ -263,6 +266,40 @@ def combine(y, inv_perm, w, out=None, stream=None):
     if out is None:
         out = torch.empty((T, H), dtype=torch.float32, device=y.device)
     _check(_combine(_ptr(y), _ptr(inv_perm), _ptr(w), T, k, H, _ptr(out), _stream(stream)))
+    return out
+
+
+def miss_list(slot_map, offsets, perm, k: int, stream=None):
+    """Pairs routed to non-resident experts (slot_map == SLOT_MISS).
+
+    slot_map int32 [E], offsets int32 [E+1], perm int32 [T*k] ->
+    (miss_pos int32 [n_miss], miss_of_pair int32 [T*k], counters int32 [4]); the count
+    n_miss (= counters[1]) is read back to size miss_pos, which synchronises the stream.
+    """
+    E = slot_map.shape[0]
+    n = perm.shape[0]
+    T = n // k
+    dev = slot_map.device
+    miss_pos = torch.empty(max(n, 1), dtype=torch.int32, device=dev)
+    miss_of_pair = torch.empty(max(n, 1), dtype=torch.int32, device=dev)
+    counters = torch.empty(4, dtype=torch.int32, device=dev)
+    _check(_miss_list(_ptr(slot_map), E, _ptr(offsets), _ptr(perm), T, k, _ptr(miss_pos),
+                      _ptr(miss_of_pair), _ptr(counters), _stream(stream)))
+    n_miss = int(counters[1].item())
+    return miss_pos[:n_miss], miss_of_pair[:n], counters
+
+
+def merge_misses(out, y_miss, miss_of_pair, w, stream=None):
+    """out fp32 [T, H] += w[t,j] * y_miss[miss_of_pair[t*k+j]] over missed pairs, j order."""
+    T, k = w.shape
+    H = out.shape[1]
+    _need(out, torch.float32, (T, H), "out")
+    _need(w, torch.float32, (T, k), "w")
+    if y_miss.shape[0] == 0:
+        return out
+    _need(y_miss, torch.float32, (y_miss.shape[0], H), "y_miss")
+    _check(_merge_misses(_ptr(out), _ptr(y_miss), _ptr(miss_of_pair), _ptr(w), T, k, H,
+                         _stream(stream)))
     return out
 
 

@@ -308,6 +308,41 @@ moe_status moe_combine(const float* y, const int32_t* inv_perm, const float* top
                     "combine");
 }
 
+moe_status moe_miss_list(const int32_t* slot_map, int32_t E, const int32_t* offsets,
+                         const int32_t* perm, int32_t T, int32_t k, int32_t* miss_pos,
+                         int32_t* miss_of_pair, int32_t* counters, void* stream) {
+  moe_status s = check_shape(T, 32, E, k);
+  if (s != MOE_OK) return s;
+  CHECK_PTR(slot_map);
+  CHECK_PTR(offsets);
+  CHECK_PTR(counters);
+  if (T > 0) {
+    CHECK_PTR(perm);
+    CHECK_PTR(miss_pos);
+    CHECK_PTR(miss_of_pair);
+  }
+  clear_stale_error();
+  return hip_status(moe::launch_miss_list(slot_map, E, offsets, perm, T * k, miss_pos,
+                                          miss_of_pair, counters, (hipStream_t)stream),
+                    "miss list");
+}
+
+moe_status moe_merge_misses(float* out, const float* y_miss, const int32_t* miss_of_pair,
+                            const float* topk_w, int32_t T, int32_t k, int32_t H,
+                            void* stream) {
+  moe_status s = check_shape(T, H, moe::kMaxE, k);
+  if (s != MOE_OK) return s;
+  if (T == 0) return ok();
+  CHECK_PTR(out);
+  CHECK_PTR(y_miss);
+  CHECK_PTR(miss_of_pair);
+  CHECK_PTR(topk_w);
+  clear_stale_error();
+  return hip_status(moe::launch_merge_misses(out, y_miss, miss_of_pair, topk_w, T, k, H,
+                                             (hipStream_t)stream),
+                    "merge misses");
+}
+
 moe_status moe_layer_workspace(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k,
                                moe_ws_layout* out) {
   if (out == nullptr) return fail(MOE_ERR_INVALID_ARG, "out is NULL");

@@ -110,6 +110,10 @@ __host__ __device__ constexpr int64_t scale_bytes_per_block(int fmt) { return fm
 // then kActStride int32 per active expert.
 constexpr int kActStride = 8;
 
+// slot_map value of an expert that is not in the pool (MOE_SLOT_MISS): its pairs get
+// zero output and raise no error flag.
+constexpr int kSlotMiss = -1;
+
 // A split router's partial logits handed to the kernel that finishes the routing (the
 // decode gate/up kernel), and where that kernel stores the routing it computes.
 //   partial [ns][T][E] fp32; ids, w [T][k]; counts [E]; offsets [E+1]; perm, inv_perm [T*k];

@@ -185,7 +185,7 @@ __global__ __launch_bounds__(kGThreads) void k_gemv(
       if (GATED) h_out[(int64_t)pos * rows + r] = 0;
       else y_out[(int64_t)pos * rows + r] = 0.f;
     }
-    if (threadIdx.x == 0 && err_flags) atomicOr(err_flags, 1u);
+    if (threadIdx.x == 0 && err_flags && slot != kSlotMiss) atomicOr(err_flags, 1u);
   } else {
     const int nb = K / 32;
     const int nc = (nb + LM::kBlocksPerChunk - 1) / LM::kBlocksPerChunk;
@@ -548,7 +548,8 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
     yl[pos][r] = sum;
     y[(int64_t)pos * H + r0 + r] = sum;
   }
-  if (!valid && busy && q == 0 && lane == 0 && err_flags) atomicOr(err_flags, 1u);
+  if (!valid && busy && q == 0 && lane == 0 && err_flags && slot != kSlotMiss)
+    atomicOr(err_flags, 1u);
   if constexpr (!COMBINE) return;
   __syncthreads();
   // 6. combine, in increasing j, as k_combine does
@@ -789,7 +790,7 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
     if (slot < 0 || slot >= n_slots) {
       for (int i = tid; i < np * 16; i += kGThreads)
         h_out[(int64_t)(lo + i / 16) * I + r0 + i % 16] = 0;
-      if (tid == 0 && err_flags) atomicOr(err_flags, 1u);
+      if (tid == 0 && err_flags && slot != kSlotMiss) atomicOr(err_flags, 1u);
       continue;
     }
     // stream this row group of the expert's gate and up rows

@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
         else y_out[(int64_t)pos * N + n] = 0.f;
       }
     }
-    if (threadIdx.x == 0 && err_flags) atomicOr(err_flags, 1u);
+    if (threadIdx.x == 0 && err_flags && slot != kSlotMiss) atomicOr(err_flags, 1u);
     return;
   }
   const int nb = K / 32;

@@ -85,4 +85,12 @@ hipError_t launch_combine(const float* y, const int32_t* inv_perm, const float* 
 hipError_t launch_pack(int fmt, int n_mats, int rows, int K, const void* sq, const void* ss,
                        void* dq, void* ds, hipStream_t stream);
 
+// Resident hits and misses (csrc/miss.hip): the list of pairs routed to experts whose slot
+// is kSlotMiss, and the merge of the caller's outputs for them.
+hipError_t launch_miss_list(const int32_t* slot_map, int E, const int32_t* offsets,
+                            const int32_t* perm, int n, int32_t* miss_pos,
+                            int32_t* miss_of_pair, int32_t* counters, hipStream_t stream);
+hipError_t launch_merge_misses(float* out, const float* y_miss, const int32_t* miss_of_pair,
+                               const float* topk_w, int T, int k, int H, hipStream_t stream);
+
 }  // namespace moe

@@ -174,6 +174,30 @@ def test_ffn_and_layer_argument_checks(lib):
     assert g(ctypes.byref(p), None, None, None, None, 0, 4, 2, None, None, 0, None, 0, None) == OK
 
 
+def test_miss_argument_checks(lib):
+    _setup(lib)
+    f = lib.moe_miss_list
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_int32, ctypes.c_int32] + [ctypes.c_void_p] * 4
+    # E > 256, k > E, k > 8, T < 0
+    for T, E, k in ((4, 300, 2), (4, 4, 5), (4, 16, 9), (-1, 8, 2)):
+        assert f(FAKE, E, FAKE, FAKE, T, k, FAKE, FAKE, FAKE, None) == INVALID
+    # NULL or misaligned outputs and inputs
+    assert f(FAKE, 8, FAKE, FAKE, 4, 2, FAKE, None, FAKE, None) == INVALID
+    assert b"miss_of_pair" in lib.moe_last_error()
+    assert f(FAKE, 8, FAKE, FAKE, 4, 2, FAKE, FAKE, None, None) == INVALID
+    assert f(MISALIGNED, 8, FAKE, FAKE, 4, 2, FAKE, FAKE, FAKE, None) == INVALID
+    g = lib.moe_merge_misses
+    g.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int32] * 3 + [ctypes.c_void_p]
+    # H not a multiple of 32, k outside [1, 8]
+    assert g(FAKE, FAKE, FAKE, FAKE, 4, 2, 48, None) == INVALID
+    assert g(FAKE, FAKE, FAKE, FAKE, 4, 9, 64, None) == INVALID
+    assert g(FAKE, None, FAKE, FAKE, 4, 2, 64, None) == INVALID
+    assert b"y_miss" in lib.moe_last_error()
+    # T = 0: nothing to do
+    assert g(None, None, None, None, 0, 2, 64, None) == OK
+
+
 def test_pack_argument_checks(lib):
     _setup(lib)
     f = lib.moe_pool_pack
