@@ -23,6 +23,9 @@ of that structure:
   misses   an expert whose slot is SLOT_MISS is not resident: its pairs are listed (in bucket
            order) for computation elsewhere, the resident pairs are combined, and the
            missed pairs' outputs are merged afterwards, per token in j order
+  staging  the batch's used, non-resident experts are copied into a window of staging
+           slots (in increasing expert index) and the slot map is rewritten to point at
+           them before the grouped expert matmul
 All arithmetic is fp64; the one rounding is h to bf16, taken directly from fp64.
 """
 from __future__ import annotations
@@ -276,4 +279,46 @@ def merge_misses(out: np.ndarray, y_miss: np.ndarray, miss_of_pair, w: np.ndarra
             m = int(miss_of_pair[t * k + j])
             if m >= 0:
                 res[t] = res[t] + float(w[t, j]) * y_miss[m]
+    return res
+
+
+# ------------------------------------------------------------------ staged prefill
+#
+# llama.cpp discussion "fixed GPU expert working set with Native CPU miss execution",
+# "Formal gate results": for a large prefill batch, the unique experts the router picked
+# are packed, copied in bulk into shared staging windows of GPU slots, the mapping is
+# rewritten to those slots, and the grouped quantized matmul runs on the rewritten map.
+# tinyserve README, "How it works" item 6: each expert of the batch is loaded once.
+# Reading: the experts to stage are the used (count > 0) experts whose slot is SLOT_MISS;
+# they take the window's slots in increasing expert index; experts beyond the window's
+# size stay SLOT_MISS (their pairs then take the miss path above).
+
+
+def stage_plan(counts, slot_map, first_slot: int, n_stage: int):
+    """Staging plan of one batch.
+
+    Returns (slot_map_out, copy_list, counters):
+      slot_map_out int32 [E]: resident experts and unused experts unchanged; the i-th staged
+                   expert (increasing index) maps to slot first_slot + i
+      copy_list    int32 [n_staged]: the staged experts, in slot order
+      counters     int32 [2]: experts staged, used non-resident experts left out (window full)
+    """
+    counts = np.asarray(counts, dtype=np.int64)
+    out = np.array(slot_map, dtype=np.int32, copy=True)
+    need = [e for e in range(counts.size) if counts[e] > 0 and int(slot_map[e]) == SLOT_MISS]
+    staged = need[:n_stage]
+    for i, e in enumerate(staged):
+        out[e] = first_slot + i
+    copy_list = np.array(staged, dtype=np.int32)
+    counters = np.array([len(staged), len(need) - len(staged)], dtype=np.int32)
+    return out, copy_list, counters
+
+
+def stage_copy(planes: dict, backing: dict, copy_list, first_slot: int) -> dict:
+    """The pool after the copy: slot first_slot + i holds every plane of expert copy_list[i]
+    taken from the backing store (indexed by expert); every other slot is unchanged."""
+    res = {n: np.array(a, copy=True) for n, a in planes.items()}
+    for i, e in enumerate(copy_list):
+        for n in res:
+            res[n][first_slot + i] = backing[n][int(e)]
     return res

@@ -314,3 +314,87 @@ def test_oracle_refuses_a_non_resident_slot():
     sm[int(ids[0, 0])] = moe.SLOT_MISS
     with pytest.raises(ValueError):
         moe.expert_ffn(L.planes, cfg.fmt, sm, L.x, cfg.k, offsets, perm)
+
+
+# ------------------------------------------------------------------ staged prefill
+
+@pytest.mark.parametrize("seed,n_stage", [(1, 16), (2, 3), (3, 0), (4, 7)])
+def test_stage_plan_matches_brute_force(seed, n_stage):
+    E = 16
+    rng = np.random.default_rng(seed)
+    counts = rng.integers(0, 3, size=E)
+    slot_map = np.full(E, moe.SLOT_MISS, dtype=np.int32)
+    resident = rng.choice(E, size=5, replace=False)
+    slot_map[resident] = np.arange(5)
+    first = 5
+    sm, copy_list, cnt = moe.stage_plan(counts, slot_map, first, n_stage)
+    want = sorted(e for e in range(E) if counts[e] > 0 and e not in set(resident.tolist()))
+    staged = want[:n_stage]
+    assert copy_list.tolist() == staged
+    assert cnt.tolist() == [len(staged), len(want) - len(staged)]
+    for e in range(E):
+        if e in staged:
+            assert sm[e] == first + staged.index(e)
+        else:
+            assert sm[e] == slot_map[e]
+    # the window's slots are distinct, inside the window, and increase with the expert index
+    ws = [int(sm[e]) for e in staged]
+    assert ws == list(range(first, first + len(staged)))
+
+
+def _resident_and_backing(L, E, resident):
+    """Backing store indexed by expert, and a pool whose first slots hold `resident`."""
+    backing = {n: a[L.slot_map] for n, a in L.planes.items()}
+    S = len(resident) + E
+    pool = {n: np.zeros((S,) + a.shape[1:], dtype=a.dtype) for n, a in backing.items()}
+    slot_map = np.full(E, moe.SLOT_MISS, dtype=np.int32)
+    for i, e in enumerate(resident):
+        slot_map[e] = i
+        for n in pool:
+            pool[n][i] = backing[n][e]
+    return backing, pool, slot_map
+
+
+def test_staged_pool_gives_the_all_resident_layer():
+    """Staging every used non-resident expert and rewriting the map reproduces, exactly, the
+    layer computed with every expert resident."""
+    cfg = synth.config("tiny", T=32)
+    L = synth.make_layer(cfg)
+    resident = [1, 4, 6]
+    backing, pool, slot_map = _resident_and_backing(L, cfg.E, resident)
+    ids, _, _ = moe.route(L.x, L.wr, None, cfg.k)
+    counts, _, _, _ = moe.bucket(ids, cfg.E)
+    first = len(resident)
+    sm, copy_list, cnt = moe.stage_plan(counts, slot_map, first, cfg.E)
+    assert cnt[1] == 0 and cnt[0] == int(((counts > 0) & (slot_map == moe.SLOT_MISS)).sum())
+    staged = moe.stage_copy(pool, backing, copy_list, first)
+    got = moe.layer(staged, cfg.fmt, sm, L.wr, None, L.x, cfg.k)
+    ref = moe.layer(L.planes, cfg.fmt, L.slot_map, L.wr, None, L.x, cfg.k)
+    assert np.array_equal(got["out"], ref["out"])
+    assert np.array_equal(got["h"], ref["h"])
+
+
+def test_window_overflow_takes_the_miss_path():
+    """With a window smaller than the batch needs, the experts left out stay non-resident;
+    their pairs computed elsewhere and merged give the full layer."""
+    cfg = synth.config("tiny", T=32)
+    L = synth.make_layer(cfg)
+    backing, pool, slot_map = _resident_and_backing(L, cfg.E, [0, 5])
+    ids, w, _ = moe.route(L.x, L.wr, None, cfg.k)
+    counts, offsets, perm, inv = moe.bucket(ids, cfg.E)
+    sm, copy_list, cnt = moe.stage_plan(counts, slot_map, 2, 2)
+    assert cnt[0] == 2 and cnt[1] > 0
+    staged = moe.stage_copy(pool, backing, copy_list, 2)
+    pos, mop, mcnt = moe.miss_list(sm, offsets, perm)
+    assert mcnt[3] == cnt[1]
+    # resident and staged pairs from the pool; missed pairs from the backing store
+    ident = np.arange(cfg.E, dtype=np.int32)
+    _, y_all, _ = moe.expert_ffn(backing, cfg.fmt, ident, L.x, cfg.k, offsets, perm)
+    hit_pos = np.setdiff1d(np.arange(perm.size), pos)
+    _, y_hit, _ = moe.expert_ffn(staged, cfg.fmt, np.where(sm < 0, 0, sm), L.x, cfg.k,
+                                 offsets, perm, hit_pos)
+    y = np.where(np.isnan(y_hit), 0.0, y_hit)
+    part = moe.combine_hits(y, inv, w, cfg.T, cfg.k, mop)
+    merged = moe.merge_misses(part, y_all[pos], mop, w, cfg.T, cfg.k)
+    assert np.allclose(merged, moe.combine(y_all, inv, w, cfg.T, cfg.k), rtol=1e-12,
+                       atol=1e-12)
