@@ -40,6 +40,10 @@ def parse():
                          "and replayed; eager: every layer call is launched from the host")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="time budget of the CPU-oracle baseline sample (0 disables it)")
+    ap.add_argument("--stage", action="store_true",
+                    help="staged prefill: every third expert is resident, the others are "
+                         "copied each step from a backing store into a window of pool slots "
+                         "(plan + copy + mapping rewrite before the expert FFN); eager launches")
     return ap.parse_args()
 
 
@@ -67,10 +71,25 @@ def main():
 
     # ---- inputs, resident in HBM before timing
     layers = []
+    staged = []             # --stage: (backing store, resident slot map) per layer
     host_keep = []          # a few layers kept on the host for the CPU baseline
+    resident = list(range(0, cfg.E, 3))
+    window = cfg.E - len(resident)
     for l in range(n_layers):
         L = synth.make_layer(cfg, l)
-        pool = qm.Pool.from_canonical(cfg.fmt, cfg.H, cfg.I, L.planes, device=dev)
+        if args.stage:
+            by_expert = {n: a[L.slot_map] for n, a in L.planes.items()}
+            backing = qm.Pool.from_canonical(cfg.fmt, cfg.H, cfg.I, by_expert, device=dev)
+            # resident experts first, then the window (holding stale experts before a copy)
+            fill = resident + [(e + 1) % cfg.E for e in range(window)]
+            pool = qm.Pool.from_canonical(cfg.fmt, cfg.H, cfg.I,
+                                          {n: a[fill] for n, a in by_expert.items()}, device=dev)
+            sm_res = np.full(cfg.E, qm.SLOT_MISS, dtype=np.int32)
+            sm_res[resident] = np.arange(len(resident), dtype=np.int32)
+            staged.append((backing, torch.from_numpy(sm_res).to(dev)))
+            del by_expert
+        else:
+            pool = qm.Pool.from_canonical(cfg.fmt, cfg.H, cfg.I, L.planes, device=dev)
         x = torch.from_numpy(L.x.view(np.int16)).to(dev).view(torch.bfloat16)
         wr = torch.from_numpy(L.wr.view(np.int16)).to(dev).view(torch.bfloat16)
         bias = None if L.bias is None else torch.from_numpy(L.bias).to(dev)
@@ -102,6 +121,17 @@ def main():
         for c in calls:
             c()
 
+    copy_ev = []
+    if args.stage:
+        if args.mode == "graph":
+            print("[bench] --stage runs eager", file=sys.stderr, flush=True)
+            args.mode = "eager"
+        timed_calls, copy_ev = staged_calls(qm, torch, layers, staged, outs, cfg, resident,
+                                            window, stream, hip, ev)
+        plain_calls = timed_calls
+
+    copy_ms = []
+
     def eager_pass(steps):
         """`steps` steps launched from the host, gate/up events read after each step."""
         ms = []
@@ -110,6 +140,7 @@ def main():
             run(timed_calls)
             stream.synchronize()
             ms.extend(hip.elapsed_ms(a, b) for a, b in ev)
+            copy_ms.extend(hip.elapsed_ms(a, b) for a, b in copy_ev)
         torch.cuda.synchronize()
         return time.perf_counter() - t0, ms
 
@@ -156,6 +187,7 @@ def main():
                 "kernel": "gate/up grouped GEMM (k_ggemm)", "work_per_launch": flops}
     else:
         bpw = 17.0 / 32.0 if cfg.fmt == "mxfp4" else 34.0 / 32.0
+        fused = T <= 4 and T * E <= 256 and H <= 4096
         # distinct experts per layer: recomputed from each layer's routing on the device
         n_distinct = []
         for li, (pool, x, wr, bias, sm) in enumerate(layers):
@@ -165,7 +197,9 @@ def main():
         achieved = bytes_per_launch / kern_avg_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "gate/up GEMV (k_gemv)", "work_per_launch": bytes_per_launch}
+                "kernel": ("gate/up with the routing finished in-kernel (k_gate_up_routed)"
+                           if fused else "gate/up GEMV (k_gemv)"),
+                "work_per_launch": bytes_per_launch}
     roof["traffic"] = measured_traffic(cfg.name)
     roof["avg_launch_us"] = round(kern_avg_s * 1e6, 3)
     roof["method"] = ("HIP events recorded on the kernel's stream around every gate/up launch "
@@ -184,11 +218,63 @@ def main():
     }
     if graph is not None:
         result["eager_ms_per_step"] = round(eager_s * 1e3 / args.steps, 4)
+    if args.stage:
+        # the bulk copy: every staged expert's six planes read from the backing store and
+        # written into the window (prefill batches use every expert: the whole window)
+        per_expert = sum(qm.plane_bytes(cfg.fmt, r, K, sc) for r, K in ((I, H), (I, H), (H, I))
+                         for sc in (False, True))
+        moved = 2.0 * window * per_expert
+        copy_s = float(np.mean(copy_ms)) * 1e-3
+        result["config"]["staging"] = {"resident": len(resident), "window": window}
+        result["stage_copy"] = {
+            "kernel": "k_stage_copy", "bound": "hbm", "bytes_per_launch": moved,
+            "avg_launch_us": round(copy_s * 1e6, 3), "achieved": round(moved / copy_s / 1e9, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(moved / copy_s / 1e9 / HBM_PEAK_GBS, 4)}
 
     # ---- CPU baseline: the oracle on a bounded sample of the same workload
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(cfg, host_keep, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def staged_calls(qm, torch, layers, staged, outs, cfg, resident, window, stream, hip, ev):
+    """Per layer: route, bucket, window plan (mapping rewrite), bulk copy of the planned
+    experts, gate/up (timed), down, combine -- each a C-ABI stage call on `stream`, with
+    every buffer allocated once here."""
+    T, k, E, H, I = cfg.T, cfg.k, cfg.E, cfg.H, cfg.I
+    dev = outs[0].device
+    i32 = dict(dtype=torch.int32, device=dev)
+    ids = torch.empty((T, k), **i32)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    counts, offsets = torch.empty(E, **i32), torch.empty(E + 1, **i32)
+    perm, inv = torch.empty(T * k, **i32), torch.empty(T * k, **i32)
+    rs = qm._scratch(qm.route_scratch_bytes(T, H, E), dev)
+    bs = qm._scratch(qm.bucket_scratch_bytes(T, k, E), dev)
+    sm2, cl, cnt = torch.empty(E, **i32), torch.empty(E, **i32), torch.empty(2, **i32)
+    h = torch.empty((T * k, I), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((T * k, H), dtype=torch.float32, device=dev)
+    copy_ev = [(hip.create(), hip.create()) for _ in layers]
+    first = len(resident)
+    calls = []
+    for li, (pool, x, wr, bias, _) in enumerate(layers):
+        backing, sm_res = staged[li]
+
+        def call(pool=pool, x=x, wr=wr, bias=bias, backing=backing, sm_res=sm_res, li=li):
+            qm.route(x, wr, bias, k, ids=ids, w=w, scratch=rs, stream=stream)
+            qm.bucket(ids, E, counts, offsets, perm, inv, scratch=bs, stream=stream)
+            qm.stage_plan(counts, sm_res, first, window, slot_map_out=sm2, copy_list=cl,
+                          counters=cnt, stream=stream)
+            hip.record(copy_ev[li][0], stream.cuda_stream)
+            qm.stage_copy(pool, backing, cl, cnt, first, window, stream=stream)
+            hip.record(copy_ev[li][1], stream.cuda_stream)
+            hip.record(ev[li][0], stream.cuda_stream)
+            qm.expert_gate_up(pool, sm2, x, k, offsets, perm, h=h, stream=stream)
+            hip.record(ev[li][1], stream.cuda_stream)
+            qm.expert_down(pool, sm2, T, k, offsets, h, y=y, stream=stream)
+            qm.combine(y, inv, w, out=outs[li], stream=stream)
+        calls.append(call)
+    return calls, copy_ev
 
 
 def library_sources_digest() -> str:
@@ -282,6 +368,12 @@ class HipEvents:
             raise RuntimeError(f"hipGraphInstantiate failed ({st})")
         self.graphs = getattr(self, "graphs", []) + [(g, ge)]
         return ge.value
+
+    def record(self, event: int, stream: int):
+        self.lib.hipEventRecord.argtypes = [self.ct.c_void_p, self.ct.c_void_p]
+        st = self.lib.hipEventRecord(self.ct.c_void_p(event), self.ct.c_void_p(stream))
+        if st != 0:
+            raise RuntimeError(f"hipEventRecord failed ({st})")
 
     def launch(self, graph_exec: int, stream: int):
         self.lib.hipGraphLaunch.argtypes = [self.ct.c_void_p, self.ct.c_void_p]

@@ -222,6 +222,46 @@ moe_status moe_merge_misses(float* out, const float* y_miss, const int32_t* miss
  * Workspace of the fused call: byte offsets (from the workspace base) of every
  * intermediate, so a caller can read them back. All offsets are 256-byte aligned.
  */
+/*
+ * Staged prefill ([L] "Formal gate results": for a large prefill batch the unique experts
+ * picked by the router are copied in bulk into shared GPU staging windows, the mapping is
+ * rewritten to those slots and the grouped quantized matmul runs on the rewritten map;
+ * [T] "How it works" 6: each expert of a batch is loaded once).
+ *
+ * moe_stage_plan -- the mapping rewrite.
+ *   counts       int32 [E]: pairs per expert (moe_bucket's counts)
+ *   slot_map     int32 [E]: resident slot, or MOE_SLOT_MISS
+ *   first_slot, n_stage: the window is pool slots [first_slot, first_slot + n_stage)
+ *   slot_map_out int32 [E] (out; may be slot_map itself): the experts with pairs and no
+ *                slot take the window's slots in increasing expert index,
+ *                slot_map_out[e] = first_slot + i for the i-th of them while i < n_stage;
+ *                every other entry is copied (experts beyond the window stay
+ *                MOE_SLOT_MISS and take the miss path above)
+ *   copy_list    int32 [E] (out): copy_list[i] = the expert staged into slot first_slot + i,
+ *                for i < counters[0]; later entries are left untouched
+ *   counters     int32 [2] (out): experts staged, experts left out because the window is
+ *                full
+ *
+ * moe_stage_copy -- the bulk copy into the window.
+ *   pool     the pool whose window slots are written (its planes are written through the
+ *            const pointers, for slots first_slot + i, i < min(counters[0], max_copies))
+ *   backing  a pool of the same format and shape in which slot e holds expert e (any
+ *            memory the device can read)
+ *   copy_list, counters: from moe_stage_plan (read on the device, so no host round trip
+ *            is needed between the plan and the copy)
+ *   max_copies: the window size n_stage given to the plan; the launch is sized for it
+ *   err_flags uint32 (nullable): bit 0 is set if a listed expert is outside the backing
+ *            store; that copy is skipped.
+ *   Errors: MOE_ERR_INVALID_ARG if the window does not fit in the pool, or the backing
+ *   store differs from the pool in format or shape.
+ */
+moe_status moe_stage_plan(const int32_t* counts, const int32_t* slot_map, int32_t E,
+                          int32_t first_slot, int32_t n_stage, int32_t* slot_map_out,
+                          int32_t* copy_list, int32_t* counters, void* stream);
+moe_status moe_stage_copy(const moe_pool* pool, const moe_pool* backing,
+                          const int32_t* copy_list, const int32_t* counters, int32_t first_slot,
+                          int32_t max_copies, uint32_t* err_flags, void* stream);
+
 typedef struct {
   size_t total;
   size_t topk_ids, topk_w, counts, offsets, perm, inv_perm, h, y, scratch;

@@ -33,7 +33,7 @@ class MoeError(RuntimeError):
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with "
-                      "`python -m quantized_routed_expert_gemv_amd.build` (hipcc, gfx950)")
+                      "`python quantized_routed_expert_gemv_amd/build.py` (hipcc, gfx950)")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -75,6 +75,9 @@ _down = _sig("moe_expert_down", _i32, ctypes.POINTER(PoolStruct), _p, _i32, _i32
 _combine = _sig("moe_combine", _i32, _p, _p, _p, _i32, _i32, _i32, _p, _p)
 _miss_list = _sig("moe_miss_list", _i32, _p, _i32, _p, _p, _i32, _i32, _p, _p, _p, _p)
 _merge_misses = _sig("moe_merge_misses", _i32, _p, _p, _p, _p, _i32, _i32, _i32, _p)
+_stage_plan = _sig("moe_stage_plan", _i32, _p, _p, _i32, _i32, _i32, _p, _p, _p, _p)
+_stage_copy = _sig("moe_stage_copy", _i32, ctypes.POINTER(PoolStruct), ctypes.POINTER(PoolStruct),
+                   _p, _p, _i32, _i32, _p, _p)
 _ws = _sig("moe_layer_workspace", _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(WsLayout))
 _layer = _sig("moe_layer", _i32, ctypes.POINTER(PoolStruct), _p, _p, _p, _p, _i32, _i32, _i32,
               _p, _p, _sz, _p, _i32, _p)
@@ -86,6 +89,7 @@ _last_error = _sig("moe_last_error", ctypes.c_char_p)
 EXPORTED = ("moe_plane_bytes", "moe_pool_pack", "moe_route_scratch_bytes", "moe_route",
             "moe_bucket_scratch_bytes", "moe_bucket", "moe_expert_ffn", "moe_expert_gate_up",
             "moe_expert_down", "moe_combine", "moe_miss_list", "moe_merge_misses",
+            "moe_stage_plan", "moe_stage_copy",
             "moe_layer_workspace", "moe_layer", "moe_layer_timed", "moe_status_string",
             "moe_last_error")
 
@@ -301,6 +305,37 @@ def merge_misses(out, y_miss, miss_of_pair, w, stream=None):
     _check(_merge_misses(_ptr(out), _ptr(y_miss), _ptr(miss_of_pair), _ptr(w), T, k, H,
                          _stream(stream)))
     return out
+
+
+def stage_plan(counts, slot_map, first_slot: int, n_stage: int, slot_map_out=None,
+               copy_list=None, counters=None, stream=None):
+    """Staging window plan (mapping rewrite) of one batch.
+
+    counts int32 [E], slot_map int32 [E] -> (slot_map_out int32 [E], copy_list int32 [E],
+    counters int32 [2]); copy_list[:counters[0]] are the staged experts in slot order.
+    Nothing is read back: the copy takes copy_list and counters on the device.
+    """
+    E = slot_map.shape[0]
+    _need(counts, torch.int32, (E,), "counts")
+    _need(slot_map, torch.int32, (E,), "slot_map")
+    dev = slot_map.device
+    if slot_map_out is None:
+        slot_map_out = torch.empty(E, dtype=torch.int32, device=dev)
+    if copy_list is None:
+        copy_list = torch.empty(E, dtype=torch.int32, device=dev)
+    if counters is None:
+        counters = torch.empty(2, dtype=torch.int32, device=dev)
+    _check(_stage_plan(_ptr(counts), _ptr(slot_map), E, first_slot, n_stage,
+                       _ptr(slot_map_out), _ptr(copy_list), _ptr(counters), _stream(stream)))
+    return slot_map_out, copy_list, counters
+
+
+def stage_copy(pool: Pool, backing: Pool, copy_list, counters, first_slot: int,
+               max_copies: int, err_flags=None, stream=None):
+    """Copy the planned experts from `backing` (slot = expert) into the pool's window."""
+    _check(_stage_copy(ctypes.byref(pool.struct), ctypes.byref(backing.struct), _ptr(copy_list),
+                       _ptr(counters), first_slot, max_copies, _ptr(err_flags),
+                       _stream(stream)))
 
 
 def _event_handles(events):

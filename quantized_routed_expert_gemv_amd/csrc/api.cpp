@@ -343,6 +343,60 @@ moe_status moe_merge_misses(float* out, const float* y_miss, const int32_t* miss
                     "merge misses");
 }
 
+moe_status moe_stage_plan(const int32_t* counts, const int32_t* slot_map, int32_t E,
+                          int32_t first_slot, int32_t n_stage, int32_t* slot_map_out,
+                          int32_t* copy_list, int32_t* counters, void* stream) {
+  if (E < 1 || E > moe::kMaxE) return fail(MOE_ERR_INVALID_ARG, "E = %d outside [1, %d]", E, moe::kMaxE);
+  if (first_slot < 0 || n_stage < 0)
+    return fail(MOE_ERR_INVALID_ARG, "first_slot = %d, n_stage = %d", first_slot, n_stage);
+  if ((int64_t)first_slot + n_stage > 0x7fffffff) return fail(MOE_ERR_INVALID_ARG, "window too large");
+  CHECK_PTR(counts);
+  CHECK_PTR(slot_map);
+  CHECK_PTR(slot_map_out);
+  CHECK_PTR(copy_list);
+  CHECK_PTR(counters);
+  clear_stale_error();
+  return hip_status(moe::launch_stage_plan(counts, slot_map, E, first_slot, n_stage,
+                                           slot_map_out, copy_list, counters,
+                                           (hipStream_t)stream),
+                    "stage plan");
+}
+
+moe_status moe_stage_copy(const moe_pool* pool, const moe_pool* backing,
+                          const int32_t* copy_list, const int32_t* counters, int32_t first_slot,
+                          int32_t max_copies, uint32_t* err_flags, void* stream) {
+  moe_status s = check_pool(pool);
+  if (s != MOE_OK) return s;
+  s = check_pool(backing);
+  if (s != MOE_OK) return s;
+  if (backing->fmt != pool->fmt || backing->H != pool->H || backing->I != pool->I)
+    return fail(MOE_ERR_INVALID_ARG, "backing store and pool differ in format or shape");
+  if (first_slot < 0 || max_copies < 0 || (int64_t)first_slot + max_copies > pool->n_slots)
+    return fail(MOE_ERR_INVALID_ARG, "window [%d, %d + %d) outside the pool's %d slots",
+                first_slot, first_slot, max_copies, pool->n_slots);
+  if (max_copies > moe::kMaxE)
+    return fail(MOE_ERR_INVALID_ARG, "max_copies = %d > %d", max_copies, moe::kMaxE);
+  if (max_copies == 0) return ok();
+  CHECK_PTR(copy_list);
+  CHECK_PTR(counters);
+  const int fmt = pool->fmt, H = pool->H, I = pool->I;
+  moe::StagePlanes pl;
+  const void* src[6] = {backing->gate_q, backing->gate_s, backing->up_q,
+                        backing->up_s,   backing->down_q, backing->down_s};
+  const void* dst[6] = {pool->gate_q, pool->gate_s, pool->up_q,
+                        pool->up_s,   pool->down_q, pool->down_s};
+  for (int p = 0; p < moe::kStagePlanes; ++p) {
+    const bool down = p >= 4, scales = p % 2 == 1;
+    pl.src[p] = (const uint8_t*)src[p];
+    pl.dst[p] = (uint8_t*)const_cast<void*>(dst[p]);
+    pl.bytes[p] = (int64_t)plane_bytes(fmt, down ? H : I, down ? I : H, scales);
+  }
+  clear_stale_error();
+  return hip_status(moe::launch_stage_copy(pl, copy_list, counters, first_slot, max_copies,
+                                           backing->n_slots, err_flags, (hipStream_t)stream),
+                    "stage copy");
+}
+
 moe_status moe_layer_workspace(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k,
                                moe_ws_layout* out) {
   if (out == nullptr) return fail(MOE_ERR_INVALID_ARG, "out is NULL");

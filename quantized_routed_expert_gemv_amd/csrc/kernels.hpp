@@ -93,4 +93,19 @@ hipError_t launch_miss_list(const int32_t* slot_map, int E, const int32_t* offse
 hipError_t launch_merge_misses(float* out, const float* y_miss, const int32_t* miss_of_pair,
                                const float* topk_w, int T, int k, int H, hipStream_t stream);
 
+// Staged prefill (csrc/stage.hip): the window plan (mapping rewrite) and the bulk copy of
+// the planned experts' planes from a backing store (indexed by expert) into the pool.
+hipError_t launch_stage_plan(const int32_t* counts, const int32_t* slot_map, int E,
+                             int first_slot, int n_stage, int32_t* slot_map_out,
+                             int32_t* copy_list, int32_t* counters, hipStream_t stream);
+constexpr int kStagePlanes = 6;   // gate, up, down x (codes, scales)
+struct StagePlanes {
+  const uint8_t* src[kStagePlanes];   // backing store: slot = expert index
+  uint8_t* dst[kStagePlanes];         // pool
+  int64_t bytes[kStagePlanes];        // bytes of one slot of each plane (multiple of 16)
+};
+hipError_t launch_stage_copy(const StagePlanes& pl, const int32_t* copy_list,
+                             const int32_t* counters, int first_slot, int max_copies,
+                             int backing_slots, uint32_t* err_flags, hipStream_t stream);
+
 }  // namespace moe

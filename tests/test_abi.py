@@ -198,6 +198,33 @@ def test_miss_argument_checks(lib):
     assert g(None, None, None, None, 0, 2, 64, None) == OK
 
 
+def test_stage_argument_checks(lib):
+    _setup(lib)
+    f = lib.moe_stage_plan
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p] + [ctypes.c_int32] * 3 + \
+                 [ctypes.c_void_p] * 4
+    assert f(FAKE, FAKE, 300, 0, 4, FAKE, FAKE, FAKE, None) == INVALID
+    assert f(FAKE, FAKE, 8, -1, 4, FAKE, FAKE, FAKE, None) == INVALID
+    assert f(FAKE, FAKE, 8, 0, -2, FAKE, FAKE, FAKE, None) == INVALID
+    assert f(FAKE, FAKE, 8, 0, 4, FAKE, FAKE, None, None) == INVALID
+    assert b"counters" in lib.moe_last_error()
+    g = lib.moe_stage_copy
+    g.argtypes = [ctypes.POINTER(Pool)] * 2 + [ctypes.c_void_p] * 2 + [ctypes.c_int32] * 2 + \
+                 [ctypes.c_void_p] * 2
+    pool, back = _pool(n_slots=8), _pool(n_slots=4)
+    # the window must fit in the pool
+    assert g(ctypes.byref(pool), ctypes.byref(back), FAKE, FAKE, 6, 3, None, None) == INVALID
+    assert g(ctypes.byref(pool), ctypes.byref(back), FAKE, FAKE, -1, 2, None, None) == INVALID
+    # backing store of another format or shape
+    other = _pool(fmt=2, n_slots=4)
+    assert g(ctypes.byref(pool), ctypes.byref(other), FAKE, FAKE, 4, 4, None, None) == INVALID
+    other = _pool(n_slots=4, I=64)
+    assert g(ctypes.byref(pool), ctypes.byref(other), FAKE, FAKE, 4, 4, None, None) == INVALID
+    assert g(ctypes.byref(pool), ctypes.byref(back), None, FAKE, 4, 4, None, None) == INVALID
+    # an empty window enqueues nothing
+    assert g(ctypes.byref(pool), ctypes.byref(back), None, None, 4, 0, None, None) == OK
+
+
 def test_pack_argument_checks(lib):
     _setup(lib)
     f = lib.moe_pool_pack
