@@ -12,6 +12,11 @@ not define them, so the definitions below are the public ones:
   * E8M0 (same spec): an unsigned power-of-two scale 2^(b-127); b = 255 is NaN.
   * MXFP4 block: 32 E2M1 codes sharing one E8M0 scale.
   * Q8_0 block (GGUF): 32 two's-complement int8 codes sharing one fp16 scale d.
+  * Q4_K (GGUF k-quant, named in "How it works" item 2 and "Formats"): super-blocks of
+    256 elements made of eight 32-element blocks; block b has a 6-bit scale sc_b and a
+    6-bit min m_b, the super-block an fp16 scale d and an fp16 min scale dmin; element
+    value d*sc_b*q - dmin*m_b for its 4-bit code q (0..15). The byte arrangement of the
+    scales is this library's own canonical one (see dequant_q4_k).
   * IEEE binary16 and bfloat16 (the upper 16 bits of an IEEE binary32).
 Every function returns exact fp64 values; all of these formats embed exactly in fp64.
 """
@@ -164,9 +169,44 @@ def dequant_q8_0(q: np.ndarray, d: np.ndarray) -> np.ndarray:
     return q * np.repeat(sc, 32, axis=1)
 
 
+def q4_k_fields(scales: np.ndarray, K: int):
+    """Split a Q4_K scale plane [rows, K/16 + K/64] (bytes) into its fields.
+
+    Per row: K/32 pairs of bytes (sc_b, m_b), then K/256 pairs of little-endian fp16
+    (d_s, dmin_s). Returns (sc, m) int [rows, K/32] and (d, dmin) fp64 [rows, K/256].
+    """
+    scales = np.asarray(scales, dtype=np.uint8)
+    nb, ns = K // 32, K // 256
+    pairs = scales[:, :2 * nb].reshape(-1, nb, 2).astype(np.int64)
+    sup = np.ascontiguousarray(scales[:, 2 * nb:2 * nb + 4 * ns]).view(np.uint16)
+    sup = sup.reshape(-1, ns, 2)
+    return pairs[..., 0], pairs[..., 1], fp16_decode(sup[..., 0]), fp16_decode(sup[..., 1])
+
+
+def dequant_q4_k(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Q4_K matrix [rows, K/2] codes + [rows, K/16 + K/64] scale bytes -> fp64 [rows, K].
+
+    Element 2j of a row is the low nibble of byte j, element 2j+1 the high nibble (as for
+    MXFP4). Weight (r, i) = d[r, s] * sc[r, b] * q[r, i] - dmin[r, s] * m[r, b] with
+    b = i // 32 and s = i // 256.
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    rows, half = codes.shape
+    K = 2 * half
+    q = np.empty((rows, K), dtype=np.float64)
+    q[:, 0::2] = codes & 0x0F
+    q[:, 1::2] = codes >> 4
+    sc, m, d, dmin = q4_k_fields(scales, K)
+    a = np.repeat(d, 8, axis=1) * sc                  # [rows, K/32]
+    c = np.repeat(dmin, 8, axis=1) * m
+    return q * np.repeat(a, 32, axis=1) - np.repeat(c, 32, axis=1)
+
+
 def dequant(fmt: str, codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     if fmt == "mxfp4":
         return dequant_mxfp4(codes, scales)
     if fmt == "q8_0":
         return dequant_q8_0(codes, scales)
+    if fmt == "q4_k":
+        return dequant_q4_k(codes, scales)
     raise ValueError(f"unknown block format {fmt!r}")

@@ -23,6 +23,9 @@ Layout of what is generated ("canonical" layout, indexed by pool slot):
           *_s uint8 [S, rows, K/32] E8M0 scale bytes
   Q8_0:   *_q int8  [S, rows, K]    two's-complement codes
           *_s uint16 [S, rows, K/32] fp16 bit patterns of the block scale d
+  Q4_K:   *_q uint8 [S, rows, K/2]  two 4-bit codes per byte, element 2j in the low nibble
+          *_s uint8 [S, rows, K/16 + K/64]  per row: (sc_b, m_b) bytes for each 32-block,
+                                      then (d_s, dmin_s) fp16 bits for each 256-super-block
   gate/up: rows = I, K = H;  down: rows = H, K = I.
 """
 from __future__ import annotations
@@ -42,7 +45,7 @@ class Config:
     I: int
     E: int
     k: int
-    fmt: str            # "mxfp4" or "q8_0"
+    fmt: str            # "mxfp4", "q8_0" or "q4_k"
     zipf_s: float | None
     slot: str           # "identity" or "perm"
     seed: int
@@ -68,6 +71,11 @@ CONFIGS: dict[str, Config] = {c.name: c for c in [
     # Qwen3-30B-A3B-shaped fine-grained layer with a Zipf(1.2) expert load
     Config("qwen_a3b_decode", 1, 2048, 768, 128, 8, "mxfp4", 1.2, "perm", 505, 64),
     Config("qwen_a3b_prefill", 8192, 2048, 768, 128, 8, "mxfp4", 1.2, "perm", 505, 1),
+    # the same two shapes with Q4_K experts (K a multiple of the 256-element super-block)
+    Config("tiny_q4k", 64, 256, 512, 8, 2, "q4_k", None, "perm", 606, 1),
+    Config("qwen_a3b_q4k_decode", 1, 2048, 768, 128, 8, "q4_k", 1.2, "perm", 707, 64),
+    Config("qwen_a3b_q4k_prefill", 8192, 2048, 768, 128, 8, "q4_k", 1.2, "perm", 707, 1),
+    Config("mixtral_q4k_decode", 1, 4096, 14336, 8, 2, "q4_k", None, "perm", 808, 8),
 ]}
 
 
@@ -153,10 +161,30 @@ def _q8_0_matrix(g: np.random.Generator, rows: int, K: int):
     return q, d
 
 
+def _q4_k_matrix(g: np.random.Generator, rows: int, K: int):
+    if K % 256:
+        raise ValueError(f"Q4_K needs K to be a multiple of 256, got {K}")
+    nb, ns = K // 32, K // 256
+    codes = g.integers(0, 256, size=(rows, K // 2), dtype=np.uint8)      # 16 codes equally likely
+    sc = g.integers(32, 64, size=(rows, nb), dtype=np.uint8)             # 6-bit scales
+    m = g.integers(32, 64, size=(rows, nb), dtype=np.uint8)              # 6-bit mins
+    d = _f64_to_fp16_bits(g.uniform(1.5e-4, 2.5e-4, size=(rows, ns)))
+    dmin = _f64_to_fp16_bits(g.uniform(1.2e-3, 2.0e-3, size=(rows, ns)))
+    scales = np.empty((rows, 2 * nb + 4 * ns), dtype=np.uint8)
+    scales[:, 0:2 * nb:2] = sc
+    scales[:, 1:2 * nb:2] = m
+    sup = np.stack([d, dmin], axis=-1).reshape(rows, 2 * ns)
+    scales[:, 2 * nb:] = np.ascontiguousarray(sup).view(np.uint8)
+    return codes, scales
+
+
+_MAKERS = {"mxfp4": _mxfp4_matrix, "q8_0": _q8_0_matrix, "q4_k": _q4_k_matrix}
+
+
 def make_expert(cfg: Config, layer: int, e: int) -> dict[str, np.ndarray]:
     """Weights of logical expert e of one layer (canonical layout, no slot axis)."""
     g = _rng(cfg.seed, _EXPERT, layer, e)
-    mk = _mxfp4_matrix if cfg.fmt == "mxfp4" else _q8_0_matrix
+    mk = _MAKERS[cfg.fmt]
     gq, gs = mk(g, cfg.I, cfg.H)
     uq, us = mk(g, cfg.I, cfg.H)
     dq, ds = mk(g, cfg.H, cfg.I)

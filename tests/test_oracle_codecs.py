@@ -162,3 +162,62 @@ def test_q8_0_block_scale_applies_per_32_elements():
     for r in range(rows):
         for i in range(K):
             assert got[r, i] == float(q[r, i]) * dv[r, i // 32]
+
+
+def _q4_k_plane(sc, m, d_bits, dmin_bits):
+    """Scale plane bytes written out field by field with struct (independent of numpy views)."""
+    import struct
+    rows, nb = sc.shape
+    ns = nb // 8
+    out = np.zeros((rows, 2 * nb + 4 * ns), dtype=np.uint8)
+    for r in range(rows):
+        raw = bytearray()
+        for b in range(nb):
+            raw += bytes([int(sc[r, b]), int(m[r, b])])
+        for s in range(ns):
+            raw += struct.pack("<HH", int(d_bits[r, s]), int(dmin_bits[r, s]))
+        out[r] = np.frombuffer(bytes(raw), dtype=np.uint8)
+    return out
+
+
+def test_q4_k_brute_force_per_element():
+    """Every element against d*sc*q - dmin*m evaluated with Python floats, the codes read
+    nibble by nibble and the fp16 fields decoded by struct's IEEE half format."""
+    import struct
+    rng = np.random.default_rng(3)
+    rows, K = 3, 512
+    codes = rng.integers(0, 256, size=(rows, K // 2), dtype=np.uint8)
+    sc = rng.integers(0, 64, size=(rows, K // 32))
+    m = rng.integers(0, 64, size=(rows, K // 32))
+    d_bits = rng.uniform(-1, 1, size=(rows, K // 256)).astype(np.float16).view(np.uint16)
+    dmin_bits = rng.uniform(-1, 1, size=(rows, K // 256)).astype(np.float16).view(np.uint16)
+    got = codecs.dequant_q4_k(codes, _q4_k_plane(sc, m, d_bits, dmin_bits))
+    for r in range(rows):
+        for i in range(K):
+            byte = int(codes[r, i // 2])
+            q = (byte >> 4) if (i % 2) else (byte & 0xF)
+            s = i // 256
+            d = struct.unpack("<e", struct.pack("<H", int(d_bits[r, s])))[0]
+            dmin = struct.unpack("<e", struct.pack("<H", int(dmin_bits[r, s])))[0]
+            want = d * int(sc[r, i // 32]) * q - dmin * int(m[r, i // 32])
+            assert got[r, i] == want, (r, i)
+
+
+def test_q4_k_closed_forms():
+    rows, K = 2, 256
+    codes = np.arange(K // 2, dtype=np.uint8).reshape(1, -1).repeat(rows, 0)
+    one = np.float16(1.0).view(np.uint16)
+    zero = np.float16(0.0).view(np.uint16)
+    full = lambda v: np.full((rows, K // 256), v, dtype=np.uint16)
+    # d = 1, every scale 1, no min: the codes themselves
+    w = codecs.dequant_q4_k(codes, _q4_k_plane(np.ones((rows, 8), int), np.zeros((rows, 8), int),
+                                               full(one), full(zero)))
+    q = np.empty((rows, K))
+    q[:, 0::2] = codes & 15
+    q[:, 1::2] = codes >> 4
+    assert np.array_equal(w, q)
+    # d = 0: only the min term, -dmin * m_b, constant over each block
+    mins = np.arange(16).reshape(2, 8)
+    w = codecs.dequant_q4_k(codes, _q4_k_plane(np.ones((rows, 8), int), mins, full(zero),
+                                               full(one)))
+    assert np.array_equal(w, -np.repeat(mins, 32, axis=1).astype(float))

@@ -398,3 +398,33 @@ def test_window_overflow_takes_the_miss_path():
     merged = moe.merge_misses(part, y_all[pos], mop, w, cfg.T, cfg.k)
     assert np.allclose(merged, moe.combine(y_all, inv, w, cfg.T, cfg.k), rtol=1e-12,
                        atol=1e-12)
+
+
+# ------------------------------------------------------------------ Q4_K experts
+
+def test_q4_k_layer_equals_the_q8_0_layer_of_the_same_weights():
+    """Q4_K experts whose scales are d = 1, sc = 1 and whose mins are 0 carry the integer
+    weights q in 0..15; the same integers as Q8_0 codes with d = 1 give the same layer."""
+    cfg = synth.config("tiny_q4k", T=8)
+    L = synth.make_layer(cfg)
+    one = np.float16(1.0).view(np.uint16)
+    planes4, planes8 = {}, {}
+    for n in ("gate", "up", "down"):
+        codes = L.planes[n + "_q"]                          # [S, rows, K/2]
+        S, rows, half = codes.shape
+        K = 2 * half
+        nb, ns = K // 32, K // 256
+        sc = np.zeros((S, rows, 2 * nb + 4 * ns), dtype=np.uint8)
+        sc[..., 0:2 * nb:2] = 1                              # sc_b = 1, m_b = 0
+        sup = np.zeros((S, rows, ns, 2), dtype=np.uint16)
+        sup[..., 0] = one                                    # d = 1, dmin = 0
+        sc[..., 2 * nb:] = sup.reshape(S, rows, 2 * ns).view(np.uint8)
+        planes4[n + "_q"], planes4[n + "_s"] = codes, sc
+        q8 = np.empty((S, rows, K), dtype=np.int8)
+        q8[..., 0::2] = codes & 15
+        q8[..., 1::2] = codes >> 4
+        planes8[n + "_q"] = q8
+        planes8[n + "_s"] = np.full((S, rows, nb), one, dtype=np.uint16)
+    a = moe.layer(planes4, "q4_k", L.slot_map, L.wr, None, L.x, cfg.k)
+    b = moe.layer(planes8, "q8_0", L.slot_map, L.wr, None, L.x, cfg.k)
+    assert np.array_equal(a["h"], b["h"]) and np.array_equal(a["out"], b["out"])
