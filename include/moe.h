@@ -52,11 +52,16 @@ typedef enum {
   MOE_ERR_HIP = 3
 } moe_status;
 
-/* Block formats of the expert weights.
+/* Block formats of the expert weights ([T] "How it works" 2 and "Formats": MXFP4 and the
+ * GGUF formats computed natively).
  * MOE_W_MXFP4: blocks of 32 E2M1 codes (4 bits each) sharing one E8M0 scale byte;
  *              weight = E2M1(code) * 2^(scale - 127). Scale bytes 1..254 are supported.
- * MOE_W_Q8_0:  blocks of 32 int8 codes sharing one fp16 scale d; weight = d * q.      */
-typedef enum { MOE_W_MXFP4 = 1, MOE_W_Q8_0 = 2 } moe_wfmt;
+ * MOE_W_Q8_0:  blocks of 32 int8 codes sharing one fp16 scale d; weight = d * q.
+ * MOE_W_Q4_K:  k-quant super-blocks of 256 elements = 8 blocks of 32; block b has a 6-bit
+ *              scale sc_b and a 6-bit min m_b, the super-block fp16 d and dmin;
+ *              weight = d * sc_b * q - dmin * m_b for the 4-bit code q (0..15). The
+ *              reduction dimension (H for gate/up, I for down) must be a multiple of 256. */
+typedef enum { MOE_W_MXFP4 = 1, MOE_W_Q8_0 = 2, MOE_W_Q4_K = 3 } moe_wfmt;
 
 /* Which expert-FFN schedule to use. AUTO picks the GEMV schedule for T <= 16 and the
  * grouped MFMA GEMM otherwise. Both give results within the same tolerance; they are not
@@ -77,6 +82,11 @@ typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_GROUPED = 2 } moe_
  *   MXFP4 scales: 1 byte at unit(r,b)
  *   Q8_0  codes : 32 bytes at unit(r,b) * 32, element i of the block at byte i
  *   Q8_0  scales: fp16 at byte unit(r,b) * 2
+ *   Q4_K  codes : as MXFP4 (16 bytes per unit, element 2j in the low nibble of byte j)
+ *   Q4_K  scales: sc_b | m_b << 8 (two bytes) at byte unit(r,b) * 2; then, from byte
+ *                 rows * nb * 2 of the matrix's scale plane, d | dmin << 16 (fp16 bits, four
+ *                 bytes) of row r's super-block s at ((r / 16) * nsb + s) * 16 + r % 16
+ *                 (nsb = K / 256), times 4
  * so the 16 rows of a row group are interleaved block by block: one 64-lane 16-byte load
  * reads 16 rows x 4 MXFP4 blocks (or 16 rows x 2 Q8_0 blocks) from one contiguous KiB.
  * Slot s of a plane starts at s * (bytes per matrix); rows of a matrix must be a multiple
@@ -102,8 +112,11 @@ size_t moe_plane_bytes(int32_t fmt, int32_t rows, int32_t K, int32_t scales);
  *   MXFP4: codes u8 [rows][K/2] (element 2j in the low nibble of byte j),
  *          scales u8 [rows][K/32]
  *   Q8_0 : codes i8 [rows][K], scales fp16 [rows][K/32]
+ *   Q4_K : codes u8 [rows][K/2] (as MXFP4), scales u8 [rows][K/16 + K/64]: per row the
+ *          pairs (sc_b, m_b) of its K/32 blocks, then the fp16 pairs (d_s, dmin_s) of its
+ *          K/256 super-blocks (little-endian)
  * src and dst must not overlap. Returns MOE_ERR_INVALID_ARG for rows % 16 != 0 or
- * K % 32 != 0, MOE_ERR_UNSUPPORTED for an unknown fmt.
+ * K % 32 != 0 (K % 256 != 0 for Q4_K), MOE_ERR_UNSUPPORTED for an unknown fmt.
  */
 moe_status moe_pool_pack(int32_t fmt, int32_t n_mats, int32_t rows, int32_t K,
                          const void* src_q, const void* src_s, void* dst_q, void* dst_s,

@@ -17,7 +17,11 @@ constexpr int kRowGroup = 16;   // rows interleaved per tile in the pool layout
 constexpr int kMaxK = 8;        // largest supported top-k
 constexpr int kMaxE = 256;      // largest supported expert count
 
-enum Fmt : int { kMXFP4 = 1, kQ8_0 = 2 };
+enum Fmt : int { kMXFP4 = 1, kQ8_0 = 2, kQ4_K = 3 };
+
+// Formats whose 32-element block is a 16-byte unit of 4-bit codes (MXFP4, Q4_K): a lane of a
+// 64-lane 16-byte load holds one whole block of one row.
+__host__ __device__ constexpr bool unit16(int fmt) { return fmt != kQ8_0; }
 
 // ---------------------------------------------------------------- scalar conversions
 
@@ -69,6 +73,23 @@ __device__ __forceinline__ uint32_t pack_bf16x2_exact(float lo, float hi) {
   return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
 }
 
+// Two unsigned 4-bit codes in byte `sel` of `v` -> bf16 pair (128 + lo, 128 + hi), exact:
+// 0x43 in the high byte of a bf16 is 2^7, and the code fills the top of its 7-bit mantissa
+// field from the bottom (128 + q for q < 128).
+template <int sel>
+__device__ __forceinline__ uint32_t u4x2_to_bf16x2_off128(uint32_t v) {
+  const uint32_t b = v >> (8 * sel);
+  return 0x43004300u | (b & 0xFu) | ((b & 0xF0u) << 12);
+}
+
+// 8 unsigned 4-bit codes (one dword, element 0 in the low nibble of byte 0) -> 8 bf16
+// values 128 + q.
+__device__ __forceinline__ bf16x8 u4x8_to_bf16x8_off128(uint32_t v) {
+  u32x4 p = {u4x2_to_bf16x2_off128<0>(v), u4x2_to_bf16x2_off128<1>(v),
+             u4x2_to_bf16x2_off128<2>(v), u4x2_to_bf16x2_off128<3>(v)};
+  return __builtin_bit_cast(bf16x8, p);
+}
+
 // 8 int8 codes (two dwords) -> 8 bf16 (exact: |q| <= 128 has at most 8 significant bits).
 __device__ __forceinline__ bf16x8 i8x8_to_bf16x8(uint32_t v0, uint32_t v1) {
   float f[8];
@@ -103,8 +124,24 @@ __device__ __forceinline__ int64_t pool_unit(int r, int b, int nb) {
   return (int64_t(r >> 4) * nb + b) * kRowGroup + (r & 15);
 }
 
-__host__ __device__ constexpr int64_t code_bytes_per_block(int fmt) { return fmt == kMXFP4 ? 16 : 32; }
+__host__ __device__ constexpr int64_t code_bytes_per_block(int fmt) { return unit16(fmt) ? 16 : 32; }
+// Scale bytes per unit (MXFP4: E8M0 byte; Q8_0: fp16 d; Q4_K: the block's 6-bit scale and
+// min in two bytes, sc | m << 8).
 __host__ __device__ constexpr int64_t scale_bytes_per_block(int fmt) { return fmt == kMXFP4 ? 1 : 2; }
+
+// Q4_K also has per-super-block scales: after the per-unit records of a matrix (rows * nb *
+// 2 bytes) come 4-byte records d | dmin << 16 (fp16 bits), one per (row, 256-element
+// super-block), tiled like the units: record (r, s) at index ((r/16) * nsb + s) * 16 + r%16.
+constexpr int kSuperBlocks = 8;      // 32-element blocks per Q4_K super-block
+constexpr int64_t kSuperBytes = 4;   // bytes of one (d, dmin) record
+__host__ __device__ constexpr int64_t scale_plane_bytes(int fmt, int64_t rows, int64_t K) {
+  return rows * (K / 32) * scale_bytes_per_block(fmt) +
+         (fmt == kQ4_K ? rows * (K / (32 * kSuperBlocks)) * kSuperBytes : 0);
+}
+// Byte offset, within a matrix's scale plane, of the super-block records (Q4_K).
+__host__ __device__ constexpr int64_t super_region(int64_t rows, int64_t K) {
+  return rows * (K / 32) * 2;
+}
 
 // Active-expert list written by the small-batch router (see route.hip): act[0] = count,
 // then kActStride int32 per active expert.

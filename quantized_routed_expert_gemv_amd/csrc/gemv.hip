@@ -18,6 +18,8 @@
 //     so results do not depend on timing.
 // Gate and up are read in the same pass and SwiGLU is applied before h is written
 // (rounded once to bf16); the down projection writes fp32 y.
+#include <type_traits>
+
 #include "common.hpp"
 #include "bucket_dev.hpp"
 #include "kernels.hpp"
@@ -68,23 +70,48 @@ __device__ int find_active_expert(const int32_t* __restrict__ offsets, int E, in
 // before issuing the next one.
 struct Chunk {
   u32x4 q;
-  uint32_t s;
+  uint32_t s;    // the block's scale record
+  uint32_t s2;   // Q4_K: its super-block's d | dmin << 16
   bool ok;
 };
 
 template <int FMT>
-__device__ __forceinline__ void load_chunk(Chunk& c, const uint8_t* q, const uint8_t* s, bool ok) {
+__device__ __forceinline__ void load_chunk(Chunk& c, const uint8_t* q, const uint8_t* s,
+                                           const uint8_t* s2, bool ok) {
   c.q = ld16_stream(q);
   if constexpr (FMT == kMXFP4) c.s = __builtin_nontemporal_load(s);
   else c.s = __builtin_nontemporal_load((const uint16_t*)s);
+  if constexpr (FMT == kQ4_K) c.s2 = __builtin_nontemporal_load((const uint32_t*)s2);
+  else c.s2 = 0;
   c.ok = ok;
 }
 
+// Where a lane's super-block records start (Q4_K; other formats: unused). plane: the
+// matrix's scale plane for the slot; rows x K: the matrix; rg: the row group. The record of
+// chunk c (blocks 4c .. 4c+3, all in super-block c/2) is 64 bytes per super-block further.
+template <int FMT>
+__device__ __forceinline__ const uint8_t* super_base(const uint8_t* plane, int rows, int K,
+                                                     int rg, int lane) {
+  if constexpr (FMT != kQ4_K) return plane;
+  const int nsb = K / (32 * kSuperBlocks);
+  return plane + super_region(rows, K) +
+         ((int64_t)rg * nsb * kRowGroup + (lane & 15)) * kSuperBytes;
+}
+
 // Weights of the chunk as bf16 pairs (MXFP4: 16 pairs, scale folded in; Q8_0: 8 pairs,
-// scale applied later to the fp32 partial).
+// scale applied later to the fp32 partial; Q4_K: 16 pairs 128 + q, scale and min applied
+// later).
 template <int FMT>
 __device__ __forceinline__ void widen(const Chunk& c, bf16x2* w) {
-  if constexpr (FMT == kMXFP4) {
+  if constexpr (FMT == kQ4_K) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      w[4 * d + 0] = __builtin_bit_cast(bf16x2, u4x2_to_bf16x2_off128<0>(c.q[d]));
+      w[4 * d + 1] = __builtin_bit_cast(bf16x2, u4x2_to_bf16x2_off128<1>(c.q[d]));
+      w[4 * d + 2] = __builtin_bit_cast(bf16x2, u4x2_to_bf16x2_off128<2>(c.q[d]));
+      w[4 * d + 3] = __builtin_bit_cast(bf16x2, u4x2_to_bf16x2_off128<3>(c.q[d]));
+    }
+  } else if constexpr (FMT == kMXFP4) {
     const float sc = c.ok ? e8m0_to_f32(c.s) : 0.f;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
@@ -104,10 +131,24 @@ __device__ __forceinline__ void widen(const Chunk& c, bf16x2* w) {
   }
 }
 
+// s: the block's scale record (0 for a masked chunk: it then adds nothing); s2: Q4_K's
+// super-block record. Q4_K: with P = sum x (128 + q) and S = sum x over the block,
+// sum x w = a (P - 128 S) - c S where a = d sc and c = dmin m (both exact in fp32).
 template <int FMT>
 __device__ __forceinline__ float dot_chunk(const bf16x2* w, const uint32_t* xv, uint32_t s,
-                                           float acc) {
-  if constexpr (FMT == kMXFP4) {
+                                           uint32_t s2, float acc) {
+  if constexpr (FMT == kQ4_K) {
+    float p = 0.f, sx = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      p = dot2_bf16(w[i], xv[i], p);
+      sx = dot2_bf16(0x3F803F80u, xv[i], sx);   // bf16 pair (1, 1)
+    }
+    const float a = fp16_to_f32((uint16_t)s2) * (float)(s & 0xFFu);
+    const float c = fp16_to_f32((uint16_t)(s2 >> 16)) * (float)((s >> 8) & 0xFFu);
+    acc = fmaf(a, fmaf(-128.f, sx, p), acc);
+    return fmaf(-c, sx, acc);
+  } else if constexpr (FMT == kMXFP4) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc = dot2_bf16(w[i], xv[i], acc);
     return acc;
@@ -125,14 +166,16 @@ __device__ __forceinline__ float dot_chunk(const bf16x2* w, const uint32_t* xv, 
 //          half l%2 of the block
 template <int FMT>
 struct LaneMap {
-  static constexpr int kBlocksPerChunk = FMT == kMXFP4 ? 4 : 2;
+  static constexpr bool k16 = unit16(FMT);
+  static constexpr int kBlocksPerChunk = k16 ? 4 : 2;
   static constexpr int kKPerChunk = 32 * kBlocksPerChunk;     // K elements per chunk
-  static constexpr int kXWords = FMT == kMXFP4 ? 16 : 8;      // u32 of x per lane per chunk
-  __device__ static int row(int lane) { return FMT == kMXFP4 ? (lane & 15) : ((lane >> 1) & 15); }
-  __device__ static int blk(int lane) { return FMT == kMXFP4 ? (lane >> 4) : (lane >> 5); }
+  static constexpr int kXWords = k16 ? 16 : 8;                // u32 of x per lane per chunk
+  static constexpr int kScaleChunk = 64 * (FMT == kQ4_K ? 2 : 1);   // scale bytes per chunk
+  __device__ static int row(int lane) { return k16 ? (lane & 15) : ((lane >> 1) & 15); }
+  __device__ static int blk(int lane) { return k16 ? (lane >> 4) : (lane >> 5); }
   // K offset of the lane's codes inside its chunk
   __device__ static int koff(int lane) {
-    return FMT == kMXFP4 ? (lane >> 4) * 32 : (lane >> 5) * 32 + (lane & 1) * 16;
+    return k16 ? (lane >> 4) * 32 : (lane >> 5) * 32 + (lane & 1) * 16;
   }
 };
 
@@ -193,9 +236,11 @@ __global__ __launch_bounds__(kGThreads) void k_gemv(
     const int64_t unit0 = (int64_t)rg * nb * 16;
     const uint8_t* qa = aq + slot * a_qslot + unit0 * cb + lane * 16;
     const uint8_t* qb = GATED ? bq + slot * a_qslot + unit0 * cb + lane * 16 : nullptr;
-    const int lane_unit = FMT == kMXFP4 ? lane : (lane >> 1);
+    const int lane_unit = unit16(FMT) ? lane : (lane >> 1);
     const uint8_t* sa = as + slot * a_sslot + (unit0 + lane_unit) * sb;
     const uint8_t* sbp = GATED ? bs + slot * a_sslot + (unit0 + lane_unit) * sb : nullptr;
+    const uint8_t* sa2 = super_base<FMT>(as + slot * a_sslot, rows, K, rg, lane);
+    const uint8_t* sbp2 = GATED ? super_base<FMT>(bs + slot * a_sslot, rows, K, rg, lane) : nullptr;
     const int lblk = LM::blk(lane);
     const int koff = LM::koff(lane);
 
@@ -243,8 +288,11 @@ __global__ __launch_bounds__(kGThreads) void k_gemv(
           const int b = c * LM::kBlocksPerChunk + lblk;
           const bool ok = c < nc && b < nb;
           const int cs = ok ? c : 0;      // chunk 0 of the row group always exists
-          load_chunk<FMT>(ca[u], qa + (int64_t)cs * 1024, sa + (int64_t)cs * 64, ok);
-          if constexpr (GATED) load_chunk<FMT>(cbk[u], qb + (int64_t)cs * 1024, sbp + (int64_t)cs * 64, ok);
+          load_chunk<FMT>(ca[u], qa + (int64_t)cs * 1024, sa + (int64_t)cs * LM::kScaleChunk,
+                          sa2 + (int64_t)(cs >> 1) * 64, ok);
+          if constexpr (GATED)
+            load_chunk<FMT>(cbk[u], qb + (int64_t)cs * 1024, sbp + (int64_t)cs * LM::kScaleChunk,
+                            sbp2 + (int64_t)(cs >> 1) * 64, ok);
         }
         __builtin_amdgcn_sched_barrier(0);   // keep the whole batch of loads ahead of its use
         __syncthreads();
@@ -273,7 +321,7 @@ __global__ __launch_bounds__(kGThreads) void k_gemv(
               xv[4 * q + 2] = v[2];
               xv[4 * q + 3] = v[3];
             }
-            acc[0][i] = dot_chunk<FMT>(w, xv, ca[u].ok ? ca[u].s : 0u, acc[0][i]);
+            acc[0][i] = dot_chunk<FMT>(w, xv, ca[u].ok ? ca[u].s : 0u, ca[u].s2, acc[0][i]);
           }
           if constexpr (GATED) {
             widen<FMT>(cbk[u], w);
@@ -287,7 +335,7 @@ __global__ __launch_bounds__(kGThreads) void k_gemv(
                 xv[4 * q + 2] = v[2];
                 xv[4 * q + 3] = v[3];
               }
-              acc[kM - 1][i] = dot_chunk<FMT>(w, xv, cbk[u].ok ? cbk[u].s : 0u, acc[kM - 1][i]);
+              acc[kM - 1][i] = dot_chunk<FMT>(w, xv, cbk[u].ok ? cbk[u].s : 0u, cbk[u].s2, acc[kM - 1][i]);
             }
           }
         }
@@ -298,7 +346,7 @@ __global__ __launch_bounds__(kGThreads) void k_gemv(
 #pragma unroll
         for (int i = 0; i < NT; ++i) {
           float v = acc[m][i];
-          if constexpr (FMT == kMXFP4) {
+          if constexpr (unit16(FMT)) {
             v += wave_xor(v, 16);
             v += wave_xor(v, 32);
           } else {
@@ -307,7 +355,7 @@ __global__ __launch_bounds__(kGThreads) void k_gemv(
           }
           acc[m][i] = v;
         }
-      const bool writer = FMT == kMXFP4 ? (lane < 16) : (lane < 32 && (lane & 1) == 0);
+      const bool writer = unit16(FMT) ? (lane < 16) : (lane < 32 && (lane & 1) == 0);
       if (writer) {
         const int r = LM::row(lane);
 #pragma unroll
@@ -376,7 +424,7 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
   const int nc = (nb + LM::kBlocksPerChunk - 1) / LM::kBlocksPerChunk;
   constexpr int64_t cb = code_bytes_per_block(FMT), sb = scale_bytes_per_block(FMT);
   const int64_t unit0 = (int64_t)rg * nb * 16;
-  const int lane_unit = FMT == kMXFP4 ? lane : (lane >> 1);
+  const int lane_unit = unit16(FMT) ? lane : (lane >> 1);
   const int lblk = LM::blk(lane);
   const int koff = LM::koff(lane);
   // 1. one round trip: the active list (or the offsets), every h row, the gate weights and
@@ -421,6 +469,7 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
   bool valid = slot >= 0 && slot < n_slots;
   const uint8_t* qa = dq + (valid ? slot : 0) * qslot + unit0 * cb + lane * 16;
   const uint8_t* sa = ds + (valid ? slot : 0) * sslot + (unit0 + lane_unit) * sb;
+  const uint8_t* sa2 = super_base<FMT>(ds + (valid ? slot : 0) * sslot, H, I, rg, lane);
   Chunk ch[kDCU];
   auto load_batch = [&](int cbase) {
 #pragma unroll
@@ -429,7 +478,8 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
       const int b = c * LM::kBlocksPerChunk + lblk;
       const bool ok = c < nc && b < nb;
       const int cs = ok ? c : 0;
-      load_chunk<FMT>(ch[u], qa + (int64_t)cs * 1024, sa + (int64_t)cs * 64, ok);
+      load_chunk<FMT>(ch[u], qa + (int64_t)cs * 1024, sa + (int64_t)cs * LM::kScaleChunk,
+                      sa2 + (int64_t)(cs >> 1) * 64, ok);
     }
   };
   if (act != nullptr && busy && valid) load_batch(q);
@@ -475,6 +525,7 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
     valid = slot >= 0 && slot < n_slots;
     qa = dq + (valid ? slot : 0) * qslot + unit0 * cb + lane * 16;
     sa = ds + (valid ? slot : 0) * sslot + (unit0 + lane_unit) * sb;
+    sa2 = super_base<FMT>(ds + (valid ? slot : 0) * sslot, H, I, rg, lane);
     if (busy && valid) load_batch(q);
   }
   // 4. consume each batch as it arrives, then load the next
@@ -502,7 +553,7 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
               xv[4 * qq + 2] = v[2];
               xv[4 * qq + 3] = v[3];
             }
-            acc[p] = dot_chunk<FMT>(w, xv, ch[u].ok ? ch[u].s : 0u, acc[p]);
+            acc[p] = dot_chunk<FMT>(w, xv, ch[u].ok ? ch[u].s : 0u, ch[u].s2, acc[p]);
           }
         }
       }
@@ -516,7 +567,7 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
 #pragma unroll
   for (int p = 0; p < kDCMaxPairs; ++p) {
     float v = acc[p];
-    if constexpr (FMT == kMXFP4) {
+    if constexpr (unit16(FMT)) {
       v += wave_xor(v, 16);
       v += wave_xor(v, 32);
     } else {
@@ -525,7 +576,7 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
     }
     acc[p] = v;
   }
-  const bool writer = FMT == kMXFP4 ? (lane < 16) : (lane < 32 && (lane & 1) == 0);
+  const bool writer = unit16(FMT) ? (lane < 16) : (lane < 32 && (lane & 1) == 0);
   if (writer) {
     const int r = LM::row(lane);
 #pragma unroll
@@ -774,7 +825,7 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
   const int nb = H / 32;
   const int nc = (nb + LM::kBlocksPerChunk - 1) / LM::kBlocksPerChunk;
   constexpr int64_t cb = code_bytes_per_block(FMT), sb = scale_bytes_per_block(FMT);
-  const int lane_unit = FMT == kMXFP4 ? lane : (lane >> 1);
+  const int lane_unit = unit16(FMT) ? lane : (lane >> 1);
   const int lblk = LM::blk(lane);
   const int koff = LM::koff(lane);
   for (int unit = blockIdx.x;; unit += gridDim.x) {
@@ -799,6 +850,8 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
     const uint8_t* qb = uq + slot * qslot + unit0 * cb + lane * 16;
     const uint8_t* sa = gsc + slot * sslot + (unit0 + lane_unit) * sb;
     const uint8_t* sbp = usc + slot * sslot + (unit0 + lane_unit) * sb;
+    const uint8_t* sa2 = super_base<FMT>(gsc + slot * sslot, I, H, rg, lane);
+    const uint8_t* sbp2 = super_base<FMT>(usc + slot * sslot, I, H, rg, lane);
     const uint16_t* xrow[NT];
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
@@ -820,8 +873,10 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
         const int b = c * LM::kBlocksPerChunk + lblk;
         const bool ok = c < nc && b < nb;
         const int cs = ok ? c : 0;
-        load_chunk<FMT>(ca[u], qa + (int64_t)cs * 1024, sa + (int64_t)cs * 64, ok);
-        load_chunk<FMT>(cbk[u], qb + (int64_t)cs * 1024, sbp + (int64_t)cs * 64, ok);
+        load_chunk<FMT>(ca[u], qa + (int64_t)cs * 1024, sa + (int64_t)cs * LM::kScaleChunk,
+                        sa2 + (int64_t)(cs >> 1) * 64, ok);
+        load_chunk<FMT>(cbk[u], qb + (int64_t)cs * 1024, sbp + (int64_t)cs * LM::kScaleChunk,
+                        sbp2 + (int64_t)(cs >> 1) * 64, ok);
       }
       __builtin_amdgcn_sched_barrier(0);   // the whole batch in flight before any is used
 #pragma unroll
@@ -844,7 +899,7 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
               xw[4 * q + 2] = xq[2];
               xw[4 * q + 3] = xq[3];
             }
-            acc[m][i] = dot_chunk<FMT>(w, xw, ch.ok ? ch.s : 0u, acc[m][i]);
+            acc[m][i] = dot_chunk<FMT>(w, xw, ch.ok ? ch.s : 0u, ch.s2, acc[m][i]);
           }
         }
       }
@@ -855,7 +910,7 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
 #pragma unroll
       for (int i = 0; i < NT; ++i) {
         float a = acc[m][i];
-        if constexpr (FMT == kMXFP4) {
+        if constexpr (unit16(FMT)) {
           a += wave_xor(a, 16);
           a += wave_xor(a, 32);
         } else {
@@ -864,7 +919,7 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
         }
         acc[m][i] = a;
       }
-    const bool writer = FMT == kMXFP4 ? (lane < 16) : (lane < 32 && (lane & 1) == 0);
+    const bool writer = unit16(FMT) ? (lane < 16) : (lane < 32 && (lane & 1) == 0);
     if (writer) {
       const int r = LM::row(lane);
 #pragma unroll
@@ -892,7 +947,7 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
 int gemv_nt(int fmt, int T) {
   if (T <= 1) return 1;
   if (T <= 2) return 2;
-  if (T <= 4 || fmt == kMXFP4) return 4;
+  if (T <= 4 || unit16(fmt)) return 4;
   return 8;
 }
 
@@ -919,6 +974,17 @@ hipError_t launch_gemv_t(const PoolView& a, const PoolView& b, const int32_t* sl
   return hipGetLastError();
 }
 
+// Calls f(std::integral_constant<int, FMT>{}) for the runtime format.
+template <class F>
+hipError_t with_fmt(int fmt, F&& f) {
+  switch (fmt) {
+    case kMXFP4: return f(std::integral_constant<int, kMXFP4>{});
+    case kQ8_0: return f(std::integral_constant<int, kQ8_0>{});
+    case kQ4_K: return f(std::integral_constant<int, kQ4_K>{});
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gate_up_gemv(int fmt, const PoolView& gate, const PoolView& up,
@@ -926,20 +992,13 @@ hipError_t launch_gate_up_gemv(int fmt, const PoolView& gate, const PoolView& up
                                int T, int k, int H, int I, const int32_t* offsets,
                                const int32_t* perm, uint16_t* h, uint32_t* err,
                                const int32_t* act, hipStream_t stream) {
-  if (act != nullptr) {
-    if (fmt == kMXFP4)
-      return launch_gemv_t<kMXFP4, true, kSrcAct>(gate, up, slot_map, n_slots, E, offsets, perm,
-                                                  T, k, x, H, I, h, nullptr, err, act, stream);
-    return launch_gemv_t<kQ8_0, true, kSrcAct>(gate, up, slot_map, n_slots, E, offsets, perm, T,
+  return with_fmt(fmt, [&](auto F) {
+    if (act != nullptr)
+      return launch_gemv_t<F(), true, kSrcAct>(gate, up, slot_map, n_slots, E, offsets, perm, T,
                                                k, x, H, I, h, nullptr, err, act, stream);
-  }
-  if (fmt == kMXFP4)
-    return launch_gemv_t<kMXFP4, true, kSrcOffsets>(gate, up, slot_map, n_slots, E, offsets, perm,
-                                                    T, k, x, H, I, h, nullptr, err, nullptr,
-                                                    stream);
-  return launch_gemv_t<kQ8_0, true, kSrcOffsets>(gate, up, slot_map, n_slots, E, offsets, perm, T,
-                                                 k, x, H, I, h, nullptr, err, nullptr,
-                                                 stream);
+    return launch_gemv_t<F(), true, kSrcOffsets>(gate, up, slot_map, n_slots, E, offsets, perm,
+                                                 T, k, x, H, I, h, nullptr, err, nullptr, stream);
+  });
 }
 
 
@@ -952,46 +1011,34 @@ hipError_t launch_gate_up_route(int fmt, const PoolView& gate, const PoolView& u
     return hipErrorInvalidValue;
   const int n_units = (I / 16) * min(E, T * k);
   dim3 grid(min(n_units, kRoutedMaxWG));
-#define MOE_ROUTED_CASE(F, N)                                                                 \
-  hipLaunchKernelGGL((k_gate_up_routed<F, N>), grid, dim3(kGThreads), 0, stream, gate.q,     \
+  const int nt = gemv_nt(fmt, T);
+  return with_fmt(fmt, [&](auto F) {
+#define MOE_ROUTED_CASE(N)                                                                    \
+  hipLaunchKernelGGL((k_gate_up_routed<F(), N>), grid, dim3(kGThreads), 0, stream, gate.q,   \
                      gate.s, up.q, up.s, gate.q_slot, gate.s_slot, slot_map, n_slots, E, k, x, \
                      H, I, h, err, rin)
-  const int nt = gemv_nt(fmt, T);
-  if (fmt == kMXFP4) {
-    if (nt == 1) MOE_ROUTED_CASE(kMXFP4, 1);
-    else if (nt == 2) MOE_ROUTED_CASE(kMXFP4, 2);
-    else MOE_ROUTED_CASE(kMXFP4, 4);
-  } else {
-    if (nt == 1) MOE_ROUTED_CASE(kQ8_0, 1);
-    else if (nt == 2) MOE_ROUTED_CASE(kQ8_0, 2);
-    else MOE_ROUTED_CASE(kQ8_0, 4);
-  }
+    if (nt == 1) MOE_ROUTED_CASE(1);
+    else if (nt == 2) MOE_ROUTED_CASE(2);
+    else MOE_ROUTED_CASE(4);
 #undef MOE_ROUTED_CASE
-  return hipGetLastError();
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_down_gemv(int fmt, const PoolView& down, const int32_t* slot_map, int n_slots,
                             int E, int T, int k, int H, int I, const int32_t* offsets,
                             const uint16_t* h, float* y, uint32_t* err, hipStream_t stream) {
-  if (down_combine_small_ok(T, k, E, I)) {   // the fused layer's kernel, without the combine
-    dim3 grid(H / 16);
-    if (fmt == kMXFP4)
-      hipLaunchKernelGGL((k_down_small<kMXFP4, false>), grid, dim3(kDCWaves * kWave), 0, stream,
-                         down.q, down.s, down.q_slot, down.s_slot, n_slots, E, nullptr, offsets,
-                         slot_map, h, T, k, H, I, nullptr, nullptr, y, nullptr, err);
-    else
-      hipLaunchKernelGGL((k_down_small<kQ8_0, false>), grid, dim3(kDCWaves * kWave), 0, stream,
-                         down.q, down.s, down.q_slot, down.s_slot, n_slots, E, nullptr, offsets,
-                         slot_map, h, T, k, H, I, nullptr, nullptr, y, nullptr, err);
-    return hipGetLastError();
-  }
-  if (fmt == kMXFP4)
-    return launch_gemv_t<kMXFP4, false, kSrcOffsets>(down, down, slot_map, n_slots, E, offsets,
-                                                     nullptr, T, k, h, I, H, nullptr, y, err,
-                                                     nullptr, stream);
-  return launch_gemv_t<kQ8_0, false, kSrcOffsets>(down, down, slot_map, n_slots, E, offsets,
-                                                  nullptr, T, k, h, I, H, nullptr, y, err, nullptr,
-                                                  stream);
+  return with_fmt(fmt, [&](auto F) {
+    if (down_combine_small_ok(T, k, E, I)) {   // the fused layer's kernel, without the combine
+      hipLaunchKernelGGL((k_down_small<F(), false>), dim3(H / 16), dim3(kDCWaves * kWave), 0,
+                         stream, down.q, down.s, down.q_slot, down.s_slot, n_slots, E, nullptr,
+                         offsets, slot_map, h, T, k, H, I, nullptr, nullptr, y, nullptr, err);
+      return hipGetLastError();
+    }
+    return launch_gemv_t<F(), false, kSrcOffsets>(down, down, slot_map, n_slots, E, offsets,
+                                                  nullptr, T, k, h, I, H, nullptr, y, err,
+                                                  nullptr, stream);
+  });
 }
 
 bool down_combine_small_ok(int T, int k, int E, int I) {
@@ -1004,16 +1051,12 @@ hipError_t launch_down_combine_small(int fmt, const PoolView& down, int n_slots,
                                      const int32_t* inv_perm, const float* topk_w, float* y,
                                      float* out, uint32_t* err, hipStream_t stream) {
   if (!down_combine_small_ok(T, k, E, I)) return hipErrorInvalidValue;
-  dim3 grid(H / 16);
-  if (fmt == kMXFP4)
-    hipLaunchKernelGGL((k_down_small<kMXFP4, true>), grid, dim3(kDCWaves * kWave), 0, stream,
+  return with_fmt(fmt, [&](auto F) {
+    hipLaunchKernelGGL((k_down_small<F(), true>), dim3(H / 16), dim3(kDCWaves * kWave), 0, stream,
                        down.q, down.s, down.q_slot, down.s_slot, n_slots, E, act, nullptr,
                        nullptr, h, T, k, H, I, inv_perm, topk_w, y, out, err);
-  else
-    hipLaunchKernelGGL((k_down_small<kQ8_0, true>), grid, dim3(kDCWaves * kWave), 0, stream,
-                       down.q, down.s, down.q_slot, down.s_slot, n_slots, E, act, nullptr,
-                       nullptr, h, T, k, H, I, inv_perm, topk_w, y, out, err);
-  return hipGetLastError();
+    return hipGetLastError();
+  });
 }
 
 }  // namespace moe

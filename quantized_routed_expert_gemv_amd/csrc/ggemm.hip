@@ -77,6 +77,8 @@ struct BStage {
   static constexpr int kRunQ = 64 * code_bytes_per_block(FMT);   // code bytes per row group
   static constexpr int kRunS = 64 * scale_bytes_per_block(FMT);  // scale bytes per row group
   static constexpr int kQPieces = 8 * kRunQ / 16 / kTThreads;    // 16-byte code pieces/thread
+  // Q4_K: the 16 rows' (d, dmin) records of the step's super-block, per row group
+  static constexpr int kRunS2 = FMT == kQ4_K ? kRowGroup * (int)kSuperBytes : 4;
 };
 
 template <int FMT, bool GATED>
@@ -91,6 +93,7 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[kBM * kLdsStride];
   __shared__ __attribute__((aligned(16))) uint8_t lds_bq[8 * BS::kRunQ];
   __shared__ __attribute__((aligned(16))) uint8_t lds_bs[8 * BS::kRunS];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_bs2[8 * BS::kRunS2];
   __shared__ int tmp4[4];
   __shared__ int sh[2];
   const int lane = threadIdx.x & (kWave - 1);
@@ -190,8 +193,19 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
     bsp = sb + (off % BS::kRunS);
     bs_blk = (off % BS::kRunS) / (16 * scale_bytes_per_block(FMT));
   }
+  // Q4_K super-block records: thread t < 128 copies row t % 16 of local row group t / 16
+  const bool s2_thread = FMT == kQ4_K && threadIdx.x < 8 * kRowGroup;
+  const uint8_t* bs2p = nullptr;
+  if constexpr (FMT == kQ4_K) {
+    const int g = (s2_thread ? threadIdx.x : 0) / kRowGroup;
+    const int rg = GATED ? n0 / 16 + (g & 3) : n0 / 16 + g;
+    const int rgc = rg * 16 < N ? rg : 0;
+    const int nsb = nb / kSuperBlocks;
+    bs2p = (GATED && g >= 4 ? s1 : s0) + super_region(N, K) +
+           ((int64_t)rgc * nsb * kRowGroup + (threadIdx.x & 15)) * kSuperBytes;
+  }
   u32x4 breg[BS::kQPieces];
-  uint32_t sreg = 0;
+  uint32_t sreg = 0, s2reg = 0;
   auto load_b = [&](int c) {
     // a step's run starts 4 blocks (64 units) after the previous one's; pieces of blocks
     // past the end of the row re-read step 0 (masked when consumed)
@@ -203,6 +217,10 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
     if (s_thread) {
       const int cs = 4 * c + bs_blk < nb ? c : 0;
       sreg = *(const uint32_t*)(bsp + (int64_t)cs * BS::kRunS);
+    }
+    if constexpr (FMT == kQ4_K) {
+      // step c's blocks 4c .. 4c+3 lie in super-block c / 2 (K is a multiple of 256)
+      if (s2_thread) s2reg = *(const uint32_t*)(bs2p + (int64_t)(c >> 1) * BS::kRunS2);
     }
   };
 
@@ -241,6 +259,8 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
     for (int p = 0; p < BS::kQPieces; ++p)
       *(u32x4*)(lds_bq + (threadIdx.x + kTThreads * p) * 16) = breg[p];
     if (s_thread) *(uint32_t*)(lds_bs + threadIdx.x * 4) = sreg;
+    if constexpr (FMT == kQ4_K)
+      if (s2_thread) *(uint32_t*)(lds_bs2 + threadIdx.x * 4) = s2reg;
     __syncthreads();
     if (c + 1 < nsteps) {
       load_a(c + 1);
@@ -271,6 +291,50 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
 #pragma unroll
           for (int f = 0; f < 4; ++f)
             acc[mf][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[f], acc[mf][f], 0, 0, 0);
+        }
+      }
+    } else if constexpr (FMT == kQ4_K) {
+      // one MFMA per 32-wide block, as for Q8_0: lane supplies K = 32 j + 8 g .. + 7 of block
+      // j, i.e. bytes 4 g .. 4 g + 3 of unit 16 j + lane%16, widened to 128 + q (exact). A
+      // fifth MFMA against ones gives each row's block sum S, and the block adds
+      // a P - (128 a + c) S with a = d sc, c = dmin m of the lane's column.
+      const bf16x8 ones = __builtin_bit_cast(
+          bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+#pragma unroll 1
+      for (int j = 0; j < 4; ++j) {
+        bf16x8 bv[4];
+        float sa[4], sbias[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          const int unit = 16 * j + mrow;
+          const uint32_t q = *(const uint32_t*)(lds_bq + fg[f] * BS::kRunQ + unit * 16 + 4 * g4);
+          bv[f] = u4x8_to_bf16x8_off128(q);
+          const uint32_t keep = (fcol[f] && 4 * c + j < nb) ? 0xffffu : 0u;
+          const uint32_t rec = *(const uint16_t*)(lds_bs + fg[f] * BS::kRunS + unit * 2) & keep;
+          const uint32_t dd = *(const uint32_t*)(lds_bs2 + fg[f] * BS::kRunS2 + mrow * 4);
+          const float a = fp16_to_f32((uint16_t)dd) * (float)(rec & 0xFFu);
+          const float cm = fp16_to_f32((uint16_t)(dd >> 16)) * (float)(rec >> 8);
+          sa[f] = a;
+          sbias[f] = fmaf(128.f, a, cm);
+        }
+#pragma unroll
+        for (int mf = 0; mf < 4; ++mf) {
+          const int row = 64 * wm + 16 * mf + mrow;
+          const bf16x8 av =
+              __builtin_bit_cast(bf16x8, *(const u32x4*)(lds_a + row * kLdsStride + (32 * j + 8 * g4) * 2));
+          const f32x4 sx =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, ones, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          f32x4 t[4];
+#pragma unroll
+          for (int f = 0; f < 4; ++f)
+            t[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[f], f32x4{0.f, 0.f, 0.f, 0.f}, 0,
+                                                           0, 0);
+#pragma unroll
+          for (int f = 0; f < 4; ++f)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              acc[mf][f][v] = fmaf(-sbias[f], sx[v], fmaf(sa[f], t[f][v], acc[mf][f][v]));
+          __builtin_amdgcn_sched_barrier(0);   // keep at most 5 products live
         }
       }
     } else {
@@ -358,22 +422,36 @@ hipError_t launch_gate_up_grouped(int fmt, const PoolView& gate, const PoolView&
                                   int T, int k, int H, int I, const int32_t* offsets,
                                   const int32_t* perm, uint16_t* h, uint32_t* err,
                                   hipStream_t stream) {
-  if (fmt == kMXFP4)
-    return launch_ggemm_t<kMXFP4, true>(gate, up, slot_map, n_slots, E, offsets, perm, T, k, x,
-                                        H, I, h, nullptr, err, stream);
-  return launch_ggemm_t<kQ8_0, true>(gate, up, slot_map, n_slots, E, offsets, perm, T, k, x, H,
-                                     I, h, nullptr, err, stream);
+  switch (fmt) {
+    case kMXFP4:
+      return launch_ggemm_t<kMXFP4, true>(gate, up, slot_map, n_slots, E, offsets, perm, T, k, x,
+                                          H, I, h, nullptr, err, stream);
+    case kQ8_0:
+      return launch_ggemm_t<kQ8_0, true>(gate, up, slot_map, n_slots, E, offsets, perm, T, k, x,
+                                         H, I, h, nullptr, err, stream);
+    case kQ4_K:
+      return launch_ggemm_t<kQ4_K, true>(gate, up, slot_map, n_slots, E, offsets, perm, T, k, x,
+                                         H, I, h, nullptr, err, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_down_grouped(int fmt, const PoolView& down, const int32_t* slot_map,
                                int n_slots, int E, int T, int k, int H, int I,
                                const int32_t* offsets, const uint16_t* h, float* y,
                                uint32_t* err, hipStream_t stream) {
-  if (fmt == kMXFP4)
-    return launch_ggemm_t<kMXFP4, false>(down, down, slot_map, n_slots, E, offsets, nullptr, T,
-                                         k, h, I, H, nullptr, y, err, stream);
-  return launch_ggemm_t<kQ8_0, false>(down, down, slot_map, n_slots, E, offsets, nullptr, T, k,
-                                      h, I, H, nullptr, y, err, stream);
+  switch (fmt) {
+    case kMXFP4:
+      return launch_ggemm_t<kMXFP4, false>(down, down, slot_map, n_slots, E, offsets, nullptr, T,
+                                           k, h, I, H, nullptr, y, err, stream);
+    case kQ8_0:
+      return launch_ggemm_t<kQ8_0, false>(down, down, slot_map, n_slots, E, offsets, nullptr, T,
+                                          k, h, I, H, nullptr, y, err, stream);
+    case kQ4_K:
+      return launch_ggemm_t<kQ4_K, false>(down, down, slot_map, n_slots, E, offsets, nullptr, T,
+                                          k, h, I, H, nullptr, y, err, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace moe

@@ -24,6 +24,24 @@ __global__ __launch_bounds__(256) void k_pack(int64_t n_units, int rows, int nb,
   if constexpr (FMT == kMXFP4) {
     *(u32x4*)(dq + u * 16) = *(const u32x4*)(sq + i * 16);
     ds[u] = ss[i];
+  } else if constexpr (FMT == kQ4_K) {
+    // canonical scale row: (sc, m) per block, then (d, dmin) fp16 per super-block
+    *(u32x4*)(dq + u * 16) = *(const u32x4*)(sq + i * 16);
+    const int nsb = nb / kSuperBlocks;
+    const int64_t row_bytes = 2 * (int64_t)nb + kSuperBytes * nsb;
+    const int64_t mat_bytes = (int64_t)rows * row_bytes;   // = the tiled plane's size
+    const uint8_t* srow = ss + mat * mat_bytes + r * row_bytes;
+    uint8_t* dmat = ds + mat * mat_bytes;
+    dmat[u % per_mat * 2 + 0] = srow[2 * b + 0];
+    dmat[u % per_mat * 2 + 1] = srow[2 * b + 1];
+    if (b % kSuperBlocks == 0) {
+      const int sblk = b / kSuperBlocks;
+      const int64_t rec = ((int64_t)(r >> 4) * nsb + sblk) * kRowGroup + (r & 15);
+      uint8_t* dst = dmat + super_region(rows, 32 * (int64_t)nb) + rec * kSuperBytes;
+      const uint8_t* src = srow + 2 * nb + kSuperBytes * sblk;
+#pragma unroll
+      for (int j = 0; j < kSuperBytes; ++j) dst[j] = src[j];
+    }
   } else {
     *(u32x4*)(dq + u * 32) = *(const u32x4*)(sq + i * 32);
     *(u32x4*)(dq + u * 32 + 16) = *(const u32x4*)(sq + i * 32 + 16);
@@ -43,7 +61,11 @@ hipError_t launch_pack(int fmt, int n_mats, int rows, int K, const void* sq, con
   if (fmt == kMXFP4)
     hipLaunchKernelGGL(k_pack<kMXFP4>, dim3((unsigned)blocks), dim3(256), 0, stream, n, rows, nb,
                        (const uint8_t*)sq, (const uint8_t*)ss, (uint8_t*)dq, (uint8_t*)ds);
-  else
+  else if (fmt == kQ4_K) {
+    if (nb % kSuperBlocks) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_pack<kQ4_K>, dim3((unsigned)blocks), dim3(256), 0, stream, n, rows, nb,
+                       (const uint8_t*)sq, (const uint8_t*)ss, (uint8_t*)dq, (uint8_t*)ds);
+  } else
     hipLaunchKernelGGL(k_pack<kQ8_0>, dim3((unsigned)blocks), dim3(256), 0, stream, n, rows, nb,
                        (const uint8_t*)sq, (const uint8_t*)ss, (uint8_t*)dq, (uint8_t*)ds);
   return hipGetLastError();

@@ -128,6 +128,23 @@ def check_h(h_gpu_bits, a_ref, slack):
     return frac
 
 
+def _accumulated_magnitude(fmt, planes, name, s, W):
+    """|term| per weight of the sums the kernels accumulate in fp32: |w| for MXFP4 and Q8_0;
+    for Q4_K the kernels sum x (128 + q) and x over a block, scaled by a = d sc and by
+    128 a + c (c = dmin m), so the magnitude is a (128 + q) + |128 a + c|."""
+    if fmt != "q4_k":
+        return np.abs(W)
+    codes = planes[name + "_q"][s]
+    K = 2 * codes.shape[1]
+    q = np.empty((codes.shape[0], K))
+    q[:, 0::2] = codes & 15
+    q[:, 1::2] = codes >> 4
+    sc, m, d, dmin = codecs.q4_k_fields(planes[name + "_s"][s], K)
+    a = np.abs(np.repeat(d, 8, axis=1) * sc)
+    c = np.repeat(dmin, 8, axis=1) * m
+    return np.repeat(a, 32, axis=1) * (128 + q) + np.repeat(np.abs(128 * a + c), 32, axis=1)
+
+
 def h_slack(planes, fmt, slot_map, x_bits, k, offsets, perm, positions, a_ref):
     """The fp32 accumulation slack of each h element at the given positions."""
     offsets = np.asarray(offsets, dtype=np.int64)
@@ -148,8 +165,8 @@ def h_slack(planes, fmt, slot_map, x_bits, k, offsets, perm, positions, a_ref):
         Wg = codecs.dequant(fmt, planes["gate_q"][s], planes["gate_s"][s])
         Wu = codecs.dequant(fmt, planes["up_q"][s], planes["up_s"][s])
         toks = perm[sel] // k
-        Sg = xa[toks] @ np.abs(Wg).T
-        Su = xa[toks] @ np.abs(Wu).T
+        Sg = xa[toks] @ _accumulated_magnitude(fmt, planes, "gate", s, Wg).T
+        Su = xa[toks] @ _accumulated_magnitude(fmt, planes, "up", s, Wu).T
         g = x_all[toks] @ Wg.T
         u = x_all[toks] @ Wu.T
         sig = 1.0 / (1.0 + np.exp(-g))

@@ -84,6 +84,10 @@ def test_plane_bytes(lib):
     assert lib.moe_plane_bytes(2, 14336, 4096, 0) == 14336 * 4096
     assert lib.moe_plane_bytes(2, 14336, 4096, 1) == 14336 * 128 * 2
     assert lib.moe_plane_bytes(7, 16, 32, 0) == 0
+    # Q4_K: 16 code bytes per block; 2 scale bytes per block + 4 per 256-element super-block
+    assert lib.moe_plane_bytes(3, 768, 2048, 0) == 768 * 2048 // 2
+    assert lib.moe_plane_bytes(3, 768, 2048, 1) == 768 * (64 * 2 + 8 * 4)
+    assert lib.moe_plane_bytes(3, 768, 2080, 1) == 0                    # K % 256
 
 
 def test_route_argument_checks(lib):
@@ -142,6 +146,8 @@ def test_ffn_and_layer_argument_checks(lib):
     p.fmt = 9
     assert f(ctypes.byref(p), FAKE, 4, FAKE, 2, 2, FAKE, FAKE, FAKE, FAKE, None, 0, None) == UNSUPPORTED
     p = _pool(I=40)
+    assert f(ctypes.byref(p), FAKE, 4, FAKE, 2, 2, FAKE, FAKE, FAKE, FAKE, None, 0, None) == INVALID
+    p = _pool(fmt=3, H=256, I=32)                  # Q4_K needs I % 256 == 0 too
     assert f(ctypes.byref(p), FAKE, 4, FAKE, 2, 2, FAKE, FAKE, FAKE, FAKE, None, 0, None) == INVALID
     p = _pool(n_slots=0)
     assert f(ctypes.byref(p), FAKE, 4, FAKE, 2, 2, FAKE, FAKE, FAKE, FAKE, None, 0, None) == INVALID
@@ -231,7 +237,8 @@ def test_pack_argument_checks(lib):
     f.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 5
     assert f(1, 1, 24, 64, FAKE, FAKE, FAKE, FAKE, None) == INVALID     # rows % 16
     assert f(1, 1, 32, 48, FAKE, FAKE, FAKE, FAKE, None) == INVALID     # K % 32
-    assert f(3, 1, 32, 64, FAKE, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+    assert f(9, 1, 32, 64, FAKE, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+    assert f(3, 1, 32, 64, FAKE, FAKE, FAKE, FAKE, None) == INVALID     # Q4_K: K % 256
     assert f(2, 1, 32, 64, FAKE, ctypes.c_void_p(0x10001), FAKE, FAKE, None) == INVALID
     assert f(1, 0, 32, 64, None, None, None, None, None) == OK
 

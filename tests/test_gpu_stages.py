@@ -116,6 +116,11 @@ FFN_CASES = [
     ("qwen_a3b_decode", None, qm.PATH_GEMV), ("qwen_a3b_decode", 40, qm.PATH_GROUPED),
     ("mixtral_q8_decode", None, qm.PATH_GEMV), ("mixtral_q8_decode", 3, qm.PATH_GEMV),
     ("mixtral_q8_decode", 24, qm.PATH_GROUPED),
+    # Q4_K: GEMV (1, 3 and 16 tokens), grouped GEMM, ragged expert sizes
+    ("tiny_q4k", 1, qm.PATH_GEMV), ("tiny_q4k", 3, qm.PATH_GEMV), ("tiny_q4k", 16, qm.PATH_GEMV),
+    ("tiny_q4k", 64, qm.PATH_GROUPED), ("tiny_q4k", 300, qm.PATH_GROUPED),
+    ("qwen_a3b_q4k_decode", None, qm.PATH_GEMV), ("qwen_a3b_q4k_decode", 40, qm.PATH_GROUPED),
+    ("mixtral_q4k_decode", None, qm.PATH_GEMV), ("mixtral_q4k_decode", 24, qm.PATH_GROUPED),
 ]
 
 
