@@ -82,7 +82,9 @@ typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_GROUPED = 2 } moe_
  *   MXFP4 scales: 1 byte at unit(r,b)
  *   Q8_0  codes : 32 bytes at unit(r,b) * 32, element i of the block at byte i
  *   Q8_0  scales: fp16 at byte unit(r,b) * 2
- *   Q4_K  codes : as MXFP4 (16 bytes per unit, element 2j in the low nibble of byte j)
+ *   Q4_K  codes : 16 bytes per unit; in each dword (8 consecutive elements of the block)
+ *                 byte j holds element j in its low nibble and element j+4 in its high
+ *                 nibble (so that each nibble plane widens to element pairs directly)
  *   Q4_K  scales: sc_b | m_b << 8 (two bytes) at byte unit(r,b) * 2; then, from byte
  *                 rows * nb * 2 of the matrix's scale plane, d | dmin << 16 (fp16 bits, four
  *                 bytes) of row r's super-block s at ((r / 16) * nsb + s) * 16 + r % 16

@@ -73,21 +73,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2_exact(float lo, float hi) {
   return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
 }
 
-// Two unsigned 4-bit codes in byte `sel` of `v` -> bf16 pair (128 + lo, 128 + hi), exact:
-// 0x43 in the high byte of a bf16 is 2^7, and the code fills the top of its 7-bit mantissa
-// field from the bottom (128 + q for q < 128).
-template <int sel>
-__device__ __forceinline__ uint32_t u4x2_to_bf16x2_off128(uint32_t v) {
-  const uint32_t b = v >> (8 * sel);
-  return 0x43004300u | (b & 0xFu) | ((b & 0xF0u) << 12);
+// 8 unsigned 4-bit codes in the pool's split order (byte j holds element j in its low
+// nibble and element j + 4 in its high nibble) -> 4 bf16 pairs (q0,q1) (q2,q3) (q4,q5)
+// (q6,q7), exact. A byte holding q in 0..15 is the FP8 E4M3 code of q * 2^-9 (subnormal for
+// q < 8, exponent field 1 for q >= 8), so the gfx950 scaled FP8 -> bf16 conversion with
+// scale 2^9 gives q; one conversion per pair.
+__device__ __forceinline__ void u4x8_split_to_bf16(uint32_t v, bf16x2* w) {
+  const uint32_t lo = v & 0x0F0F0F0Fu, hi = (v >> 4) & 0x0F0F0F0Fu;
+  w[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, false);
+  w[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, true);
+  w[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, false);
+  w[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, true);
 }
-
-// 8 unsigned 4-bit codes (one dword, element 0 in the low nibble of byte 0) -> 8 bf16
-// values 128 + q.
-__device__ __forceinline__ bf16x8 u4x8_to_bf16x8_off128(uint32_t v) {
-  u32x4 p = {u4x2_to_bf16x2_off128<0>(v), u4x2_to_bf16x2_off128<1>(v),
-             u4x2_to_bf16x2_off128<2>(v), u4x2_to_bf16x2_off128<3>(v)};
-  return __builtin_bit_cast(bf16x8, p);
+__device__ __forceinline__ bf16x8 u4x8_split_to_bf16x8(uint32_t v) {
+  bf16x2 w[4];
+  u4x8_split_to_bf16(v, w);
+  return bf16x8{w[0][0], w[0][1], w[1][0], w[1][1], w[2][0], w[2][1], w[3][0], w[3][1]};
 }
 
 // 8 int8 codes (two dwords) -> 8 bf16 (exact: |q| <= 128 has at most 8 significant bits).

@@ -99,18 +99,13 @@ __device__ __forceinline__ const uint8_t* super_base(const uint8_t* plane, int r
 }
 
 // Weights of the chunk as bf16 pairs (MXFP4: 16 pairs, scale folded in; Q8_0: 8 pairs,
-// scale applied later to the fp32 partial; Q4_K: 16 pairs 128 + q, scale and min applied
-// later).
+// scale applied later to the fp32 partial; Q4_K: 16 pairs of the codes q, scale and min
+// applied later).
 template <int FMT>
 __device__ __forceinline__ void widen(const Chunk& c, bf16x2* w) {
   if constexpr (FMT == kQ4_K) {
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      w[4 * d + 0] = __builtin_bit_cast(bf16x2, u4x2_to_bf16x2_off128<0>(c.q[d]));
-      w[4 * d + 1] = __builtin_bit_cast(bf16x2, u4x2_to_bf16x2_off128<1>(c.q[d]));
-      w[4 * d + 2] = __builtin_bit_cast(bf16x2, u4x2_to_bf16x2_off128<2>(c.q[d]));
-      w[4 * d + 3] = __builtin_bit_cast(bf16x2, u4x2_to_bf16x2_off128<3>(c.q[d]));
-    }
+    for (int d = 0; d < 4; ++d) u4x8_split_to_bf16(c.q[d], w + 4 * d);
   } else if constexpr (FMT == kMXFP4) {
     const float sc = c.ok ? e8m0_to_f32(c.s) : 0.f;
 #pragma unroll
@@ -132,8 +127,8 @@ __device__ __forceinline__ void widen(const Chunk& c, bf16x2* w) {
 }
 
 // s: the block's scale record (0 for a masked chunk: it then adds nothing); s2: Q4_K's
-// super-block record. Q4_K: with P = sum x (128 + q) and S = sum x over the block,
-// sum x w = a (P - 128 S) - c S where a = d sc and c = dmin m (both exact in fp32).
+// super-block record. Q4_K: with P = sum x q and S = sum x over the block,
+// sum x w = a P - c S where a = d sc and c = dmin m (both exact in fp32).
 template <int FMT>
 __device__ __forceinline__ float dot_chunk(const bf16x2* w, const uint32_t* xv, uint32_t s,
                                            uint32_t s2, float acc) {
@@ -146,8 +141,7 @@ __device__ __forceinline__ float dot_chunk(const bf16x2* w, const uint32_t* xv, 
     }
     const float a = fp16_to_f32((uint16_t)s2) * (float)(s & 0xFFu);
     const float c = fp16_to_f32((uint16_t)(s2 >> 16)) * (float)((s >> 8) & 0xFFu);
-    acc = fmaf(a, fmaf(-128.f, sx, p), acc);
-    return fmaf(-c, sx, acc);
+    return fmaf(-c, sx, fmaf(a, p, acc));
   } else if constexpr (FMT == kMXFP4) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc = dot2_bf16(w[i], xv[i], acc);
@@ -158,6 +152,35 @@ __device__ __forceinline__ float dot_chunk(const bf16x2* w, const uint32_t* xv, 
     for (int i = 0; i < 8; ++i) part = dot2_bf16(w[i], xv[i], part);
     return fmaf(fp16_to_f32((uint16_t)s), part, acc);   // s is 0 for masked chunks
   }
+}
+
+// dot_chunk with the block sum S = sum x given (Q4_K; other formats ignore it). S taken
+// as block_sum() computes it gives the same result as dot_chunk bit for bit.
+template <int FMT>
+__device__ __forceinline__ float dot_chunk_s(const bf16x2* w, const uint32_t* xv, uint32_t s,
+                                             uint32_t s2, float sx, float acc) {
+  if constexpr (FMT == kQ4_K) {
+    float p = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p = dot2_bf16(w[i], xv[i], p);
+    const float a = fp16_to_f32((uint16_t)s2) * (float)(s & 0xFFu);
+    const float c = fp16_to_f32((uint16_t)(s2 >> 16)) * (float)((s >> 8) & 0xFFu);
+    return fmaf(-c, sx, fmaf(a, p, acc));
+  } else {
+    return dot_chunk<FMT>(w, xv, s, s2, acc);
+  }
+}
+
+// Sum of the 32 bf16 values at p (LDS), in the order dot_chunk<kQ4_K> sums them.
+__device__ __forceinline__ float block_sum(const uint16_t* p) {
+  float sx = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const u32x4 v = *(const u32x4*)(p + q * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sx = dot2_bf16(0x3F803F80u, v[i], sx);
+  }
+  return sx;
 }
 
 // Geometry of a lane within a 1 KiB chunk of the tiled layout.
@@ -415,6 +438,8 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
   __shared__ float tw_l[kDCMaxPairs];
   __shared__ int ip_l[kDCMaxPairs];
   __shared__ int tmp[kDCWaves];
+  // Q4_K: the block sums of the staged h rows
+  __shared__ float hsum_l[FMT == kQ4_K ? kDCMaxH / 32 : 1];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int rg = blockIdx.x;
@@ -512,6 +537,10 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
     if (i < hp) *(u32x4*)&hs[i * 8] = hv[r];
   }
   __syncthreads();
+  if constexpr (FMT == kQ4_K) {
+    for (int i = threadIdx.x; i < np * I / 32; i += NTH) hsum_l[i] = block_sum(&hs[i * 32]);
+    __syncthreads();
+  }
   if (act == nullptr) {
     n_act = actl[0];
     per = kDCWaves / n_act;
@@ -553,7 +582,8 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
               xv[4 * qq + 2] = v[2];
               xv[4 * qq + 3] = v[3];
             }
-            acc[p] = dot_chunk<FMT>(w, xv, ch[u].ok ? ch[u].s : 0u, ch[u].s2, acc[p]);
+            const float sx = FMT == kQ4_K ? hsum_l[(lo + p) * (I / 32) + kx / 32] : 0.f;
+            acc[p] = dot_chunk_s<FMT>(w, xv, ch[u].ok ? ch[u].s : 0u, ch[u].s2, sx, acc[p]);
           }
         }
       }
@@ -649,6 +679,8 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
   __shared__ int nact_l;
   __shared__ int rank_l[kWave];
   __shared__ float red[kGWaves][NT][2][16];
+  // Q4_K: the block sums of the tokens' activation rows, shared by every row of every unit
+  __shared__ float xsum_l[FMT == kQ4_K ? NT * kRouteMaxH / 32 : 1];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -678,6 +710,10 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
     if (i < xp_n) *(u32x4*)&xs[i * 8] = xv[r];
   }
   __syncthreads();
+  if constexpr (FMT == kQ4_K) {   // read after the routing's barriers
+    const int nbx = H / 32;
+    for (int i = tid; i < T * nbx; i += kGThreads) xsum_l[i] = block_sum(&xs[i * 32]);
+  }
 
   // steps 2 and 3 for any T (used unless the one-token path below applies)
   auto route_general = [&]() {
@@ -853,10 +889,12 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
     const uint8_t* sa2 = super_base<FMT>(gsc + slot * sslot, I, H, rg, lane);
     const uint8_t* sbp2 = super_base<FMT>(usc + slot * sslot, I, H, rg, lane);
     const uint16_t* xrow[NT];
+    const float* xsum[NT];
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
       const int t = act_l[j][4 + (i < 4 ? i : 3)];
       xrow[i] = &xs[(t >= 0 ? t : 0) * H];
+      xsum[i] = &xsum_l[FMT == kQ4_K ? (t >= 0 ? t : 0) * (H / 32) : 0];
     }
     float acc[2][NT];
 #pragma unroll
@@ -899,7 +937,8 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
               xw[4 * q + 2] = xq[2];
               xw[4 * q + 3] = xq[3];
             }
-            acc[m][i] = dot_chunk<FMT>(w, xw, ch.ok ? ch.s : 0u, ch.s2, acc[m][i]);
+            const float sx = FMT == kQ4_K ? xsum[i][xo / 32] : 0.f;
+            acc[m][i] = dot_chunk_s<FMT>(w, xw, ch.ok ? ch.s : 0u, ch.s2, sx, acc[m][i]);
           }
         }
       }

@@ -295,9 +295,9 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
       }
     } else if constexpr (FMT == kQ4_K) {
       // one MFMA per 32-wide block, as for Q8_0: lane supplies K = 32 j + 8 g .. + 7 of block
-      // j, i.e. bytes 4 g .. 4 g + 3 of unit 16 j + lane%16, widened to 128 + q (exact). A
-      // fifth MFMA against ones gives each row's block sum S, and the block adds
-      // a P - (128 a + c) S with a = d sc, c = dmin m of the lane's column.
+      // j, i.e. bytes 4 g .. 4 g + 3 of unit 16 j + lane%16, widened to bf16 q (exact). A
+      // fifth MFMA against ones gives each row's block sum S, and the block adds a P - c S
+      // with a = d sc, c = dmin m of the lane's column.
       const bf16x8 ones = __builtin_bit_cast(
           bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 #pragma unroll 1
@@ -308,14 +308,14 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
         for (int f = 0; f < 4; ++f) {
           const int unit = 16 * j + mrow;
           const uint32_t q = *(const uint32_t*)(lds_bq + fg[f] * BS::kRunQ + unit * 16 + 4 * g4);
-          bv[f] = u4x8_to_bf16x8_off128(q);
+          bv[f] = u4x8_split_to_bf16x8(q);
           const uint32_t keep = (fcol[f] && 4 * c + j < nb) ? 0xffffu : 0u;
           const uint32_t rec = *(const uint16_t*)(lds_bs + fg[f] * BS::kRunS + unit * 2) & keep;
           const uint32_t dd = *(const uint32_t*)(lds_bs2 + fg[f] * BS::kRunS2 + mrow * 4);
           const float a = fp16_to_f32((uint16_t)dd) * (float)(rec & 0xFFu);
           const float cm = fp16_to_f32((uint16_t)(dd >> 16)) * (float)(rec >> 8);
           sa[f] = a;
-          sbias[f] = fmaf(128.f, a, cm);
+          sbias[f] = cm;
         }
 #pragma unroll
         for (int mf = 0; mf < 4; ++mf) {

@@ -25,8 +25,22 @@ __global__ __launch_bounds__(256) void k_pack(int64_t n_units, int rows, int nb,
     *(u32x4*)(dq + u * 16) = *(const u32x4*)(sq + i * 16);
     ds[u] = ss[i];
   } else if constexpr (FMT == kQ4_K) {
+    // codes: canonical element 2j / 2j+1 in byte j's low / high nibble -> the pool's split
+    // order, in each dword (8 elements) byte j holding element j (low) and j + 4 (high)
+    const u32x4 cw = *(const u32x4*)(sq + i * 16);
+    u32x4 pw;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      uint32_t e[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) e[t] = (cw[d] >> (4 * t)) & 0xFu;   // element t of the dword
+      uint32_t o = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o |= (e[j] | (e[j + 4] << 4)) << (8 * j);
+      pw[d] = o;
+    }
+    *(u32x4*)(dq + u * 16) = pw;
     // canonical scale row: (sc, m) per block, then (d, dmin) fp16 per super-block
-    *(u32x4*)(dq + u * 16) = *(const u32x4*)(sq + i * 16);
     const int nsb = nb / kSuperBlocks;
     const int64_t row_bytes = 2 * (int64_t)nb + kSuperBytes * nsb;
     const int64_t mat_bytes = (int64_t)rows * row_bytes;   // = the tiled plane's size

@@ -130,8 +130,8 @@ def check_h(h_gpu_bits, a_ref, slack):
 
 def _accumulated_magnitude(fmt, planes, name, s, W):
     """|term| per weight of the sums the kernels accumulate in fp32: |w| for MXFP4 and Q8_0;
-    for Q4_K the kernels sum x (128 + q) and x over a block, scaled by a = d sc and by
-    128 a + c (c = dmin m), so the magnitude is a (128 + q) + |128 a + c|."""
+    for Q4_K the kernels sum x q and x over a block, scaled by a = d sc and by c = dmin m,
+    so the magnitude is a q + |c|."""
     if fmt != "q4_k":
         return np.abs(W)
     codes = planes[name + "_q"][s]
@@ -142,7 +142,7 @@ def _accumulated_magnitude(fmt, planes, name, s, W):
     sc, m, d, dmin = codecs.q4_k_fields(planes[name + "_s"][s], K)
     a = np.abs(np.repeat(d, 8, axis=1) * sc)
     c = np.repeat(dmin, 8, axis=1) * m
-    return np.repeat(a, 32, axis=1) * (128 + q) + np.repeat(np.abs(128 * a + c), 32, axis=1)
+    return np.repeat(a, 32, axis=1) * q + np.repeat(np.abs(c), 32, axis=1)
 
 
 def h_slack(planes, fmt, slot_map, x_bits, k, offsets, perm, positions, a_ref):
