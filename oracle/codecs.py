@@ -17,6 +17,8 @@ not define them, so the definitions below are the public ones:
     6-bit min m_b, the super-block an fp16 scale d and an fp16 min scale dmin; element
     value d*sc_b*q - dmin*m_b for its 4-bit code q (0..15). The byte arrangement of the
     scales is this library's own canonical one (see dequant_q4_k).
+  * Q5_K (GGUF k-quant, same pages): Q4_K's scales and mins with a 5-bit code
+    q = low nibble + 16 * high bit (0..31).
   * IEEE binary16 and bfloat16 (the upper 16 bits of an IEEE binary32).
 Every function returns exact fp64 values; all of these formats embed exactly in fp64.
 """
@@ -202,6 +204,36 @@ def dequant_q4_k(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return q * np.repeat(a, 32, axis=1) - np.repeat(c, 32, axis=1)
 
 
+def q5_k_codes(codes: np.ndarray) -> np.ndarray:
+    """5-bit codes of a Q5_K code plane [rows, K/2 + K/8] -> int [rows, K].
+
+    Per row: K/2 bytes of low nibbles (element 2j in the low nibble of byte j), then K/8
+    bytes of high bits (element 8j + i in bit i of byte j).
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    rows, n = codes.shape
+    K = n * 8 // 5
+    lo = codes[:, :K // 2]
+    hb = codes[:, K // 2:K // 2 + K // 8]
+    q = np.empty((rows, K), dtype=np.int64)
+    q[:, 0::2] = lo & 0x0F
+    q[:, 1::2] = lo >> 4
+    for i in range(8):
+        q[:, i::8] += 16 * ((hb >> i) & 1)
+    return q
+
+
+def dequant_q5_k(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Q5_K matrix [rows, K/2 + K/8] codes + [rows, K/16 + K/64] scale bytes (as Q4_K)
+    -> fp64 [rows, K]: weight (r, i) = d[r, s] * sc[r, b] * q[r, i] - dmin[r, s] * m[r, b]."""
+    q = q5_k_codes(codes).astype(np.float64)
+    K = q.shape[1]
+    sc, m, d, dmin = q4_k_fields(scales, K)
+    a = np.repeat(d, 8, axis=1) * sc
+    c = np.repeat(dmin, 8, axis=1) * m
+    return q * np.repeat(a, 32, axis=1) - np.repeat(c, 32, axis=1)
+
+
 def dequant(fmt: str, codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     if fmt == "mxfp4":
         return dequant_mxfp4(codes, scales)
@@ -209,4 +241,6 @@ def dequant(fmt: str, codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
         return dequant_q8_0(codes, scales)
     if fmt == "q4_k":
         return dequant_q4_k(codes, scales)
+    if fmt == "q5_k":
+        return dequant_q5_k(codes, scales)
     raise ValueError(f"unknown block format {fmt!r}")

@@ -26,6 +26,8 @@ Layout of what is generated ("canonical" layout, indexed by pool slot):
   Q4_K:   *_q uint8 [S, rows, K/2]  two 4-bit codes per byte, element 2j in the low nibble
           *_s uint8 [S, rows, K/16 + K/64]  per row: (sc_b, m_b) bytes for each 32-block,
                                       then (d_s, dmin_s) fp16 bits for each 256-super-block
+  Q5_K:   *_q uint8 [S, rows, K/2 + K/8]  low nibbles as Q4_K, then the high bits (element
+                                      8j + i in bit i of byte j); *_s as Q4_K
   gate/up: rows = I, K = H;  down: rows = H, K = I.
 """
 from __future__ import annotations
@@ -45,7 +47,7 @@ class Config:
     I: int
     E: int
     k: int
-    fmt: str            # "mxfp4", "q8_0" or "q4_k"
+    fmt: str            # "mxfp4", "q8_0", "q4_k" or "q5_k"
     zipf_s: float | None
     slot: str           # "identity" or "perm"
     seed: int
@@ -76,6 +78,11 @@ CONFIGS: dict[str, Config] = {c.name: c for c in [
     Config("qwen_a3b_q4k_decode", 1, 2048, 768, 128, 8, "q4_k", 1.2, "perm", 707, 64),
     Config("qwen_a3b_q4k_prefill", 8192, 2048, 768, 128, 8, "q4_k", 1.2, "perm", 707, 1),
     Config("mixtral_q4k_decode", 1, 4096, 14336, 8, 2, "q4_k", None, "perm", 808, 8),
+    # Q5_K experts on the same shapes
+    Config("tiny_q5k", 64, 256, 512, 8, 2, "q5_k", None, "perm", 909, 1),
+    Config("qwen_a3b_q5k_decode", 1, 2048, 768, 128, 8, "q5_k", 1.2, "perm", 1010, 64),
+    Config("qwen_a3b_q5k_prefill", 8192, 2048, 768, 128, 8, "q5_k", 1.2, "perm", 1010, 1),
+    Config("mixtral_q5k_decode", 1, 4096, 14336, 8, 2, "q5_k", None, "perm", 1111, 8),
 ]}
 
 
@@ -178,7 +185,20 @@ def _q4_k_matrix(g: np.random.Generator, rows: int, K: int):
     return codes, scales
 
 
-_MAKERS = {"mxfp4": _mxfp4_matrix, "q8_0": _q8_0_matrix, "q4_k": _q4_k_matrix}
+def _q5_k_matrix(g: np.random.Generator, rows: int, K: int):
+    lo, scales = _q4_k_matrix(g, rows, K)
+    # d halved: with codes 0..31 (mean 15.5) the weights keep Q4_K's spread and a mean
+    # near zero against the same mins
+    nb, ns = K // 32, K // 256
+    sup = np.ascontiguousarray(scales[:, 2 * nb:]).view(np.uint16).reshape(rows, ns, 2)
+    sup[..., 0] = _f64_to_fp16_bits(g.uniform(0.75e-4, 1.25e-4, size=(rows, ns)))
+    scales[:, 2 * nb:] = sup.reshape(rows, 2 * ns).view(np.uint8)
+    hb = g.integers(0, 256, size=(rows, K // 8), dtype=np.uint8)
+    return np.concatenate([lo, hb], axis=1), scales
+
+
+_MAKERS = {"mxfp4": _mxfp4_matrix, "q8_0": _q8_0_matrix, "q4_k": _q4_k_matrix,
+           "q5_k": _q5_k_matrix}
 
 
 def make_expert(cfg: Config, layer: int, e: int) -> dict[str, np.ndarray]:

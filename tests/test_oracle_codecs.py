@@ -221,3 +221,49 @@ def test_q4_k_closed_forms():
     w = codecs.dequant_q4_k(codes, _q4_k_plane(np.ones((rows, 8), int), mins, full(zero),
                                                full(one)))
     assert np.array_equal(w, -np.repeat(mins, 32, axis=1).astype(float))
+
+
+def test_q5_k_brute_force_per_element():
+    """Q5_K: each element's code rebuilt bit by bit (low nibble, then bit i of high byte j
+    for element 8j + i) and its weight evaluated with Python floats."""
+    import struct
+    rng = np.random.default_rng(4)
+    rows, K = 2, 512
+    lo = rng.integers(0, 256, size=(rows, K // 2), dtype=np.uint8)
+    hb = rng.integers(0, 256, size=(rows, K // 8), dtype=np.uint8)
+    sc = rng.integers(0, 64, size=(rows, K // 32))
+    m = rng.integers(0, 64, size=(rows, K // 32))
+    d_bits = rng.uniform(-1, 1, size=(rows, K // 256)).astype(np.float16).view(np.uint16)
+    dmin_bits = rng.uniform(-1, 1, size=(rows, K // 256)).astype(np.float16).view(np.uint16)
+    got = codecs.dequant_q5_k(np.concatenate([lo, hb], axis=1),
+                              _q4_k_plane(sc, m, d_bits, dmin_bits))
+    for r in range(rows):
+        for i in range(K):
+            byte = int(lo[r, i // 2])
+            q = ((byte >> 4) if (i % 2) else (byte & 0xF)) + 16 * ((int(hb[r, i // 8]) >> (i % 8)) & 1)
+            s = i // 256
+            d = struct.unpack("<e", struct.pack("<H", int(d_bits[r, s])))[0]
+            dmin = struct.unpack("<e", struct.pack("<H", int(dmin_bits[r, s])))[0]
+            assert got[r, i] == d * int(sc[r, i // 32]) * q - dmin * int(m[r, i // 32]), (r, i)
+
+
+def test_q5_k_reduces_to_q4_k_and_to_its_high_bits():
+    rng = np.random.default_rng(5)
+    rows, K = 2, 256
+    lo = rng.integers(0, 256, size=(rows, K // 2), dtype=np.uint8)
+    sc = rng.integers(0, 64, size=(rows, K // 32))
+    m = rng.integers(0, 64, size=(rows, K // 32))
+    d_bits = rng.uniform(0, 1, size=(rows, 1)).astype(np.float16).view(np.uint16)
+    dmin_bits = rng.uniform(0, 1, size=(rows, 1)).astype(np.float16).view(np.uint16)
+    plane = _q4_k_plane(sc, m, d_bits, dmin_bits)
+    # no high bits: the Q4_K matrix of the same low nibbles and scales
+    zeros = np.zeros((rows, K // 8), dtype=np.uint8)
+    assert np.array_equal(codecs.dequant_q5_k(np.concatenate([lo, zeros], axis=1), plane),
+                          codecs.dequant_q4_k(lo, plane))
+    # no low nibbles, every high bit set: 16 d sc - dmin m
+    ones = np.full((rows, K // 8), 255, dtype=np.uint8)
+    w = codecs.dequant_q5_k(np.concatenate([np.zeros_like(lo), ones], axis=1), plane)
+    d = d_bits.view(np.float16).astype(np.float64)
+    dmin = dmin_bits.view(np.float16).astype(np.float64)
+    want = np.repeat(16 * d * sc - dmin * m, 32, axis=1)
+    assert np.array_equal(w, want)
