@@ -60,8 +60,10 @@ typedef enum {
  * MOE_W_Q4_K:  k-quant super-blocks of 256 elements = 8 blocks of 32; block b has a 6-bit
  *              scale sc_b and a 6-bit min m_b, the super-block fp16 d and dmin;
  *              weight = d * sc_b * q - dmin * m_b for the 4-bit code q (0..15). The
- *              reduction dimension (H for gate/up, I for down) must be a multiple of 256. */
-typedef enum { MOE_W_MXFP4 = 1, MOE_W_Q8_0 = 2, MOE_W_Q4_K = 3 } moe_wfmt;
+ *              reduction dimension (H for gate/up, I for down) must be a multiple of 256.
+ * MOE_W_Q5_K:  Q4_K's scales and mins with a 5-bit code q = low nibble + 16 * high bit
+ *              (0..31); the same multiple-of-256 rule.                                  */
+typedef enum { MOE_W_MXFP4 = 1, MOE_W_Q8_0 = 2, MOE_W_Q4_K = 3, MOE_W_Q5_K = 4 } moe_wfmt;
 
 /* Which expert-FFN schedule to use. AUTO picks the GEMV schedule for T <= 16 and the
  * grouped MFMA GEMM otherwise. Both give results within the same tolerance; they are not
@@ -89,6 +91,10 @@ typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_GROUPED = 2 } moe_
  *                 rows * nb * 2 of the matrix's scale plane, d | dmin << 16 (fp16 bits, four
  *                 bytes) of row r's super-block s at ((r / 16) * nsb + s) * 16 + r % 16
  *                 (nsb = K / 256), times 4
+ *   Q5_K  codes : the low nibbles as Q4_K's codes; then, from byte rows * nb * 16 of the
+ *                 matrix's code plane, one dword per unit at unit(r,b) * 4 whose bit 8j + s
+ *                 is the high bit of element 8 (s / 2) + j + 4 (s % 2) of the block
+ *   Q5_K  scales: as Q4_K
  * so the 16 rows of a row group are interleaved block by block: one 64-lane 16-byte load
  * reads 16 rows x 4 MXFP4 blocks (or 16 rows x 2 Q8_0 blocks) from one contiguous KiB.
  * Slot s of a plane starts at s * (bytes per matrix); rows of a matrix must be a multiple
@@ -117,8 +123,10 @@ size_t moe_plane_bytes(int32_t fmt, int32_t rows, int32_t K, int32_t scales);
  *   Q4_K : codes u8 [rows][K/2] (as MXFP4), scales u8 [rows][K/16 + K/64]: per row the
  *          pairs (sc_b, m_b) of its K/32 blocks, then the fp16 pairs (d_s, dmin_s) of its
  *          K/256 super-blocks (little-endian)
+ *   Q5_K : codes u8 [rows][K/2 + K/8]: per row the low nibbles (as Q4_K), then the high
+ *          bits (element 8j + i in bit i of byte j); scales as Q4_K
  * src and dst must not overlap. Returns MOE_ERR_INVALID_ARG for rows % 16 != 0 or
- * K % 32 != 0 (K % 256 != 0 for Q4_K), MOE_ERR_UNSUPPORTED for an unknown fmt.
+ * K % 32 != 0 (K % 256 != 0 for Q4_K and Q5_K), MOE_ERR_UNSUPPORTED for an unknown fmt.
  */
 moe_status moe_pool_pack(int32_t fmt, int32_t n_mats, int32_t rows, int32_t K,
                          const void* src_q, const void* src_s, void* dst_q, void* dst_s,

@@ -33,7 +33,11 @@ moe_status hip_status(hipError_t e, const char* where) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-bool known_fmt(int fmt) { return fmt == MOE_W_MXFP4 || fmt == MOE_W_Q8_0 || fmt == MOE_W_Q4_K; }
+bool known_fmt(int fmt) {
+  return fmt == MOE_W_MXFP4 || fmt == MOE_W_Q8_0 || fmt == MOE_W_Q4_K || fmt == MOE_W_Q5_K;
+}
+// k-quant formats: the reduction dimension must be a multiple of the 256-element super-block
+bool superblocked(int fmt) { return fmt == MOE_W_Q4_K || fmt == MOE_W_Q5_K; }
 
 // Launch errors are read back with hipGetLastError; drop any error an earlier, unrelated
 // HIP call left behind so it is not reported as this call's failure.
@@ -62,8 +66,8 @@ moe_status check_pool(const moe_pool* pool) {
   if (pool->n_slots < 1) return fail(MOE_ERR_INVALID_ARG, "n_slots = %d < 1", pool->n_slots);
   if (pool->H <= 0 || pool->H % 32) return fail(MOE_ERR_INVALID_ARG, "pool H = %d", pool->H);
   if (pool->I <= 0 || pool->I % 32) return fail(MOE_ERR_INVALID_ARG, "pool I = %d", pool->I);
-  if (pool->fmt == MOE_W_Q4_K && (pool->H % 256 || pool->I % 256))
-    return fail(MOE_ERR_INVALID_ARG, "Q4_K needs H and I to be multiples of 256 (H = %d, I = %d)",
+  if (superblocked(pool->fmt) && (pool->H % 256 || pool->I % 256))
+    return fail(MOE_ERR_INVALID_ARG, "k-quant pools need H and I to be multiples of 256 (H = %d, I = %d)",
                 pool->H, pool->I);
   CHECK_PTR(pool->gate_q);
   CHECK_PTR(pool->up_q);
@@ -76,7 +80,7 @@ moe_status check_pool(const moe_pool* pool) {
 
 size_t plane_bytes(int fmt, int64_t rows, int64_t K, bool scales) {
   if (scales) return (size_t)moe::scale_plane_bytes(fmt, rows, K);
-  return (size_t)(rows * (K / 32) * moe::code_bytes_per_block(fmt));
+  return (size_t)moe::code_plane_bytes(fmt, rows, K);
 }
 
 void pool_views(const moe_pool* p, moe::PoolView* g, moe::PoolView* u, moe::PoolView* d) {
@@ -177,7 +181,7 @@ const char* moe_status_string(moe_status s) {
 const char* moe_last_error(void) { return g_err; }
 
 size_t moe_plane_bytes(int32_t fmt, int32_t rows, int32_t K, int32_t scales) {
-  if (!known_fmt(fmt) || rows < 0 || K < 0 || (fmt == MOE_W_Q4_K && K % 256)) return 0;
+  if (!known_fmt(fmt) || rows < 0 || K < 0 || (superblocked(fmt) && K % 256)) return 0;
   return plane_bytes(fmt, rows, K, scales != 0);
 }
 
@@ -188,8 +192,8 @@ moe_status moe_pool_pack(int32_t fmt, int32_t n_mats, int32_t rows, int32_t K,
   if (n_mats < 0 || rows < 0 || K < 0) return fail(MOE_ERR_INVALID_ARG, "negative size");
   if (rows % 16) return fail(MOE_ERR_INVALID_ARG, "rows = %d is not a multiple of 16", rows);
   if (K % 32) return fail(MOE_ERR_INVALID_ARG, "K = %d is not a multiple of 32", K);
-  if (fmt == MOE_W_Q4_K && K % 256)
-    return fail(MOE_ERR_INVALID_ARG, "Q4_K needs K = %d to be a multiple of 256", K);
+  if (superblocked(fmt) && K % 256)
+    return fail(MOE_ERR_INVALID_ARG, "k-quants need K = %d to be a multiple of 256", K);
   if (n_mats == 0 || rows == 0 || K == 0) return ok();
   CHECK_PTR(src_q);
   CHECK_PTR(dst_q);

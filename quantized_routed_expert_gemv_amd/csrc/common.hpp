@@ -17,11 +17,14 @@ constexpr int kRowGroup = 16;   // rows interleaved per tile in the pool layout
 constexpr int kMaxK = 8;        // largest supported top-k
 constexpr int kMaxE = 256;      // largest supported expert count
 
-enum Fmt : int { kMXFP4 = 1, kQ8_0 = 2, kQ4_K = 3 };
+enum Fmt : int { kMXFP4 = 1, kQ8_0 = 2, kQ4_K = 3, kQ5_K = 4 };
 
-// Formats whose 32-element block is a 16-byte unit of 4-bit codes (MXFP4, Q4_K): a lane of a
-// 64-lane 16-byte load holds one whole block of one row.
+// Formats whose 32-element block is a 16-byte unit of 4-bit codes (MXFP4, Q4_K, and Q5_K's
+// low nibbles): a lane of a 64-lane 16-byte load holds one whole block of one row.
 __host__ __device__ constexpr bool unit16(int fmt) { return fmt != kQ8_0; }
+// k-quants with Q4_K's scales: 6-bit scale and min per block, fp16 d and dmin per
+// 256-element super-block.
+__host__ __device__ constexpr bool kquant(int fmt) { return fmt == kQ4_K || fmt == kQ5_K; }
 
 // ---------------------------------------------------------------- scalar conversions
 
@@ -137,8 +140,18 @@ constexpr int kSuperBlocks = 8;      // 32-element blocks per Q4_K super-block
 constexpr int64_t kSuperBytes = 4;   // bytes of one (d, dmin) record
 __host__ __device__ constexpr int64_t scale_plane_bytes(int fmt, int64_t rows, int64_t K) {
   return rows * (K / 32) * scale_bytes_per_block(fmt) +
-         (fmt == kQ4_K ? rows * (K / (32 * kSuperBlocks)) * kSuperBytes : 0);
+         (kquant(fmt) ? rows * (K / (32 * kSuperBlocks)) * kSuperBytes : 0);
 }
+// Q5_K's fifth code bit: after the 16-byte units of a matrix's code plane (rows * nb * 16
+// bytes) comes one dword per unit, at unit index * 4. Bit 8j + s of the dword is the high
+// bit of element 8 (s / 2) + j + 4 (s % 2) of the block, so that (dword >> s) & 0x01010101
+// gives, as bytes, the high bits of the four elements whose low nibbles form a nibble plane
+// of dword s / 2 of the unit (the low plane for even s, the high plane for odd s).
+__host__ __device__ constexpr int64_t hi_bytes_per_block(int fmt) { return fmt == kQ5_K ? 4 : 0; }
+__host__ __device__ constexpr int64_t code_plane_bytes(int fmt, int64_t rows, int64_t K) {
+  return rows * (K / 32) * (code_bytes_per_block(fmt) + hi_bytes_per_block(fmt));
+}
+__host__ __device__ constexpr int64_t hi_region(int64_t rows, int64_t K) { return rows * (K / 32) * 16; }
 // Byte offset, within a matrix's scale plane, of the super-block records (Q4_K).
 __host__ __device__ constexpr int64_t super_region(int64_t rows, int64_t K) {
   return rows * (K / 32) * 2;

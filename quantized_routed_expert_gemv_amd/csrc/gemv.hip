@@ -71,19 +71,31 @@ __device__ int find_active_expert(const int32_t* __restrict__ offsets, int E, in
 struct Chunk {
   u32x4 q;
   uint32_t s;    // the block's scale record
-  uint32_t s2;   // Q4_K: its super-block's d | dmin << 16
+  uint32_t s2;   // k-quants: its super-block's d | dmin << 16
+  uint32_t h;    // Q5_K: the block's high-bit dword
   bool ok;
 };
 
 template <int FMT>
 __device__ __forceinline__ void load_chunk(Chunk& c, const uint8_t* q, const uint8_t* s,
-                                           const uint8_t* s2, bool ok) {
+                                           const uint8_t* s2, const uint8_t* hq, bool ok) {
   c.q = ld16_stream(q);
   if constexpr (FMT == kMXFP4) c.s = __builtin_nontemporal_load(s);
   else c.s = __builtin_nontemporal_load((const uint16_t*)s);
-  if constexpr (FMT == kQ4_K) c.s2 = __builtin_nontemporal_load((const uint32_t*)s2);
+  if constexpr (kquant(FMT)) c.s2 = __builtin_nontemporal_load((const uint32_t*)s2);
   else c.s2 = 0;
+  if constexpr (FMT == kQ5_K) c.h = __builtin_nontemporal_load((const uint32_t*)hq);
+  else c.h = 0;
   c.ok = ok;
+}
+
+// Where a lane's high-bit dwords start (Q5_K; other formats: unused). plane: the matrix's
+// code plane for the slot; unit: the lane's unit of chunk 0. Chunk c is 256 bytes further.
+template <int FMT>
+__device__ __forceinline__ const uint8_t* hi_base(const uint8_t* plane, int rows, int K,
+                                                  int64_t unit) {
+  if constexpr (FMT != kQ5_K) return plane;
+  return plane + hi_region(rows, K) + unit * 4;
 }
 
 // Where a lane's super-block records start (Q4_K; other formats: unused). plane: the
@@ -92,7 +104,7 @@ __device__ __forceinline__ void load_chunk(Chunk& c, const uint8_t* q, const uin
 template <int FMT>
 __device__ __forceinline__ const uint8_t* super_base(const uint8_t* plane, int rows, int K,
                                                      int rg, int lane) {
-  if constexpr (FMT != kQ4_K) return plane;
+  if constexpr (!kquant(FMT)) return plane;
   const int nsb = K / (32 * kSuperBlocks);
   return plane + super_region(rows, K) +
          ((int64_t)rg * nsb * kRowGroup + (lane & 15)) * kSuperBytes;
@@ -100,12 +112,25 @@ __device__ __forceinline__ const uint8_t* super_base(const uint8_t* plane, int r
 
 // Weights of the chunk as bf16 pairs (MXFP4: 16 pairs, scale folded in; Q8_0: 8 pairs,
 // scale applied later to the fp32 partial; Q4_K: 16 pairs of the codes q, scale and min
-// applied later).
+// applied later; Q5_K: 16 pairs of the low nibbles, then 16 pairs of 16 x the high bits,
+// pair i + 16 covering the same elements as pair i).
 template <int FMT>
 __device__ __forceinline__ void widen(const Chunk& c, bf16x2* w) {
-  if constexpr (FMT == kQ4_K) {
+  if constexpr (kquant(FMT)) {
 #pragma unroll
     for (int d = 0; d < 4; ++d) u4x8_split_to_bf16(c.q[d], w + 4 * d);
+    if constexpr (FMT == kQ5_K) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        // bytes 0/1 are the E4M3 codes of 0 and 2^-9; scale 2^13 gives 0 or 16, exactly
+        const uint32_t lo = (c.h >> (2 * d)) & 0x01010101u;
+        const uint32_t hi = (c.h >> (2 * d + 1)) & 0x01010101u;
+        w[16 + 4 * d + 0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 8192.0f, false);
+        w[16 + 4 * d + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 8192.0f, true);
+        w[16 + 4 * d + 2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 8192.0f, false);
+        w[16 + 4 * d + 3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 8192.0f, true);
+      }
+    }
   } else if constexpr (FMT == kMXFP4) {
     const float sc = c.ok ? e8m0_to_f32(c.s) : 0.f;
 #pragma unroll
@@ -126,22 +151,31 @@ __device__ __forceinline__ void widen(const Chunk& c, bf16x2* w) {
   }
 }
 
-// s: the block's scale record (0 for a masked chunk: it then adds nothing); s2: Q4_K's
-// super-block record. Q4_K: with P = sum x q and S = sum x over the block,
-// sum x w = a P - c S where a = d sc and c = dmin m (both exact in fp32).
+// A k-quant block: with P = sum x q and S = sum x over the block, sum x w = a P - c S where
+// a = d sc and c = dmin m (both exact in fp32). P runs over the chunk's pairs (Q5_K: the low
+// nibbles' pairs, then the high bits').
+template <int FMT>
+__device__ __forceinline__ float kq_block(const bf16x2* w, const uint32_t* xv, uint32_t s,
+                                          uint32_t s2, float sx, float acc) {
+  constexpr int kPairs = FMT == kQ5_K ? 32 : 16;
+  float p = 0.f;
+#pragma unroll
+  for (int i = 0; i < kPairs; ++i) p = dot2_bf16(w[i], xv[i & 15], p);
+  const float a = fp16_to_f32((uint16_t)s2) * (float)(s & 0xFFu);
+  const float c = fp16_to_f32((uint16_t)(s2 >> 16)) * (float)((s >> 8) & 0xFFu);
+  return fmaf(-c, sx, fmaf(a, p, acc));
+}
+
+// s: the block's scale record (0 for a masked chunk: it then adds nothing); s2: a
+// k-quant's super-block record.
 template <int FMT>
 __device__ __forceinline__ float dot_chunk(const bf16x2* w, const uint32_t* xv, uint32_t s,
                                            uint32_t s2, float acc) {
-  if constexpr (FMT == kQ4_K) {
-    float p = 0.f, sx = 0.f;
+  if constexpr (kquant(FMT)) {
+    float sx = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      p = dot2_bf16(w[i], xv[i], p);
-      sx = dot2_bf16(0x3F803F80u, xv[i], sx);   // bf16 pair (1, 1)
-    }
-    const float a = fp16_to_f32((uint16_t)s2) * (float)(s & 0xFFu);
-    const float c = fp16_to_f32((uint16_t)(s2 >> 16)) * (float)((s >> 8) & 0xFFu);
-    return fmaf(-c, sx, fmaf(a, p, acc));
+    for (int i = 0; i < 16; ++i) sx = dot2_bf16(0x3F803F80u, xv[i], sx);   // bf16 pair (1, 1)
+    return kq_block<FMT>(w, xv, s, s2, sx, acc);
   } else if constexpr (FMT == kMXFP4) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc = dot2_bf16(w[i], xv[i], acc);
@@ -154,24 +188,19 @@ __device__ __forceinline__ float dot_chunk(const bf16x2* w, const uint32_t* xv, 
   }
 }
 
-// dot_chunk with the block sum S = sum x given (Q4_K; other formats ignore it). S taken
+// dot_chunk with the block sum S = sum x given (k-quants; other formats ignore it). S taken
 // as block_sum() computes it gives the same result as dot_chunk bit for bit.
 template <int FMT>
 __device__ __forceinline__ float dot_chunk_s(const bf16x2* w, const uint32_t* xv, uint32_t s,
                                              uint32_t s2, float sx, float acc) {
-  if constexpr (FMT == kQ4_K) {
-    float p = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) p = dot2_bf16(w[i], xv[i], p);
-    const float a = fp16_to_f32((uint16_t)s2) * (float)(s & 0xFFu);
-    const float c = fp16_to_f32((uint16_t)(s2 >> 16)) * (float)((s >> 8) & 0xFFu);
-    return fmaf(-c, sx, fmaf(a, p, acc));
+  if constexpr (kquant(FMT)) {
+    return kq_block<FMT>(w, xv, s, s2, sx, acc);
   } else {
     return dot_chunk<FMT>(w, xv, s, s2, acc);
   }
 }
 
-// Sum of the 32 bf16 values at p (LDS), in the order dot_chunk<kQ4_K> sums them.
+// Sum of the 32 bf16 values at p (LDS), in the order dot_chunk sums them for k-quants.
 __device__ __forceinline__ float block_sum(const uint16_t* p) {
   float sx = 0.f;
 #pragma unroll
@@ -193,7 +222,8 @@ struct LaneMap {
   static constexpr int kBlocksPerChunk = k16 ? 4 : 2;
   static constexpr int kKPerChunk = 32 * kBlocksPerChunk;     // K elements per chunk
   static constexpr int kXWords = k16 ? 16 : 8;                // u32 of x per lane per chunk
-  static constexpr int kScaleChunk = 64 * (FMT == kQ4_K ? 2 : 1);   // scale bytes per chunk
+  static constexpr int kScaleChunk = 64 * (kquant(FMT) ? 2 : 1);   // scale bytes per chunk
+  static constexpr int kWPairs = FMT == kQ5_K ? 32 : 16;            // widened pairs per chunk
   __device__ static int row(int lane) { return k16 ? (lane & 15) : ((lane >> 1) & 15); }
   __device__ static int blk(int lane) { return k16 ? (lane >> 4) : (lane >> 5); }
   // K offset of the lane's codes inside its chunk
@@ -264,6 +294,8 @@ __global__ __launch_bounds__(kGThreads) void k_gemv(
     const uint8_t* sbp = GATED ? bs + slot * a_sslot + (unit0 + lane_unit) * sb : nullptr;
     const uint8_t* sa2 = super_base<FMT>(as + slot * a_sslot, rows, K, rg, lane);
     const uint8_t* sbp2 = GATED ? super_base<FMT>(bs + slot * a_sslot, rows, K, rg, lane) : nullptr;
+    const uint8_t* ha = hi_base<FMT>(aq + slot * a_qslot, rows, K, unit0 + lane);
+    const uint8_t* hb = GATED ? hi_base<FMT>(bq + slot * a_qslot, rows, K, unit0 + lane) : nullptr;
     const int lblk = LM::blk(lane);
     const int koff = LM::koff(lane);
 
@@ -312,10 +344,10 @@ __global__ __launch_bounds__(kGThreads) void k_gemv(
           const bool ok = c < nc && b < nb;
           const int cs = ok ? c : 0;      // chunk 0 of the row group always exists
           load_chunk<FMT>(ca[u], qa + (int64_t)cs * 1024, sa + (int64_t)cs * LM::kScaleChunk,
-                          sa2 + (int64_t)(cs >> 1) * 64, ok);
+                          sa2 + (int64_t)(cs >> 1) * 64, ha + (int64_t)cs * 256, ok);
           if constexpr (GATED)
             load_chunk<FMT>(cbk[u], qb + (int64_t)cs * 1024, sbp + (int64_t)cs * LM::kScaleChunk,
-                            sbp2 + (int64_t)(cs >> 1) * 64, ok);
+                            sbp2 + (int64_t)(cs >> 1) * 64, hb + (int64_t)cs * 256, ok);
         }
         __builtin_amdgcn_sched_barrier(0);   // keep the whole batch of loads ahead of its use
         __syncthreads();
@@ -331,7 +363,7 @@ __global__ __launch_bounds__(kGThreads) void k_gemv(
         for (int u = 0; u < kU; ++u) {
           const int c = cbase + wave + kGWaves * u;
           const int xo = (c - cbase) * LM::kKPerChunk + koff;
-          bf16x2 w[16];
+          bf16x2 w[LM::kWPairs];
           uint32_t xv[LM::kXWords];
           widen<FMT>(ca[u], w);
 #pragma unroll
@@ -439,7 +471,7 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
   __shared__ int ip_l[kDCMaxPairs];
   __shared__ int tmp[kDCWaves];
   // Q4_K: the block sums of the staged h rows
-  __shared__ float hsum_l[FMT == kQ4_K ? kDCMaxH / 32 : 1];
+  __shared__ float hsum_l[kquant(FMT) ? kDCMaxH / 32 : 1];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int rg = blockIdx.x;
@@ -495,6 +527,7 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
   const uint8_t* qa = dq + (valid ? slot : 0) * qslot + unit0 * cb + lane * 16;
   const uint8_t* sa = ds + (valid ? slot : 0) * sslot + (unit0 + lane_unit) * sb;
   const uint8_t* sa2 = super_base<FMT>(ds + (valid ? slot : 0) * sslot, H, I, rg, lane);
+  const uint8_t* ha = hi_base<FMT>(dq + (valid ? slot : 0) * qslot, H, I, unit0 + lane);
   Chunk ch[kDCU];
   auto load_batch = [&](int cbase) {
 #pragma unroll
@@ -504,7 +537,7 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
       const bool ok = c < nc && b < nb;
       const int cs = ok ? c : 0;
       load_chunk<FMT>(ch[u], qa + (int64_t)cs * 1024, sa + (int64_t)cs * LM::kScaleChunk,
-                      sa2 + (int64_t)(cs >> 1) * 64, ok);
+                      sa2 + (int64_t)(cs >> 1) * 64, ha + (int64_t)cs * 256, ok);
     }
   };
   if (act != nullptr && busy && valid) load_batch(q);
@@ -537,7 +570,7 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
     if (i < hp) *(u32x4*)&hs[i * 8] = hv[r];
   }
   __syncthreads();
-  if constexpr (FMT == kQ4_K) {
+  if constexpr (kquant(FMT)) {
     for (int i = threadIdx.x; i < np * I / 32; i += NTH) hsum_l[i] = block_sum(&hs[i * 32]);
     __syncthreads();
   }
@@ -555,6 +588,7 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
     qa = dq + (valid ? slot : 0) * qslot + unit0 * cb + lane * 16;
     sa = ds + (valid ? slot : 0) * sslot + (unit0 + lane_unit) * sb;
     sa2 = super_base<FMT>(ds + (valid ? slot : 0) * sslot, H, I, rg, lane);
+    ha = hi_base<FMT>(dq + (valid ? slot : 0) * qslot, H, I, unit0 + lane);
     if (busy && valid) load_batch(q);
   }
   // 4. consume each batch as it arrives, then load the next
@@ -567,7 +601,7 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
       for (int u = 0; u < kDCU; ++u) {
         const int c = cbase + u * per;
         const int kx = ch[u].ok ? c * LM::kKPerChunk + koff : 0;   // masked lanes: any valid row part
-        bf16x2 w[16];
+        bf16x2 w[LM::kWPairs];
         uint32_t xv[LM::kXWords];
         widen<FMT>(ch[u], w);
 #pragma unroll
@@ -582,7 +616,7 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
               xv[4 * qq + 2] = v[2];
               xv[4 * qq + 3] = v[3];
             }
-            const float sx = FMT == kQ4_K ? hsum_l[(lo + p) * (I / 32) + kx / 32] : 0.f;
+            const float sx = kquant(FMT) ? hsum_l[(lo + p) * (I / 32) + kx / 32] : 0.f;
             acc[p] = dot_chunk_s<FMT>(w, xv, ch[u].ok ? ch[u].s : 0u, ch[u].s2, sx, acc[p]);
           }
         }
@@ -680,7 +714,7 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
   __shared__ int rank_l[kWave];
   __shared__ float red[kGWaves][NT][2][16];
   // Q4_K: the block sums of the tokens' activation rows, shared by every row of every unit
-  __shared__ float xsum_l[FMT == kQ4_K ? NT * kRouteMaxH / 32 : 1];
+  __shared__ float xsum_l[kquant(FMT) ? NT * kRouteMaxH / 32 : 1];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -710,7 +744,7 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
     if (i < xp_n) *(u32x4*)&xs[i * 8] = xv[r];
   }
   __syncthreads();
-  if constexpr (FMT == kQ4_K) {   // read after the routing's barriers
+  if constexpr (kquant(FMT)) {   // read after the routing's barriers
     const int nbx = H / 32;
     for (int i = tid; i < T * nbx; i += kGThreads) xsum_l[i] = block_sum(&xs[i * 32]);
   }
@@ -888,21 +922,26 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
     const uint8_t* sbp = usc + slot * sslot + (unit0 + lane_unit) * sb;
     const uint8_t* sa2 = super_base<FMT>(gsc + slot * sslot, I, H, rg, lane);
     const uint8_t* sbp2 = super_base<FMT>(usc + slot * sslot, I, H, rg, lane);
+    const uint8_t* ha = hi_base<FMT>(gq + slot * qslot, I, H, unit0 + lane);
+    const uint8_t* hb = hi_base<FMT>(uq + slot * qslot, I, H, unit0 + lane);
     const uint16_t* xrow[NT];
     const float* xsum[NT];
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
       const int t = act_l[j][4 + (i < 4 ? i : 3)];
       xrow[i] = &xs[(t >= 0 ? t : 0) * H];
-      xsum[i] = &xsum_l[FMT == kQ4_K ? (t >= 0 ? t : 0) * (H / 32) : 0];
+      xsum[i] = &xsum_l[kquant(FMT) ? (t >= 0 ? t : 0) * (H / 32) : 0];
     }
     float acc[2][NT];
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int i = 0; i < NT; ++i) acc[m][i] = 0.f;
-    constexpr int kRU = NT >= 4 ? 6 : kU;   // chunks per wave per batch (fewer live
-                                            // registers with 4 tokens)
+    // chunks per wave per batch: fewer with more tokens and with the k-quants' larger
+    // chunk records, so that the batch stays in registers
+    constexpr int kRU = FMT == kQ4_K ? (NT >= 4 ? 3 : NT >= 2 ? 4 : 6)
+                      : FMT == kQ5_K ? (NT >= 4 ? 2 : NT >= 2 ? 3 : 4)
+                      : NT >= 4 ? 6 : kU;
     for (int cbase = 0; cbase < nc; cbase += kGWaves * kRU) {
       Chunk ca[kRU], cbk[kRU];
 #pragma unroll
@@ -912,16 +951,16 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
         const bool ok = c < nc && b < nb;
         const int cs = ok ? c : 0;
         load_chunk<FMT>(ca[u], qa + (int64_t)cs * 1024, sa + (int64_t)cs * LM::kScaleChunk,
-                        sa2 + (int64_t)(cs >> 1) * 64, ok);
+                        sa2 + (int64_t)(cs >> 1) * 64, ha + (int64_t)cs * 256, ok);
         load_chunk<FMT>(cbk[u], qb + (int64_t)cs * 1024, sbp + (int64_t)cs * LM::kScaleChunk,
-                        sbp2 + (int64_t)(cs >> 1) * 64, ok);
+                        sbp2 + (int64_t)(cs >> 1) * 64, hb + (int64_t)cs * 256, ok);
       }
       __builtin_amdgcn_sched_barrier(0);   // the whole batch in flight before any is used
 #pragma unroll
       for (int u = 0; u < kRU; ++u) {
         const int c = cbase + wave + kGWaves * u;
         const int xo = ca[u].ok ? c * LM::kKPerChunk + koff : 0;   // masked: any valid part
-        bf16x2 w[16];
+        bf16x2 w[LM::kWPairs];
         uint32_t xw[LM::kXWords];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
@@ -937,7 +976,7 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
               xw[4 * q + 2] = xq[2];
               xw[4 * q + 3] = xq[3];
             }
-            const float sx = FMT == kQ4_K ? xsum[i][xo / 32] : 0.f;
+            const float sx = kquant(FMT) ? xsum[i][xo / 32] : 0.f;
             acc[m][i] = dot_chunk_s<FMT>(w, xw, ch.ok ? ch.s : 0u, ch.s2, sx, acc[m][i]);
           }
         }
@@ -1020,6 +1059,7 @@ hipError_t with_fmt(int fmt, F&& f) {
     case kMXFP4: return f(std::integral_constant<int, kMXFP4>{});
     case kQ8_0: return f(std::integral_constant<int, kQ8_0>{});
     case kQ4_K: return f(std::integral_constant<int, kQ4_K>{});
+    case kQ5_K: return f(std::integral_constant<int, kQ5_K>{});
     default: return hipErrorInvalidValue;
   }
 }

@@ -78,7 +78,9 @@ struct BStage {
   static constexpr int kRunS = 64 * scale_bytes_per_block(FMT);  // scale bytes per row group
   static constexpr int kQPieces = 8 * kRunQ / 16 / kTThreads;    // 16-byte code pieces/thread
   // Q4_K: the 16 rows' (d, dmin) records of the step's super-block, per row group
-  static constexpr int kRunS2 = FMT == kQ4_K ? kRowGroup * (int)kSuperBytes : 4;
+  static constexpr int kRunS2 = kquant(FMT) ? kRowGroup * (int)kSuperBytes : 4;
+  // Q5_K: the high-bit dwords of the run's 64 units
+  static constexpr int kRunH = FMT == kQ5_K ? 64 * 4 : 4;
 };
 
 template <int FMT, bool GATED>
@@ -94,6 +96,7 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
   __shared__ __attribute__((aligned(16))) uint8_t lds_bq[8 * BS::kRunQ];
   __shared__ __attribute__((aligned(16))) uint8_t lds_bs[8 * BS::kRunS];
   __shared__ __attribute__((aligned(16))) uint8_t lds_bs2[8 * BS::kRunS2];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_bh[8 * BS::kRunH];
   __shared__ int tmp4[4];
   __shared__ int sh[2];
   const int lane = threadIdx.x & (kWave - 1);
@@ -194,9 +197,9 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
     bs_blk = (off % BS::kRunS) / (16 * scale_bytes_per_block(FMT));
   }
   // Q4_K super-block records: thread t < 128 copies row t % 16 of local row group t / 16
-  const bool s2_thread = FMT == kQ4_K && threadIdx.x < 8 * kRowGroup;
+  const bool s2_thread = kquant(FMT) && threadIdx.x < 8 * kRowGroup;
   const uint8_t* bs2p = nullptr;
-  if constexpr (FMT == kQ4_K) {
+  if constexpr (kquant(FMT)) {
     const int g = (s2_thread ? threadIdx.x : 0) / kRowGroup;
     const int rg = GATED ? n0 / 16 + (g & 3) : n0 / 16 + g;
     const int rgc = rg * 16 < N ? rg : 0;
@@ -204,8 +207,21 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
     bs2p = (GATED && g >= 4 ? s1 : s0) + super_region(N, K) +
            ((int64_t)rgc * nsb * kRowGroup + (threadIdx.x & 15)) * kSuperBytes;
   }
+  // Q5_K high-bit dwords: thread t copies dwords t and t + 256 of the 8 runs (64 per run)
+  const uint8_t* bhp[2] = {nullptr, nullptr};
+  if constexpr (FMT == kQ5_K) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int dw = threadIdx.x + kTThreads * h;
+      const int g = dw / 64;
+      const int rg = GATED ? n0 / 16 + (g & 3) : n0 / 16 + g;
+      const int rgc = rg * 16 < N ? rg : 0;
+      bhp[h] = (GATED && g >= 4 ? q1 : q0) + hi_region(N, K) +
+               ((int64_t)rgc * nb * 16 + dw % 64) * 4;
+    }
+  }
   u32x4 breg[BS::kQPieces];
-  uint32_t sreg = 0, s2reg = 0;
+  uint32_t sreg = 0, s2reg = 0, hreg[2] = {0u, 0u};
   auto load_b = [&](int c) {
     // a step's run starts 4 blocks (64 units) after the previous one's; pieces of blocks
     // past the end of the row re-read step 0 (masked when consumed)
@@ -218,9 +234,13 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
       const int cs = 4 * c + bs_blk < nb ? c : 0;
       sreg = *(const uint32_t*)(bsp + (int64_t)cs * BS::kRunS);
     }
-    if constexpr (FMT == kQ4_K) {
+    if constexpr (kquant(FMT)) {
       // step c's blocks 4c .. 4c+3 lie in super-block c / 2 (K is a multiple of 256)
       if (s2_thread) s2reg = *(const uint32_t*)(bs2p + (int64_t)(c >> 1) * BS::kRunS2);
+    }
+    if constexpr (FMT == kQ5_K) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) hreg[h] = *(const uint32_t*)(bhp[h] + (int64_t)c * BS::kRunH);
     }
   };
 
@@ -259,8 +279,12 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
     for (int p = 0; p < BS::kQPieces; ++p)
       *(u32x4*)(lds_bq + (threadIdx.x + kTThreads * p) * 16) = breg[p];
     if (s_thread) *(uint32_t*)(lds_bs + threadIdx.x * 4) = sreg;
-    if constexpr (FMT == kQ4_K)
+    if constexpr (kquant(FMT))
       if (s2_thread) *(uint32_t*)(lds_bs2 + threadIdx.x * 4) = s2reg;
+    if constexpr (FMT == kQ5_K) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) *(uint32_t*)(lds_bh + (threadIdx.x + kTThreads * h) * 4) = hreg[h];
+    }
     __syncthreads();
     if (c + 1 < nsteps) {
       load_a(c + 1);
@@ -293,7 +317,7 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
             acc[mf][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[f], acc[mf][f], 0, 0, 0);
         }
       }
-    } else if constexpr (FMT == kQ4_K) {
+    } else if constexpr (kquant(FMT)) {
       // one MFMA per 32-wide block, as for Q8_0: lane supplies K = 32 j + 8 g .. + 7 of block
       // j, i.e. bytes 4 g .. 4 g + 3 of unit 16 j + lane%16, widened to bf16 q (exact). A
       // fifth MFMA against ones gives each row's block sum S, and the block adds a P - c S
@@ -302,13 +326,23 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
           bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 #pragma unroll 1
       for (int j = 0; j < 4; ++j) {
-        bf16x8 bv[4];
+        bf16x8 bv[4], bvh[4];
         float sa[4], sbias[4];
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
           const int unit = 16 * j + mrow;
           const uint32_t q = *(const uint32_t*)(lds_bq + fg[f] * BS::kRunQ + unit * 16 + 4 * g4);
           bv[f] = u4x8_split_to_bf16x8(q);
+          if constexpr (FMT == kQ5_K) {
+            // 16 x the high bits of the same 8 elements (bytes 0/1 -> E4M3 0 / 2^-9, x 2^13)
+            const uint32_t hw = *(const uint32_t*)(lds_bh + fg[f] * BS::kRunH + unit * 4);
+            const uint32_t lo = (hw >> (2 * g4)) & 0x01010101u, hi = (hw >> (2 * g4 + 1)) & 0x01010101u;
+            const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 8192.0f, false);
+            const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 8192.0f, true);
+            const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 8192.0f, false);
+            const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 8192.0f, true);
+            bvh[f] = bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+          }
           const uint32_t keep = (fcol[f] && 4 * c + j < nb) ? 0xffffu : 0u;
           const uint32_t rec = *(const uint16_t*)(lds_bs + fg[f] * BS::kRunS + unit * 2) & keep;
           const uint32_t dd = *(const uint32_t*)(lds_bs2 + fg[f] * BS::kRunS2 + mrow * 4);
@@ -326,9 +360,12 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
               __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, ones, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
           f32x4 t[4];
 #pragma unroll
-          for (int f = 0; f < 4; ++f)
+          for (int f = 0; f < 4; ++f) {
             t[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[f], f32x4{0.f, 0.f, 0.f, 0.f}, 0,
                                                            0, 0);
+            if constexpr (FMT == kQ5_K)
+              t[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bvh[f], t[f], 0, 0, 0);
+          }
 #pragma unroll
           for (int f = 0; f < 4; ++f)
 #pragma unroll
@@ -432,6 +469,9 @@ hipError_t launch_gate_up_grouped(int fmt, const PoolView& gate, const PoolView&
     case kQ4_K:
       return launch_ggemm_t<kQ4_K, true>(gate, up, slot_map, n_slots, E, offsets, perm, T, k, x,
                                          H, I, h, nullptr, err, stream);
+    case kQ5_K:
+      return launch_ggemm_t<kQ5_K, true>(gate, up, slot_map, n_slots, E, offsets, perm, T, k, x,
+                                         H, I, h, nullptr, err, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -449,6 +489,9 @@ hipError_t launch_down_grouped(int fmt, const PoolView& down, const int32_t* slo
                                           k, h, I, H, nullptr, y, err, stream);
     case kQ4_K:
       return launch_ggemm_t<kQ4_K, false>(down, down, slot_map, n_slots, E, offsets, nullptr, T,
+                                          k, h, I, H, nullptr, y, err, stream);
+    case kQ5_K:
+      return launch_ggemm_t<kQ5_K, false>(down, down, slot_map, n_slots, E, offsets, nullptr, T,
                                           k, h, I, H, nullptr, y, err, stream);
     default: return hipErrorInvalidValue;
   }

@@ -24,10 +24,15 @@ __global__ __launch_bounds__(256) void k_pack(int64_t n_units, int rows, int nb,
   if constexpr (FMT == kMXFP4) {
     *(u32x4*)(dq + u * 16) = *(const u32x4*)(sq + i * 16);
     ds[u] = ss[i];
-  } else if constexpr (FMT == kQ4_K) {
+  } else if constexpr (kquant(FMT)) {
     // codes: canonical element 2j / 2j+1 in byte j's low / high nibble -> the pool's split
     // order, in each dword (8 elements) byte j holding element j (low) and j + 4 (high)
-    const u32x4 cw = *(const u32x4*)(sq + i * 16);
+    const int64_t K = 32 * (int64_t)nb;
+    const int64_t crow = (int64_t)nb * (16 + hi_bytes_per_block(FMT));   // canonical row bytes
+    const uint8_t* scrow = sq + (mat * rows + r) * crow;
+    uint8_t* dqmat = dq + mat * code_plane_bytes(FMT, rows, K);
+    const int64_t um = pool_unit(r, b, nb);                               // unit in the matrix
+    const u32x4 cw = *(const u32x4*)(scrow + 16 * (int64_t)b);
     u32x4 pw;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
@@ -39,7 +44,21 @@ __global__ __launch_bounds__(256) void k_pack(int64_t n_units, int rows, int nb,
       for (int j = 0; j < 4; ++j) o |= (e[j] | (e[j + 4] << 4)) << (8 * j);
       pw[d] = o;
     }
-    *(u32x4*)(dq + u * 16) = pw;
+    *(u32x4*)(dqmat + um * 16) = pw;
+    if constexpr (FMT == kQ5_K) {
+      // canonical high bits of the block (bit e = element e) -> the pool's dword, whose bit
+      // 8j + s is element 8 (s / 2) + j + 4 (s % 2)
+      const uint8_t* hb = scrow + 16 * (int64_t)nb + 4 * (int64_t)b;
+      const uint32_t h32 = (uint32_t)hb[0] | ((uint32_t)hb[1] << 8) | ((uint32_t)hb[2] << 16) |
+                           ((uint32_t)hb[3] << 24);
+      uint32_t g = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int sh = 0; sh < 8; ++sh)
+          g |= ((h32 >> (8 * (sh >> 1) + j + 4 * (sh & 1))) & 1u) << (8 * j + sh);
+      *(uint32_t*)(dqmat + hi_region(rows, K) + um * 4) = g;
+    }
     // canonical scale row: (sc, m) per block, then (d, dmin) fp16 per super-block
     const int nsb = nb / kSuperBlocks;
     const int64_t row_bytes = 2 * (int64_t)nb + kSuperBytes * nsb;
@@ -75,10 +94,14 @@ hipError_t launch_pack(int fmt, int n_mats, int rows, int K, const void* sq, con
   if (fmt == kMXFP4)
     hipLaunchKernelGGL(k_pack<kMXFP4>, dim3((unsigned)blocks), dim3(256), 0, stream, n, rows, nb,
                        (const uint8_t*)sq, (const uint8_t*)ss, (uint8_t*)dq, (uint8_t*)ds);
-  else if (fmt == kQ4_K) {
+  else if (fmt == kQ4_K || fmt == kQ5_K) {
     if (nb % kSuperBlocks) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_pack<kQ4_K>, dim3((unsigned)blocks), dim3(256), 0, stream, n, rows, nb,
-                       (const uint8_t*)sq, (const uint8_t*)ss, (uint8_t*)dq, (uint8_t*)ds);
+    if (fmt == kQ4_K)
+      hipLaunchKernelGGL(k_pack<kQ4_K>, dim3((unsigned)blocks), dim3(256), 0, stream, n, rows,
+                         nb, (const uint8_t*)sq, (const uint8_t*)ss, (uint8_t*)dq, (uint8_t*)ds);
+    else
+      hipLaunchKernelGGL(k_pack<kQ5_K>, dim3((unsigned)blocks), dim3(256), 0, stream, n, rows,
+                         nb, (const uint8_t*)sq, (const uint8_t*)ss, (uint8_t*)dq, (uint8_t*)ds);
   } else
     hipLaunchKernelGGL(k_pack<kQ8_0>, dim3((unsigned)blocks), dim3(256), 0, stream, n, rows, nb,
                        (const uint8_t*)sq, (const uint8_t*)ss, (uint8_t*)dq, (uint8_t*)ds);

@@ -130,15 +130,18 @@ def check_h(h_gpu_bits, a_ref, slack):
 
 def _accumulated_magnitude(fmt, planes, name, s, W):
     """|term| per weight of the sums the kernels accumulate in fp32: |w| for MXFP4 and Q8_0;
-    for Q4_K the kernels sum x q and x over a block, scaled by a = d sc and by c = dmin m,
-    so the magnitude is a q + |c|."""
-    if fmt != "q4_k":
+    for Q4_K and Q5_K the kernels sum x q and x over a block, scaled by a = d sc and by
+    c = dmin m, so the magnitude is a q + |c|."""
+    if fmt not in ("q4_k", "q5_k"):
         return np.abs(W)
     codes = planes[name + "_q"][s]
-    K = 2 * codes.shape[1]
-    q = np.empty((codes.shape[0], K))
-    q[:, 0::2] = codes & 15
-    q[:, 1::2] = codes >> 4
+    if fmt == "q5_k":
+        q = codecs.q5_k_codes(codes).astype(np.float64)
+    else:
+        q = np.empty((codes.shape[0], 2 * codes.shape[1]))
+        q[:, 0::2] = codes & 15
+        q[:, 1::2] = codes >> 4
+    K = q.shape[1]
     sc, m, d, dmin = codecs.q4_k_fields(planes[name + "_s"][s], K)
     a = np.abs(np.repeat(d, 8, axis=1) * sc)
     c = np.repeat(dmin, 8, axis=1) * m

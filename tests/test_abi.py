@@ -88,6 +88,9 @@ def test_plane_bytes(lib):
     assert lib.moe_plane_bytes(3, 768, 2048, 0) == 768 * 2048 // 2
     assert lib.moe_plane_bytes(3, 768, 2048, 1) == 768 * (64 * 2 + 8 * 4)
     assert lib.moe_plane_bytes(3, 768, 2080, 1) == 0                    # K % 256
+    # Q5_K: Q4_K's planes plus 4 bytes of high bits per block in the code plane
+    assert lib.moe_plane_bytes(4, 768, 2048, 0) == 768 * 64 * (16 + 4)
+    assert lib.moe_plane_bytes(4, 768, 2048, 1) == 768 * (64 * 2 + 8 * 4)
 
 
 def test_route_argument_checks(lib):
