@@ -19,6 +19,10 @@ not define them, so the definitions below are the public ones:
     scales is this library's own canonical one (see dequant_q4_k).
   * Q5_K (GGUF k-quant, same pages): Q4_K's scales and mins with a 5-bit code
     q = low nibble + 16 * high bit (0..31).
+  * Q6_K (GGUF k-quant, same pages): super-blocks of 256 elements made of sixteen
+    16-element sub-blocks, each with a signed 8-bit scale sc_j, and an fp16 scale d per
+    super-block; a 6-bit code q = low nibble + 16 * (2-bit high part) (0..63); element
+    value d * sc_j * (q - 32).
   * IEEE binary16 and bfloat16 (the upper 16 bits of an IEEE binary32).
 Every function returns exact fp64 values; all of these formats embed exactly in fp64.
 """
@@ -234,6 +238,40 @@ def dequant_q5_k(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return q * np.repeat(a, 32, axis=1) - np.repeat(c, 32, axis=1)
 
 
+def q6_k_codes(codes: np.ndarray) -> np.ndarray:
+    """6-bit codes of a Q6_K code plane [rows, K/2 + K/4] -> int [rows, K].
+
+    Per row: K/2 bytes of low nibbles (element 2j in the low nibble of byte j), then K/4
+    bytes of 2-bit high parts (element 4j + i in bits 2i, 2i+1 of byte j).
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    rows, n = codes.shape
+    K = n * 4 // 3
+    lo = codes[:, :K // 2]
+    hi = codes[:, K // 2:K // 2 + K // 4]
+    q = np.empty((rows, K), dtype=np.int64)
+    q[:, 0::2] = lo & 0x0F
+    q[:, 1::2] = lo >> 4
+    for i in range(4):
+        q[:, i::4] += 16 * ((hi >> (2 * i)) & 3)
+    return q
+
+
+def dequant_q6_k(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Q6_K matrix [rows, K/2 + K/4] codes + [rows, K/16 + K/128] scale bytes -> fp64.
+
+    Scale plane per row: K/16 signed bytes sc_j (one per 16-element sub-block), then K/256
+    little-endian fp16 d_s. Weight (r, i) = d[r, i // 256] * sc[r, i // 16] * (q[r, i] - 32).
+    """
+    q = q6_k_codes(codes).astype(np.float64)
+    K = q.shape[1]
+    scales = np.asarray(scales, dtype=np.uint8)
+    sc = scales[:, :K // 16].view(np.int8).astype(np.float64)
+    d = fp16_decode(np.ascontiguousarray(scales[:, K // 16:K // 16 + K // 128]).view(np.uint16))
+    a = np.repeat(d, 16, axis=1) * sc                  # [rows, K/16]
+    return (q - 32.0) * np.repeat(a, 16, axis=1)
+
+
 def dequant(fmt: str, codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     if fmt == "mxfp4":
         return dequant_mxfp4(codes, scales)
@@ -243,4 +281,6 @@ def dequant(fmt: str, codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
         return dequant_q4_k(codes, scales)
     if fmt == "q5_k":
         return dequant_q5_k(codes, scales)
+    if fmt == "q6_k":
+        return dequant_q6_k(codes, scales)
     raise ValueError(f"unknown block format {fmt!r}")

@@ -28,6 +28,10 @@ Layout of what is generated ("canonical" layout, indexed by pool slot):
                                       then (d_s, dmin_s) fp16 bits for each 256-super-block
   Q5_K:   *_q uint8 [S, rows, K/2 + K/8]  low nibbles as Q4_K, then the high bits (element
                                       8j + i in bit i of byte j); *_s as Q4_K
+  Q6_K:   *_q uint8 [S, rows, K/2 + K/4]  low nibbles as Q4_K, then 2-bit high parts
+                                      (element 4j + i in bits 2i, 2i+1 of byte j)
+          *_s uint8 [S, rows, K/16 + K/128] int8 scale per 16-element sub-block, then fp16 d
+                                      per 256-element super-block
   gate/up: rows = I, K = H;  down: rows = H, K = I.
 """
 from __future__ import annotations
@@ -47,7 +51,7 @@ class Config:
     I: int
     E: int
     k: int
-    fmt: str            # "mxfp4", "q8_0", "q4_k" or "q5_k"
+    fmt: str            # "mxfp4", "q8_0", "q4_k", "q5_k" or "q6_k"
     zipf_s: float | None
     slot: str           # "identity" or "perm"
     seed: int
@@ -83,6 +87,11 @@ CONFIGS: dict[str, Config] = {c.name: c for c in [
     Config("qwen_a3b_q5k_decode", 1, 2048, 768, 128, 8, "q5_k", 1.2, "perm", 1010, 64),
     Config("qwen_a3b_q5k_prefill", 8192, 2048, 768, 128, 8, "q5_k", 1.2, "perm", 1010, 1),
     Config("mixtral_q5k_decode", 1, 4096, 14336, 8, 2, "q5_k", None, "perm", 1111, 8),
+    # Q6_K experts on the same shapes
+    Config("tiny_q6k", 64, 256, 512, 8, 2, "q6_k", None, "perm", 1212, 1),
+    Config("qwen_a3b_q6k_decode", 1, 2048, 768, 128, 8, "q6_k", 1.2, "perm", 1313, 64),
+    Config("qwen_a3b_q6k_prefill", 8192, 2048, 768, 128, 8, "q6_k", 1.2, "perm", 1313, 1),
+    Config("mixtral_q6k_decode", 1, 4096, 14336, 8, 2, "q6_k", None, "perm", 1414, 8),
 ]}
 
 
@@ -197,8 +206,18 @@ def _q5_k_matrix(g: np.random.Generator, rows: int, K: int):
     return np.concatenate([lo, hb], axis=1), scales
 
 
+def _q6_k_matrix(g: np.random.Generator, rows: int, K: int):
+    if K % 256:
+        raise ValueError(f"Q6_K needs K to be a multiple of 256, got {K}")
+    codes = g.integers(0, 256, size=(rows, K // 2 + K // 4), dtype=np.uint8)   # q uniform 0..63
+    sc = g.integers(-127, 128, size=(rows, K // 16)).astype(np.int8)          # signed scales
+    d = _f64_to_fp16_bits(g.uniform(3.0e-5, 5.0e-5, size=(rows, K // 256)))
+    scales = np.concatenate([sc.view(np.uint8), np.ascontiguousarray(d).view(np.uint8)], axis=1)
+    return codes, scales
+
+
 _MAKERS = {"mxfp4": _mxfp4_matrix, "q8_0": _q8_0_matrix, "q4_k": _q4_k_matrix,
-           "q5_k": _q5_k_matrix}
+           "q5_k": _q5_k_matrix, "q6_k": _q6_k_matrix}
 
 
 def make_expert(cfg: Config, layer: int, e: int) -> dict[str, np.ndarray]:

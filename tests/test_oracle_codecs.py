@@ -267,3 +267,50 @@ def test_q5_k_reduces_to_q4_k_and_to_its_high_bits():
     dmin = dmin_bits.view(np.float16).astype(np.float64)
     want = np.repeat(16 * d * sc - dmin * m, 32, axis=1)
     assert np.array_equal(w, want)
+
+
+def _q6_k_plane(sc, d_bits):
+    """Q6_K scale plane bytes written field by field with struct."""
+    import struct
+    rows, nsub = sc.shape
+    out = np.zeros((rows, nsub + 2 * (nsub // 16)), dtype=np.uint8)
+    for r in range(rows):
+        raw = struct.pack(f"<{nsub}b", *[int(v) for v in sc[r]])
+        raw += struct.pack(f"<{nsub // 16}H", *[int(v) for v in d_bits[r]])
+        out[r] = np.frombuffer(raw, dtype=np.uint8)
+    return out
+
+
+def test_q6_k_brute_force_per_element():
+    """Q6_K: each code rebuilt from its nibble and its 2-bit high part, each weight evaluated
+    with Python floats and the fp16 d decoded by struct."""
+    import struct
+    rng = np.random.default_rng(6)
+    rows, K = 2, 512
+    lo = rng.integers(0, 256, size=(rows, K // 2), dtype=np.uint8)
+    hi = rng.integers(0, 256, size=(rows, K // 4), dtype=np.uint8)
+    sc = rng.integers(-128, 128, size=(rows, K // 16))
+    d_bits = rng.uniform(-1, 1, size=(rows, K // 256)).astype(np.float16).view(np.uint16)
+    got = codecs.dequant_q6_k(np.concatenate([lo, hi], axis=1), _q6_k_plane(sc, d_bits))
+    for r in range(rows):
+        for i in range(K):
+            byte = int(lo[r, i // 2])
+            q = ((byte >> 4) if (i % 2) else (byte & 0xF)) + 16 * ((int(hi[r, i // 4]) >> (2 * (i % 4))) & 3)
+            d = struct.unpack("<e", struct.pack("<H", int(d_bits[r, i // 256])))[0]
+            assert got[r, i] == d * int(sc[r, i // 16]) * (q - 32), (r, i)
+
+
+def test_q6_k_closed_forms():
+    rows, K = 1, 256
+    one = np.full((rows, 1), np.float16(1.0).view(np.uint16), dtype=np.uint16)
+    # every code 32 (nibble 0, high part 2): all weights zero whatever the scales
+    lo = np.zeros((rows, K // 2), dtype=np.uint8)
+    hi = np.full((rows, K // 4), 0b10101010, dtype=np.uint8)
+    sc = np.arange(-8, 8).reshape(1, 16) * 15
+    w = codecs.dequant_q6_k(np.concatenate([lo, hi], axis=1), _q6_k_plane(sc, one))
+    assert np.array_equal(w, np.zeros((rows, K)))
+    # every code 63 with d = 1: 31 * sc of each 16-element sub-block
+    lo = np.full((rows, K // 2), 0xFF, dtype=np.uint8)
+    hi = np.full((rows, K // 4), 0xFF, dtype=np.uint8)
+    w = codecs.dequant_q6_k(np.concatenate([lo, hi], axis=1), _q6_k_plane(sc, one))
+    assert np.array_equal(w, np.repeat(31.0 * sc, 16, axis=1))

@@ -428,3 +428,31 @@ def test_q4_k_layer_equals_the_q8_0_layer_of_the_same_weights():
     a = moe.layer(planes4, "q4_k", L.slot_map, L.wr, None, L.x, cfg.k)
     b = moe.layer(planes8, "q8_0", L.slot_map, L.wr, None, L.x, cfg.k)
     assert np.array_equal(a["h"], b["h"]) and np.array_equal(a["out"], b["out"])
+
+
+def test_q6_k_layer_equals_the_q8_0_layer_of_the_same_weights():
+    """Q6_K experts with d = 1 and every sub-block scale 1 carry the integer weights q - 32;
+    the same integers as Q8_0 codes with d = 1 give the same layer."""
+    cfg = synth.config("tiny_q6k", T=8)
+    L = synth.make_layer(cfg)
+    one = np.float16(1.0).view(np.uint16)
+    planes6, planes8 = {}, {}
+    for n in ("gate", "up", "down"):
+        codes = L.planes[n + "_q"]                          # [S, rows, K/2 + K/4]
+        S, rows, nbytes = codes.shape
+        K = nbytes * 4 // 3
+        sc = np.ones((S, rows, K // 16), dtype=np.uint8)
+        d = np.full((S, rows, K // 256), one, dtype=np.uint16)
+        planes6[n + "_q"] = codes
+        planes6[n + "_s"] = np.concatenate([sc, d.view(np.uint8)], axis=2)
+        lo, hi = codes[..., :K // 2], codes[..., K // 2:]
+        q = np.empty((S, rows, K), dtype=np.int64)
+        q[..., 0::2] = lo & 15
+        q[..., 1::2] = lo >> 4
+        for i in range(4):
+            q[..., i::4] += 16 * ((hi >> (2 * i)) & 3)
+        planes8[n + "_q"] = (q - 32).astype(np.int8)
+        planes8[n + "_s"] = np.full((S, rows, K // 32), one, dtype=np.uint16)
+    a = moe.layer(planes6, "q6_k", L.slot_map, L.wr, None, L.x, cfg.k)
+    b = moe.layer(planes8, "q8_0", L.slot_map, L.wr, None, L.x, cfg.k)
+    assert np.array_equal(a["h"], b["h"]) and np.array_equal(a["out"], b["out"])
