@@ -186,11 +186,11 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
                 "kernel": "gate/up grouped GEMM (k_ggemm)", "work_per_launch": flops}
     else:
-        # bytes per weight of the format: MXFP4 16+1 and Q8_0 32+2 per 32; Q4_K 144 and
-        # Q5_K 176 per 256 (the pool keeps 0.5 more per 32: the 6-bit scale and min in two
-        # whole bytes)
+        # bytes per weight of the format: MXFP4 16+1 and Q8_0 32+2 per 32; Q4_K 144, Q5_K
+        # 176 and Q6_K 210 per 256 (the pool keeps 0.5 more per 32 for Q4_K / Q5_K, the 6-bit
+        # scale and min in two whole bytes, and 0.25 more for Q6_K, d in a 4-byte record)
         bpw = {"mxfp4": 17.0 / 32.0, "q8_0": 34.0 / 32.0, "q4_k": 18.0 / 32.0,
-               "q5_k": 22.0 / 32.0}[cfg.fmt]
+               "q5_k": 22.0 / 32.0, "q6_k": 26.25 / 32.0}[cfg.fmt]
         fused = T <= 4 and T * E <= 256 and H <= 4096
         # distinct experts per layer: recomputed from each layer's routing on the device
         n_distinct = []

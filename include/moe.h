@@ -62,8 +62,14 @@ typedef enum {
  *              weight = d * sc_b * q - dmin * m_b for the 4-bit code q (0..15). The
  *              reduction dimension (H for gate/up, I for down) must be a multiple of 256.
  * MOE_W_Q5_K:  Q4_K's scales and mins with a 5-bit code q = low nibble + 16 * high bit
- *              (0..31); the same multiple-of-256 rule.                                  */
-typedef enum { MOE_W_MXFP4 = 1, MOE_W_Q8_0 = 2, MOE_W_Q4_K = 3, MOE_W_Q5_K = 4 } moe_wfmt;
+ *              (0..31); the same multiple-of-256 rule.
+ * MOE_W_Q6_K:  k-quant super-blocks of 256 elements = 16 sub-blocks of 16 with a signed
+ *              8-bit scale sc_j each and an fp16 d per super-block; weight = d * sc_j *
+ *              (q - 32) for the 6-bit code q = low nibble + 16 * high part (0..63); the
+ *              same multiple-of-256 rule.                                               */
+typedef enum {
+  MOE_W_MXFP4 = 1, MOE_W_Q8_0 = 2, MOE_W_Q4_K = 3, MOE_W_Q5_K = 4, MOE_W_Q6_K = 5
+} moe_wfmt;
 
 /* Which expert-FFN schedule to use. AUTO picks the GEMV schedule for T <= 16 and the
  * grouped MFMA GEMM otherwise. Both give results within the same tolerance; they are not
@@ -95,6 +101,13 @@ typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_GROUPED = 2 } moe_
  *                 matrix's code plane, one dword per unit at unit(r,b) * 4 whose bit 8j + s
  *                 is the high bit of element 8 (s / 2) + j + 4 (s % 2) of the block
  *   Q5_K  scales: as Q4_K
+ *   Q6_K  codes : the low nibbles as Q4_K's codes; then, from byte rows * nb * 16, two
+ *                 dwords per unit at unit(r,b) * 8: dword g covers code dwords 2g, 2g+1 of
+ *                 the unit, its bits 8j + s and 8j + s + 1 (s = 0, 2, 4, 6) holding the
+ *                 2-bit high part of element 8 (2g + s / 4) + j + 4 ((s / 2) % 2)
+ *   Q6_K  scales: the two sub-block scales (int8) of block b at unit(r,b) * 2; then, from
+ *                 byte rows * nb * 2, d (fp16 bits, in a four-byte record whose high half
+ *                 is unused) tiled as Q4_K's (d, dmin)
  * so the 16 rows of a row group are interleaved block by block: one 64-lane 16-byte load
  * reads 16 rows x 4 MXFP4 blocks (or 16 rows x 2 Q8_0 blocks) from one contiguous KiB.
  * Slot s of a plane starts at s * (bytes per matrix); rows of a matrix must be a multiple
@@ -125,8 +138,12 @@ size_t moe_plane_bytes(int32_t fmt, int32_t rows, int32_t K, int32_t scales);
  *          K/256 super-blocks (little-endian)
  *   Q5_K : codes u8 [rows][K/2 + K/8]: per row the low nibbles (as Q4_K), then the high
  *          bits (element 8j + i in bit i of byte j); scales as Q4_K
+ *   Q6_K : codes u8 [rows][K/2 + K/4]: per row the low nibbles (as Q4_K), then the 2-bit
+ *          high parts (element 4j + i in bits 2i, 2i+1 of byte j); scales u8
+ *          [rows][K/16 + K/128]: per row the int8 sub-block scales, then fp16 d per
+ *          super-block
  * src and dst must not overlap. Returns MOE_ERR_INVALID_ARG for rows % 16 != 0 or
- * K % 32 != 0 (K % 256 != 0 for Q4_K and Q5_K), MOE_ERR_UNSUPPORTED for an unknown fmt.
+ * K % 32 != 0 (K % 256 != 0 for the k-quants), MOE_ERR_UNSUPPORTED for an unknown fmt.
  */
 moe_status moe_pool_pack(int32_t fmt, int32_t n_mats, int32_t rows, int32_t K,
                          const void* src_q, const void* src_s, void* dst_q, void* dst_s,

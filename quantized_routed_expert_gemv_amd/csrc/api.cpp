@@ -34,10 +34,11 @@ moe_status hip_status(hipError_t e, const char* where) {
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 bool known_fmt(int fmt) {
-  return fmt == MOE_W_MXFP4 || fmt == MOE_W_Q8_0 || fmt == MOE_W_Q4_K || fmt == MOE_W_Q5_K;
+  return fmt == MOE_W_MXFP4 || fmt == MOE_W_Q8_0 || fmt == MOE_W_Q4_K || fmt == MOE_W_Q5_K ||
+         fmt == MOE_W_Q6_K;
 }
 // k-quant formats: the reduction dimension must be a multiple of the 256-element super-block
-bool superblocked(int fmt) { return fmt == MOE_W_Q4_K || fmt == MOE_W_Q5_K; }
+bool superblocked(int fmt) { return fmt == MOE_W_Q4_K || fmt == MOE_W_Q5_K || fmt == MOE_W_Q6_K; }
 
 // Launch errors are read back with hipGetLastError; drop any error an earlier, unrelated
 // HIP call left behind so it is not reported as this call's failure.

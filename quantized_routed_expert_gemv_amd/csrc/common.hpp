@@ -17,14 +17,19 @@ constexpr int kRowGroup = 16;   // rows interleaved per tile in the pool layout
 constexpr int kMaxK = 8;        // largest supported top-k
 constexpr int kMaxE = 256;      // largest supported expert count
 
-enum Fmt : int { kMXFP4 = 1, kQ8_0 = 2, kQ4_K = 3, kQ5_K = 4 };
+enum Fmt : int { kMXFP4 = 1, kQ8_0 = 2, kQ4_K = 3, kQ5_K = 4, kQ6_K = 5 };
 
 // Formats whose 32-element block is a 16-byte unit of 4-bit codes (MXFP4, Q4_K, and Q5_K's
 // low nibbles): a lane of a 64-lane 16-byte load holds one whole block of one row.
 __host__ __device__ constexpr bool unit16(int fmt) { return fmt != kQ8_0; }
-// k-quants with Q4_K's scales: 6-bit scale and min per block, fp16 d and dmin per
-// 256-element super-block.
-__host__ __device__ constexpr bool kquant(int fmt) { return fmt == kQ4_K || fmt == kQ5_K; }
+// k-quants: per-unit scale records of two bytes and one 4-byte record per (row,
+// 256-element super-block). Q4_K and Q5_K: 6-bit scale and min per block, fp16 d and dmin
+// per super-block. Q6_K: a signed 8-bit scale per 16-element half block, fp16 d per
+// super-block (the record's high half unused).
+__host__ __device__ constexpr bool kquant(int fmt) { return fmt == kQ4_K || fmt == kQ5_K || fmt == kQ6_K; }
+// Block sums the k-quant kernels need per 32-element block: Q6_K's two halves have their
+// own scales.
+__host__ __device__ constexpr int sums_per_block(int fmt) { return fmt == kQ6_K ? 2 : 1; }
 
 // ---------------------------------------------------------------- scalar conversions
 
@@ -147,7 +152,13 @@ __host__ __device__ constexpr int64_t scale_plane_bytes(int fmt, int64_t rows, i
 // bit of element 8 (s / 2) + j + 4 (s % 2) of the block, so that (dword >> s) & 0x01010101
 // gives, as bytes, the high bits of the four elements whose low nibbles form a nibble plane
 // of dword s / 2 of the unit (the low plane for even s, the high plane for odd s).
-__host__ __device__ constexpr int64_t hi_bytes_per_block(int fmt) { return fmt == kQ5_K ? 4 : 0; }
+// Q6_K's 2-bit high parts: two dwords per unit at unit index * 8; dword g covers the unit's
+// code dwords 2g and 2g + 1, its bits 8j + s, 8j + s + 1 holding the high part of element
+// 8 (2g + s / 4) + j + 4 ((s / 2) % 2) (s even), so that (dword >> s) & 0x03030303 gives one
+// nibble plane's high parts as bytes.
+__host__ __device__ constexpr int64_t hi_bytes_per_block(int fmt) {
+  return fmt == kQ5_K ? 4 : fmt == kQ6_K ? 8 : 0;
+}
 __host__ __device__ constexpr int64_t code_plane_bytes(int fmt, int64_t rows, int64_t K) {
   return rows * (K / 32) * (code_bytes_per_block(fmt) + hi_bytes_per_block(fmt));
 }

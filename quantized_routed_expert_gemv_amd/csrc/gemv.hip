@@ -72,7 +72,7 @@ struct Chunk {
   u32x4 q;
   uint32_t s;    // the block's scale record
   uint32_t s2;   // k-quants: its super-block's d | dmin << 16
-  uint32_t h;    // Q5_K: the block's high-bit dword
+  u32x2 h;       // Q5_K: the block's high-bit dword; Q6_K: its two high-part dwords
   bool ok;
 };
 
@@ -84,18 +84,20 @@ __device__ __forceinline__ void load_chunk(Chunk& c, const uint8_t* q, const uin
   else c.s = __builtin_nontemporal_load((const uint16_t*)s);
   if constexpr (kquant(FMT)) c.s2 = __builtin_nontemporal_load((const uint32_t*)s2);
   else c.s2 = 0;
-  if constexpr (FMT == kQ5_K) c.h = __builtin_nontemporal_load((const uint32_t*)hq);
-  else c.h = 0;
+  if constexpr (FMT == kQ5_K) c.h = u32x2{__builtin_nontemporal_load((const uint32_t*)hq), 0u};
+  else if constexpr (FMT == kQ6_K) c.h = __builtin_nontemporal_load((const u32x2*)hq);
+  else c.h = u32x2{0u, 0u};
   c.ok = ok;
 }
 
-// Where a lane's high-bit dwords start (Q5_K; other formats: unused). plane: the matrix's
-// code plane for the slot; unit: the lane's unit of chunk 0. Chunk c is 256 bytes further.
+// Where a lane's high-bit dwords start (Q5_K, Q6_K; other formats: unused). plane: the
+// matrix's code plane for the slot; unit: the lane's unit of chunk 0. Chunk c is
+// 64 * hi_bytes_per_block further.
 template <int FMT>
 __device__ __forceinline__ const uint8_t* hi_base(const uint8_t* plane, int rows, int K,
                                                   int64_t unit) {
-  if constexpr (FMT != kQ5_K) return plane;
-  return plane + hi_region(rows, K) + unit * 4;
+  if constexpr (hi_bytes_per_block(FMT) == 0) return plane;
+  return plane + hi_region(rows, K) + unit * hi_bytes_per_block(FMT);
 }
 
 // Where a lane's super-block records start (Q4_K; other formats: unused). plane: the
@@ -123,8 +125,21 @@ __device__ __forceinline__ void widen(const Chunk& c, bf16x2* w) {
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         // bytes 0/1 are the E4M3 codes of 0 and 2^-9; scale 2^13 gives 0 or 16, exactly
-        const uint32_t lo = (c.h >> (2 * d)) & 0x01010101u;
-        const uint32_t hi = (c.h >> (2 * d + 1)) & 0x01010101u;
+        const uint32_t lo = (c.h[0] >> (2 * d)) & 0x01010101u;
+        const uint32_t hi = (c.h[0] >> (2 * d + 1)) & 0x01010101u;
+        w[16 + 4 * d + 0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 8192.0f, false);
+        w[16 + 4 * d + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 8192.0f, true);
+        w[16 + 4 * d + 2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 8192.0f, false);
+        w[16 + 4 * d + 3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 8192.0f, true);
+      }
+    } else if constexpr (FMT == kQ6_K) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        // bytes 0..3 are the E4M3 codes of 0 .. 3 * 2^-9; scale 2^13 gives 16 x the high part
+        const uint32_t g = c.h[d >> 1];
+        const int sh = 4 * (d & 1);
+        const uint32_t lo = (g >> sh) & 0x03030303u;
+        const uint32_t hi = (g >> (sh + 2)) & 0x03030303u;
         w[16 + 4 * d + 0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 8192.0f, false);
         w[16 + 4 * d + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 8192.0f, true);
         w[16 + 4 * d + 2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 8192.0f, false);
@@ -151,19 +166,36 @@ __device__ __forceinline__ void widen(const Chunk& c, bf16x2* w) {
   }
 }
 
-// A k-quant block: with P = sum x q and S = sum x over the block, sum x w = a P - c S where
-// a = d sc and c = dmin m (both exact in fp32). P runs over the chunk's pairs (Q5_K: the low
-// nibbles' pairs, then the high bits').
+// A k-quant block. Q4_K / Q5_K: with P = sum x q and S = sum x over the block,
+// sum x w = a P - c S where a = d sc and c = dmin m (both exact in fp32); P runs over the
+// chunk's pairs (Q5_K: the low nibbles' pairs, then the high bits'). Q6_K: per 16-element
+// half h, a_h (P_h - 32 S_h) with a_h = d sc_h (exact). sx: S (Q6_K: S_0, S_1).
 template <int FMT>
 __device__ __forceinline__ float kq_block(const bf16x2* w, const uint32_t* xv, uint32_t s,
-                                          uint32_t s2, float sx, float acc) {
-  constexpr int kPairs = FMT == kQ5_K ? 32 : 16;
-  float p = 0.f;
+                                          uint32_t s2, const float* sx, float acc) {
+  if constexpr (FMT == kQ6_K) {
+    const float d = fp16_to_f32((uint16_t)s2);
 #pragma unroll
-  for (int i = 0; i < kPairs; ++i) p = dot2_bf16(w[i], xv[i & 15], p);
-  const float a = fp16_to_f32((uint16_t)s2) * (float)(s & 0xFFu);
-  const float c = fp16_to_f32((uint16_t)(s2 >> 16)) * (float)((s >> 8) & 0xFFu);
-  return fmaf(-c, sx, fmaf(a, p, acc));
+    for (int h = 0; h < 2; ++h) {
+      float p = 0.f;
+#pragma unroll
+      for (int i = 8 * h; i < 8 * h + 8; ++i) {
+        p = dot2_bf16(w[i], xv[i], p);
+        p = dot2_bf16(w[16 + i], xv[i], p);
+      }
+      const float a = d * (float)(int8_t)(s >> (8 * h));
+      acc = fmaf(a, fmaf(-32.f, sx[h], p), acc);
+    }
+    return acc;
+  } else {
+    constexpr int kPairs = FMT == kQ5_K ? 32 : 16;
+    float p = 0.f;
+#pragma unroll
+    for (int i = 0; i < kPairs; ++i) p = dot2_bf16(w[i], xv[i & 15], p);
+    const float a = fp16_to_f32((uint16_t)s2) * (float)(s & 0xFFu);
+    const float c = fp16_to_f32((uint16_t)(s2 >> 16)) * (float)((s >> 8) & 0xFFu);
+    return fmaf(-c, sx[0], fmaf(a, p, acc));
+  }
 }
 
 // s: the block's scale record (0 for a masked chunk: it then adds nothing); s2: a
@@ -172,9 +204,12 @@ template <int FMT>
 __device__ __forceinline__ float dot_chunk(const bf16x2* w, const uint32_t* xv, uint32_t s,
                                            uint32_t s2, float acc) {
   if constexpr (kquant(FMT)) {
-    float sx = 0.f;
+    // block sums (Q6_K: of each half), in the order block_sums() takes them
+    float sx[2] = {0.f, 0.f};
+    constexpr int kWordsPerSum = 16 / sums_per_block(FMT);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sx = dot2_bf16(0x3F803F80u, xv[i], sx);   // bf16 pair (1, 1)
+    for (int i = 0; i < 16; ++i)
+      sx[i / kWordsPerSum] = dot2_bf16(0x3F803F80u, xv[i], sx[i / kWordsPerSum]);   // (1, 1)
     return kq_block<FMT>(w, xv, s, s2, sx, acc);
   } else if constexpr (FMT == kMXFP4) {
 #pragma unroll
@@ -188,11 +223,11 @@ __device__ __forceinline__ float dot_chunk(const bf16x2* w, const uint32_t* xv, 
   }
 }
 
-// dot_chunk with the block sum S = sum x given (k-quants; other formats ignore it). S taken
-// as block_sum() computes it gives the same result as dot_chunk bit for bit.
+// dot_chunk with the block sums given (k-quants; other formats ignore them). Sums taken as
+// block_sums() computes them give the same result as dot_chunk bit for bit.
 template <int FMT>
 __device__ __forceinline__ float dot_chunk_s(const bf16x2* w, const uint32_t* xv, uint32_t s,
-                                             uint32_t s2, float sx, float acc) {
+                                             uint32_t s2, const float* sx, float acc) {
   if constexpr (kquant(FMT)) {
     return kq_block<FMT>(w, xv, s, s2, sx, acc);
   } else {
@@ -200,16 +235,21 @@ __device__ __forceinline__ float dot_chunk_s(const bf16x2* w, const uint32_t* xv
   }
 }
 
-// Sum of the 32 bf16 values at p (LDS), in the order dot_chunk sums them for k-quants.
-__device__ __forceinline__ float block_sum(const uint16_t* p) {
-  float sx = 0.f;
+// Sums of the 32 bf16 values of a block at p (LDS) -- one sum, or one per 16-element half
+// (Q6_K) -- into out, in the order dot_chunk takes them for the k-quants.
+template <int FMT>
+__device__ __forceinline__ void block_sums(const uint16_t* p, float* out) {
+  constexpr int kWordsPerSum = 16 / sums_per_block(FMT);
+  float sx[2] = {0.f, 0.f};
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const u32x4 v = *(const u32x4*)(p + q * 8);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sx = dot2_bf16(0x3F803F80u, v[i], sx);
+    for (int i = 0; i < 4; ++i)
+      sx[(4 * q + i) / kWordsPerSum] = dot2_bf16(0x3F803F80u, v[i], sx[(4 * q + i) / kWordsPerSum]);
   }
-  return sx;
+#pragma unroll
+  for (int h = 0; h < sums_per_block(FMT); ++h) out[h] = sx[h];
 }
 
 // Geometry of a lane within a 1 KiB chunk of the tiled layout.
@@ -223,7 +263,8 @@ struct LaneMap {
   static constexpr int kKPerChunk = 32 * kBlocksPerChunk;     // K elements per chunk
   static constexpr int kXWords = k16 ? 16 : 8;                // u32 of x per lane per chunk
   static constexpr int kScaleChunk = 64 * (kquant(FMT) ? 2 : 1);   // scale bytes per chunk
-  static constexpr int kWPairs = FMT == kQ5_K ? 32 : 16;            // widened pairs per chunk
+  static constexpr int kWPairs = hi_bytes_per_block(FMT) ? 32 : 16;   // widened pairs per chunk
+  static constexpr int kHiChunk = 64 * (int)hi_bytes_per_block(FMT);  // high-bit bytes per chunk
   __device__ static int row(int lane) { return k16 ? (lane & 15) : ((lane >> 1) & 15); }
   __device__ static int blk(int lane) { return k16 ? (lane >> 4) : (lane >> 5); }
   // K offset of the lane's codes inside its chunk
@@ -344,10 +385,10 @@ __global__ __launch_bounds__(kGThreads) void k_gemv(
           const bool ok = c < nc && b < nb;
           const int cs = ok ? c : 0;      // chunk 0 of the row group always exists
           load_chunk<FMT>(ca[u], qa + (int64_t)cs * 1024, sa + (int64_t)cs * LM::kScaleChunk,
-                          sa2 + (int64_t)(cs >> 1) * 64, ha + (int64_t)cs * 256, ok);
+                          sa2 + (int64_t)(cs >> 1) * 64, ha + (int64_t)cs * LM::kHiChunk, ok);
           if constexpr (GATED)
             load_chunk<FMT>(cbk[u], qb + (int64_t)cs * 1024, sbp + (int64_t)cs * LM::kScaleChunk,
-                            sbp2 + (int64_t)(cs >> 1) * 64, hb + (int64_t)cs * 256, ok);
+                            sbp2 + (int64_t)(cs >> 1) * 64, hb + (int64_t)cs * LM::kHiChunk, ok);
         }
         __builtin_amdgcn_sched_barrier(0);   // keep the whole batch of loads ahead of its use
         __syncthreads();
@@ -471,7 +512,7 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
   __shared__ int ip_l[kDCMaxPairs];
   __shared__ int tmp[kDCWaves];
   // Q4_K: the block sums of the staged h rows
-  __shared__ float hsum_l[kquant(FMT) ? kDCMaxH / 32 : 1];
+  __shared__ float hsum_l[kquant(FMT) ? kDCMaxH / 32 * sums_per_block(FMT) : 1];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int rg = blockIdx.x;
@@ -537,7 +578,7 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
       const bool ok = c < nc && b < nb;
       const int cs = ok ? c : 0;
       load_chunk<FMT>(ch[u], qa + (int64_t)cs * 1024, sa + (int64_t)cs * LM::kScaleChunk,
-                      sa2 + (int64_t)(cs >> 1) * 64, ha + (int64_t)cs * 256, ok);
+                      sa2 + (int64_t)(cs >> 1) * 64, ha + (int64_t)cs * LM::kHiChunk, ok);
     }
   };
   if (act != nullptr && busy && valid) load_batch(q);
@@ -571,7 +612,8 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
   }
   __syncthreads();
   if constexpr (kquant(FMT)) {
-    for (int i = threadIdx.x; i < np * I / 32; i += NTH) hsum_l[i] = block_sum(&hs[i * 32]);
+    for (int i = threadIdx.x; i < np * I / 32; i += NTH)
+      block_sums<FMT>(&hs[i * 32], &hsum_l[i * sums_per_block(FMT)]);
     __syncthreads();
   }
   if (act == nullptr) {
@@ -616,7 +658,7 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
               xv[4 * qq + 2] = v[2];
               xv[4 * qq + 3] = v[3];
             }
-            const float sx = kquant(FMT) ? hsum_l[(lo + p) * (I / 32) + kx / 32] : 0.f;
+            const float* sx = &hsum_l[kquant(FMT) ? ((lo + p) * (I / 32) + kx / 32) * sums_per_block(FMT) : 0];
             acc[p] = dot_chunk_s<FMT>(w, xv, ch[u].ok ? ch[u].s : 0u, ch[u].s2, sx, acc[p]);
           }
         }
@@ -714,7 +756,7 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
   __shared__ int rank_l[kWave];
   __shared__ float red[kGWaves][NT][2][16];
   // Q4_K: the block sums of the tokens' activation rows, shared by every row of every unit
-  __shared__ float xsum_l[kquant(FMT) ? NT * kRouteMaxH / 32 : 1];
+  __shared__ float xsum_l[kquant(FMT) ? NT * kRouteMaxH / 32 * sums_per_block(FMT) : 1];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -746,7 +788,8 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
   __syncthreads();
   if constexpr (kquant(FMT)) {   // read after the routing's barriers
     const int nbx = H / 32;
-    for (int i = tid; i < T * nbx; i += kGThreads) xsum_l[i] = block_sum(&xs[i * 32]);
+    for (int i = tid; i < T * nbx; i += kGThreads)
+      block_sums<FMT>(&xs[i * 32], &xsum_l[i * sums_per_block(FMT)]);
   }
 
   // steps 2 and 3 for any T (used unless the one-token path below applies)
@@ -930,7 +973,7 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
     for (int i = 0; i < NT; ++i) {
       const int t = act_l[j][4 + (i < 4 ? i : 3)];
       xrow[i] = &xs[(t >= 0 ? t : 0) * H];
-      xsum[i] = &xsum_l[kquant(FMT) ? (t >= 0 ? t : 0) * (H / 32) : 0];
+      xsum[i] = &xsum_l[kquant(FMT) ? (t >= 0 ? t : 0) * (H / 32) * sums_per_block(FMT) : 0];
     }
     float acc[2][NT];
 #pragma unroll
@@ -940,7 +983,7 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
     // chunks per wave per batch: fewer with more tokens and with the k-quants' larger
     // chunk records, so that the batch stays in registers
     constexpr int kRU = FMT == kQ4_K ? (NT >= 4 ? 3 : NT >= 2 ? 4 : 6)
-                      : FMT == kQ5_K ? (NT >= 4 ? 2 : NT >= 2 ? 3 : 4)
+                      : FMT == kQ5_K || FMT == kQ6_K ? (NT >= 4 ? 2 : NT >= 2 ? 3 : 4)
                       : NT >= 4 ? 6 : kU;
     for (int cbase = 0; cbase < nc; cbase += kGWaves * kRU) {
       Chunk ca[kRU], cbk[kRU];
@@ -951,9 +994,9 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
         const bool ok = c < nc && b < nb;
         const int cs = ok ? c : 0;
         load_chunk<FMT>(ca[u], qa + (int64_t)cs * 1024, sa + (int64_t)cs * LM::kScaleChunk,
-                        sa2 + (int64_t)(cs >> 1) * 64, ha + (int64_t)cs * 256, ok);
+                        sa2 + (int64_t)(cs >> 1) * 64, ha + (int64_t)cs * LM::kHiChunk, ok);
         load_chunk<FMT>(cbk[u], qb + (int64_t)cs * 1024, sbp + (int64_t)cs * LM::kScaleChunk,
-                        sbp2 + (int64_t)(cs >> 1) * 64, hb + (int64_t)cs * 256, ok);
+                        sbp2 + (int64_t)(cs >> 1) * 64, hb + (int64_t)cs * LM::kHiChunk, ok);
       }
       __builtin_amdgcn_sched_barrier(0);   // the whole batch in flight before any is used
 #pragma unroll
@@ -976,7 +1019,7 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
               xw[4 * q + 2] = xq[2];
               xw[4 * q + 3] = xq[3];
             }
-            const float sx = kquant(FMT) ? xsum[i][xo / 32] : 0.f;
+            const float* sx = xsum[i] + (kquant(FMT) ? xo / 32 * sums_per_block(FMT) : 0);
             acc[m][i] = dot_chunk_s<FMT>(w, xw, ch.ok ? ch.s : 0u, ch.s2, sx, acc[m][i]);
           }
         }
@@ -1060,6 +1103,7 @@ hipError_t with_fmt(int fmt, F&& f) {
     case kQ8_0: return f(std::integral_constant<int, kQ8_0>{});
     case kQ4_K: return f(std::integral_constant<int, kQ4_K>{});
     case kQ5_K: return f(std::integral_constant<int, kQ5_K>{});
+    case kQ6_K: return f(std::integral_constant<int, kQ6_K>{});
     default: return hipErrorInvalidValue;
   }
 }

@@ -80,7 +80,8 @@ struct BStage {
   // Q4_K: the 16 rows' (d, dmin) records of the step's super-block, per row group
   static constexpr int kRunS2 = kquant(FMT) ? kRowGroup * (int)kSuperBytes : 4;
   // Q5_K: the high-bit dwords of the run's 64 units
-  static constexpr int kRunH = FMT == kQ5_K ? 64 * 4 : 4;
+  static constexpr int kRunH = hi_bytes_per_block(FMT) ? 64 * (int)hi_bytes_per_block(FMT) : 4;
+  static constexpr int kHDwords = 8 * kRunH / 4 / kTThreads;   // high-part dwords per thread
 };
 
 template <int FMT, bool GATED>
@@ -207,21 +208,29 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
     bs2p = (GATED && g >= 4 ? s1 : s0) + super_region(N, K) +
            ((int64_t)rgc * nsb * kRowGroup + (threadIdx.x & 15)) * kSuperBytes;
   }
-  // Q5_K high-bit dwords: thread t copies dwords t and t + 256 of the 8 runs (64 per run)
-  const uint8_t* bhp[2] = {nullptr, nullptr};
-  if constexpr (FMT == kQ5_K) {
+  // Q5_K / Q6_K high-part dwords: thread t copies dwords t + 256 h of the 8 runs
+  // (kRunH / 4 per run)
+  constexpr int kHD = BS::kHDwords > 0 ? BS::kHDwords : 1;
+  const uint8_t* bhp[kHD];
+  uint32_t hreg[kHD];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < kHD; ++h) {
+    bhp[h] = nullptr;
+    hreg[h] = 0u;
+  }
+  if constexpr (hi_bytes_per_block(FMT) > 0) {
+#pragma unroll
+    for (int h = 0; h < kHD; ++h) {
       const int dw = threadIdx.x + kTThreads * h;
-      const int g = dw / 64;
+      const int g = dw / (BS::kRunH / 4);
       const int rg = GATED ? n0 / 16 + (g & 3) : n0 / 16 + g;
       const int rgc = rg * 16 < N ? rg : 0;
       bhp[h] = (GATED && g >= 4 ? q1 : q0) + hi_region(N, K) +
-               ((int64_t)rgc * nb * 16 + dw % 64) * 4;
+               (int64_t)rgc * nb * 16 * hi_bytes_per_block(FMT) + (dw % (BS::kRunH / 4)) * 4;
     }
   }
   u32x4 breg[BS::kQPieces];
-  uint32_t sreg = 0, s2reg = 0, hreg[2] = {0u, 0u};
+  uint32_t sreg = 0, s2reg = 0;
   auto load_b = [&](int c) {
     // a step's run starts 4 blocks (64 units) after the previous one's; pieces of blocks
     // past the end of the row re-read step 0 (masked when consumed)
@@ -238,9 +247,9 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
       // step c's blocks 4c .. 4c+3 lie in super-block c / 2 (K is a multiple of 256)
       if (s2_thread) s2reg = *(const uint32_t*)(bs2p + (int64_t)(c >> 1) * BS::kRunS2);
     }
-    if constexpr (FMT == kQ5_K) {
+    if constexpr (hi_bytes_per_block(FMT) > 0) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) hreg[h] = *(const uint32_t*)(bhp[h] + (int64_t)c * BS::kRunH);
+      for (int h = 0; h < kHD; ++h) hreg[h] = *(const uint32_t*)(bhp[h] + (int64_t)c * BS::kRunH);
     }
   };
 
@@ -281,9 +290,9 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
     if (s_thread) *(uint32_t*)(lds_bs + threadIdx.x * 4) = sreg;
     if constexpr (kquant(FMT))
       if (s2_thread) *(uint32_t*)(lds_bs2 + threadIdx.x * 4) = s2reg;
-    if constexpr (FMT == kQ5_K) {
+    if constexpr (hi_bytes_per_block(FMT) > 0) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) *(uint32_t*)(lds_bh + (threadIdx.x + kTThreads * h) * 4) = hreg[h];
+      for (int h = 0; h < kHD; ++h) *(uint32_t*)(lds_bh + (threadIdx.x + kTThreads * h) * 4) = hreg[h];
     }
     __syncthreads();
     if (c + 1 < nsteps) {
@@ -315,6 +324,63 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
 #pragma unroll
           for (int f = 0; f < 4; ++f)
             acc[mf][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[f], acc[mf][f], 0, 0, 0);
+        }
+      }
+    } else if constexpr (FMT == kQ6_K) {
+      // per block: lanes g = 0, 1 supply K 0..15 (half 0), g = 2, 3 K 16..31 (half 1). A
+      // with the other half's lanes zeroed gives each half its own MFMAs: codes as low
+      // nibbles plus 16 x the high part (two MFMAs into one sum), and the half's row sums
+      // against ones; the half adds d sc_h (P_h - 32 S_h).
+      const bf16x8 ones = __builtin_bit_cast(
+          bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+      const bf16x8 zero = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+#pragma unroll 1
+      for (int j = 0; j < 4; ++j) {
+        bf16x8 bv[4], bvh[4];
+        float a0[4], a1[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          const int unit = 16 * j + mrow;
+          const uint32_t q = *(const uint32_t*)(lds_bq + fg[f] * BS::kRunQ + unit * 16 + 4 * g4);
+          bv[f] = u4x8_split_to_bf16x8(q);
+          // high parts of the same 8 elements: dword g4 / 2 of the unit, planes at bit
+          // 4 (g4 % 2) and 4 (g4 % 2) + 2; bytes 0..3 -> E4M3 0..3 * 2^-9, x 2^13
+          const uint32_t hw = *(const uint32_t*)(lds_bh + fg[f] * BS::kRunH + unit * 8 + 4 * (g4 >> 1));
+          const int sh = 4 * (g4 & 1);
+          const uint32_t lo = (hw >> sh) & 0x03030303u, hi = (hw >> (sh + 2)) & 0x03030303u;
+          const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 8192.0f, false);
+          const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 8192.0f, true);
+          const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 8192.0f, false);
+          const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 8192.0f, true);
+          bvh[f] = bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+          const uint32_t keep = (fcol[f] && 4 * c + j < nb) ? 0xffffu : 0u;
+          const uint32_t rec = *(const uint16_t*)(lds_bs + fg[f] * BS::kRunS + unit * 2) & keep;
+          const float d = fp16_to_f32(*(const uint16_t*)(lds_bs2 + fg[f] * BS::kRunS2 + mrow * 4));
+          a0[f] = d * (float)(int8_t)(rec & 0xFFu);
+          a1[f] = d * (float)(int8_t)(rec >> 8);
+        }
+#pragma unroll
+        for (int mf = 0; mf < 4; ++mf) {
+          const int row = 64 * wm + 16 * mf + mrow;
+          const bf16x8 av =
+              __builtin_bit_cast(bf16x8, *(const u32x4*)(lds_a + row * kLdsStride + (32 * j + 8 * g4) * 2));
+          const bf16x8 av0 = g4 < 2 ? av : zero, av1 = g4 < 2 ? zero : av;
+          const f32x4 z4 = f32x4{0.f, 0.f, 0.f, 0.f};
+          const f32x4 s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av0, ones, z4, 0, 0, 0);
+          const f32x4 s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av1, ones, z4, 0, 0, 0);
+#pragma unroll
+          for (int f = 0; f < 4; ++f) {
+            f32x4 t0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av0, bv[f], z4, 0, 0, 0);
+            t0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av0, bvh[f], t0, 0, 0, 0);
+            f32x4 t1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av1, bv[f], z4, 0, 0, 0);
+            t1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av1, bvh[f], t1, 0, 0, 0);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              acc[mf][f][v] = fmaf(a0[f], fmaf(-32.f, s0[v], t0[v]), acc[mf][f][v]);
+              acc[mf][f][v] = fmaf(a1[f], fmaf(-32.f, s1[v], t1[v]), acc[mf][f][v]);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     } else if constexpr (kquant(FMT)) {
@@ -472,6 +538,9 @@ hipError_t launch_gate_up_grouped(int fmt, const PoolView& gate, const PoolView&
     case kQ5_K:
       return launch_ggemm_t<kQ5_K, true>(gate, up, slot_map, n_slots, E, offsets, perm, T, k, x,
                                          H, I, h, nullptr, err, stream);
+    case kQ6_K:
+      return launch_ggemm_t<kQ6_K, true>(gate, up, slot_map, n_slots, E, offsets, perm, T, k, x,
+                                         H, I, h, nullptr, err, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -492,6 +561,9 @@ hipError_t launch_down_grouped(int fmt, const PoolView& down, const int32_t* slo
                                           k, h, I, H, nullptr, y, err, stream);
     case kQ5_K:
       return launch_ggemm_t<kQ5_K, false>(down, down, slot_map, n_slots, E, offsets, nullptr, T,
+                                          k, h, I, H, nullptr, y, err, stream);
+    case kQ6_K:
+      return launch_ggemm_t<kQ6_K, false>(down, down, slot_map, n_slots, E, offsets, nullptr, T,
                                           k, h, I, H, nullptr, y, err, stream);
     default: return hipErrorInvalidValue;
   }

@@ -59,21 +59,42 @@ __global__ __launch_bounds__(256) void k_pack(int64_t n_units, int rows, int nb,
           g |= ((h32 >> (8 * (sh >> 1) + j + 4 * (sh & 1))) & 1u) << (8 * j + sh);
       *(uint32_t*)(dqmat + hi_region(rows, K) + um * 4) = g;
     }
-    // canonical scale row: (sc, m) per block, then (d, dmin) fp16 per super-block
+    if constexpr (FMT == kQ6_K) {
+      // canonical 2-bit high parts of the block (bits 2e, 2e+1 = element e) -> the pool's
+      // two dwords: dword g, bits 8j + s + t (s even) = bit t of element
+      // 8 (2g + s / 4) + j + 4 ((s / 2) % 2)
+      const uint8_t* hb = scrow + 16 * (int64_t)nb + 8 * (int64_t)b;
+      uint64_t h64 = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) h64 |= (uint64_t)hb[j] << (8 * j);
+      uint32_t g2[2] = {0u, 0u};
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int sh = 0; sh < 8; sh += 2) {
+            const int e = 8 * (2 * g + sh / 4) + j + 4 * ((sh / 2) % 2);
+            g2[g] |= (uint32_t)((h64 >> (2 * e)) & 3u) << (8 * j + sh);
+          }
+      *(u32x2*)(dqmat + hi_region(rows, K) + um * 8) = u32x2{g2[0], g2[1]};
+    }
+    // canonical scale row: Q4_K / Q5_K (sc, m) per block, then (d, dmin) fp16 per
+    // super-block; Q6_K the two int8 sub-block scales per block, then fp16 d per super-block
     const int nsb = nb / kSuperBlocks;
-    const int64_t row_bytes = 2 * (int64_t)nb + kSuperBytes * nsb;
-    const int64_t mat_bytes = (int64_t)rows * row_bytes;   // = the tiled plane's size
-    const uint8_t* srow = ss + mat * mat_bytes + r * row_bytes;
-    uint8_t* dmat = ds + mat * mat_bytes;
-    dmat[u % per_mat * 2 + 0] = srow[2 * b + 0];
-    dmat[u % per_mat * 2 + 1] = srow[2 * b + 1];
+    const int64_t srow_sup = FMT == kQ6_K ? 2 : kSuperBytes;     // canonical bytes per super-block
+    const int64_t row_bytes = 2 * (int64_t)nb + srow_sup * nsb;
+    const uint8_t* srow = ss + (mat * rows + r) * row_bytes;
+    uint8_t* dmat = ds + mat * scale_plane_bytes(FMT, rows, K);
+    dmat[um * 2 + 0] = srow[2 * b + 0];
+    dmat[um * 2 + 1] = srow[2 * b + 1];
     if (b % kSuperBlocks == 0) {
       const int sblk = b / kSuperBlocks;
       const int64_t rec = ((int64_t)(r >> 4) * nsb + sblk) * kRowGroup + (r & 15);
-      uint8_t* dst = dmat + super_region(rows, 32 * (int64_t)nb) + rec * kSuperBytes;
-      const uint8_t* src = srow + 2 * nb + kSuperBytes * sblk;
+      uint8_t* dst = dmat + super_region(rows, K) + rec * kSuperBytes;
+      const uint8_t* src = srow + 2 * nb + srow_sup * sblk;
 #pragma unroll
-      for (int j = 0; j < kSuperBytes; ++j) dst[j] = src[j];
+      for (int j = 0; j < kSuperBytes; ++j) dst[j] = j < srow_sup ? src[j] : 0;
     }
   } else {
     *(u32x4*)(dq + u * 32) = *(const u32x4*)(sq + i * 32);
@@ -94,10 +115,13 @@ hipError_t launch_pack(int fmt, int n_mats, int rows, int K, const void* sq, con
   if (fmt == kMXFP4)
     hipLaunchKernelGGL(k_pack<kMXFP4>, dim3((unsigned)blocks), dim3(256), 0, stream, n, rows, nb,
                        (const uint8_t*)sq, (const uint8_t*)ss, (uint8_t*)dq, (uint8_t*)ds);
-  else if (fmt == kQ4_K || fmt == kQ5_K) {
+  else if (fmt == kQ4_K || fmt == kQ5_K || fmt == kQ6_K) {
     if (nb % kSuperBlocks) return hipErrorInvalidValue;
     if (fmt == kQ4_K)
       hipLaunchKernelGGL(k_pack<kQ4_K>, dim3((unsigned)blocks), dim3(256), 0, stream, n, rows,
+                         nb, (const uint8_t*)sq, (const uint8_t*)ss, (uint8_t*)dq, (uint8_t*)ds);
+    else if (fmt == kQ6_K)
+      hipLaunchKernelGGL(k_pack<kQ6_K>, dim3((unsigned)blocks), dim3(256), 0, stream, n, rows,
                          nb, (const uint8_t*)sq, (const uint8_t*)ss, (uint8_t*)dq, (uint8_t*)ds);
     else
       hipLaunchKernelGGL(k_pack<kQ5_K>, dim3((unsigned)blocks), dim3(256), 0, stream, n, rows,

@@ -131,10 +131,19 @@ def check_h(h_gpu_bits, a_ref, slack):
 def _accumulated_magnitude(fmt, planes, name, s, W):
     """|term| per weight of the sums the kernels accumulate in fp32: |w| for MXFP4 and Q8_0;
     for Q4_K and Q5_K the kernels sum x q and x over a block, scaled by a = d sc and by
-    c = dmin m, so the magnitude is a q + |c|."""
-    if fmt not in ("q4_k", "q5_k"):
+    c = dmin m, so the magnitude is a q + |c|. Q6_K: per 16-element half, x q and x scaled
+    by a = d sc, the latter times 32: |a| (q + 32)."""
+    if fmt not in ("q4_k", "q5_k", "q6_k"):
         return np.abs(W)
     codes = planes[name + "_q"][s]
+    if fmt == "q6_k":
+        q = codecs.q6_k_codes(codes).astype(np.float64)
+        K = q.shape[1]
+        sp = np.asarray(planes[name + "_s"][s], dtype=np.uint8)
+        sc = sp[:, :K // 16].view(np.int8).astype(np.float64)
+        d = codecs.fp16_decode(np.ascontiguousarray(sp[:, K // 16:K // 16 + K // 128]).view(np.uint16))
+        a = np.abs(np.repeat(d, 16, axis=1) * sc)
+        return np.repeat(a, 16, axis=1) * (q + 32)
     if fmt == "q5_k":
         q = codecs.q5_k_codes(codes).astype(np.float64)
     else:

@@ -91,6 +91,9 @@ def test_plane_bytes(lib):
     # Q5_K: Q4_K's planes plus 4 bytes of high bits per block in the code plane
     assert lib.moe_plane_bytes(4, 768, 2048, 0) == 768 * 64 * (16 + 4)
     assert lib.moe_plane_bytes(4, 768, 2048, 1) == 768 * (64 * 2 + 8 * 4)
+    # Q6_K: 8 bytes of 2-bit high parts per block; d in a 4-byte record per super-block
+    assert lib.moe_plane_bytes(5, 768, 2048, 0) == 768 * 64 * (16 + 8)
+    assert lib.moe_plane_bytes(5, 768, 2048, 1) == 768 * (64 * 2 + 8 * 4)
 
 
 def test_route_argument_checks(lib):

@@ -72,7 +72,9 @@ SMALL = [("tiny", qm.PATH_AUTO), ("tiny", qm.PATH_GEMV), ("gptoss_decode_t1", qm
          ("tiny_q4k", qm.PATH_AUTO), ("tiny_q4k", qm.PATH_GEMV),
          ("qwen_a3b_q4k_decode", qm.PATH_AUTO), ("mixtral_q4k_decode", qm.PATH_AUTO),
          ("tiny_q5k", qm.PATH_AUTO), ("tiny_q5k", qm.PATH_GEMV),
-         ("qwen_a3b_q5k_decode", qm.PATH_AUTO), ("mixtral_q5k_decode", qm.PATH_AUTO)]
+         ("qwen_a3b_q5k_decode", qm.PATH_AUTO), ("mixtral_q5k_decode", qm.PATH_AUTO),
+         ("tiny_q6k", qm.PATH_AUTO), ("tiny_q6k", qm.PATH_GEMV),
+         ("qwen_a3b_q6k_decode", qm.PATH_AUTO), ("mixtral_q6k_decode", qm.PATH_AUTO)]
 
 
 @pytest.mark.parametrize("name,path", SMALL)
@@ -87,7 +89,8 @@ def test_layer_parity_decode_last_of_24_layers():
 
 
 @pytest.mark.parametrize("name", ["gptoss_prefill", "qwen_a3b_prefill", "mixtral_q8_prefill",
-                                  "qwen_a3b_q4k_prefill", "qwen_a3b_q5k_prefill"])
+                                  "qwen_a3b_q4k_prefill", "qwen_a3b_q5k_prefill",
+                                  "qwen_a3b_q6k_prefill"])
 def test_layer_parity_full_size_prefill(name):
     print(f"layer {name} (full size, sampled)", flush=True)
     run_layer(synth.CONFIGS[name], sample=True)

@@ -126,6 +126,11 @@ FFN_CASES = [
     ("tiny_q5k", 64, qm.PATH_GROUPED), ("tiny_q5k", 300, qm.PATH_GROUPED),
     ("qwen_a3b_q5k_decode", None, qm.PATH_GEMV), ("qwen_a3b_q5k_decode", 40, qm.PATH_GROUPED),
     ("mixtral_q5k_decode", None, qm.PATH_GEMV), ("mixtral_q5k_decode", 24, qm.PATH_GROUPED),
+    # Q6_K: the same paths
+    ("tiny_q6k", 1, qm.PATH_GEMV), ("tiny_q6k", 3, qm.PATH_GEMV), ("tiny_q6k", 16, qm.PATH_GEMV),
+    ("tiny_q6k", 64, qm.PATH_GROUPED), ("tiny_q6k", 300, qm.PATH_GROUPED),
+    ("qwen_a3b_q6k_decode", None, qm.PATH_GEMV), ("qwen_a3b_q6k_decode", 40, qm.PATH_GROUPED),
+    ("mixtral_q6k_decode", None, qm.PATH_GEMV), ("mixtral_q6k_decode", 24, qm.PATH_GROUPED),
 ]
 
 
