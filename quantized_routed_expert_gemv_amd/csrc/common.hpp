@@ -16,6 +16,7 @@ constexpr int kBlock = 32;      // elements per quantization block (MXFP4 and Q8
 constexpr int kRowGroup = 16;   // rows interleaved per tile in the pool layout
 constexpr int kMaxK = 8;        // largest supported top-k
 constexpr int kMaxE = 256;      // largest supported expert count
+constexpr int kMaxGridY = 65535;   // largest grid.y a launch takes
 
 enum Fmt : int { kMXFP4 = 1, kQ8_0 = 2, kQ4_K = 3, kQ5_K = 4, kQ6_K = 5 };
 

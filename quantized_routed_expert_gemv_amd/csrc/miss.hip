@@ -65,33 +65,35 @@ __global__ __launch_bounds__(kMissThreads) void k_miss_list(
 }
 
 // out[t, 4c..4c+3] += w[t,j] * y_miss[m_j, 4c..4c+3] for the missed pairs j of token t, in
-// increasing j. One thread per 4 columns of one token; grid (ceil(H/4/256), T).
+// increasing j. One thread per 4 columns of a token; grid (ceil(H/4/256), min(T, 65535)),
+// tokens t = blockIdx.y, + gridDim.y, ...
 __global__ __launch_bounds__(256) void k_merge_misses(float* __restrict__ out,
                                                       const float* __restrict__ y_miss,
                                                       const int32_t* __restrict__ miss_of_pair,
-                                                      const float* __restrict__ topk_w, int k,
-                                                      int H) {
-  const int t = blockIdx.y;
+                                                      const float* __restrict__ topk_w, int T,
+                                                      int k, int H) {
   const int c4 = blockIdx.x * blockDim.x + threadIdx.x;
   if (c4 * 4 >= H) return;
-  int m[kMaxK];
-  float w[kMaxK];
+  for (int t = blockIdx.y; t < T; t += gridDim.y) {
+    int m[kMaxK];
+    float w[kMaxK];
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {   // every load first (clamped to a valid pair)
-    const int p = t * k + min(j, k - 1);
-    m[j] = miss_of_pair[p];
-    w[j] = topk_w[p];
-  }
-  f32x4 acc = *(const f32x4*)(out + (int64_t)t * H + c4 * 4);
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    if (j < k && m[j] >= 0) {
-      const f32x4 v = *(const f32x4*)(y_miss + (int64_t)m[j] * H + c4 * 4);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] = fmaf(w[j], v[q], acc[q]);
+    for (int j = 0; j < kMaxK; ++j) {   // every load first (clamped to a valid pair)
+      const int64_t p = (int64_t)t * k + min(j, k - 1);
+      m[j] = miss_of_pair[p];
+      w[j] = topk_w[p];
     }
+    f32x4 acc = *(const f32x4*)(out + (int64_t)t * H + c4 * 4);
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j < k && m[j] >= 0) {
+        const f32x4 v = *(const f32x4*)(y_miss + (int64_t)m[j] * H + c4 * 4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] = fmaf(w[j], v[q], acc[q]);
+      }
+    }
+    *(f32x4*)(out + (int64_t)t * H + c4 * 4) = acc;
   }
-  *(f32x4*)(out + (int64_t)t * H + c4 * 4) = acc;
 }
 
 }  // namespace
@@ -109,9 +111,9 @@ hipError_t launch_merge_misses(float* out, const float* y_miss, const int32_t* m
                                const float* topk_w, int T, int k, int H, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
   if (k < 1 || k > kMaxK || H % 4) return hipErrorInvalidValue;
-  dim3 grid((H / 4 + 255) / 256, T);
+  dim3 grid((H / 4 + 255) / 256, min(T, kMaxGridY));
   hipLaunchKernelGGL(k_merge_misses, grid, dim3(256), 0, stream, out, y_miss, miss_of_pair,
-                     topk_w, k, H);
+                     topk_w, T, k, H);
   return hipGetLastError();
 }
 

@@ -69,6 +69,25 @@ def _close(got, ref, rel):
     return bool(np.all(np.abs(got - ref) <= rel * (np.abs(ref) + np.abs(ref).max())))
 
 
+@pytest.mark.parametrize("T,k,H", [(5, 4, 256), (70000, 2, 32)])   # the latter > grid.y limit
+def test_merge_misses_matches_oracle(T, k, H):
+    print(f"merge T={T} k={k} H={H}", flush=True)
+    rng = np.random.default_rng(T)
+    out0 = rng.standard_normal((T, H)).astype(np.float32)
+    w = rng.random((T, k)).astype(np.float32)
+    missed = rng.random(T * k) < 0.4
+    mop = np.full(T * k, -1, dtype=np.int32)
+    mop[missed] = rng.permutation(int(missed.sum())).astype(np.int32)
+    y_miss = rng.standard_normal((int(missed.sum()), H)).astype(np.float32)
+    out = torch.from_numpy(out0.copy()).cuda()
+    qm.merge_misses(out, torch.from_numpy(y_miss).cuda(), torch.from_numpy(mop).cuda(),
+                    torch.from_numpy(w).cuda())
+    torch.cuda.synchronize()
+    ref = omoe.merge_misses(out0.astype(np.float64), y_miss.astype(np.float64), mop,
+                            w.astype(np.float64), T, k)
+    assert _close(out.cpu().numpy(), ref, 1e-6)
+
+
 def _layer(pool, sm, wr, bias, x, k, path):
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     out, ws = qm.layer(pool, sm, wr, bias, x, k, err_flags=err, path=path)

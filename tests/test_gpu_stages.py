@@ -198,7 +198,8 @@ def test_expert_ffn_invalid_slot_sets_flag_and_zeroes():
 
 # ----------------------------------------------------------------------------- combine
 
-@pytest.mark.parametrize("T,k,H", [(1, 4, 2880), (64, 2, 256), (1000, 8, 2048), (3, 1, 32)])
+@pytest.mark.parametrize("T,k,H", [(1, 4, 2880), (64, 2, 256), (1000, 8, 2048), (3, 1, 32),
+                                   (70000, 2, 32)])   # more tokens than a launch's grid.y
 def test_combine_parity(T, k, H):
     rng = np.random.default_rng(T)
     y = rng.standard_normal((T * k, H)).astype(np.float32)
