@@ -122,7 +122,10 @@ typedef struct {
   const void* down_q; const void* down_s;
 } moe_pool;
 
-/* Bytes of one matrix's code plane / scale plane for one slot. */
+/* Bytes of one matrix's code plane (scales = 0) or scale plane (scales != 0) for one slot
+ * of the tiled pool; 0 for an unknown format, or for a k-quant with K not a multiple of 256.
+ * (The canonical planes moe_pool_pack reads are the same size, except Q6_K's canonical
+ * scale plane: K/16 + K/128 bytes per row against the pool's K/16 + K/64.) */
 size_t moe_plane_bytes(int32_t fmt, int32_t rows, int32_t K, int32_t scales);
 
 /*
