@@ -119,6 +119,11 @@ def test_layer_dense_and_full_mixture_special_cases():
     synth.Config("q8_t3", 3, 256, 512, 16, 3, "q8_0", None, "perm", 33, 1),
     # 2 tokens sharing experts (8 experts, 6 choices each)
     synth.Config("shared_t2", 2, 256, 256, 8, 6, "mxfp4", None, "perm", 34, 1),
+    # past the fused decode's activation limit (H > 4096): split router finished by its own
+    # kernel, then the GEMV path; 256 experts, top-8
+    synth.Config("h7168_e256_t1", 1, 7168, 512, 256, 8, "mxfp4", 1.2, "perm", 35, 1),
+    synth.Config("h6144_t4_q8", 4, 6144, 256, 16, 4, "q8_0", None, "perm", 36, 1),
+    synth.Config("h7168_t2_q6k", 2, 7168, 512, 64, 6, "q6_k", None, "perm", 37, 1),
 ])
 def test_layer_decode_routing_edge_cases(cfg):
     """Shapes at the edges of the decode path that finishes the routing in the gate/up
