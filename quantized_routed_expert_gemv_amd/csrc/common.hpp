@@ -79,7 +79,8 @@ __device__ __forceinline__ void i8x4_to_f32(uint32_t v, float* o) {
 
 // 2 fp32 holding bf16-exact values -> packed bf16x2 (truncation is exact here).
 __device__ __forceinline__ uint32_t pack_bf16x2_exact(float lo, float hi) {
-  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+  // one v_perm_b32: bytes 2, 3 of lo, then bytes 2, 3 of hi
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
 
 // 8 unsigned 4-bit codes in the pool's split order (byte j holds element j in its low

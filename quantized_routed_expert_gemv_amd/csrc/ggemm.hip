@@ -275,6 +275,15 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
 #pragma unroll
     for (int f = 0; f < 4; ++f) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Q8_0 products waiting to be scaled (zero scale: a no-op before the first block)
+  f32x4 q8_t[4];
+  float q8_d[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    q8_t[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+    q8_d[f] = 0.f;
+  }
+
   load_a(0);
   load_b(0);
   const int g4 = lane >> 4;
@@ -442,7 +451,9 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
       }
     } else {
       // one MFMA per 32-wide block; lane supplies K = 32 j + 8 g .. + 7 of block j, i.e.
-      // bytes 8 g .. of unit 16 j + lane%16 of its row group's run
+      // bytes 8 g .. of unit 16 j + lane%16 of its row group's run. The block's fp32
+      // products of one 16-row fragment are scaled into the accumulators while the next
+      // fragment's MFMAs run: (q8_t, q8_d) carry them one fragment, across blocks and steps.
 #pragma unroll 1
       for (int j = 0; j < 4; ++j) {
         bf16x8 bv[4];
@@ -466,14 +477,28 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
           for (int f = 0; f < 4; ++f)
             t[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[f], f32x4{0.f, 0.f, 0.f, 0.f}, 0,
                                                            0, 0);
+          // the previous fragment: mf - 1 of this block, or fragment 3 of the block before
+          constexpr int kPrev[4] = {3, 0, 1, 2};
 #pragma unroll
           for (int f = 0; f < 4; ++f)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[mf][f][v] = fmaf(ds[f], t[f][v], acc[mf][f][v]);
-          __builtin_amdgcn_sched_barrier(0);   // keep at most 4 products live
+            for (int v = 0; v < 4; ++v)
+              acc[kPrev[mf]][f][v] = fmaf(q8_d[f], q8_t[f][v], acc[kPrev[mf]][f][v]);
+#pragma unroll
+          for (int f = 0; f < 4; ++f) {
+            q8_t[f] = t[f];
+            q8_d[f] = ds[f];
+          }
+          __builtin_amdgcn_sched_barrier(0);   // keep at most 8 products live
         }
       }
     }
+  }
+  if constexpr (FMT == kQ8_0) {   // the last fragment's products
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[3][f][v] = fmaf(q8_d[f], q8_t[f][v], acc[3][f][v]);
   }
 
   // ---- epilogue: lane holds D[row 4*(lane/16) + v][col lane%16] of each 16x16 tile
