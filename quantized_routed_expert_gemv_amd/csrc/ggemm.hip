@@ -275,14 +275,29 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
 #pragma unroll
     for (int f = 0; f < 4; ++f) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Q8_0 products waiting to be scaled (zero scale: a no-op before the first block)
-  f32x4 q8_t[4];
-  float q8_d[4];
+  // Q8_0, Q4_K, Q5_K: the fp32 products of one 16-row fragment are scaled into the
+  // accumulators while the next fragment's MFMAs run; pend_* carry them one fragment,
+  // across blocks and steps (zero scales: a no-op before the first block)
+  constexpr bool kPend = FMT == kQ8_0 || FMT == kQ4_K || FMT == kQ5_K;
+  f32x4 pend_t[4], pend_s = f32x4{0.f, 0.f, 0.f, 0.f};
+  float pend_a[4], pend_c[4];
 #pragma unroll
   for (int f = 0; f < 4; ++f) {
-    q8_t[f] = f32x4{0.f, 0.f, 0.f, 0.f};
-    q8_d[f] = 0.f;
+    pend_t[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+    pend_a[f] = 0.f;
+    pend_c[f] = 0.f;
   }
+  // acc[mf] += the pending products (a P - c S for the k-quants, d P for Q8_0)
+  auto apply_pending = [&](f32x4* accf) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float r = fmaf(pend_a[f], pend_t[f][v], accf[f][v]);
+        accf[f][v] = FMT == kQ8_0 ? r : fmaf(-pend_c[f], pend_s[v], r);
+      }
+  };
+  constexpr int kPrev[4] = {3, 0, 1, 2};   // the fragment before mf (3: previous block)
 
   load_a(0);
   load_b(0);
@@ -396,7 +411,7 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
       // one MFMA per 32-wide block, as for Q8_0: lane supplies K = 32 j + 8 g .. + 7 of block
       // j, i.e. bytes 4 g .. 4 g + 3 of unit 16 j + lane%16, widened to bf16 q (exact). A
       // fifth MFMA against ones gives each row's block sum S, and the block adds a P - c S
-      // with a = d sc, c = dmin m of the lane's column.
+      // with a = d sc, c = dmin m of the lane's column (one fragment later, as for Q8_0).
       const bf16x8 ones = __builtin_bit_cast(
           bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 #pragma unroll 1
@@ -441,19 +456,21 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
             if constexpr (FMT == kQ5_K)
               t[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bvh[f], t[f], 0, 0, 0);
           }
+          apply_pending(acc[kPrev[mf]]);
 #pragma unroll
-          for (int f = 0; f < 4; ++f)
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              acc[mf][f][v] = fmaf(-sbias[f], sx[v], fmaf(sa[f], t[f][v], acc[mf][f][v]));
-          __builtin_amdgcn_sched_barrier(0);   // keep at most 5 products live
+          for (int f = 0; f < 4; ++f) {
+            pend_t[f] = t[f];
+            pend_a[f] = sa[f];
+            pend_c[f] = sbias[f];
+          }
+          pend_s = sx;
+          __builtin_amdgcn_sched_barrier(0);   // keep at most 10 products live
         }
       }
     } else {
       // one MFMA per 32-wide block; lane supplies K = 32 j + 8 g .. + 7 of block j, i.e.
-      // bytes 8 g .. of unit 16 j + lane%16 of its row group's run. The block's fp32
-      // products of one 16-row fragment are scaled into the accumulators while the next
-      // fragment's MFMAs run: (q8_t, q8_d) carry them one fragment, across blocks and steps.
+      // bytes 8 g .. of unit 16 j + lane%16 of its row group's run; the block scale d
+      // multiplies the fp32 products one fragment later.
 #pragma unroll 1
       for (int j = 0; j < 4; ++j) {
         bf16x8 bv[4];
@@ -477,29 +494,18 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
           for (int f = 0; f < 4; ++f)
             t[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[f], f32x4{0.f, 0.f, 0.f, 0.f}, 0,
                                                            0, 0);
-          // the previous fragment: mf - 1 of this block, or fragment 3 of the block before
-          constexpr int kPrev[4] = {3, 0, 1, 2};
-#pragma unroll
-          for (int f = 0; f < 4; ++f)
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              acc[kPrev[mf]][f][v] = fmaf(q8_d[f], q8_t[f][v], acc[kPrev[mf]][f][v]);
+          apply_pending(acc[kPrev[mf]]);
 #pragma unroll
           for (int f = 0; f < 4; ++f) {
-            q8_t[f] = t[f];
-            q8_d[f] = ds[f];
+            pend_t[f] = t[f];
+            pend_a[f] = ds[f];
           }
           __builtin_amdgcn_sched_barrier(0);   // keep at most 8 products live
         }
       }
     }
   }
-  if constexpr (FMT == kQ8_0) {   // the last fragment's products
-#pragma unroll
-    for (int f = 0; f < 4; ++f)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) acc[3][f][v] = fmaf(q8_d[f], q8_t[f][v], acc[3][f][v]);
-  }
+  if constexpr (kPend) apply_pending(acc[3]);   // the last fragment's products
 
   // ---- epilogue: lane holds D[row 4*(lane/16) + v][col lane%16] of each 16x16 tile
   const int g = g4;
