@@ -90,7 +90,7 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
     int64_t sslot, const uint8_t* __restrict__ bq, const uint8_t* __restrict__ bs,
     const int32_t* __restrict__ slot_map, int n_slots, int E,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm, int k,
-    const uint16_t* __restrict__ src, int K, int N, int n_ntiles,
+    const uint16_t* __restrict__ src, int K, int N, int n_mtiles, int n_ntiles,
     uint16_t* __restrict__ h_out, float* __restrict__ y_out, uint32_t* __restrict__ err_flags) {
   using BS = BStage<FMT>;
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[kBM * kLdsStride];
@@ -103,8 +103,21 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int wm = wave >> 1, wn = wave & 1;
-  const int mt = blockIdx.x / n_ntiles;
-  const int nt = blockIdx.x % n_ntiles;
+  // XCD-aware 2-D order: workgroups are dealt to the 8 XCDs in turn (XCD x runs
+  // workgroups x, x + 8, ...). Tile i of a list that walks super-tiles of 8 row tiles x 8
+  // column tiles (row-major inside each) goes to the XCD of the 64-tile run it lies in, so
+  // an XCD's L2 serves A rows to 8 column tiles and B slices to 8 row tiles.
+  const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+  const int64_t i = (int64_t)(local >> 6) * 512 + xcd * 64 + (local & 63);
+  if (i >= (int64_t)n_mtiles * n_ntiles) return;   // padding of the grid
+  const int sr = (int)(i / (8LL * n_ntiles));       // super-row: row tiles 8 sr ..
+  const int h = min(8, n_mtiles - 8 * sr);          // its row tiles
+  const int jj = (int)(i - 8LL * n_ntiles * sr);
+  const int gcol = jj / (8 * h);                    // column group: column tiles 8 gcol ..
+  const int w = min(8, n_ntiles - 8 * gcol);        // its column tiles
+  const int kk = jj - 8 * h * gcol;
+  const int mt = 8 * sr + kk / w;
+  const int nt = 8 * gcol + kk % w;
   int e, m0;
   if (!map_row_tile(offsets, E, mt, &e, &m0, tmp4, sh)) return;
   const int mend = offsets[e + 1];
@@ -541,11 +554,11 @@ hipError_t launch_ggemm_t(const PoolView& a, const PoolView& b, const int32_t* s
   const int pairs = T * k;
   const int max_mtiles = (pairs + kBM - 1) / kBM + min(E, pairs);
   const int n_ntiles = GATED ? (N + 63) / 64 : (N + 127) / 128;
-  const int64_t grid = (int64_t)max_mtiles * n_ntiles;
+  const int64_t grid = ((int64_t)max_mtiles * n_ntiles + 511) / 512 * 512;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL((k_ggemm<FMT, GATED>), dim3((unsigned)grid), dim3(kTThreads), 0, stream,
                      a.q, a.s, a.q_slot, a.s_slot, b.q, b.s, slot_map, n_slots, E, offsets, perm,
-                     k, src, K, N, n_ntiles, h, y, err);
+                     k, src, K, N, max_mtiles, n_ntiles, h, y, err);
   return hipGetLastError();
 }
 
