@@ -235,6 +235,34 @@ __device__ __forceinline__ float dot_chunk_s(const bf16x2* w, const uint32_t* xv
   }
 }
 
+// MXFP4 with 2 to 4 tokens: a chunk is 4 MFMAs (v_mfma_f32_16x16x32_bf16) instead of one
+// dot2 pass per token, which leaves the kernel bound by HBM rather than by VALU issue. MFMA
+// q takes from lane l (row l%16, block l/16 of the chunk) elements 8q .. 8q+7 of its block
+// as B, and from the same lane the same K of token l%16 as A (zero past the tokens): the
+// 32-wide K of MFMA q is a fixed choice of the chunk's 128, applied to both. The result,
+// D[token][row], sits in lanes l < 16, tokens 0..3 of row l.
+constexpr bool mma_path(int fmt, int nt) { return fmt == kMXFP4 && nt >= 2 && nt <= 4; }
+
+// A fragments of a chunk: token row xr (LDS) at the lane's K offset, or zeros.
+__device__ __forceinline__ void mma_a(const uint16_t* xr, bool live, bf16x8* av) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const u32x4 v = *(const u32x4*)(xr + 8 * q);
+    av[q] = __builtin_bit_cast(bf16x8, live ? v : u32x4{0u, 0u, 0u, 0u});
+  }
+}
+
+// One widened MXFP4 chunk (w: 16 bf16 pairs in K order) into D.
+__device__ __forceinline__ f32x4 mma_chunk(const bf16x2* w, const bf16x8* av, f32x4 acc) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const bf16x8 b = {w[4 * q][0], w[4 * q][1], w[4 * q + 1][0], w[4 * q + 1][1],
+                      w[4 * q + 2][0], w[4 * q + 2][1], w[4 * q + 3][0], w[4 * q + 3][1]};
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[q], b, acc, 0, 0, 0);
+  }
+  return acc;
+}
+
 // Sums of the 32 bf16 values of a block at p (LDS) -- one sum, or one per 16-element half
 // (Q6_K) -- into out, in the order dot_chunk takes them for the k-quants.
 template <int FMT>
@@ -355,11 +383,15 @@ __global__ __launch_bounds__(kGThreads) void k_gemv(
         }
         xrow[i] = src + row * K;
       }
+      constexpr bool kMma = mma_path(FMT, NT);
       float acc[kM][NT];
+      f32x4 acc4[kM];
 #pragma unroll
-      for (int m = 0; m < kM; ++m)
+      for (int m = 0; m < kM; ++m) {
+        acc4[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < NT; ++i) acc[m][i] = 0.f;
+      }
 
       for (int cbase = 0; cbase < nc; cbase += kGWaves * kU) {
         // 1. the batch's K range of every token's activation row (L2-resident): loads first,
@@ -400,6 +432,24 @@ __global__ __launch_bounds__(kGThreads) void k_gemv(
         }
         __syncthreads();
         // 3. consume (chunks past the end of the row carry a zero scale and add nothing)
+        if constexpr (kMma) {
+          const int tm = lane & 15;   // the lane's token row of A
+#pragma unroll
+          for (int u = 0; u < kU; ++u) {
+            const int c = cbase + wave + kGWaves * u;
+            const int xo = (c - cbase) * LM::kKPerChunk + koff;
+            bf16x8 av[4];
+            mma_a(&xs[tm < NT ? tm : 0][xo], tm < NT, av);
+            bf16x2 w[LM::kWPairs];
+            widen<FMT>(ca[u], w);
+            acc4[0] = mma_chunk(w, av, acc4[0]);
+            if constexpr (GATED) {
+              widen<FMT>(cbk[u], w);
+              acc4[kM - 1] = mma_chunk(w, av, acc4[kM - 1]);
+            }
+          }
+          continue;
+        }
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
           const int c = cbase + wave + kGWaves * u;
@@ -436,28 +486,38 @@ __global__ __launch_bounds__(kGThreads) void k_gemv(
           }
         }
       }
-      // lanes that share a row: MXFP4 {l, l^16, l^32, l^48}; Q8_0 {l, l^1, l^32, l^33}
+      if constexpr (kMma) {
+        // D: lane l < 16 holds tokens 0..3 of row l
+        if (lane < 16) {
 #pragma unroll
-      for (int m = 0; m < kM; ++m)
+          for (int m = 0; m < kM; ++m)
 #pragma unroll
-        for (int i = 0; i < NT; ++i) {
-          float v = acc[m][i];
-          if constexpr (unit16(FMT)) {
-            v += wave_xor(v, 16);
-            v += wave_xor(v, 32);
-          } else {
-            v += wave_xor(v, 1);
-            v += wave_xor(v, 32);
-          }
-          acc[m][i] = v;
+            for (int i = 0; i < NT; ++i) red[wave][i][m][lane] = acc4[m][i];
         }
-      const bool writer = unit16(FMT) ? (lane < 16) : (lane < 32 && (lane & 1) == 0);
-      if (writer) {
-        const int r = LM::row(lane);
+      } else {
+        // lanes that share a row: MXFP4 {l, l^16, l^32, l^48}; Q8_0 {l, l^1, l^32, l^33}
 #pragma unroll
         for (int m = 0; m < kM; ++m)
 #pragma unroll
-          for (int i = 0; i < NT; ++i) red[wave][i][m][r] = acc[m][i];
+          for (int i = 0; i < NT; ++i) {
+            float v = acc[m][i];
+            if constexpr (unit16(FMT)) {
+              v += wave_xor(v, 16);
+              v += wave_xor(v, 32);
+            } else {
+              v += wave_xor(v, 1);
+              v += wave_xor(v, 32);
+            }
+            acc[m][i] = v;
+          }
+        const bool writer = unit16(FMT) ? (lane < 16) : (lane < 32 && (lane & 1) == 0);
+        if (writer) {
+          const int r = LM::row(lane);
+#pragma unroll
+          for (int m = 0; m < kM; ++m)
+#pragma unroll
+            for (int i = 0; i < NT; ++i) red[wave][i][m][r] = acc[m][i];
+        }
       }
       __syncthreads();
       if (threadIdx.x < NT * 16) {
@@ -975,11 +1035,15 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
       xrow[i] = &xs[(t >= 0 ? t : 0) * H];
       xsum[i] = &xsum_l[kquant(FMT) ? (t >= 0 ? t : 0) * (H / 32) * sums_per_block(FMT) : 0];
     }
+    constexpr bool kMma = mma_path(FMT, NT);
     float acc[2][NT];
+    f32x4 acc4[2];
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < 2; ++m) {
+      acc4[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < NT; ++i) acc[m][i] = 0.f;
+    }
     // chunks per wave per batch: fewer with more tokens and with the k-quants' larger
     // chunk records, so that the batch stays in registers
     constexpr int kRU = FMT == kQ4_K ? (NT >= 4 ? 3 : NT >= 2 ? 4 : 6)
@@ -999,6 +1063,25 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
                         sbp2 + (int64_t)(cs >> 1) * 64, hb + (int64_t)cs * LM::kHiChunk, ok);
       }
       __builtin_amdgcn_sched_barrier(0);   // the whole batch in flight before any is used
+      if constexpr (kMma) {
+        const int tm = lane & 15;   // the lane's token row of A
+        const uint16_t* xr = xrow[0];
+#pragma unroll
+        for (int i = 1; i < NT; ++i) xr = tm == i ? xrow[i] : xr;
+#pragma unroll
+        for (int u = 0; u < kRU; ++u) {
+          const int c = cbase + wave + kGWaves * u;
+          const int xo = ca[u].ok ? c * LM::kKPerChunk + koff : 0;   // masked: any valid part
+          bf16x8 av[4];
+          mma_a(xr + xo, tm < NT, av);
+          bf16x2 w[LM::kWPairs];
+          widen<FMT>(ca[u], w);
+          acc4[0] = mma_chunk(w, av, acc4[0]);
+          widen<FMT>(cbk[u], w);
+          acc4[1] = mma_chunk(w, av, acc4[1]);
+        }
+        continue;
+      }
 #pragma unroll
       for (int u = 0; u < kRU; ++u) {
         const int c = cbase + wave + kGWaves * u;
@@ -1026,27 +1109,36 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
       }
     }
     // 5. lanes that share a row, then the 4 waves in a fixed order; SwiGLU; h in bf16
+    if constexpr (kMma) {
+      if (lane < 16) {   // D: lane l < 16 holds tokens 0..3 of row l
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+        for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int i = 0; i < NT; ++i) {
-        float a = acc[m][i];
-        if constexpr (unit16(FMT)) {
-          a += wave_xor(a, 16);
-          a += wave_xor(a, 32);
-        } else {
-          a += wave_xor(a, 1);
-          a += wave_xor(a, 32);
-        }
-        acc[m][i] = a;
+          for (int i = 0; i < NT; ++i) red[wave][i][m][lane] = acc4[m][i];
       }
-    const bool writer = unit16(FMT) ? (lane < 16) : (lane < 32 && (lane & 1) == 0);
-    if (writer) {
-      const int r = LM::row(lane);
+    } else {
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int i = 0; i < NT; ++i) red[wave][i][m][r] = acc[m][i];
+        for (int i = 0; i < NT; ++i) {
+          float a = acc[m][i];
+          if constexpr (unit16(FMT)) {
+            a += wave_xor(a, 16);
+            a += wave_xor(a, 32);
+          } else {
+            a += wave_xor(a, 1);
+            a += wave_xor(a, 32);
+          }
+          acc[m][i] = a;
+        }
+      const bool writer = unit16(FMT) ? (lane < 16) : (lane < 32 && (lane & 1) == 0);
+      if (writer) {
+        const int r = LM::row(lane);
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int i = 0; i < NT; ++i) red[wave][i][m][r] = acc[m][i];
+      }
     }
     __syncthreads();
     if (tid < NT * 16) {

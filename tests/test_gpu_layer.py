@@ -83,6 +83,14 @@ def test_layer_parity_small(name, path):
     run_layer(synth.CONFIGS[name], path)
 
 
+@pytest.mark.parametrize("T", [2, 3])
+def test_layer_parity_decode_two_and_three_tokens(T):
+    """Decode with fewer tokens than the 4-token kernel's rows (MXFP4 runs them on MFMA with
+    the empty token rows of A zeroed)."""
+    print(f"layer gptoss_decode_t4 T={T}", flush=True)
+    run_layer(synth.config("gptoss_decode_t4", T=T))
+
+
 def test_layer_parity_decode_last_of_24_layers():
     print("layer gptoss_decode_t1 layer 23", flush=True)
     run_layer(synth.CONFIGS["gptoss_decode_t1"], layer=23)
@@ -243,6 +251,8 @@ def _stages(pool, sm, wr, bias, x, k, path):
 
 
 @pytest.mark.parametrize("name,T,path", [("gptoss_decode_t4", 1, qm.PATH_GEMV),
+                                         ("gptoss_decode_t4", 2, qm.PATH_GEMV),
+                                         ("gptoss_decode_t4", 3, qm.PATH_GEMV),
                                          ("gptoss_decode_t4", 4, qm.PATH_GEMV),
                                          ("qwen_a3b_decode", 16, qm.PATH_GEMV),
                                          ("mixtral_q8_decode", 3, qm.PATH_GEMV),
