@@ -18,6 +18,8 @@
 //     in bf16, and the block scale d multiplies the fp32 MFMA result before accumulation;
 //   * gate and up tiles of the same columns live in the same wave, so SwiGLU is applied in
 //     registers and h is written once, rounded to bf16; the down projection writes fp32 y.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -312,6 +314,9 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
   };
   constexpr int kPrev[4] = {3, 0, 1, 2};   // the fragment before mf (3: previous block)
 
+  // 16-row fragments of this wave's half of the tile that hold at least one bucket row
+  // (wave-uniform; the tile's last rows repeat its last pair and are never stored)
+  const int nmf = min(4, max(0, (mend - (m0 + 64 * wm) + 15) >> 4));
   load_a(0);
   load_b(0);
   const int g4 = lane >> 4;
@@ -337,32 +342,40 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
       load_b(c + 1);
     }
     if constexpr (FMT == kMXFP4) {
-      // lane's operand: unit `lane` of its row group's run = block 4c + lane/16 of row lane%16
-      u32x4 bqv[4];
-      float bsc[4];
+      // lane's operand: unit `lane` of its row group's run = block 4c + lane/16 of row lane%16.
+      // FULL: all 4 of the wave's 16-row fragments hold a bucket row; otherwise only the
+      // first nmf do, and the others (past the expert's last pair) run no MFMA at all.
+      auto mx_step = [&](auto full) {
+        constexpr bool kFull = decltype(full)::value;
+        u32x4 bqv[4];
+        float bsc[4];
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        bqv[f] = *(const u32x4*)(lds_bq + fg[f] * BS::kRunQ + lane * 16);
-        // read unconditionally, mask arithmetically (a conditional read becomes a branch)
-        const uint32_t sb = lds_bs[fg[f] * BS::kRunS + lane];
-        const uint32_t keep = (fcol[f] && 4 * c + g4 < nb) ? 0xffffffffu : 0u;
-        bsc[f] = __uint_as_float((sb << 23) & keep);   // E8M0 -> 2^(b-127), or +0
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        bf16x8 bv[4];
-#pragma unroll
-        for (int f = 0; f < 4; ++f) bv[f] = fp4x8_to_bf16x8(bqv[f][i], bsc[f]);
-#pragma unroll
-        for (int mf = 0; mf < 4; ++mf) {
-          const int row = 64 * wm + 16 * mf + mrow;
-          const bf16x8 av =
-              __builtin_bit_cast(bf16x8, *(const u32x4*)(lds_a + row * kLdsStride + (32 * g4 + 8 * i) * 2));
-#pragma unroll
-          for (int f = 0; f < 4; ++f)
-            acc[mf][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[f], acc[mf][f], 0, 0, 0);
+        for (int f = 0; f < 4; ++f) {
+          bqv[f] = *(const u32x4*)(lds_bq + fg[f] * BS::kRunQ + lane * 16);
+          // read unconditionally, mask arithmetically (a conditional read becomes a branch)
+          const uint32_t sb = lds_bs[fg[f] * BS::kRunS + lane];
+          const uint32_t keep = (fcol[f] && 4 * c + g4 < nb) ? 0xffffffffu : 0u;
+          bsc[f] = __uint_as_float((sb << 23) & keep);   // E8M0 -> 2^(b-127), or +0
         }
-      }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          bf16x8 bv[4];
+#pragma unroll
+          for (int f = 0; f < 4; ++f) bv[f] = fp4x8_to_bf16x8(bqv[f][i], bsc[f]);
+#pragma unroll
+          for (int mf = 0; mf < 4; ++mf) {
+            if (!kFull && mf >= nmf) continue;
+            const int row = 64 * wm + 16 * mf + mrow;
+            const bf16x8 av = __builtin_bit_cast(
+                bf16x8, *(const u32x4*)(lds_a + row * kLdsStride + (32 * g4 + 8 * i) * 2));
+#pragma unroll
+            for (int f = 0; f < 4; ++f)
+              acc[mf][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[f], acc[mf][f], 0, 0, 0);
+          }
+        }
+      };
+      if (nmf == 4) mx_step(std::true_type{});
+      else if (nmf > 0) mx_step(std::false_type{});
     } else if constexpr (FMT == kQ6_K) {
       // per block: lanes g = 0, 1 supply K 0..15 (half 0), g = 2, 3 K 16..31 (half 1). A
       // with the other half's lanes zeroed gives each half its own MFMAs: codes as low
