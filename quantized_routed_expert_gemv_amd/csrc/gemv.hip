@@ -813,7 +813,7 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
   __shared__ unsigned long long hit_l[kMaxE / 64];
   __shared__ int act_l[kFuseMaxPairs][kActStride];
   __shared__ int nact_l;
-  __shared__ int rank_l[kWave];
+  __shared__ int rank_l[kMaxE];
   __shared__ float red[kGWaves][NT][2][16];
   // Q4_K: the block sums of the tokens' activation rows, shared by every row of every unit
   __shared__ float xsum_l[kquant(FMT) ? NT * kRouteMaxH / 32 * sums_per_block(FMT) : 1];
@@ -837,7 +837,7 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
   for (int r = 0; r < kXP; ++r)
     xv[r] = *(const u32x4*)(x + (int64_t)min(tid + r * kGThreads, xp_n - 1) * 8);
   if (tid < kMaxE / 64) hit_l[tid] = 0ull;
-  if (tid < kWave) rank_l[tid] = 0;
+  if (tid < kMaxE) rank_l[tid] = 0;
   if (tid < E) slot_l[tid] = sm;
   if (tid < TE) lg_l[tid] = finish_logit(v, ns, bz);
 #pragma unroll
@@ -911,62 +911,81 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
       if (lane == 0) nact_l = nact;
     }
   };
-  if constexpr (NT == 1) {   // NT == 1 means T == 1
-    if (E <= kWave) {
-      // 2'. one token, at most 64 experts: every wave holds all E keys (lane e) and counts,
-      //     for each, the keys above it among its quarter of the experts (broadcast with
-      //     readlane); the four counts meet in rank_l. Same keys and ranks as
-      //     wave_topk_softmax, so the same choices and order.
-      float v = lane < E ? lg_l[lane] : -INFINITY;
-      v = (v != v) ? -INFINITY : v;
-      const uint64_t key = lane < E ? topk_key(v, lane) : 0ull;
-      const uint32_t key_hi = (uint32_t)(key >> 32), key_lo = (uint32_t)key;
-      constexpr int kPerWave = kWave / kGWaves;
-      int r = 0;
-  #pragma unroll
+  // 2'. one token: lane l holds the keys of experts l, l + 64, ... (SLOTS of them). Every
+  //     wave counts, for each of those keys, the keys above it among lanes [16 w, 16 w + 16)
+  //     of every slot (broadcast with readlane); the four counts meet in rank_l. Same keys
+  //     and ranks as wave_topk_softmax, so the same choices and order.
+  // 3'. the k pairs of the one token (distinct experts): pair j goes to position
+  //     #{j' : e_j' < e_j}, and is its expert's only pair.
+  auto route_one_token = [&](auto slots) {
+    constexpr int SLOTS = decltype(slots)::value;
+    float v[SLOTS];
+    uint64_t key[SLOTS];
+    int r[SLOTS];
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) {
+      const int e = s * kWave + lane;
+      float x = e < E ? lg_l[e] : -INFINITY;
+      x = (x != x) ? -INFINITY : x;
+      v[s] = x;
+      key[s] = e < E ? topk_key(x, e) : 0ull;
+      r[s] = 0;
+    }
+    constexpr int kPerWave = kWave / kGWaves;
+#pragma unroll
+    for (int sc = 0; sc < SLOTS; ++sc) {
+      const uint32_t key_hi = (uint32_t)(key[sc] >> 32), key_lo = (uint32_t)key[sc];
+#pragma unroll
       for (int q = 0; q < kPerWave; ++q) {
         const int c = wave * kPerWave + q;
         // readlane returns a signed int: widen each half as unsigned
         const uint64_t kc =
             ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)key_hi, c) << 32) |
             (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)key_lo, c);
-        r += kc > key ? 1 : 0;
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s) r[s] += kc > key[s] ? 1 : 0;
       }
-      atomicAdd(&rank_l[lane], r);
-      __syncthreads();
-      if (wave == 0) {
-        const int rank = rank_l[lane];
-        if (lane < E && rank < k) {
-          ids_l[rank] = lane;
-          tk_l[0].zs[rank] = v;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-        wave_softmax_chosen(tk_l[0].zs, k, w_l);
-        // 3'. the k pairs of the one token (distinct experts): pair j goes to position
-        //     #{j' : e_j' < e_j}, and is its expert's only pair
-        const int ej = lane < k ? ids_l[lane] : 0x7fffffff;
-        int pos = 0;
-        for (int q = 0; q < k; ++q) pos += __builtin_amdgcn_readlane(ej, q) < ej ? 1 : 0;
-        if (lane < k) {
-          perm_l[pos] = lane;
-          inv_l[lane] = pos;
-          int* a = act_l[pos];
-          a[0] = ej;
-          a[1] = slot_l[ej];
-          a[2] = pos;
-          a[3] = pos + 1;
-          a[4] = 0;
-          a[5] = -1;
-          a[6] = -1;
-          a[7] = -1;
-        }
-        if (lane == 0) nact_l = k;
-      }
-    } else {
-      route_general();
     }
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) atomicAdd(&rank_l[s * kWave + lane], r[s]);
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int s = 0; s < SLOTS; ++s) {
+        const int e = s * kWave + lane;
+        const int rank = rank_l[e];
+        if (e < E && rank < k) {
+          ids_l[rank] = e;
+          tk_l[0].zs[rank] = v[s];
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      wave_softmax_chosen(tk_l[0].zs, k, w_l);
+      const int ej = lane < k ? ids_l[lane] : 0x7fffffff;
+      int pos = 0;
+      for (int q = 0; q < k; ++q) pos += __builtin_amdgcn_readlane(ej, q) < ej ? 1 : 0;
+      if (lane < k) {
+        perm_l[pos] = lane;
+        inv_l[lane] = pos;
+        int* a = act_l[pos];
+        a[0] = ej;
+        a[1] = slot_l[ej];
+        a[2] = pos;
+        a[3] = pos + 1;
+        a[4] = 0;
+        a[5] = -1;
+        a[6] = -1;
+        a[7] = -1;
+      }
+      if (lane == 0) nact_l = k;
+    }
+  };
+  if constexpr (NT == 1) {   // NT == 1 means T == 1
+    if (E <= kWave) route_one_token(std::integral_constant<int, 1>{});
+    else if (E <= 2 * kWave) route_one_token(std::integral_constant<int, 2>{});
+    else route_one_token(std::integral_constant<int, kMaxE / kWave>{});
   } else {
     route_general();
   }

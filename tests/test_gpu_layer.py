@@ -121,6 +121,9 @@ def test_layer_dense_and_full_mixture_special_cases():
 @pytest.mark.parametrize("cfg", [
     # 256 experts: four logits per lane in the top-k; 8 experts chosen
     synth.Config("e256_t1", 1, 256, 512, 256, 8, "mxfp4", 1.2, "perm", 31, 1),
+    # 100 and 200 experts: the last of two / four logits per lane only partly used
+    synth.Config("e100_t1", 1, 256, 512, 100, 6, "mxfp4", 1.1, "perm", 38, 1),
+    synth.Config("e200_t1_q8", 1, 256, 512, 200, 8, "q8_0", None, "perm", 39, 1),
     # 4 tokens x 8 choices = 32 pairs, 64 experts (256 logits): the fused decode limits
     synth.Config("e64_t4_k8", 4, 512, 256, 64, 8, "mxfp4", 1.1, "perm", 32, 1),
     # 3 tokens (a partly used 4-token pass), Q8_0
@@ -138,6 +141,41 @@ def test_layer_decode_routing_edge_cases(cfg):
     kernel (up to 4 tokens, up to 256 (token, expert) logits, up to 32 pairs)."""
     print(f"layer {cfg.name}", flush=True)
     run_layer(cfg)
+
+
+@pytest.mark.parametrize("E,k,tied", [
+    (40, 4, (3, 17, 33)),                  # one key per lane
+    (100, 6, (5, 64, 70, 99)),             # two per lane, the second slot partly used
+    (200, 8, (1, 66, 130, 197)),           # four per lane, the last slot partly used
+    (256, 8, (0, 63, 64, 127, 128, 255)),  # every slot's first and last lane
+])
+def test_layer_one_token_ties_across_lanes_and_slots(E, k, tied):
+    """One token whose top logit is shared by several experts spread over the lanes and
+    key slots of the in-kernel top-k: the tied experts come first, lowest index first, and
+    the layer's routing equals the stand-alone route's bit for bit."""
+    print(f"layer ties E={E} k={k}", flush=True)
+    cfg = synth.Config(f"ties_e{E}", 1, 256, 256, E, k, "mxfp4", None, "perm", 41, 1)
+    L = synth.make_layer(cfg)
+    top = int(np.argmax(omoe.router_logits(L.x, L.wr, None)[0]))
+    for e in tied:
+        L.wr[e] = L.wr[top]
+    ids_ref, w_ref, _ = omoe.route(L.x, L.wr, None, k)
+    lg = np.sort(omoe.router_logits(L.x, L.wr, None)[0])[::-1]
+    # the tie is exact; every other gap among the top k + 1 keeps the routing margin
+    others = np.diff(np.unique(lg[: k + 1]))
+    assert len(set(tied) | {top}) <= k and np.all(np.abs(others) > 1e-4)
+    assert list(ids_ref[0, : len(set(tied) | {top})]) == sorted(set(tied) | {top})
+    pool, x, wr, bias, sm = to_device(L)
+    out, ws = qm.layer(pool, sm, wr, None, x, k)
+    ids_s, w_s = qm.route(x, wr, None, k)
+    torch.cuda.synchronize()
+    got = ws.intermediates()
+    assert np.array_equal(got["ids"].cpu().numpy(), ids_ref)
+    assert torch.equal(got["ids"].cpu(), ids_s.cpu()) and torch.equal(got["w"].cpu(), w_s.cpu())
+    assert np.abs(got["w"].cpu().numpy() - w_ref).max() <= W_ABS
+    counts, offsets, perm, inv = omoe.bucket(ids_ref, E)
+    for n, ref in (("counts", counts), ("offsets", offsets), ("perm", perm), ("inv_perm", inv)):
+        assert np.array_equal(got[n].cpu().numpy(), ref), n
 
 
 def test_layer_decode_invalid_slot_sets_flag_and_zeroes():
