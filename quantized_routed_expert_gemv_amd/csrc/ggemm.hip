@@ -28,7 +28,6 @@ namespace moe {
 namespace {
 
 constexpr int kTThreads = 256;
-constexpr int kBM = 128;          // pairs per tile
 constexpr int kBK = 128;          // K per pipeline step
 constexpr int kLdsStride = kBK * 2 + 16;   // bytes per A row in LDS (padded)
 
@@ -36,15 +35,15 @@ __device__ __forceinline__ u32x4 ldg16(const void* p) { return *(const u32x4*)p;
 __device__ __forceinline__ u32x2 ldg8(const void* p) { return *(const u32x2*)p; }
 
 // Which (expert, first position) a row tile index maps to; returns false if none.
-__device__ bool map_row_tile(const int32_t* __restrict__ offsets, int E, int mt, int* e_out,
-                             int* m0_out, int* tmp4, int* sh) {
+__device__ bool map_row_tile(const int32_t* __restrict__ offsets, int E, int bm, int mt,
+                             int* e_out, int* m0_out, int* tmp4, int* sh) {
   const int e = threadIdx.x;
   int lo = 0, n = 0;
   if (e < E) {
     lo = offsets[e];
     n = offsets[e + 1] - lo;
   }
-  const int nt = (n + kBM - 1) / kBM;
+  const int nt = (n + bm - 1) / bm;
   // exclusive scan of nt over the workgroup
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -62,7 +61,7 @@ __device__ bool map_row_tile(const int32_t* __restrict__ offsets, int E, int mt,
   const int cum = base + inc - nt;
   if (e < E && mt >= cum && mt < cum + nt) {
     sh[0] = e;
-    sh[1] = lo + (mt - cum) * kBM;
+    sh[1] = lo + (mt - cum) * bm;
   }
   __syncthreads();
   *e_out = sh[0];
@@ -70,23 +69,26 @@ __device__ bool map_row_tile(const int32_t* __restrict__ offsets, int E, int mt,
   return sh[0] >= 0;
 }
 
-// B of one K step (4 blocks = 128 K) for the workgroup's 8 row groups (128 weight rows):
+// B of one K step (4 blocks = 128 K) for the workgroup's NG row groups (16 NG weight rows):
 // in the tiled pool layout each row group's step is one contiguous run of 64 units
 // (4 blocks x 16 rows), so the step is copied verbatim into LDS and a lane's MFMA operand
 // is unit `lane` (MXFP4) or units 16 j + lane % 16 (Q8_0) of its row group's run.
-template <int FMT>
+template <int FMT, int NG>   // NG: weight row groups (16 rows each) per tile
 struct BStage {
   static constexpr int kRunQ = 64 * code_bytes_per_block(FMT);   // code bytes per row group
   static constexpr int kRunS = 64 * scale_bytes_per_block(FMT);  // scale bytes per row group
-  static constexpr int kQPieces = 8 * kRunQ / 16 / kTThreads;    // 16-byte code pieces/thread
+  static constexpr int kQPieces = NG * kRunQ / 16 / kTThreads;   // 16-byte code pieces/thread
   // Q4_K: the 16 rows' (d, dmin) records of the step's super-block, per row group
   static constexpr int kRunS2 = kquant(FMT) ? kRowGroup * (int)kSuperBytes : 4;
   // Q5_K: the high-bit dwords of the run's 64 units
   static constexpr int kRunH = hi_bytes_per_block(FMT) ? 64 * (int)hi_bytes_per_block(FMT) : 4;
-  static constexpr int kHDwords = 8 * kRunH / 4 / kTThreads;   // high-part dwords per thread
+  static constexpr int kHDwords = NG * kRunH / 4 / kTThreads;  // high-part dwords per thread
 };
 
-template <int FMT, bool GATED>
+// BM: bucket rows per tile, 128 (waves 2 x 2) or 64 (waves 1 x 4). Each wave computes a
+// 64 x 64 block of the tile (gate/up: 32 gate + the same 32 up columns, twice), so a tile
+// spans 64 * 4 / (BM / 64) columns of weight rows: fewer A bytes per flop at BM = 64.
+template <int FMT, bool GATED, int BM>
 __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
     const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as, int64_t qslot,
     int64_t sslot, const uint8_t* __restrict__ bq, const uint8_t* __restrict__ bs,
@@ -94,17 +96,21 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm, int k,
     const uint16_t* __restrict__ src, int K, int N, int n_mtiles, int n_ntiles,
     uint16_t* __restrict__ h_out, float* __restrict__ y_out, uint32_t* __restrict__ err_flags) {
-  using BS = BStage<FMT>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[kBM * kLdsStride];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_bq[8 * BS::kRunQ];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_bs[8 * BS::kRunS];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_bs2[8 * BS::kRunS2];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_bh[8 * BS::kRunH];
+  constexpr int WM = BM / 64, WN = 4 / WM;   // waves along rows / columns
+  constexpr int NG = 4 * WN;                  // weight row groups per tile
+  constexpr int RPT = BM / 16;                // A rows staged per thread
+  static_assert(BM == 64 || BM == 128, "64 or 128 rows per tile");
+  using BS = BStage<FMT, NG>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[BM * kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_bq[NG * BS::kRunQ];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_bs[NG * BS::kRunS];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_bs2[NG * BS::kRunS2];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_bh[NG * BS::kRunH];
   __shared__ int tmp4[4];
   __shared__ int sh[2];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   // XCD-aware 2-D order: workgroups are dealt to the 8 XCDs in turn (XCD x runs
   // workgroups x, x + 8, ...). Tile i of a list that walks super-tiles of 8 row tiles x 8
   // column tiles (row-major inside each) goes to the XCD of the 64-tile run it lies in, so
@@ -121,14 +127,14 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
   const int mt = 8 * sr + kk / w;
   const int nt = 8 * gcol + kk % w;
   int e, m0;
-  if (!map_row_tile(offsets, E, mt, &e, &m0, tmp4, sh)) return;
+  if (!map_row_tile(offsets, E, BM, mt, &e, &m0, tmp4, sh)) return;
   const int mend = offsets[e + 1];
   const int slot = slot_map[e];
-  // columns of this workgroup: GATED -> 64 gate + the same 64 up columns; else 128
-  const int n0 = GATED ? nt * 64 : nt * 128;
+  // columns of this workgroup: GATED -> 32 WN gate + the same 32 WN up columns; else 64 WN
+  const int n0 = GATED ? nt * 32 * WN : nt * 64 * WN;
   if (slot < 0 || slot >= n_slots) {
-    const int ncols = GATED ? 64 : 128;
-    for (int i = threadIdx.x; i < kBM * ncols; i += kTThreads) {
+    const int ncols = GATED ? 32 * WN : 64 * WN;
+    for (int i = threadIdx.x; i < BM * ncols; i += kTThreads) {
       const int pos = m0 + i / ncols, n = n0 + i % ncols;
       if (pos < mend && n < N) {
         if (GATED) h_out[(int64_t)pos * N + n] = 0;
@@ -146,46 +152,46 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
   // last K step (past K) is masked to zeros, so that nothing but zeros meets the masked B.
   const int piece = threadIdx.x & 15;
   const int rbase = threadIdx.x >> 4;
-  uint32_t arow[8];   // element offset of the thread's piece in each of its 8 rows
+  uint32_t arow[RPT];   // element offset of the thread's piece in each of its rows
   {
-    int prow[8];
+    int prow[RPT];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)   // all perm loads first
+    for (int j = 0; j < RPT; ++j)   // all perm loads first
       prow[j] = GATED ? perm[min(m0 + rbase + 16 * j, mend - 1)] : min(m0 + rbase + 16 * j, mend - 1);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < RPT; ++j)
       arow[j] = (uint32_t)(GATED ? prow[j] / k : prow[j]) * (uint32_t)K + piece * 8;
   }
-  u32x4 areg[8];
+  u32x4 areg[RPT];
   auto load_a = [&](int c) {
     const int kk = c * kBK;
     if (kk + kBK <= K) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) areg[j] = ldg16(src + arow[j] + kk);
+      for (int j = 0; j < RPT; ++j) areg[j] = ldg16(src + arow[j] + kk);
     } else {
       const bool ok = kk + piece * 8 < K;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < RPT; ++j) {
         const u32x4 v = ldg16(src + arow[j] + (ok ? kk : 0));
         areg[j] = ok ? v : u32x4{0, 0, 0, 0};
       }
     }
   };
 
-  // ---- B staging: local row group g (0..7) of the tile. GATED: g < 4 -> gate rows
-  // n0/16 + g, g >= 4 -> up rows n0/16 + g - 4; else rows n0/16 + g. A row group past N
-  // reads group 0 (its columns are never stored). Thread t copies code pieces
-  // t + 256 p of the 8 runs and, for t < 8 * kRunS / 4, one dword of scales.
+  // ---- B staging: local row group g (0 .. NG-1) of the tile. GATED: g < NG/2 -> gate rows
+  // n0/16 + g, g >= NG/2 -> up rows n0/16 + g - NG/2; else rows n0/16 + g. A row group past
+  // N reads group 0 (its columns are never stored). Thread t copies code pieces
+  // t + 256 p of the NG runs and, for t < NG * kRunS / 4, one dword of scales.
   const uint8_t* q0 = aq + (int64_t)slot * qslot;
   const uint8_t* s0 = as + (int64_t)slot * sslot;
   const uint8_t* q1 = GATED ? bq + (int64_t)slot * qslot : q0;
   const uint8_t* s1 = GATED ? bs + (int64_t)slot * sslot : s0;
   auto group_base = [&](int g, const uint8_t** qb, const uint8_t** sb) {
-    const int rg = GATED ? n0 / 16 + (g & 3) : n0 / 16 + g;
+    const int rg = GATED ? n0 / 16 + g % (NG / 2) : n0 / 16 + g;
     const int rgc = rg * 16 < N ? rg : 0;
     const int64_t u0 = (int64_t)rgc * nb * 16;   // first unit of the row group
-    *qb = (GATED && g >= 4 ? q1 : q0) + u0 * code_bytes_per_block(FMT);
-    *sb = (GATED && g >= 4 ? s1 : s0) + u0 * scale_bytes_per_block(FMT);
+    *qb = (GATED && g >= NG / 2 ? q1 : q0) + u0 * code_bytes_per_block(FMT);
+    *sb = (GATED && g >= NG / 2 ? s1 : s0) + u0 * scale_bytes_per_block(FMT);
   };
   const uint8_t* bqp[BS::kQPieces];
   int bq_blk[BS::kQPieces];   // block of the step that the piece lies in
@@ -199,7 +205,8 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
     bqp[p] = qb + (off % BS::kRunQ);
     bq_blk[p] = (off % BS::kRunQ) / (16 * code_bytes_per_block(FMT));
   }
-  constexpr int kSDwords = 8 * BS::kRunS / 4;
+  constexpr int kSDwords = NG * BS::kRunS / 4;
+  static_assert(kSDwords <= kTThreads, "one scale dword per thread at most");
   const bool s_thread = threadIdx.x < kSDwords;
   const uint8_t* bsp;
   int bs_blk;
@@ -213,14 +220,15 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
     bs_blk = (off % BS::kRunS) / (16 * scale_bytes_per_block(FMT));
   }
   // Q4_K super-block records: thread t < 128 copies row t % 16 of local row group t / 16
-  const bool s2_thread = kquant(FMT) && threadIdx.x < 8 * kRowGroup;
+  static_assert(!kquant(FMT) || NG * kRowGroup <= kTThreads, "one record per thread");
+  const bool s2_thread = kquant(FMT) && threadIdx.x < NG * kRowGroup;
   const uint8_t* bs2p = nullptr;
   if constexpr (kquant(FMT)) {
     const int g = (s2_thread ? threadIdx.x : 0) / kRowGroup;
-    const int rg = GATED ? n0 / 16 + (g & 3) : n0 / 16 + g;
+    const int rg = GATED ? n0 / 16 + g % (NG / 2) : n0 / 16 + g;
     const int rgc = rg * 16 < N ? rg : 0;
     const int nsb = nb / kSuperBlocks;
-    bs2p = (GATED && g >= 4 ? s1 : s0) + super_region(N, K) +
+    bs2p = (GATED && g >= NG / 2 ? s1 : s0) + super_region(N, K) +
            ((int64_t)rgc * nsb * kRowGroup + (threadIdx.x & 15)) * kSuperBytes;
   }
   // Q5_K / Q6_K high-part dwords: thread t copies dwords t + 256 h of the 8 runs
@@ -238,9 +246,9 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
     for (int h = 0; h < kHD; ++h) {
       const int dw = threadIdx.x + kTThreads * h;
       const int g = dw / (BS::kRunH / 4);
-      const int rg = GATED ? n0 / 16 + (g & 3) : n0 / 16 + g;
+      const int rg = GATED ? n0 / 16 + g % (NG / 2) : n0 / 16 + g;
       const int rgc = rg * 16 < N ? rg : 0;
-      bhp[h] = (GATED && g >= 4 ? q1 : q0) + hi_region(N, K) +
+      bhp[h] = (GATED && g >= NG / 2 ? q1 : q0) + hi_region(N, K) +
                (int64_t)rgc * nb * 16 * hi_bytes_per_block(FMT) + (dw % (BS::kRunH / 4)) * 4;
     }
   }
@@ -276,7 +284,7 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
     int col0;
     if (GATED) {
       col0 = n0 + 32 * wn + 16 * (f & 1);
-      fg[f] = (f < 2 ? 0 : 4) + 2 * wn + (f & 1);
+      fg[f] = (f < 2 ? 0 : NG / 2) + 2 * wn + (f & 1);
     } else {
       col0 = n0 + 64 * wn + 16 * f;
       fg[f] = 4 * wn + f;
@@ -324,7 +332,7 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
   for (int c = 0; c < nsteps; ++c) {
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < RPT; ++j)
       *(u32x4*)(lds_a + (rbase + 16 * j) * kLdsStride + piece * 16) = areg[j];
 #pragma unroll
     for (int p = 0; p < BS::kQPieces; ++p)
@@ -559,17 +567,22 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
   }
 }
 
-template <int FMT, bool GATED>
+// MXFP4 tiles are 64 rows x 256 weight rows: its B is the smallest per weight, so a wider
+// tile cuts the A (activation) bytes that each CU pulls in per flop.
+constexpr int kMxfp4BM = 64;
+
+template <int FMT, bool GATED, int BM = 128>
 hipError_t launch_ggemm_t(const PoolView& a, const PoolView& b, const int32_t* slot_map,
                           int n_slots, int E, const int32_t* offsets, const int32_t* perm,
                           int T, int k, const uint16_t* src, int K, int N, uint16_t* h,
                           float* y, uint32_t* err, hipStream_t stream) {
   const int pairs = T * k;
-  const int max_mtiles = (pairs + kBM - 1) / kBM + min(E, pairs);
-  const int n_ntiles = GATED ? (N + 63) / 64 : (N + 127) / 128;
+  const int max_mtiles = (pairs + BM - 1) / BM + min(E, pairs);
+  constexpr int kCols = GATED ? 32 * (256 / BM) : 64 * (256 / BM);   // columns per tile
+  const int n_ntiles = (N + kCols - 1) / kCols;
   const int64_t grid = ((int64_t)max_mtiles * n_ntiles + 511) / 512 * 512;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_ggemm<FMT, GATED>), dim3((unsigned)grid), dim3(kTThreads), 0, stream,
+  hipLaunchKernelGGL((k_ggemm<FMT, GATED, BM>), dim3((unsigned)grid), dim3(kTThreads), 0, stream,
                      a.q, a.s, a.q_slot, a.s_slot, b.q, b.s, slot_map, n_slots, E, offsets, perm,
                      k, src, K, N, max_mtiles, n_ntiles, h, y, err);
   return hipGetLastError();
@@ -584,7 +597,7 @@ hipError_t launch_gate_up_grouped(int fmt, const PoolView& gate, const PoolView&
                                   hipStream_t stream) {
   switch (fmt) {
     case kMXFP4:
-      return launch_ggemm_t<kMXFP4, true>(gate, up, slot_map, n_slots, E, offsets, perm, T, k, x,
+      return launch_ggemm_t<kMXFP4, true, kMxfp4BM>(gate, up, slot_map, n_slots, E, offsets, perm, T, k, x,
                                           H, I, h, nullptr, err, stream);
     case kQ8_0:
       return launch_ggemm_t<kQ8_0, true>(gate, up, slot_map, n_slots, E, offsets, perm, T, k, x,
@@ -608,7 +621,7 @@ hipError_t launch_down_grouped(int fmt, const PoolView& down, const int32_t* slo
                                uint32_t* err, hipStream_t stream) {
   switch (fmt) {
     case kMXFP4:
-      return launch_ggemm_t<kMXFP4, false>(down, down, slot_map, n_slots, E, offsets, nullptr, T,
+      return launch_ggemm_t<kMXFP4, false, kMxfp4BM>(down, down, slot_map, n_slots, E, offsets, nullptr, T,
                                            k, h, I, H, nullptr, y, err, stream);
     case kQ8_0:
       return launch_ggemm_t<kQ8_0, false>(down, down, slot_map, n_slots, E, offsets, nullptr, T,
