@@ -9,8 +9,10 @@
 // accumulate in fp32. A workgroup owns 16 tokens and all E experts; its 4 waves split the
 // reduction dimension and their partial tiles are summed in LDS in a fixed order, so the
 // result is deterministic. For small T the reduction dimension is also split across
-// workgroups (grid.y) and a second, single-workgroup kernel sums the partials in a fixed
-// order, takes the top-k and (in the fused layer) also bucket-sorts the pairs. A kernel
+// workgroups and a later kernel (a single-workgroup finish, or every workgroup of the
+// decode gate/up kernel) sums the partials in a fixed order, takes the top-k and, in the
+// fused layer, also bucket-sorts the pairs; the decode split runs one wave per slice
+// (k_router_part), whose few steps need no reduction across waves. A kernel
 // boundary, not an arrival counter, hands the partials over: on this chip a device-scope
 // release in every workgroup writes back the whole L2 of its XCD, which costs far more
 // than a launch.
@@ -147,6 +149,76 @@ __global__ __launch_bounds__(256) void k_router(const uint16_t* __restrict__ x,
   }
 }
 
+// Partial logits of the split router for a small batch (T <= 16): one wave per slice z of
+// the reduction dimension (the slices of router_tile, whole pairs of 32-wide steps), its
+// steps accumulated in increasing order in one MFMA chain and stored from registers as
+// partial[z][t][e]. A slice holds at most a few steps, so the wave issues the loads of RB
+// steps before the MFMAs that consume them; rows past T or E are loaded from a valid row
+// and zeroed when consumed.
+template <int NF>
+__global__ __launch_bounds__(kWave) void k_router_part(const uint16_t* __restrict__ x,
+                                                       const uint16_t* __restrict__ wr, int T,
+                                                       int H, int E, float* __restrict__ partial) {
+  // a slice of the fused decode split is at most 2 pairs of steps
+  constexpr int RB = router_rb<NF>() < 4 ? router_rb<NF>() : 4;
+  const int lane = threadIdx.x;
+  const int z = blockIdx.x, nsplit = gridDim.x;
+  const int nsteps = H / 32;
+  const int npairs = (nsteps + 1) / 2;
+  const int s_begin = 2 * (int)((int64_t)npairs * z / nsplit);
+  const int s_end = min(nsteps, 2 * (int)((int64_t)npairs * (z + 1) / nsplit));
+  const int row = lane & 15;        // token (A) / expert (B) within the 16-tile
+  const int kq = (lane >> 4) * 8;   // this lane's 8-element slice of the 32-step
+  const bool tok_ok = row < T;
+  const uint16_t* xr = x + (int64_t)(tok_ok ? row : 0) * H + kq;
+  const uint16_t* wrow[NF];
+  bool e_ok[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    e_ok[f] = f * 16 + row < E;
+    wrow[f] = wr + (int64_t)(e_ok[f] ? f * 16 + row : 0) * H + kq;
+  }
+  f32x4 acc[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const u32x4 zero = {0, 0, 0, 0};
+  for (int s0 = s_begin; s0 < s_end; s0 += RB) {
+    u32x4 a[RB], bq[RB][NF];
+    bool ok[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const int s = s0 + r;
+      ok[r] = s < s_end;
+      const int ss = ok[r] ? s : s_begin;
+      a[r] = *(const u32x4*)(xr + ss * 32);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) bq[r][f] = *(const u32x4*)(wrow[f] + ss * 32);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      if (!ok[r]) continue;
+      const bf16x8 av = __builtin_bit_cast(bf16x8, tok_ok ? a[r] : zero);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, e_ok[f] ? bq[r][f] : zero);
+        acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[f], 0, 0, 0);
+      }
+    }
+  }
+  // lane holds D[token 4*(lane/16)+v][expert 16f + lane%16]
+  float* dst = partial + (int64_t)z * T * E;
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const int e = f * 16 + row;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int t = 4 * (lane >> 4) + v;
+      if (t < T && e < E) dst[(int64_t)t * E + e] = acc[f][v];
+    }
+  }
+}
+
 // Finish a split router for a small batch (T <= 16) in one workgroup: load every split's
 // partial logits (all loads issued before any is used), sum them in increasing split order,
 // add the bias, take top-k and softmax per token, and, with BUCKET, bucket-sort the pairs.
@@ -274,11 +346,10 @@ bool route_fused_ok(int T, int H, int E) {
 hipError_t launch_router_partials(const uint16_t* x, const uint16_t* wr, int T, int H, int E,
                                   int ns, float* partial, hipStream_t stream) {
   if (T < 1 || T > kRouteTok || ns < 2 || ns > kMaxSplit) return hipErrorInvalidValue;
-  dim3 grid(1, ns);
 #define MOE_PART_CASE(N)                                                                     \
   case N:                                                                                   \
-    hipLaunchKernelGGL(k_router<N>, grid, dim3(256), 0, stream, x, wr, nullptr, T, H, E, 1, \
-                       partial, nullptr, nullptr);                                          \
+    hipLaunchKernelGGL(k_router_part<N>, dim3(ns), dim3(kWave), 0, stream, x, wr, T, H, E,  \
+                       partial);                                                            \
     break;
   switch ((E + 15) / 16) {
     MOE_PART_CASE(1) MOE_PART_CASE(2) MOE_PART_CASE(3) MOE_PART_CASE(4)
