@@ -554,7 +554,9 @@ constexpr int kDCMaxPairs = 8;
 constexpr int kDCMaxH = 57344 / 2;   // bf16 elements of h staged in LDS (pairs x I)
 constexpr int kDCU = 12;             // chunks per wave per load batch
 
-template <int FMT, bool COMBINE>
+// NP: most pairs of one expert (every pair of an expert is a different token, so NP >= T
+// suffices); the per-expert accumulators and the unrolled chunk loop are sized by it.
+template <int FMT, bool COMBINE, int NP>
 __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
     const uint8_t* __restrict__ dq, const uint8_t* __restrict__ ds, int64_t qslot,
     int64_t sslot, int n_slots, int E, const int32_t* __restrict__ act,
@@ -694,9 +696,10 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
     if (busy && valid) load_batch(q);
   }
   // 4. consume each batch as it arrives, then load the next
-  float acc[kDCMaxPairs];
+  static_assert(NP >= 1 && NP <= kDCMaxPairs, "pairs per expert");
+  float acc[NP];
 #pragma unroll
-  for (int p = 0; p < kDCMaxPairs; ++p) acc[p] = 0.f;
+  for (int p = 0; p < NP; ++p) acc[p] = 0.f;
   if (busy && valid) {
     for (int cbase = q;;) {
 #pragma unroll
@@ -707,7 +710,7 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
         uint32_t xv[LM::kXWords];
         widen<FMT>(ch[u], w);
 #pragma unroll
-        for (int p = 0; p < kDCMaxPairs; ++p) {
+        for (int p = 0; p < NP; ++p) {
           if (lo + p < hi) {
             const uint16_t* hrow = &hs[(lo + p) * I + kx];
 #pragma unroll
@@ -731,7 +734,7 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
   }
   // 5. rows of the wave's partials, then fixed-order sums over the waves of each expert
 #pragma unroll
-  for (int p = 0; p < kDCMaxPairs; ++p) {
+  for (int p = 0; p < NP; ++p) {
     float v = acc[p];
     if constexpr (unit16(FMT)) {
       v += wave_xor(v, 16);
@@ -746,7 +749,7 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
   if (writer) {
     const int r = LM::row(lane);
 #pragma unroll
-    for (int p = 0; p < kDCMaxPairs; ++p) red[wave][p][r] = acc[p];
+    for (int p = 0; p < NP; ++p) red[wave][p][r] = acc[p];
   }
   __syncthreads();
   if (threadIdx.x < np * 16) {
@@ -1259,14 +1262,26 @@ hipError_t launch_gate_up_route(int fmt, const PoolView& gate, const PoolView& u
   });
 }
 
+// The small-batch down kernel's bound on pairs per expert for T tokens: 1, 2, 4 or 8.
+template <typename Fn>
+void with_pairs_per_expert(int T, Fn&& fn) {
+  if (T <= 1) fn(std::integral_constant<int, 1>{});
+  else if (T <= 2) fn(std::integral_constant<int, 2>{});
+  else if (T <= 4) fn(std::integral_constant<int, 4>{});
+  else fn(std::integral_constant<int, kDCMaxPairs>{});
+}
+
 hipError_t launch_down_gemv(int fmt, const PoolView& down, const int32_t* slot_map, int n_slots,
                             int E, int T, int k, int H, int I, const int32_t* offsets,
                             const uint16_t* h, float* y, uint32_t* err, hipStream_t stream) {
   return with_fmt(fmt, [&](auto F) {
     if (down_combine_small_ok(T, k, E, I)) {   // the fused layer's kernel, without the combine
-      hipLaunchKernelGGL((k_down_small<F(), false>), dim3(H / 16), dim3(kDCWaves * kWave), 0,
-                         stream, down.q, down.s, down.q_slot, down.s_slot, n_slots, E, nullptr,
-                         offsets, slot_map, h, T, k, H, I, nullptr, nullptr, y, nullptr, err);
+      with_pairs_per_expert(T, [&](auto NP) {
+        hipLaunchKernelGGL((k_down_small<F(), false, NP()>), dim3(H / 16),
+                           dim3(kDCWaves * kWave), 0, stream, down.q, down.s, down.q_slot,
+                           down.s_slot, n_slots, E, nullptr, offsets, slot_map, h, T, k, H, I,
+                           nullptr, nullptr, y, nullptr, err);
+      });
       return hipGetLastError();
     }
     return launch_gemv_t<F(), false, kSrcOffsets>(down, down, slot_map, n_slots, E, offsets,
@@ -1286,9 +1301,11 @@ hipError_t launch_down_combine_small(int fmt, const PoolView& down, int n_slots,
                                      float* out, uint32_t* err, hipStream_t stream) {
   if (!down_combine_small_ok(T, k, E, I)) return hipErrorInvalidValue;
   return with_fmt(fmt, [&](auto F) {
-    hipLaunchKernelGGL((k_down_small<F(), true>), dim3(H / 16), dim3(kDCWaves * kWave), 0, stream,
-                       down.q, down.s, down.q_slot, down.s_slot, n_slots, E, act, nullptr,
-                       nullptr, h, T, k, H, I, inv_perm, topk_w, y, out, err);
+    with_pairs_per_expert(T, [&](auto NP) {
+      hipLaunchKernelGGL((k_down_small<F(), true, NP()>), dim3(H / 16), dim3(kDCWaves * kWave), 0,
+                         stream, down.q, down.s, down.q_slot, down.s_slot, n_slots, E, act,
+                         nullptr, nullptr, h, T, k, H, I, inv_perm, topk_w, y, out, err);
+    });
     return hipGetLastError();
   });
 }
