@@ -102,7 +102,10 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
   static_assert(BM == 64 || BM == 128, "64 or 128 rows per tile");
   using BS = BStage<FMT, NG>;
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[BM * kLdsStride];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_bq[NG * BS::kRunQ];
+  // Q8_0 codes are staged already widened to bf16 (2 bytes per code): both waves that
+  // read a B fragment would otherwise widen it each
+  constexpr int kBqWiden = FMT == kQ8_0 ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_bq[NG * BS::kRunQ * kBqWiden];
   __shared__ __attribute__((aligned(16))) uint8_t lds_bs[NG * BS::kRunS];
   __shared__ __attribute__((aligned(16))) uint8_t lds_bs2[NG * BS::kRunS2];
   __shared__ __attribute__((aligned(16))) uint8_t lds_bh[NG * BS::kRunH];
@@ -334,9 +337,18 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
 #pragma unroll
     for (int j = 0; j < RPT; ++j)
       *(u32x4*)(lds_a + (rbase + 16 * j) * kLdsStride + piece * 16) = areg[j];
+    if constexpr (FMT == kQ8_0) {   // 16 int8 codes -> 16 bf16 (exact), 32 bytes
 #pragma unroll
-    for (int p = 0; p < BS::kQPieces; ++p)
-      *(u32x4*)(lds_bq + (threadIdx.x + kTThreads * p) * 16) = breg[p];
+      for (int p = 0; p < BS::kQPieces; ++p) {
+        uint8_t* dst = lds_bq + (threadIdx.x + kTThreads * p) * 32;
+        *(bf16x8*)dst = i8x8_to_bf16x8(breg[p][0], breg[p][1]);
+        *(bf16x8*)(dst + 16) = i8x8_to_bf16x8(breg[p][2], breg[p][3]);
+      }
+    } else {
+#pragma unroll
+      for (int p = 0; p < BS::kQPieces; ++p)
+        *(u32x4*)(lds_bq + (threadIdx.x + kTThreads * p) * 16) = breg[p];
+    }
     if (s_thread) *(uint32_t*)(lds_bs + threadIdx.x * 4) = sreg;
     if constexpr (kquant(FMT))
       if (s2_thread) *(uint32_t*)(lds_bs2 + threadIdx.x * 4) = s2reg;
@@ -503,8 +515,8 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
       }
     } else {
       // one MFMA per 32-wide block; lane supplies K = 32 j + 8 g .. + 7 of block j, i.e.
-      // bytes 8 g .. of unit 16 j + lane%16 of its row group's run; the block scale d
-      // multiplies the fp32 products one fragment later.
+      // codes 8 g .. of unit 16 j + lane%16 of its row group's run (staged as bf16); the
+      // block scale d multiplies the fp32 products one fragment later.
 #pragma unroll 1
       for (int j = 0; j < 4; ++j) {
         bf16x8 bv[4];
@@ -512,8 +524,7 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
           const int unit = 16 * j + mrow;
-          const u32x2 q = *(const u32x2*)(lds_bq + fg[f] * BS::kRunQ + unit * 32 + 8 * g4);
-          bv[f] = i8x8_to_bf16x8(q[0], q[1]);
+          bv[f] = *(const bf16x8*)(lds_bq + (fg[f] * BS::kRunQ + unit * 32 + 8 * g4) * 2);
           const uint32_t db = *(const uint16_t*)(lds_bs + fg[f] * BS::kRunS + unit * 2);
           const uint32_t keep = (fcol[f] && 4 * c + j < nb) ? 0xffffu : 0u;
           ds[f] = fp16_to_f32((uint16_t)(db & keep));   // fp16 +0 when masked
