@@ -178,6 +178,21 @@ def test_layer_one_token_ties_across_lanes_and_slots(E, k, tied):
         assert np.array_equal(got[n].cpu().numpy(), ref), n
 
 
+@pytest.mark.parametrize("cfg", [
+    # the small-batch down + combine kernel is sized by the most pairs one expert can hold
+    # (its token count T, rounded up to 1, 2, 4 or 8); these cover each bound partly used
+    synth.Config("np8_t6_k1", 6, 256, 512, 8, 1, "mxfp4", 1.1, "perm", 51, 1),
+    synth.Config("np8_t8_k1_q8", 8, 256, 256, 4, 1, "q8_0", None, "perm", 52, 1),
+    synth.Config("np4_t3_k2", 3, 512, 256, 16, 2, "mxfp4", None, "perm", 53, 1),
+    synth.Config("np2_t2_k3_q6k", 2, 256, 512, 6, 3, "q6_k", None, "perm", 54, 1),
+])
+def test_layer_small_batch_down_pair_bounds(cfg):
+    """Layers whose down projection runs the fused small-batch down + combine kernel with
+    each of its per-expert pair bounds, against the oracle."""
+    print(f"layer {cfg.name}", flush=True)
+    run_layer(cfg)
+
+
 def test_layer_decode_invalid_slot_sets_flag_and_zeroes():
     """A slot outside the pool: the flag is set and that expert adds nothing."""
     cfg = synth.config("gptoss_decode_t4", T=2, H=256, I=512)
