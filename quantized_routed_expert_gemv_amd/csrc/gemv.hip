@@ -796,7 +796,9 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
 // gate and up rows of this row group are streamed and each chunk is consumed as it
 // arrives. Chunk order, per-lane accumulation and the reduction are those of k_gemv, so
 // the two give bit-identical h.
-template <int FMT, int NT>
+// RU: chunks per wave per load batch (0: by format and token count); the one-token MXFP4
+// launch sizes it to the row so that no batch slot is spent on a masked chunk.
+template <int FMT, int NT, int RU = 0>
 __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
     const uint8_t* __restrict__ gq, const uint8_t* __restrict__ gsc,
     const uint8_t* __restrict__ uq, const uint8_t* __restrict__ usc, int64_t qslot,
@@ -1068,7 +1070,8 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
     }
     // chunks per wave per batch: fewer with more tokens and with the k-quants' larger
     // chunk records, so that the batch stays in registers
-    constexpr int kRU = FMT == kQ4_K ? (NT >= 4 ? 3 : NT >= 2 ? 4 : 6)
+    constexpr int kRU = RU > 0 ? RU
+                      : FMT == kQ4_K ? (NT >= 4 ? 3 : NT >= 2 ? 4 : 6)
                       : FMT == kQ5_K || FMT == kQ6_K ? (NT >= 4 ? 2 : NT >= 2 ? 3 : 4)
                       : NT >= 4 ? 6 : kU;
     for (int cbase = 0; cbase < nc; cbase += kGWaves * kRU) {
@@ -1250,13 +1253,17 @@ hipError_t launch_gate_up_route(int fmt, const PoolView& gate, const PoolView& u
   dim3 grid(min(n_units, kRoutedMaxWG));
   const int nt = gemv_nt(fmt, T);
   return with_fmt(fmt, [&](auto F) {
-#define MOE_ROUTED_CASE(N)                                                                    \
-  hipLaunchKernelGGL((k_gate_up_routed<F(), N>), grid, dim3(kGThreads), 0, stream, gate.q,   \
+#define MOE_ROUTED_CASE(N, R)                                                                 \
+  hipLaunchKernelGGL((k_gate_up_routed<F(), N, R>), grid, dim3(kGThreads), 0, stream, gate.q, \
                      gate.s, up.q, up.s, gate.q_slot, gate.s_slot, slot_map, n_slots, E, k, x, \
                      H, I, h, err, rin)
-    if (nt == 1) MOE_ROUTED_CASE(1);
-    else if (nt == 2) MOE_ROUTED_CASE(2);
-    else MOE_ROUTED_CASE(4);
+    // one MXFP4 token: as many chunks per wave as the row needs (4 waves share a row)
+    const int nc = (H / 32 + 3) / 4;
+    if (nt == 1 && F() == kMXFP4 && nc <= 4 * 4) MOE_ROUTED_CASE(1, 4);
+    else if (nt == 1 && F() == kMXFP4 && nc <= 4 * 6) MOE_ROUTED_CASE(1, 6);
+    else if (nt == 1) MOE_ROUTED_CASE(1, 0);
+    else if (nt == 2) MOE_ROUTED_CASE(2, 0);
+    else MOE_ROUTED_CASE(4, 0);
 #undef MOE_ROUTED_CASE
     return hipGetLastError();
   });
