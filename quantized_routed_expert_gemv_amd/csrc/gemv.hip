@@ -556,7 +556,9 @@ constexpr int kDCU = 12;             // chunks per wave per load batch
 
 // NP: most pairs of one expert (every pair of an expert is a different token, so NP >= T
 // suffices); the per-expert accumulators and the unrolled chunk loop are sized by it.
-template <int FMT, bool COMBINE, int NP>
+// DCU: chunks per wave per load batch (one token: as many as the wave's share needs, at
+// most kDCU).
+template <int FMT, bool COMBINE, int NP, int DCU = kDCU>
 __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
     const uint8_t* __restrict__ dq, const uint8_t* __restrict__ ds, int64_t qslot,
     int64_t sslot, int n_slots, int E, const int32_t* __restrict__ act,
@@ -631,10 +633,10 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
   const uint8_t* sa = ds + (valid ? slot : 0) * sslot + (unit0 + lane_unit) * sb;
   const uint8_t* sa2 = super_base<FMT>(ds + (valid ? slot : 0) * sslot, H, I, rg, lane);
   const uint8_t* ha = hi_base<FMT>(dq + (valid ? slot : 0) * qslot, H, I, unit0 + lane);
-  Chunk ch[kDCU];
+  Chunk ch[DCU];
   auto load_batch = [&](int cbase) {
 #pragma unroll
-    for (int u = 0; u < kDCU; ++u) {
+    for (int u = 0; u < DCU; ++u) {
       const int c = cbase + u * per;
       const int b = c * LM::kBlocksPerChunk + lblk;
       const bool ok = c < nc && b < nb;
@@ -703,7 +705,7 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
   if (busy && valid) {
     for (int cbase = q;;) {
 #pragma unroll
-      for (int u = 0; u < kDCU; ++u) {
+      for (int u = 0; u < DCU; ++u) {
         const int c = cbase + u * per;
         const int kx = ch[u].ok ? c * LM::kKPerChunk + koff : 0;   // masked lanes: any valid row part
         bf16x2 w[LM::kWPairs];
@@ -726,7 +728,7 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
           }
         }
       }
-      cbase += per * kDCU;
+      cbase += per * DCU;
       if (cbase >= nc) break;
       load_batch(cbase);
       __builtin_amdgcn_sched_barrier(0);
@@ -1257,16 +1259,31 @@ hipError_t launch_gate_up_route(int fmt, const PoolView& gate, const PoolView& u
   hipLaunchKernelGGL((k_gate_up_routed<F(), N, R>), grid, dim3(kGThreads), 0, stream, gate.q, \
                      gate.s, up.q, up.s, gate.q_slot, gate.s_slot, slot_map, n_slots, E, k, x, \
                      H, I, h, err, rin)
-    // one MXFP4 token: as many chunks per wave as the row needs (4 waves share a row)
-    const int nc = (H / 32 + 3) / 4;
-    if (nt == 1 && F() == kMXFP4 && nc <= 4 * 4) MOE_ROUTED_CASE(1, 4);
-    else if (nt == 1 && F() == kMXFP4 && nc <= 4 * 6) MOE_ROUTED_CASE(1, 6);
+    // one token: no more chunks per wave than the row needs (4 waves share a row), where
+    // that is fewer than the format's default batch (8 chunks; Q4_K 6; Q5_K, Q6_K 4)
+    const int bpc = LaneMap<F()>::kBlocksPerChunk;
+    const int need = ((H / 32 + bpc - 1) / bpc + kGWaves - 1) / kGWaves;
+    const int dflt = F() == kQ4_K ? 6 : (F() == kQ5_K || F() == kQ6_K) ? 4 : kU;
+    if (nt == 1 && need <= 4 && dflt > 4) MOE_ROUTED_CASE(1, 4);
+    else if (nt == 1 && need <= 6 && dflt > 6) MOE_ROUTED_CASE(1, 6);
     else if (nt == 1) MOE_ROUTED_CASE(1, 0);
     else if (nt == 2) MOE_ROUTED_CASE(2, 0);
     else MOE_ROUTED_CASE(4, 0);
 #undef MOE_ROUTED_CASE
     return hipGetLastError();
   });
+}
+
+// One token: its k experts (all distinct) share the 8 waves, kDCWaves / k of them per
+// expert, so each wave streams ceil(chunks / (kDCWaves / k)) chunks of the row; a batch of
+// kDCUShort covers that when it is short (e.g. I = 768 with 8 experts: 6 chunks a wave).
+constexpr int kDCUShort = 6;
+inline bool down_short_batch(int fmt, int T, int k, int I) {
+  if (T != 1 || k < 1 || k > kDCWaves) return false;
+  const int bpc = unit16(fmt) ? 4 : 2;   // blocks per 1 KiB chunk (LaneMap)
+  const int nc = (I / 32 + bpc - 1) / bpc;
+  const int per = kDCWaves / k;
+  return (nc + per - 1) / per <= kDCUShort;
 }
 
 // The small-batch down kernel's bound on pairs per expert for T tokens: 1, 2, 4 or 8.
@@ -1283,7 +1300,17 @@ hipError_t launch_down_gemv(int fmt, const PoolView& down, const int32_t* slot_m
                             const uint16_t* h, float* y, uint32_t* err, hipStream_t stream) {
   return with_fmt(fmt, [&](auto F) {
     if (down_combine_small_ok(T, k, E, I)) {   // the fused layer's kernel, without the combine
+      const bool short_batch = down_short_batch(F(), T, k, I);
       with_pairs_per_expert(T, [&](auto NP) {
+        if constexpr (NP() == 1) {
+          if (short_batch) {
+            hipLaunchKernelGGL((k_down_small<F(), false, 1, kDCUShort>), dim3(H / 16),
+                               dim3(kDCWaves * kWave), 0, stream, down.q, down.s, down.q_slot,
+                               down.s_slot, n_slots, E, nullptr, offsets, slot_map, h, T, k, H,
+                               I, nullptr, nullptr, y, nullptr, err);
+            return;
+          }
+        }
         hipLaunchKernelGGL((k_down_small<F(), false, NP()>), dim3(H / 16),
                            dim3(kDCWaves * kWave), 0, stream, down.q, down.s, down.q_slot,
                            down.s_slot, n_slots, E, nullptr, offsets, slot_map, h, T, k, H, I,
@@ -1308,7 +1335,17 @@ hipError_t launch_down_combine_small(int fmt, const PoolView& down, int n_slots,
                                      float* out, uint32_t* err, hipStream_t stream) {
   if (!down_combine_small_ok(T, k, E, I)) return hipErrorInvalidValue;
   return with_fmt(fmt, [&](auto F) {
+    const bool short_batch = down_short_batch(F(), T, k, I);
     with_pairs_per_expert(T, [&](auto NP) {
+      if constexpr (NP() == 1) {
+        if (short_batch) {
+          hipLaunchKernelGGL((k_down_small<F(), true, 1, kDCUShort>), dim3(H / 16),
+                             dim3(kDCWaves * kWave), 0, stream, down.q, down.s, down.q_slot,
+                             down.s_slot, n_slots, E, act, nullptr, nullptr, h, T, k, H, I,
+                             inv_perm, topk_w, y, out, err);
+          return;
+        }
+      }
       hipLaunchKernelGGL((k_down_small<F(), true, NP()>), dim3(H / 16), dim3(kDCWaves * kWave), 0,
                          stream, down.q, down.s, down.q_slot, down.s_slot, n_slots, E, act,
                          nullptr, nullptr, h, T, k, H, I, inv_perm, topk_w, y, out, err);
