@@ -306,7 +306,8 @@ struct LaneMap {
 //   kSrcAct      the small-batch router's active-expert list
 constexpr int kSrcOffsets = 0, kSrcAct = 1;
 
-template <int FMT, bool GATED, int SRC, int NT>
+// RU: chunks per wave per batch (kU, or 6 where the row needs no more).
+template <int FMT, bool GATED, int SRC, int NT, int RU = kU>
 __global__ __launch_bounds__(kGThreads) void k_gemv(
     const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as, int64_t a_qslot,
     int64_t a_sslot, const uint8_t* __restrict__ bq, const uint8_t* __restrict__ bs,
@@ -316,7 +317,8 @@ __global__ __launch_bounds__(kGThreads) void k_gemv(
     float* __restrict__ y_out, uint32_t* __restrict__ err_flags, const int32_t* __restrict__ act) {
   using LM = LaneMap<FMT>;
   constexpr int kM = GATED ? 2 : 1;
-  constexpr int kSlice = kGWaves * kU * LM::kKPerChunk;   // K elements staged per batch
+  constexpr int kSlice = kGWaves * RU * LM::kKPerChunk;   // K elements staged per batch
+  static_assert(NT * (kSlice / 8) % kGThreads == 0, "whole 16-byte pieces per thread");
   __shared__ __attribute__((aligned(16))) uint16_t xs[NT][kSlice];
   __shared__ float red[kGWaves][NT][kM][16];
   const int lane = threadIdx.x & (kWave - 1);
@@ -393,7 +395,7 @@ __global__ __launch_bounds__(kGThreads) void k_gemv(
         for (int i = 0; i < NT; ++i) acc[m][i] = 0.f;
       }
 
-      for (int cbase = 0; cbase < nc; cbase += kGWaves * kU) {
+      for (int cbase = 0; cbase < nc; cbase += kGWaves * RU) {
         // 1. the batch's K range of every token's activation row (L2-resident): loads first,
         //    LDS writes after the weight loads are issued
         constexpr int kPieces = NT * (kSlice / 8) / kGThreads;   // 16-byte pieces per thread
@@ -409,9 +411,9 @@ __global__ __launch_bounds__(kGThreads) void k_gemv(
           xp[it] = ld16(xrow[i] + (xok[it] ? kk : 0));
         }
         // 2. this wave's weight chunks of the batch, all in flight at once
-        Chunk ca[kU], cbk[kU];
+        Chunk ca[RU], cbk[RU];
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
+        for (int u = 0; u < RU; ++u) {
           const int c = cbase + wave + kGWaves * u;
           const int b = c * LM::kBlocksPerChunk + lblk;
           const bool ok = c < nc && b < nb;
@@ -435,7 +437,7 @@ __global__ __launch_bounds__(kGThreads) void k_gemv(
         if constexpr (kMma) {
           const int tm = lane & 15;   // the lane's token row of A
 #pragma unroll
-          for (int u = 0; u < kU; ++u) {
+          for (int u = 0; u < RU; ++u) {
             const int c = cbase + wave + kGWaves * u;
             const int xo = (c - cbase) * LM::kKPerChunk + koff;
             bf16x8 av[4];
@@ -451,7 +453,7 @@ __global__ __launch_bounds__(kGThreads) void k_gemv(
           continue;
         }
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
+        for (int u = 0; u < RU; ++u) {
           const int c = cbase + wave + kGWaves * u;
           const int xo = (c - cbase) * LM::kKPerChunk + koff;
           bf16x2 w[LM::kWPairs];
@@ -1198,16 +1200,31 @@ hipError_t launch_gemv_t(const PoolView& a, const PoolView& b, const int32_t* sl
                          float* y, uint32_t* err, const int32_t* act, hipStream_t stream) {
   const int n_act = min(E, T * k);
   dim3 grid(rows / 16, n_act);
-#define MOE_GEMV_CASE(N)                                                                        \
-  hipLaunchKernelGGL((k_gemv<FMT, GATED, SRC, N>), grid, dim3(kGThreads), 0, stream, a.q, a.s,  \
-                     a.q_slot, a.s_slot, b.q, b.s, slot_map, n_slots, E, offsets, perm, k,      \
+#define MOE_GEMV_CASE(N, R)                                                                     \
+  hipLaunchKernelGGL((k_gemv<FMT, GATED, SRC, N, R>), grid, dim3(kGThreads), 0, stream, a.q,    \
+                     a.s, a.q_slot, a.s_slot, b.q, b.s, slot_map, n_slots, E, offsets, perm, k, \
                      src, K, rows, h, y, err, act)
+  // 2 or 4 tokens of a 16-byte-unit format: a batch of 6 chunks per wave when the row
+  // needs no more (4 waves share a row), e.g. K = 2880: 23 chunks
+  const int need = ((K / 32 + LaneMap<FMT>::kBlocksPerChunk - 1) / LaneMap<FMT>::kBlocksPerChunk +
+                    kGWaves - 1) / kGWaves;
+  const bool six = unit16(FMT) && need <= 6;
   switch (gemv_nt(FMT, T)) {
-    case 1: MOE_GEMV_CASE(1); break;
-    case 2: MOE_GEMV_CASE(2); break;
-    case 4: MOE_GEMV_CASE(4); break;
+    case 1: MOE_GEMV_CASE(1, kU); break;
+    case 2:
+      if constexpr (unit16(FMT)) {
+        if (six) { MOE_GEMV_CASE(2, 6); break; }
+      }
+      MOE_GEMV_CASE(2, kU);
+      break;
+    case 4:
+      if constexpr (unit16(FMT)) {
+        if (six) { MOE_GEMV_CASE(4, 6); break; }
+      }
+      MOE_GEMV_CASE(4, kU);
+      break;
     default:
-      if constexpr (FMT == kQ8_0) MOE_GEMV_CASE(8);
+      if constexpr (FMT == kQ8_0) MOE_GEMV_CASE(8, kU);
       break;
   }
 #undef MOE_GEMV_CASE
