@@ -1276,13 +1276,18 @@ hipError_t launch_gate_up_route(int fmt, const PoolView& gate, const PoolView& u
   hipLaunchKernelGGL((k_gate_up_routed<F(), N, R>), grid, dim3(kGThreads), 0, stream, gate.q, \
                      gate.s, up.q, up.s, gate.q_slot, gate.s_slot, slot_map, n_slots, E, k, x, \
                      H, I, h, err, rin)
-    // one token: no more chunks per wave than the row needs (4 waves share a row), where
-    // that is fewer than the format's default batch (8 chunks; Q4_K 6; Q5_K, Q6_K 4)
+    // one token: a batch of chunks per wave (4 waves share a row) that wastes fewer slots
+    // on masked chunks than the format's default (8 chunks; Q4_K 6; Q5_K, Q6_K 4)
     const int bpc = LaneMap<F()>::kBlocksPerChunk;
     const int need = ((H / 32 + bpc - 1) / bpc + kGWaves - 1) / kGWaves;
     const int dflt = F() == kQ4_K ? 6 : (F() == kQ5_K || F() == kQ6_K) ? 4 : kU;
-    if (nt == 1 && need <= 4 && dflt > 4) MOE_ROUTED_CASE(1, 4);
-    else if (nt == 1 && need <= 6 && dflt > 6) MOE_ROUTED_CASE(1, 6);
+    // the batch (4, 6 or the default) that leaves the fewest masked slots, larger on ties
+    auto slots = [&](int ru) { return (need + ru - 1) / ru * ru; };
+    int ru = dflt;
+    if (6 < dflt && slots(6) < slots(ru)) ru = 6;
+    if (4 < dflt && slots(4) < slots(ru)) ru = 4;
+    if (nt == 1 && ru == 4 && dflt != 4) MOE_ROUTED_CASE(1, 4);
+    else if (nt == 1 && ru == 6 && dflt != 6) MOE_ROUTED_CASE(1, 6);
     else if (nt == 1) MOE_ROUTED_CASE(1, 0);
     else if (nt == 2) MOE_ROUTED_CASE(2, 0);
     else MOE_ROUTED_CASE(4, 0);
