@@ -60,6 +60,20 @@ moe_status check_shape(int32_t T, int32_t H, int32_t E, int32_t k) {
   return MOE_OK;
 }
 
+// The grouped GEMM addresses gathered activation rows (x, and h for the down projection)
+// as 32-bit indices of 16-byte units, so each of x [T x H] and h [T*k x I] must hold fewer
+// than 2^35 bf16 elements (64 GiB).
+constexpr int64_t kMaxActElems = int64_t(1) << 35;
+moe_status check_extent(int32_t T, int32_t k, int32_t H, int32_t I) {
+  if ((int64_t)T * H >= kMaxActElems)
+    return fail(MOE_ERR_INVALID_ARG, "x holds T*H = %lld elements, limit 2^35",
+                (long long)T * H);
+  if ((int64_t)T * k * I >= kMaxActElems)
+    return fail(MOE_ERR_INVALID_ARG, "h holds T*k*I = %lld elements, limit 2^35",
+                (long long)T * k * I);
+  return MOE_OK;
+}
+
 moe_status check_pool(const moe_pool* pool) {
   if (pool == nullptr) return fail(MOE_ERR_INVALID_ARG, "pool is NULL");
   if (!known_fmt(pool->fmt))
@@ -154,6 +168,8 @@ moe_status check_ffn_args(const moe_pool* pool, const int32_t* slot_map, int32_t
   moe_status s = check_pool(pool);
   if (s != MOE_OK) return s;
   s = check_shape(T, pool->H, E, k);
+  if (s != MOE_OK) return s;
+  s = check_extent(T, k, pool->H, pool->I);
   if (s != MOE_OK) return s;
   if (path < MOE_PATH_AUTO || path > MOE_PATH_GROUPED)
     return fail(MOE_ERR_INVALID_ARG, "path = %d", path);
@@ -413,6 +429,8 @@ moe_status moe_layer_workspace(int32_t T, int32_t H, int32_t I, int32_t E, int32
   moe_status s = check_shape(T, H, E, k);
   if (s != MOE_OK) return s;
   if (I <= 0 || I % 32) return fail(MOE_ERR_INVALID_ARG, "I = %d", I);
+  s = check_extent(T, k, H, I);
+  if (s != MOE_OK) return s;
   const size_t n = (size_t)T * k;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -479,6 +497,8 @@ static moe_status layer_impl(const moe_pool* pool, const int32_t* slot_map,
   moe_status s = check_pool(pool);
   if (s != MOE_OK) return s;
   s = check_shape(T, pool->H, E, k);
+  if (s != MOE_OK) return s;
+  s = check_extent(T, k, pool->H, pool->I);
   if (s != MOE_OK) return s;
   if (path < MOE_PATH_AUTO || path > MOE_PATH_GROUPED)
     return fail(MOE_ERR_INVALID_ARG, "path = %d", path);

@@ -800,8 +800,10 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
 // gate and up rows of this row group are streamed and each chunk is consumed as it
 // arrives. Chunk order, per-lane accumulation and the reduction are those of k_gemv, so
 // the two give bit-identical h.
-// RU: chunks per wave per load batch (0: by format and token count); the one-token MXFP4
-// launch sizes it to the row so that no batch slot is spent on a masked chunk.
+// RU: chunks per wave per load batch (0: by format and token count). At one token the
+// launch picks, for every format, whichever of 4, 6 and the format's default leaves the
+// fewest masked slots in the row's batches (the larger on a tie); some masked slots may
+// remain (gpt-oss MXFP4: 23 chunks in 24 slots).
 template <int FMT, int NT, int RU = 0>
 __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
     const uint8_t* __restrict__ gq, const uint8_t* __restrict__ gsc,

@@ -32,7 +32,6 @@ constexpr int kBK = 128;          // K per pipeline step
 constexpr int kLdsStride = kBK * 2 + 16;   // bytes per A row in LDS (padded)
 
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *(const u32x4*)p; }
-__device__ __forceinline__ u32x2 ldg8(const void* p) { return *(const u32x2*)p; }
 
 // Which (expert, first position) a row tile index maps to; returns false if none.
 __device__ bool map_row_tile(const int32_t* __restrict__ offsets, int E, int bm, int mt,
@@ -153,9 +152,14 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
   // ---- A staging: thread handles 16-byte piece (tid % 16) of rows tid/16 + 16 j. Rows
   // past the tile's end repeat its last row: their results are never stored. Only the
   // last K step (past K) is masked to zeros, so that nothing but zeros meets the masked B.
+  // The thread's pieces are addressed as 16-byte units of src: a 32-bit unit index reaches
+  // 2^35 elements (64 GiB of bf16), the limit the host checks for x and h, where an
+  // element offset would wrap at 2^32 and costs a second register per row as 64 bits.
   const int piece = threadIdx.x & 15;
   const int rbase = threadIdx.x >> 4;
-  uint32_t arow[RPT];   // element offset of the thread's piece in each of its rows
+  const u32x4* src16 = (const u32x4*)src;
+  const uint32_t kp = (uint32_t)K / 8;   // 16-byte units per row
+  uint32_t arow[RPT];   // unit index of the thread's piece in each of its rows
   {
     int prow[RPT];
 #pragma unroll
@@ -163,19 +167,19 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
       prow[j] = GATED ? perm[min(m0 + rbase + 16 * j, mend - 1)] : min(m0 + rbase + 16 * j, mend - 1);
 #pragma unroll
     for (int j = 0; j < RPT; ++j)
-      arow[j] = (uint32_t)(GATED ? prow[j] / k : prow[j]) * (uint32_t)K + piece * 8;
+      arow[j] = (uint32_t)(GATED ? prow[j] / k : prow[j]) * kp + (uint32_t)piece;
   }
   u32x4 areg[RPT];
   auto load_a = [&](int c) {
     const int kk = c * kBK;
     if (kk + kBK <= K) {
 #pragma unroll
-      for (int j = 0; j < RPT; ++j) areg[j] = ldg16(src + arow[j] + kk);
+      for (int j = 0; j < RPT; ++j) areg[j] = src16[arow[j] + (uint32_t)(kk / 8)];
     } else {
       const bool ok = kk + piece * 8 < K;
 #pragma unroll
       for (int j = 0; j < RPT; ++j) {
-        const u32x4 v = ldg16(src + arow[j] + (ok ? kk : 0));
+        const u32x4 v = src16[arow[j] + (uint32_t)(ok ? kk / 8 : 0)];
         areg[j] = ok ? v : u32x4{0, 0, 0, 0};
       }
     }

@@ -262,3 +262,33 @@ def test_workspace_layout_struct_matches_library(lib):
     import quantized_routed_expert_gemv_amd as qm
     assert [f[0] for f in qm.WsLayout._fields_] == [f[0] for f in Ws._fields_]
 
+
+
+def test_activation_extent_limit(lib):
+    """x [T x H] and h [T*k x I] must each hold fewer than 2^35 elements (the grouped GEMM
+    addresses gathered rows as 32-bit indices of 16-byte units); past that the layer, the
+    expert FFN and the workspace query refuse on the host."""
+    _setup(lib)
+    ws = Ws()
+    lib.moe_layer_workspace.argtypes = [ctypes.c_int32] * 5 + [ctypes.POINTER(Ws)]
+    # h: T*k*I = 2^35 exactly (T = 2^20, k = 2, I = 2^14) is refused; one token less fits
+    assert lib.moe_layer_workspace(1 << 20, 256, 1 << 14, 8, 2, ctypes.byref(ws)) == INVALID
+    assert b"T*k*I" in lib.moe_last_error()
+    assert lib.moe_layer_workspace((1 << 20) - 1, 256, 1 << 14, 8, 2, ctypes.byref(ws)) == OK
+    # x: T*H = 2^35 (T = 2^23, H = 4096), with h small enough (I = 32, k = 1)
+    assert lib.moe_layer_workspace(1 << 23, 4096, 32, 8, 1, ctypes.byref(ws)) == INVALID
+    assert b"T*H" in lib.moe_last_error()
+    f = lib.moe_expert_ffn
+    f.argtypes = [ctypes.POINTER(Pool), ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                  ctypes.c_int32, ctypes.c_int32] + [ctypes.c_void_p] * 5 + [ctypes.c_int32,
+                                                                             ctypes.c_void_p]
+    p = _pool(fmt=2, n_slots=8, H=256, I=1 << 14)
+    assert f(ctypes.byref(p), FAKE, 8, FAKE, 1 << 20, 2, FAKE, FAKE, FAKE, FAKE, None, 0,
+             None) == INVALID
+    g = lib.moe_layer
+    g.argtypes = [ctypes.POINTER(Pool)] + [ctypes.c_void_p] * 4 + [ctypes.c_int32] * 3 + \
+                 [ctypes.c_void_p] * 2 + [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int32,
+                                          ctypes.c_void_p]
+    assert g(ctypes.byref(p), FAKE, FAKE, None, FAKE, 1 << 20, 8, 2, FAKE, FAKE, 1 << 62, None,
+             0, None) == INVALID
+    assert b"T*k*I" in lib.moe_last_error()

@@ -135,6 +135,8 @@ def test_layer_dense_and_full_mixture_special_cases():
     synth.Config("h7168_e256_t1", 1, 7168, 512, 256, 8, "mxfp4", 1.2, "perm", 35, 1),
     synth.Config("h6144_t4_q8", 4, 6144, 256, 16, 4, "q8_0", None, "perm", 36, 1),
     synth.Config("h7168_t2_q6k", 2, 7168, 512, 64, 6, "q6_k", None, "perm", 37, 1),
+    # one Q8_0 token at the gpt-oss shape: 45 chunks per row, two batches of 6 per wave
+    synth.Config("gptoss_q8_t1", 1, 2880, 2880, 32, 4, "q8_0", None, "perm", 40, 1),
 ])
 def test_layer_decode_routing_edge_cases(cfg):
     """Shapes at the edges of the decode path that finishes the routing in the gate/up

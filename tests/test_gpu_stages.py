@@ -214,3 +214,53 @@ def test_combine_parity(T, k, H):
     for j in range(k):
         seq = (w[:, j:j + 1] * y[inv.reshape(T, k)[:, j]] + seq).astype(np.float32)
     np.testing.assert_allclose(out, seq, rtol=1e-6, atol=1e-6)
+
+
+def test_expert_ffn_grouped_past_2e32_h_elements():
+    """The grouped GEMM's gathered rows past 2^32 elements of h: Q8_0 experts of the
+    Mixtral shape's I = 14336 with H = 256 and 150,016 tokens x top-2 = 300,032 pairs, so
+    bucket positions from 299,594 on start past element 2^32 of h. Checked on sampled
+    positions, among them the last 64, through a compacted oracle bucketing (the oracle
+    of the sampled pairs only)."""
+    cfg = synth.config("mixtral_q8_prefill", T=150016, H=256)
+    k = cfg.k
+    print(f"ffn past 2^32 h elements: T={cfg.T} H={cfg.H} I={cfg.I} pairs={cfg.T * k}",
+          flush=True)
+    L = make_case(cfg)
+    ids, _, _ = omoe.route(L.x, L.wr, None, k)
+    counts, offsets, perm, inv = omoe.bucket(ids, cfg.E)
+    n = perm.size
+    first_wrap = (1 << 32) // cfg.I + 1
+    assert n > first_wrap + 64
+    pool, x, wr, bias, sm = to_device(L)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    h, y = qm.expert_ffn(pool, sm, x, k, _t(offsets), _t(perm), err_flags=err,
+                         path=qm.PATH_GROUPED)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    positions = np.union1d(sample_positions(offsets, n_uniform=96),
+                           np.r_[np.arange(n - 64, n), first_wrap - 2, first_wrap - 1,
+                                 first_wrap, first_wrap + 1]).astype(np.int64)
+    pt = torch.from_numpy(positions).cuda()
+    hb = h_bits(h[pt])
+    yg = y[pt].cpu().numpy()
+    del h, y
+    # the sampled pairs as a bucketing of their own: same experts, same tokens, in order
+    perm_s = perm[positions].astype(np.int32)
+    exp_of_pos = np.searchsorted(offsets, positions, side="right") - 1
+    off_s = np.zeros(cfg.E + 1, dtype=np.int64)
+    off_s[1:] = np.cumsum(np.bincount(exp_of_pos, minlength=cfg.E))
+    h_ref, _, a_ref = omoe.expert_ffn(L.planes, cfg.fmt, L.slot_map, L.x, k, off_s, perm_s)
+    from parity import _ulp_bf16
+    from oracle import codecs
+    off = np.abs(codecs.bf16_decode(hb) - a_ref) >= _ulp_bf16(a_ref)
+    slack = np.zeros_like(a_ref)
+    rows = np.nonzero(off.any(axis=1))[0]
+    if rows.size:
+        slack[rows] = h_slack(L.planes, cfg.fmt, L.slot_map, L.x, k, off_s, perm_s, rows,
+                              a_ref)
+    frac = check_h(hb, a_ref, slack)
+    y_at_gpu_h = omoe.down_proj(L.planes, cfg.fmt, L.slot_map, hb, off_s)
+    r, e = assert_close_rows(yg, y_at_gpu_h, "y")
+    print(f"  {positions.size} positions, h mismatch {frac:.2e}, y rel L2 {r:.2e}, elem {e:.2e}",
+          flush=True)
