@@ -345,6 +345,27 @@ moe_status moe_layer_timed(const moe_pool* pool, const int32_t* slot_map,
                            int32_t path, void* stream, void* ev_gate_up_begin,
                            void* ev_gate_up_end);
 
+/*
+ * moe_layer_noalloc -- moe_layer for callers that cannot allocate device memory: code that
+ * runs under HIP graph capture and may not call hipMalloc, tight serving loops, and
+ * harnesses that forbid allocation. Same arguments and results as moe_layer, without the
+ * workspace: the layer's intermediates live in a static device array of
+ * MOE_NOALLOC_WS_BYTES bytes that the library holds on each device it runs on until the
+ * process ends. The call enqueues the same kernels and allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine).
+ *   Limit: the layer's workspace (moe_layer_workspace(...).total) must fit in
+ *   MOE_NOALLOC_WS_BYTES; larger calls return MOE_ERR_INVALID_ARG and launch nothing.
+ *   The first call on a device looks up the array's device address (hipGetSymbolAddress,
+ *   with the stream's device current); make that first call outside a stream capture.
+ *   Every call on a device shares that device's array and leaves its contents there: calls
+ *   that overlap in time on one device race, as calls sharing a moe_layer workspace do.
+ */
+#define MOE_NOALLOC_WS_BYTES (32u << 20)
+moe_status moe_layer_noalloc(const moe_pool* pool, const int32_t* slot_map,
+                             const uint16_t* w_router, const float* bias, const uint16_t* x,
+                             int32_t T, int32_t E, int32_t k, float* out, uint32_t* err_flags,
+                             int32_t path, void* stream);
+
 const char* moe_status_string(moe_status s);
 const char* moe_last_error(void);
 

@@ -83,6 +83,8 @@ _layer = _sig("moe_layer", _i32, ctypes.POINTER(PoolStruct), _p, _p, _p, _p, _i3
               _p, _p, _sz, _p, _i32, _p)
 _layer_timed = _sig("moe_layer_timed", _i32, ctypes.POINTER(PoolStruct), _p, _p, _p, _p, _i32,
                     _i32, _i32, _p, _p, _sz, _p, _i32, _p, _p, _p)
+_layer_noalloc = _sig("moe_layer_noalloc", _i32, ctypes.POINTER(PoolStruct), _p, _p, _p, _p,
+                      _i32, _i32, _i32, _p, _p, _i32, _p)
 _status_string = _sig("moe_status_string", ctypes.c_char_p, _i32)
 _last_error = _sig("moe_last_error", ctypes.c_char_p)
 
@@ -90,8 +92,10 @@ EXPORTED = ("moe_plane_bytes", "moe_pool_pack", "moe_route_scratch_bytes", "moe_
             "moe_bucket_scratch_bytes", "moe_bucket", "moe_expert_ffn", "moe_expert_gate_up",
             "moe_expert_down", "moe_combine", "moe_miss_list", "moe_merge_misses",
             "moe_stage_plan", "moe_stage_copy",
-            "moe_layer_workspace", "moe_layer", "moe_layer_timed", "moe_status_string",
-            "moe_last_error")
+            "moe_layer_workspace", "moe_layer", "moe_layer_timed", "moe_layer_noalloc",
+            "moe_status_string", "moe_last_error")
+
+NOALLOC_WS_BYTES = 32 << 20   # MOE_NOALLOC_WS_BYTES
 
 
 def _check(status: int):
@@ -416,6 +420,25 @@ def layer(pool: Pool, slot_map, w_router, bias, x, k: int, out=None, workspace=N
     else:   # (begin, end) torch.cuda.Event pair recorded around the gate/up launch
         _check(_layer_timed(*args, *_event_handles(events)))
     return out, workspace
+
+
+def layer_noalloc(pool: Pool, slot_map, w_router, bias, x, k: int, out=None, err_flags=None,
+                  path=PATH_AUTO, stream=None):
+    """moe_layer_noalloc: the fused layer with the library's static device workspace
+    (no workspace argument). x bf16 [T, H] -> out fp32 [T, H]."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    _need(x, torch.bfloat16, (T, pool.H), "x")
+    _need(w_router, torch.bfloat16, (E, pool.H), "w_router")
+    _need(slot_map, torch.int32, (E,), "slot_map")
+    if bias is not None:
+        _need(bias, torch.float32, (E,), "bias")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    _need(out, torch.float32, (T, pool.H), "out")
+    _check(_layer_noalloc(ctypes.byref(pool.struct), _ptr(slot_map), _ptr(w_router), _ptr(bias),
+                          _ptr(x), T, E, k, _ptr(out), _ptr(err_flags), path, _stream(stream)))
+    return out
 
 
 class LayerCall:

@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "kernels.hpp"
@@ -181,6 +182,50 @@ moe_status check_ffn_args(const moe_pool* pool, const int32_t* slot_map, int32_t
   return MOE_OK;
 }
 
+}  // namespace
+
+// ---- moe_layer_noalloc: moe_layer with its workspace in a file-scope device array
+
+// One array per device, held for the life of the process. In host code its name is only a
+// stand-in for the symbol: kernels are given the device address that hipGetSymbolAddress
+// returns for the current device, never the name itself.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_WS_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // address of `scratch` on each device, looked up once
+
+// The device address of `scratch` on the device that `stream` belongs to, looked up (with
+// that device current) on the first call for the device.
+moe_status noalloc_workspace(hipStream_t stream, void** out) {
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  int dev = cur;
+  if (stream != nullptr) {
+    hipDevice_t d = -1;
+    e = hipStreamGetDevice(stream, &d);
+    if (e != hipSuccess) return hip_status(e, "hipStreamGetDevice");
+    dev = (int)d;
+  }
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_INVALID_ARG, "device %d outside [0, %d)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return hip_status(e, "hipSetDevice");
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t back = dev != cur ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (back != hipSuccess) return hip_status(back, "hipSetDevice (restore)");
+    if (p == nullptr || ((uintptr_t)p & 255))
+      return fail(MOE_ERR_HIP, "static workspace at %p is not 256-byte aligned", p);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -600,6 +645,30 @@ moe_status moe_layer(const moe_pool* pool, const int32_t* slot_map, const uint16
                      float* out, void* workspace, size_t workspace_bytes, uint32_t* err_flags,
                      int32_t path, void* stream) {
   return layer_impl(pool, slot_map, w_router, bias, x, T, E, k, out, workspace, workspace_bytes,
+                    err_flags, path, stream, nullptr, nullptr);
+}
+
+moe_status moe_layer_noalloc(const moe_pool* pool, const int32_t* slot_map,
+                             const uint16_t* w_router, const float* bias, const uint16_t* x,
+                             int32_t T, int32_t E, int32_t k, float* out, uint32_t* err_flags,
+                             int32_t path, void* stream) {
+  moe_status s = check_pool(pool);
+  if (s != MOE_OK) return s;
+  s = check_shape(T, pool->H, E, k);
+  if (s != MOE_OK) return s;
+  if (T == 0) return ok();
+  moe_ws_layout L;
+  s = moe_layer_workspace(T, pool->H, pool->I, E, k, &L);
+  if (s != MOE_OK) return s;
+  if (L.total > (size_t)MOE_NOALLOC_WS_BYTES)
+    return fail(MOE_ERR_INVALID_ARG,
+                "moe_layer_noalloc: the layer needs %zu bytes of workspace, more than the "
+                "%zu-byte static workspace (T = %d; use moe_layer with a caller workspace)",
+                L.total, (size_t)MOE_NOALLOC_WS_BYTES, T);
+  void* ws = nullptr;
+  s = noalloc_workspace((hipStream_t)stream, &ws);
+  if (s != MOE_OK) return s;
+  return layer_impl(pool, slot_map, w_router, bias, x, T, E, k, out, ws, MOE_NOALLOC_WS_BYTES,
                     err_flags, path, stream, nullptr, nullptr);
 }
 
