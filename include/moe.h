@@ -73,8 +73,17 @@ typedef enum {
 
 /* Which expert-FFN schedule to use. AUTO picks the GEMV schedule for T <= 16 and the
  * grouped MFMA GEMM otherwise. Both give results within the same tolerance; they are not
- * bitwise equal to each other. */
-typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_GROUPED = 2 } moe_path;
+ * bitwise equal to each other.
+ * PERSISTENT (moe_layer only; the stage calls treat it as GEMV): for 1 <= T <= 4 tokens,
+ * T * E <= 256 and H <= 4096, the layer after the router's partial logits is one
+ * persistent kernel -- routing, gate/up + SwiGLU, down and combine -- whose workgroups
+ * hand each expert's h over through device-scope counters ([L] original post: launch
+ * overhead matters at decode; [T] "How it works" 2: gate, up and down launches per
+ * expert). It meets the same tolerances; on the workloads measured here it is no faster
+ * than the default launch sequence, so AUTO does not choose it. Other shapes run GEMV. */
+typedef enum {
+  MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_GROUPED = 2, MOE_PATH_PERSISTENT = 3
+} moe_path;
 
 /*
  * Resident expert pool ([T] "How it works" 3: a GPU slot map in front of cached experts;
@@ -308,7 +317,8 @@ moe_status moe_stage_copy(const moe_pool* pool, const moe_pool* backing,
 typedef struct {
   size_t total;
   size_t topk_ids, topk_w, counts, offsets, perm, inv_perm, h, y, scratch;
-  size_t act;   /* int32 list of the active experts, written for small batches */
+  size_t act;       /* int32 list of the active experts, written for small batches */
+  size_t sync;      /* int32 words the decode kernels synchronise through (H/16 + 256) */
 } moe_ws_layout;
 
 moe_status moe_layer_workspace(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k,

@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MXFP4, Q8_0, Q4_K, Q5_K, Q6_K = 1, 2, 3, 4, 5
-PATH_AUTO, PATH_GEMV, PATH_GROUPED = 0, 1, 2
+PATH_AUTO, PATH_GEMV, PATH_GROUPED, PATH_PERSISTENT = 0, 1, 2, 3
 SLOT_MISS = -1      # slot_map value of an expert that is not in the pool (MOE_SLOT_MISS)
 _FMT = {"mxfp4": MXFP4, "q8_0": Q8_0, "q4_k": Q4_K, "q5_k": Q5_K, "q6_k": Q6_K}
 
@@ -50,7 +50,7 @@ class PoolStruct(ctypes.Structure):
 
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, _sz) for n in ("total", "topk_ids", "topk_w", "counts", "offsets", "perm",
-                                   "inv_perm", "h", "y", "scratch", "act")]
+                                   "inv_perm", "h", "y", "scratch", "act", "sync")]
 
 
 def _sig(name, res, *args):

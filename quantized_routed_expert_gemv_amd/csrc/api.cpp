@@ -119,7 +119,8 @@ size_t route_scratch(int32_t T, int32_t H, int32_t E) {
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 bool use_gemv(int32_t path, int32_t T) {
-  return path == MOE_PATH_GEMV || (path == MOE_PATH_AUTO && T <= 16);
+  return path == MOE_PATH_GEMV || path == MOE_PATH_PERSISTENT ||
+         (path == MOE_PATH_AUTO && T <= 16);
 }
 
 moe_status gate_up_dispatch(const moe_pool* pool, const int32_t* slot_map, int32_t E,
@@ -172,7 +173,7 @@ moe_status check_ffn_args(const moe_pool* pool, const int32_t* slot_map, int32_t
   if (s != MOE_OK) return s;
   s = check_extent(T, k, pool->H, pool->I);
   if (s != MOE_OK) return s;
-  if (path < MOE_PATH_AUTO || path > MOE_PATH_GROUPED)
+  if (path < MOE_PATH_AUTO || path > MOE_PATH_PERSISTENT)
     return fail(MOE_ERR_INVALID_ARG, "path = %d", path);
   if (T == 0) return MOE_OK;
   CHECK_PTR(slot_map);
@@ -495,6 +496,7 @@ moe_status moe_layer_workspace(int32_t T, int32_t H, int32_t I, int32_t E, int32
   const size_t bs = T > 0 ? moe::bucket_scratch_bytes((int)n, E) : 0;
   out->scratch = take(rs > bs ? rs : bs);
   out->act = take((size_t)moe::act_ints(E) * sizeof(int32_t));
+  out->sync = take((size_t)moe::sync_ints(H) * sizeof(int32_t));
   out->total = off;
   return ok();
 }
@@ -506,8 +508,20 @@ static moe_status down_combine_tail(const moe_pool* pool, const int32_t* slot_ma
                                     const int32_t* act, const uint16_t* h,
                                     const int32_t* inv_perm, const float* w, float* y,
                                     float* out, uint32_t* err_flags, int32_t path,
-                                    hipStream_t st) {
-  if (act != nullptr && use_gemv(path, T) && moe::down_combine_small_ok(T, k, E, pool->I)) {
+                                    hipStream_t st, int32_t* tickets = nullptr) {
+  const bool small = moe::down_small_preferred(pool->fmt, T, k, E, pool->I);
+  if (act != nullptr && tickets != nullptr && use_gemv(path, T) && !small &&
+      moe::down_ticket_ok(T, k, E)) {
+    // decode: the tickets were zeroed by the routed gate/up kernel
+    clear_stale_error();
+    moe::PoolView g, u, d;
+    pool_views(pool, &g, &u, &d);
+    return hip_status(moe::launch_down_ticket(pool->fmt, d, pool->n_slots, E, T, k, pool->H,
+                                              pool->I, act, h, inv_perm, w, y, out, tickets,
+                                              err_flags, st),
+                      "down+combine (tickets)");
+  }
+  if (act != nullptr && use_gemv(path, T) && small) {
     clear_stale_error();
     moe::PoolView g, u, d;
     pool_views(pool, &g, &u, &d);
@@ -545,7 +559,7 @@ static moe_status layer_impl(const moe_pool* pool, const int32_t* slot_map,
   if (s != MOE_OK) return s;
   s = check_extent(T, k, pool->H, pool->I);
   if (s != MOE_OK) return s;
-  if (path < MOE_PATH_AUTO || path > MOE_PATH_GROUPED)
+  if (path < MOE_PATH_AUTO || path > MOE_PATH_PERSISTENT)
     return fail(MOE_ERR_INVALID_ARG, "path = %d", path);
   if (T == 0) return ok();
   CHECK_PTR(slot_map);
@@ -573,6 +587,7 @@ static moe_status layer_impl(const moe_pool* pool, const int32_t* slot_map,
   float* y = (float*)(ws + L.y);
   void* scratch = ws + L.scratch;
   int32_t* act = (int32_t*)(ws + L.act);
+  int32_t* sync = (int32_t*)(ws + L.sync);   // tickets first, then the hand-off counters
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
   bool have_act = false;
@@ -584,8 +599,27 @@ static moe_status layer_impl(const moe_pool* pool, const int32_t* slot_map,
     // router partials over slices of H; the gate/up GEMV finishes the routing itself (or,
     // for the grouped path, one workgroup finishes it and bucket-sorts)
     const int ns = moe::route_fused_split(pool->H);
-    e = moe::launch_router_partials(x, w_router, T, pool->H, E, ns, (float*)scratch, st);
+    const bool fused = path == MOE_PATH_PERSISTENT && moe::decode_fused_ok(T, pool->H, E);
+    e = moe::launch_router_partials(x, w_router, T, pool->H, E, ns, (float*)scratch, st,
+                                    fused ? sync : nullptr, moe::sync_ints(pool->H));
     if (e != hipSuccess) return hip_status(e, "router");
+    if (fused) {
+      // one persistent kernel: routing, gate/up + SwiGLU, down and combine
+      if (ev_begin != nullptr) {
+        s = record_event((hipEvent_t)ev_begin, st);
+        if (s != MOE_OK) return s;
+      }
+      moe::PoolView g, u, d;
+      pool_views(pool, &g, &u, &d);
+      const moe::RouteIn rin{(const float*)scratch, ns, bias, T, ids, w, counts, offsets, perm,
+                             inv_perm, act, nullptr, 0};
+      clear_stale_error();
+      e = moe::launch_decode_fused(pool->fmt, g, u, d, slot_map, pool->n_slots, E, x, T, k,
+                                   pool->H, pool->I, rin, h, y, out, sync, err_flags, st);
+      if (e != hipSuccess) return hip_status(e, "fused decode layer");
+      if (ev_end != nullptr) return record_event((hipEvent_t)ev_end, st);
+      return ok();
+    }
     if (gemv) {
       if (ev_begin != nullptr) {
         s = record_event((hipEvent_t)ev_begin, st);
@@ -594,7 +628,7 @@ static moe_status layer_impl(const moe_pool* pool, const int32_t* slot_map,
       moe::PoolView g, u, d;
       pool_views(pool, &g, &u, &d);
       const moe::RouteIn rin{(const float*)scratch, ns, bias, T, ids, w, counts, offsets, perm,
-                             inv_perm, act};
+                             inv_perm, act, sync, pool->H / 16};
       clear_stale_error();
       e = moe::launch_gate_up_route(pool->fmt, g, u, slot_map, pool->n_slots, E, x, T, k,
                                     pool->H, pool->I, rin, h, err_flags, st);
@@ -604,7 +638,7 @@ static moe_status layer_impl(const moe_pool* pool, const int32_t* slot_map,
         if (s != MOE_OK) return s;
       }
       return down_combine_tail(pool, slot_map, E, T, k, offsets, act, h, inv_perm, w, y, out,
-                               err_flags, path, st);
+                               err_flags, path, st, sync);
     }
     e = moe::launch_router_finish((const float*)scratch, ns, bias, T, E, k, ids, w, counts,
                                   offsets, perm, inv_perm, st);

@@ -199,8 +199,63 @@ struct RouteIn {
   int32_t* perm;
   int32_t* inv_perm;
   int32_t* act;
+  int32_t* tickets;   // the down kernel's per-row-group tickets, zeroed here (NULL: none)
+  int n_tickets;
 };
 __host__ __device__ constexpr int act_ints(int E) { return 1 + kActStride * E; }
+
+// The fused decode layer's down kernel combines without a separate launch: each of a row
+// group's workgroups (one per active expert) stores its y rows with device-coherent
+// stores, waits for them to complete and takes a ticket; the one that draws the last
+// ticket reads the group's y rows back (device-coherent loads) and writes out.
+struct DownTail {
+  const int32_t* inv_perm;   // [T*k]
+  const float* w;            // [T*k]
+  float* out;                // [T][H]
+  int32_t* tickets;          // [H/16], zero on entry
+  int T;
+};
+
+// The fused decode layer (one persistent kernel for the routing, gate/up, down and
+// combine; see gemv.hip) hands each expert's h from its gate/up workgroups to its down
+// workgroups in two levels: the gate/up unit of row group rg of active expert j, once its h
+// rows are stored device-coherently, adds one to counters[j][rg % kHandoffSplit]; the unit
+// that completes a sub-counter (handoff_units of them) adds one to ready[j]; a down unit of
+// expert j waits until ready[j] counts every sub-counter that has units. The sub-counters
+// keep an expert's I/16 atomics from queueing on one address, and the waiting workgroups
+// poll one word per expert, each on a cache line of its own, with a pause between polls:
+// hundreds of workgroups polling every sub-counter back to back slowed the whole launch
+// several times over. Every wait is bounded: after spin_limit polls it gives up and sets
+// bit 1 of err_flags.
+constexpr int kHandoffSplit = 8;
+constexpr int kReadyStride = 32;     // int32 between two experts' ready words (128 bytes)
+constexpr int kSpinLimit = 1 << 15;
+constexpr int kPollSleep = 20;       // s_sleep between two polls (x 64 clocks)
+struct FusedDown {
+  const uint8_t* q;     // down code plane, slot 0
+  const uint8_t* s;     // down scale plane, slot 0
+  int64_t q_slot, s_slot;
+  float* y;             // [T*k][H]
+  float* out;           // [T][H]
+  int32_t* counters;    // [kFuseMaxPairs][kHandoffSplit], zero on entry
+  int32_t* ready;       // [kFuseMaxPairs][kReadyStride] (word 0 used), zero on entry
+  int32_t* tickets;     // [H/16], zero on entry
+  int spin_limit;
+};
+// Gate/up units of an expert counted by sub-counter q: the row groups rg < n_rg with
+// rg % kHandoffSplit == q.
+__host__ __device__ constexpr int handoff_units(int n_rg, int q) {
+  return q < n_rg ? (n_rg - q + kHandoffSplit - 1) / kHandoffSplit : 0;
+}
+// int32 words of the fused layer's synchronisation region: the tickets, the sub-counters,
+// then the ready words
+__host__ __device__ constexpr int sync_ints(int H) {
+  return H / 16 + kFuseMaxPairs * kHandoffSplit + kFuseMaxPairs * kReadyStride;
+}
+
+// s_waitcnt with only vmcnt(0): every vector memory access the wave issued has completed
+// (expcnt and lgkmcnt fields at their no-wait maxima).
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 struct PoolView {
   const uint8_t* q;   // code plane, slot 0

@@ -41,6 +41,15 @@ __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
   return __builtin_nontemporal_load((const u32x4*)p);
 }
 
+// 16 bytes read device-coherently (two agent-scope 8-byte loads): data another workgroup
+// of the same kernel stored with agent-scope stores, possibly on another XCD.
+__device__ __forceinline__ u32x4 ld16_coherent(const void* p) {
+  const uint64_t* q = (const uint64_t*)p;
+  const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32)};
+}
+
 // Find the j-th expert (in expert order) with a non-empty bucket; -1 if there are fewer.
 // *n_active receives the number of non-empty buckets. Every lane of the wave gets both.
 __device__ int find_active_expert(const int32_t* __restrict__ offsets, int E, int j,
@@ -306,19 +315,26 @@ struct LaneMap {
 //   kSrcAct      the small-batch router's active-expert list
 constexpr int kSrcOffsets = 0, kSrcAct = 1;
 
-// RU: chunks per wave per batch (kU, or 6 where the row needs no more).
-template <int FMT, bool GATED, int SRC, int NT, int RU = kU>
+// RU: chunks per wave per batch (kU, or fewer where the row needs no more).
+// TICKET (down projection from the active list, every expert's pairs within NT <= 4): the
+// workgroups of a row group, one per active expert, finish with the combine of that row
+// group (DownTail): wave 0 stores the unit's y rows device-coherently, waits for them and
+// takes the row group's ticket; the last one to draw reads every pair's y row back and
+// writes out[t] = sum_j w[t, j] y[inv_perm[t k + j]] in increasing j, as k_combine does.
+template <int FMT, bool GATED, int SRC, int NT, int RU = kU, bool TICKET = false>
 __global__ __launch_bounds__(kGThreads) void k_gemv(
     const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as, int64_t a_qslot,
     int64_t a_sslot, const uint8_t* __restrict__ bq, const uint8_t* __restrict__ bs,
     const int32_t* __restrict__ slot_map, int n_slots, int E,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm, int k,
     const uint16_t* __restrict__ src, int K, int rows, uint16_t* __restrict__ h_out,
-    float* __restrict__ y_out, uint32_t* __restrict__ err_flags, const int32_t* __restrict__ act) {
+    float* __restrict__ y_out, uint32_t* __restrict__ err_flags, const int32_t* __restrict__ act,
+    DownTail tail) {
+  static_assert(!TICKET || (!GATED && SRC == kSrcAct && NT <= 4), "ticket combine: down, <= 4 pairs");
   using LM = LaneMap<FMT>;
   constexpr int kM = GATED ? 2 : 1;
   constexpr int kSlice = kGWaves * RU * LM::kKPerChunk;   // K elements staged per batch
-  static_assert(NT * (kSlice / 8) % kGThreads == 0, "whole 16-byte pieces per thread");
+  constexpr int kSlicePieces = NT * (kSlice / 8);   // 16-byte pieces staged per batch
   __shared__ __attribute__((aligned(16))) uint16_t xs[NT][kSlice];
   __shared__ float red[kGWaves][NT][kM][16];
   const int lane = threadIdx.x & (kWave - 1);
@@ -326,10 +342,11 @@ __global__ __launch_bounds__(kGThreads) void k_gemv(
   const int rg = blockIdx.x;
   int e, lo, hi, slot;
   int atok[4] = {0, 0, 0, 0};
+  int n_act = 0;
   if constexpr (SRC == kSrcAct) {
     // the small-batch router's active list: one round trip for expert, slot, range, tokens
     const int32_t* a = act + 1 + kActStride * blockIdx.y;
-    const int n_act = act[0];
+    n_act = act[0];
     e = a[0];
     slot = a[1];
     lo = a[2];
@@ -350,6 +367,8 @@ __global__ __launch_bounds__(kGThreads) void k_gemv(
     for (int i = threadIdx.x; i < (hi - lo) * 16; i += kGThreads) {
       const int pos = lo + i / 16, r = r0 + i % 16;
       if (GATED) h_out[(int64_t)pos * rows + r] = 0;
+      else if (TICKET) __hip_atomic_store(&y_out[(int64_t)pos * rows + r], 0.f, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);   // wave 0 (<= 64 values)
       else y_out[(int64_t)pos * rows + r] = 0.f;
     }
     if (threadIdx.x == 0 && err_flags && slot != kSlotMiss) atomicOr(err_flags, 1u);
@@ -398,16 +417,18 @@ __global__ __launch_bounds__(kGThreads) void k_gemv(
       for (int cbase = 0; cbase < nc; cbase += kGWaves * RU) {
         // 1. the batch's K range of every token's activation row (L2-resident): loads first,
         //    LDS writes after the weight loads are issued
-        constexpr int kPieces = NT * (kSlice / 8) / kGThreads;   // 16-byte pieces per thread
+        // 16-byte pieces per thread (threads past the slice's pieces stage none)
+        constexpr int kPieces = (kSlicePieces + kGThreads - 1) / kGThreads;
         const int k0 = cbase * LM::kKPerChunk;
         u32x4 xp[kPieces];
         bool xok[kPieces];
 #pragma unroll
         for (int it = 0; it < kPieces; ++it) {
-          const int idx = threadIdx.x + it * kGThreads;
+          const int idx0 = threadIdx.x + it * kGThreads;
+          const int idx = idx0 < kSlicePieces ? idx0 : 0;
           const int i = idx / (kSlice / 8), q = idx % (kSlice / 8);
           const int kk = k0 + q * 8;
-          xok[it] = c0 + i < hi && kk < K;
+          xok[it] = idx0 < kSlicePieces && c0 + i < hi && kk < K;
           xp[it] = ld16(xrow[i] + (xok[it] ? kk : 0));
         }
         // 2. this wave's weight chunks of the batch, all in flight at once
@@ -430,7 +451,7 @@ __global__ __launch_bounds__(kGThreads) void k_gemv(
         for (int it = 0; it < kPieces; ++it) {
           const int idx = threadIdx.x + it * kGThreads;
           const int i = idx / (kSlice / 8), q = idx % (kSlice / 8);
-          *(u32x4*)&xs[i][q * 8] = xok[it] ? xp[it] : u32x4{0, 0, 0, 0};
+          if (idx < kSlicePieces) *(u32x4*)&xs[i][q * 8] = xok[it] ? xp[it] : u32x4{0, 0, 0, 0};
         }
         __syncthreads();
         // 3. consume (chunks past the end of the row carry a zero scale and add nothing)
@@ -535,10 +556,41 @@ __global__ __launch_bounds__(kGThreads) void k_gemv(
             v[m] = sum;
           }
           if constexpr (GATED) h_out[(int64_t)pos * rows + r0 + r] = f32_to_bf16_rne(silu_mul(v[0], v[1]));
+          else if constexpr (TICKET)
+            __hip_atomic_store(&y_out[(int64_t)pos * rows + r0 + r], v[0], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
           else y_out[(int64_t)pos * rows + r0 + r] = v[0];
         }
       }
       __syncthreads();
+    }
+  }
+  if constexpr (TICKET) {
+    // wave 0 holds every y store of this unit: once they have completed, the row group's
+    // ticket; the workgroup that draws ticket n_act - 1 is the last of the group
+    if (wave != 0) return;
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    int ticket = 0;
+    if (lane == 0)
+      ticket = __hip_atomic_fetch_add(&tail.tickets[rg], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    ticket = __builtin_amdgcn_readfirstlane(ticket);
+    if (ticket != n_act - 1) return;
+    if (lane < tail.T * 16) {
+      const int t = lane >> 4, r = lane & 15;
+      float yv[kMaxK], wv[kMaxK];
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j) {   // every load issued before the first use
+        const int p = t * k + (j < k ? j : 0);
+        const int pos = tail.inv_perm[p];
+        wv[j] = tail.w[p];
+        yv[j] = __hip_atomic_load(&y_out[(int64_t)pos * rows + r0 + r], __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+      }
+      float a = 0.f;
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j)
+        if (j < k) a = fmaf(wv[j], yv[j], a);
+      tail.out[(int64_t)t * rows + r0 + r] = a;
     }
   }
 }
@@ -804,13 +856,24 @@ __global__ __launch_bounds__(kDCWaves * kWave) void k_down_small(
 // launch picks, for every format, whichever of 4, 6 and the format's default leaves the
 // fewest masked slots in the row's batches (the larger on a tie); some masked slots may
 // remain (gpt-oss MXFP4: 23 chunks in 24 slots).
-template <int FMT, int NT, int RU = 0>
+//
+// RUD > 0: the fused decode layer. The workgroups stay for the down projection and the
+// combine: each gate/up unit stores its h rows device-coherently and then counts itself
+// done for its expert (FusedDown); after its gate/up units a workgroup serves down units
+// (16-row group of out, active expert) v = blockIdx.x, + gridDim.x, ...: it issues the
+// unit's first batch of down weights (RUD chunks per wave), waits until every gate/up unit
+// of the expert is done, reads the expert's h rows device-coherently and finishes as the
+// ticket-combining down kernel does (k_gemv with TICKET). The grid must fit on the device
+// at once (the launcher caps it at the co-resident workgroup count), since a down unit
+// waits on gate/up units of other workgroups; the waits are bounded (FusedDown).
+template <int FMT, int NT, int RU = 0, int RUD = 0>
 __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
     const uint8_t* __restrict__ gq, const uint8_t* __restrict__ gsc,
     const uint8_t* __restrict__ uq, const uint8_t* __restrict__ usc, int64_t qslot,
     int64_t sslot, const int32_t* __restrict__ slot_map, int n_slots, int E, int k,
     const uint16_t* __restrict__ x, int H, int I, uint16_t* __restrict__ h_out,
-    uint32_t* __restrict__ err_flags, RouteIn rin) {
+    uint32_t* __restrict__ err_flags, RouteIn rin, FusedDown fd) {
+  constexpr bool kFused = RUD > 0;
   using LM = LaneMap<FMT>;
   typedef int i32x4 __attribute__((ext_vector_type(4)));
   __shared__ __attribute__((aligned(16))) uint16_t xs[NT * kRouteMaxH];
@@ -824,7 +887,6 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
   __shared__ unsigned long long hit_l[kMaxE / 64];
   __shared__ int act_l[kFuseMaxPairs][kActStride];
   __shared__ int nact_l;
-  __shared__ int rank_l[kMaxE];
   __shared__ float red[kGWaves][NT][2][16];
   // Q4_K: the block sums of the tokens' activation rows, shared by every row of every unit
   __shared__ float xsum_l[kquant(FMT) ? NT * kRouteMaxH / 32 * sums_per_block(FMT) : 1];
@@ -848,7 +910,6 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
   for (int r = 0; r < kXP; ++r)
     xv[r] = *(const u32x4*)(x + (int64_t)min(tid + r * kGThreads, xp_n - 1) * 8);
   if (tid < kMaxE / 64) hit_l[tid] = 0ull;
-  if (tid < kMaxE) rank_l[tid] = 0;
   if (tid < E) slot_l[tid] = sm;
   if (tid < TE) lg_l[tid] = finish_logit(v, ns, bz);
 #pragma unroll
@@ -922,76 +983,59 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
       if (lane == 0) nact_l = nact;
     }
   };
-  // 2'. one token: lane l holds the keys of experts l, l + 64, ... (SLOTS of them). Every
-  //     wave counts, for each of those keys, the keys above it among lanes [16 w, 16 w + 16)
-  //     of every slot (broadcast with readlane); the four counts meet in rank_l. Same keys
-  //     and ranks as wave_topk_softmax, so the same choices and order.
+  // 2'. one token, by wave 0 alone in registers: k rounds of a wave-wide maximum over the
+  //     unique keys of wave_topk_softmax (each round takes the largest remaining key, which
+  //     is the key of rank r: the same choices in the same order), then the softmax of the
+  //     chosen logits exactly as wave_softmax_chosen computes it.
   // 3'. the k pairs of the one token (distinct experts): pair j goes to position
   //     #{j' : e_j' < e_j}, and is its expert's only pair.
   auto route_one_token = [&](auto slots) {
     constexpr int SLOTS = decltype(slots)::value;
-    float v[SLOTS];
+    if (wave != 0) return;
     uint64_t key[SLOTS];
-    int r[SLOTS];
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) {
       const int e = s * kWave + lane;
       float x = e < E ? lg_l[e] : -INFINITY;
       x = (x != x) ? -INFINITY : x;
-      v[s] = x;
       key[s] = e < E ? topk_key(x, e) : 0ull;
-      r[s] = 0;
     }
-    constexpr int kPerWave = kWave / kGWaves;
+    uint64_t mine = 0ull;   // lane r < k: the key chosen in round r
+    for (int r = 0; r < k; ++r) {
+      uint64_t m = key[0];
 #pragma unroll
-    for (int sc = 0; sc < SLOTS; ++sc) {
-      const uint32_t key_hi = (uint32_t)(key[sc] >> 32), key_lo = (uint32_t)key[sc];
+      for (int s = 1; s < SLOTS; ++s) m = umax64(m, key[s]);
+      m = wave_max_u64(m);
+      mine = lane == r ? m : mine;
 #pragma unroll
-      for (int q = 0; q < kPerWave; ++q) {
-        const int c = wave * kPerWave + q;
-        // readlane returns a signed int: widen each half as unsigned
-        const uint64_t kc =
-            ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)key_hi, c) << 32) |
-            (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)key_lo, c);
-#pragma unroll
-        for (int s = 0; s < SLOTS; ++s) r[s] += kc > key[s] ? 1 : 0;
-      }
+      for (int s = 0; s < SLOTS; ++s) key[s] = key[s] == m ? 0ull : key[s];
     }
-#pragma unroll
-    for (int s = 0; s < SLOTS; ++s) atomicAdd(&rank_l[s * kWave + lane], r[s]);
-    __syncthreads();
-    if (wave == 0) {
-#pragma unroll
-      for (int s = 0; s < SLOTS; ++s) {
-        const int e = s * kWave + lane;
-        const int rank = rank_l[e];
-        if (e < E && rank < k) {
-          ids_l[rank] = e;
-          tk_l[0].zs[rank] = v[s];
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-      wave_softmax_chosen(tk_l[0].zs, k, w_l);
-      const int ej = lane < k ? ids_l[lane] : 0x7fffffff;
-      int pos = 0;
-      for (int q = 0; q < k; ++q) pos += __builtin_amdgcn_readlane(ej, q) < ej ? 1 : 0;
-      if (lane < k) {
-        perm_l[pos] = lane;
-        inv_l[lane] = pos;
-        int* a = act_l[pos];
-        a[0] = ej;
-        a[1] = slot_l[ej];
-        a[2] = pos;
-        a[3] = pos + 1;
-        a[4] = 0;
-        a[5] = -1;
-        a[6] = -1;
-        a[7] = -1;
-      }
-      if (lane == 0) nact_l = k;
+    const int ej = lane < k ? key_index(mine) : 0x7fffffff;
+    // the value the key orders by: the logit itself, except that -0 comes back as +0,
+    // which gives the same differences below
+    const float val = lane < k ? key_value(mine) : 0.f;
+    const float l0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(val), 0));
+    const float z = lane < k ? expf(val - l0) : 0.f;
+    float sum = 0.f;
+    for (int j = 0; j < k; ++j) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), j));
+    int pos = 0;
+    for (int q = 0; q < k; ++q) pos += __builtin_amdgcn_readlane(ej, q) < ej ? 1 : 0;
+    if (lane < k) {
+      ids_l[lane] = ej;
+      w_l[lane] = z / sum;
+      perm_l[pos] = lane;
+      inv_l[lane] = pos;
+      int* a = act_l[pos];
+      a[0] = ej;
+      a[1] = slot_l[ej];
+      a[2] = pos;
+      a[3] = pos + 1;
+      a[4] = 0;
+      a[5] = -1;
+      a[6] = -1;
+      a[7] = -1;
     }
+    if (lane == 0) nact_l = k;
   };
   if constexpr (NT == 1) {   // NT == 1 means T == 1
     if (E <= kWave) route_one_token(std::integral_constant<int, 1>{});
@@ -1021,6 +1065,8 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
     }
     for (int i = tid; i < na * kActStride; i += kGThreads) rin.act[1 + i] = (&act_l[0][0])[i];
     if (tid == 0) rin.act[0] = na;
+    if (!kFused && rin.tickets != nullptr)   // the down kernel's tickets start at zero
+      for (int i = tid; i < rin.n_tickets; i += kGThreads) rin.tickets[i] = 0;
   }
   // 4. the workgroup's units u = blockIdx.x, + gridDim.x, ...: unit u is row group
   //    u % n_rg of active expert u / n_rg (the routing above is paid once per workgroup)
@@ -1041,10 +1087,30 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
     const int lo = min(max(act_l[j][2], 0), n);
     const int np = min(max(act_l[j][3] - lo, 0), min(NT, n - lo));
     const int r0 = rg * 16;
+    // fused: once wave 0's h stores of the unit have completed, the unit counts itself
+    // done for its expert
+    auto publish = [&]() {
+      if (kFused && wave == 0) {
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        if (lane == 0) {
+          // the unit that completes its sub-counter adds one to the expert's ready count
+          const int q = rg % kHandoffSplit;
+          const int old = __hip_atomic_fetch_add(&fd.counters[j * kHandoffSplit + q], 1,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (old == handoff_units(n_rg, q) - 1)
+            __hip_atomic_fetch_add(&fd.ready[j * kReadyStride], 1, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    };
     if (slot < 0 || slot >= n_slots) {
-      for (int i = tid; i < np * 16; i += kGThreads)
-        h_out[(int64_t)(lo + i / 16) * I + r0 + i % 16] = 0;
+      for (int i = tid; i < np * 16; i += kGThreads) {   // wave 0: np * 16 <= 64
+        uint16_t* dst = &h_out[(int64_t)(lo + i / 16) * I + r0 + i % 16];
+        if constexpr (kFused) __hip_atomic_store(dst, (uint16_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else *dst = 0;
+      }
       if (tid == 0 && err_flags && slot != kSlotMiss) atomicOr(err_flags, 1u);
+      publish();
       continue;
     }
     // stream this row group of the expert's gate and up rows
@@ -1181,10 +1247,207 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
           g += red[q][i][0][r];
           u += red[q][i][1][r];
         }
-        h_out[(int64_t)(lo + i) * I + r0 + r] = f32_to_bf16_rne(silu_mul(g, u));
+        const uint16_t hv = f32_to_bf16_rne(silu_mul(g, u));
+        uint16_t* dst = &h_out[(int64_t)(lo + i) * I + r0 + r];
+        if constexpr (kFused) __hip_atomic_store(dst, hv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else *dst = hv;
       }
     }
+    publish();
     __syncthreads();   // red is rewritten by the next unit
+  }
+  if constexpr (kFused) {
+    // ---- down units v = blockIdx.x, + gridDim.x, ...: row group v % n_rgh of out, active
+    //      expert v / n_rgh. The staged activation rows are no longer needed: xs now holds
+    //      a batch's K slice of the unit's h rows, [NT][kSliceD].
+    constexpr int kSliceD = kGWaves * RUD * LM::kKPerChunk;
+    static_assert(NT * kSliceD <= NT * kRouteMaxH, "an h slice fits in the activation rows");
+    constexpr int kSlicePieces = NT * (kSliceD / 8);
+    constexpr int kPieces = (kSlicePieces + kGThreads - 1) / kGThreads;
+    constexpr bool kMmaD = mma_path(FMT, NT);
+    const int n_rgh = H / 16;
+    const int nbd = I / 32;
+    const int ncd = (nbd + LM::kBlocksPerChunk - 1) / LM::kBlocksPerChunk;
+    const int n_rgi = I / 16;   // gate/up units of an expert
+    uint16_t* hs = xs;
+    __syncthreads();   // every wave is past its last read of the activation rows
+    for (int v = blockIdx.x;; v += gridDim.x) {
+      const int j = v / n_rgh;
+      if (j >= na) break;
+      const int rg = v % n_rgh;
+      const int slot = act_l[j][1];
+      const int lo = min(max(act_l[j][2], 0), n);
+      const int np = min(max(act_l[j][3] - lo, 0), min(NT, n - lo));
+      const int r0 = rg * 16;
+      const bool valid = slot >= 0 && slot < n_slots;
+      float acc[NT];
+      f32x4 acc4 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < NT; ++i) acc[i] = 0.f;
+      if (valid) {
+        const int64_t unit0 = (int64_t)rg * nbd * 16;
+        const uint8_t* qa = fd.q + slot * fd.q_slot + unit0 * cb + lane * 16;
+        const uint8_t* sa = fd.s + slot * fd.s_slot + (unit0 + lane_unit) * sb;
+        const uint8_t* sa2 = super_base<FMT>(fd.s + slot * fd.s_slot, H, I, rg, lane);
+        const uint8_t* ha = hi_base<FMT>(fd.q + slot * fd.q_slot, H, I, unit0 + lane);
+        for (int cbase = 0; cbase < ncd; cbase += kGWaves * RUD) {
+          // 1. this wave's weight chunks of the batch (they do not depend on h)
+          Chunk ca[RUD];
+#pragma unroll
+          for (int u = 0; u < RUD; ++u) {
+            const int c = cbase + wave + kGWaves * u;
+            const int b = c * LM::kBlocksPerChunk + lblk;
+            const bool ok = c < ncd && b < nbd;
+            const int cs = ok ? c : 0;
+            load_chunk<FMT>(ca[u], qa + (int64_t)cs * 1024, sa + (int64_t)cs * LM::kScaleChunk,
+                            sa2 + (int64_t)(cs >> 1) * 64, ha + (int64_t)cs * LM::kHiChunk, ok);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          // 2. first batch: wait until every gate/up unit of expert j has published its h
+          if (cbase == 0) {
+            if (tid == 0) {
+              const int need = min(kHandoffSplit, n_rgi);   // sub-counters with units
+              for (int spins = 0;; ++spins) {
+                const int got = __hip_atomic_load(&fd.ready[j * kReadyStride], __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+                if (got >= need) break;
+                if (spins >= fd.spin_limit) {
+                  if (err_flags) atomicOr(err_flags, 2u);
+                  break;
+                }
+                __builtin_amdgcn_s_sleep(kPollSleep);
+              }
+            }
+            __syncthreads();
+          }
+          // 3. the batch's K slice of the unit's h rows (device-coherent: stored by other
+          //    workgroups of this launch), then into LDS
+          const int k0 = cbase * LM::kKPerChunk;
+          u32x4 xp[kPieces];
+          bool xok[kPieces];
+#pragma unroll
+          for (int it = 0; it < kPieces; ++it) {
+            const int idx0 = tid + it * kGThreads;
+            const int idx = idx0 < kSlicePieces ? idx0 : 0;
+            const int i = idx / (kSliceD / 8), q = idx % (kSliceD / 8);
+            const int kk = k0 + q * 8;
+            xok[it] = idx0 < kSlicePieces && i < np && kk < I;
+            xp[it] = ld16_coherent(h_out + (int64_t)(lo + (xok[it] ? i : 0)) * I + (xok[it] ? kk : 0));
+          }
+          __syncthreads();   // the previous batch's reads of hs are done
+#pragma unroll
+          for (int it = 0; it < kPieces; ++it) {
+            const int idx = tid + it * kGThreads;
+            const int i = idx / (kSliceD / 8), q = idx % (kSliceD / 8);
+            if (idx < kSlicePieces) *(u32x4*)&hs[i * kSliceD + q * 8] = xok[it] ? xp[it] : u32x4{0, 0, 0, 0};
+          }
+          __syncthreads();
+          // 4. consume, as k_gemv does
+          if constexpr (kMmaD) {
+            const int tm = lane & 15;
+#pragma unroll
+            for (int u = 0; u < RUD; ++u) {
+              const int c = cbase + wave + kGWaves * u;
+              const int xo = (c - cbase) * LM::kKPerChunk + koff;
+              bf16x8 av[4];
+              mma_a(&hs[(tm < NT ? tm : 0) * kSliceD + xo], tm < NT, av);
+              bf16x2 w[LM::kWPairs];
+              widen<FMT>(ca[u], w);
+              acc4 = mma_chunk(w, av, acc4);
+            }
+          } else {
+#pragma unroll
+            for (int u = 0; u < RUD; ++u) {
+              const int c = cbase + wave + kGWaves * u;
+              const int xo = (c - cbase) * LM::kKPerChunk + koff;
+              bf16x2 w[LM::kWPairs];
+              uint32_t xw[LM::kXWords];
+              widen<FMT>(ca[u], w);
+#pragma unroll
+              for (int i = 0; i < NT; ++i) {
+#pragma unroll
+                for (int q = 0; q < LM::kXWords / 4; ++q) {
+                  const u32x4 hq = *(const u32x4*)&hs[i * kSliceD + xo + q * 8];
+                  xw[4 * q + 0] = hq[0];
+                  xw[4 * q + 1] = hq[1];
+                  xw[4 * q + 2] = hq[2];
+                  xw[4 * q + 3] = hq[3];
+                }
+                acc[i] = dot_chunk<FMT>(w, xw, ca[u].ok ? ca[u].s : 0u, ca[u].s2, acc[i]);
+              }
+            }
+          }
+        }
+      } else if (tid == 0 && err_flags && slot != kSlotMiss) {
+        atomicOr(err_flags, 1u);
+      }
+      // 5. lanes that share a row, then the 4 waves in a fixed order (as k_gemv)
+      if constexpr (kMmaD) {
+        if (lane < 16) {
+#pragma unroll
+          for (int i = 0; i < NT; ++i) red[wave][i][0][lane] = acc4[i];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+          float a = acc[i];
+          if constexpr (unit16(FMT)) {
+            a += wave_xor(a, 16);
+            a += wave_xor(a, 32);
+          } else {
+            a += wave_xor(a, 1);
+            a += wave_xor(a, 32);
+          }
+          acc[i] = a;
+        }
+        const bool writer = unit16(FMT) ? (lane < 16) : (lane < 32 && (lane & 1) == 0);
+        if (writer) {
+          const int r = LM::row(lane);
+#pragma unroll
+          for (int i = 0; i < NT; ++i) red[wave][i][0][r] = acc[i];
+        }
+      }
+      __syncthreads();
+      // 6. wave 0: y rows (device-coherent), the row group's ticket, and the combine by the
+      //    workgroup that draws the last one
+      if (wave == 0) {
+        if (lane < NT * 16) {
+          const int i = lane / 16, r = lane % 16;
+          if (i < np) {
+            float sum = 0.f;
+            if (valid) {
+              sum = red[0][i][0][r];
+#pragma unroll
+              for (int q = 1; q < kGWaves; ++q) sum += red[q][i][0][r];
+            }
+            __hip_atomic_store(&fd.y[(int64_t)(lo + i) * H + r0 + r], sum, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        int ticket = 0;
+        if (lane == 0)
+          ticket = __hip_atomic_fetch_add(&fd.tickets[rg], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ticket = __builtin_amdgcn_readfirstlane(ticket);
+        if (ticket == na - 1 && lane < T * 16) {
+          const int t = lane >> 4, r = lane & 15;
+          float yv[kMaxK], wv[kMaxK];
+#pragma unroll
+          for (int jj = 0; jj < kMaxK; ++jj) {   // every load issued before the first use
+            const int p = t * k + (jj < k ? jj : 0);
+            wv[jj] = w_l[p];
+            yv[jj] = __hip_atomic_load(&fd.y[(int64_t)inv_l[p] * H + r0 + r], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+          }
+          float a = 0.f;
+#pragma unroll
+          for (int jj = 0; jj < kMaxK; ++jj)
+            if (jj < k) a = fmaf(wv[jj], yv[jj], a);
+          fd.out[(int64_t)t * H + r0 + r] = a;
+        }
+      }
+      __syncthreads();   // red and hs are rewritten by the next unit
+    }
   }
 }
 
@@ -1205,7 +1468,7 @@ hipError_t launch_gemv_t(const PoolView& a, const PoolView& b, const int32_t* sl
 #define MOE_GEMV_CASE(N, R)                                                                     \
   hipLaunchKernelGGL((k_gemv<FMT, GATED, SRC, N, R>), grid, dim3(kGThreads), 0, stream, a.q,    \
                      a.s, a.q_slot, a.s_slot, b.q, b.s, slot_map, n_slots, E, offsets, perm, k, \
-                     src, K, rows, h, y, err, act)
+                     src, K, rows, h, y, err, act, DownTail{})
   // 2 or 4 tokens of a 16-byte-unit format: a batch of 6 chunks per wave when the row
   // needs no more (4 waves share a row), e.g. K = 2880: 23 chunks
   const int need = ((K / 32 + LaneMap<FMT>::kBlocksPerChunk - 1) / LaneMap<FMT>::kBlocksPerChunk +
@@ -1277,7 +1540,7 @@ hipError_t launch_gate_up_route(int fmt, const PoolView& gate, const PoolView& u
 #define MOE_ROUTED_CASE(N, R)                                                                 \
   hipLaunchKernelGGL((k_gate_up_routed<F(), N, R>), grid, dim3(kGThreads), 0, stream, gate.q, \
                      gate.s, up.q, up.s, gate.q_slot, gate.s_slot, slot_map, n_slots, E, k, x, \
-                     H, I, h, err, rin)
+                     H, I, h, err, rin, FusedDown{})
     // one token: a batch of chunks per wave (4 waves share a row) that wastes fewer slots
     // on masked chunks than the format's default (8 chunks; Q4_K 6; Q5_K, Q6_K 4)
     const int bpc = LaneMap<F()>::kBlocksPerChunk;
@@ -1288,14 +1551,65 @@ hipError_t launch_gate_up_route(int fmt, const PoolView& gate, const PoolView& u
     int ru = dflt;
     if (6 < dflt && slots(6) < slots(ru)) ru = 6;
     if (4 < dflt && slots(4) < slots(ru)) ru = 4;
-    if (nt == 1 && ru == 4 && dflt != 4) MOE_ROUTED_CASE(1, 4);
-    else if (nt == 1 && ru == 6 && dflt != 6) MOE_ROUTED_CASE(1, 6);
-    else if (nt == 1) MOE_ROUTED_CASE(1, 0);
+    constexpr int kDflt = F() == kQ4_K ? 6 : (F() == kQ5_K || F() == kQ6_K) ? 4 : kU;
+    bool done = false;
+    if constexpr (kDflt > 4)
+      if (nt == 1 && ru == 4) {
+        MOE_ROUTED_CASE(1, 4);
+        done = true;
+      }
+    if constexpr (kDflt > 6)
+      if (!done && nt == 1 && ru == 6) {
+        MOE_ROUTED_CASE(1, 6);
+        done = true;
+      }
+    if (done) {
+    } else if (nt == 1) MOE_ROUTED_CASE(1, 0);
     else if (nt == 2) MOE_ROUTED_CASE(2, 0);
     else MOE_ROUTED_CASE(4, 0);
 #undef MOE_ROUTED_CASE
     return hipGetLastError();
   });
+}
+
+// Workgroups of `kern` (256 threads) that fit on the stream's device at once.
+hipError_t coresident_wgs(const void* kern, hipStream_t stream, int* out) {
+  int dev = 0;
+  hipError_t e;
+  if (stream != nullptr) {
+    hipDevice_t d = 0;
+    e = hipStreamGetDevice(stream, &d);
+    dev = (int)d;
+  } else {
+    e = hipGetDevice(&dev);
+  }
+  if (e != hipSuccess) return e;
+  int ncu = 0, per_cu = 0;
+  e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kGThreads, 0);
+  if (e != hipSuccess) return e;
+  *out = ncu * per_cu;
+  return hipSuccess;
+}
+
+template <int FMT, int NT, int RU, int RUD>
+hipError_t launch_fused_t(const PoolView& gate, const PoolView& up, const PoolView& down,
+                          const int32_t* slot_map, int n_slots, int E, const uint16_t* x, int T,
+                          int k, int H, int I, const RouteIn& rin, uint16_t* h,
+                          const FusedDown& fd, uint32_t* err, hipStream_t stream) {
+  const void* kern = reinterpret_cast<const void*>(&k_gate_up_routed<FMT, NT, RU, RUD>);
+  int cap = 0;
+  hipError_t e = coresident_wgs(kern, stream, &cap);
+  if (e != hipSuccess) return e;
+  const int n_act = min(E, T * k);
+  const int units = max(I / 16, H / 16) * n_act;
+  const int grid = min(units, cap);
+  if (grid < 1) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((k_gate_up_routed<FMT, NT, RU, RUD>), dim3(grid), dim3(kGThreads), 0, stream,
+                     gate.q, gate.s, up.q, up.s, gate.q_slot, gate.s_slot, slot_map, n_slots, E,
+                     k, x, H, I, h, err, rin, fd);
+  return hipGetLastError();
 }
 
 // One token: its k experts (all distinct) share the 8 waves, kDCWaves / k of them per
@@ -1322,8 +1636,10 @@ void with_pairs_per_expert(int T, Fn&& fn) {
 hipError_t launch_down_gemv(int fmt, const PoolView& down, const int32_t* slot_map, int n_slots,
                             int E, int T, int k, int H, int I, const int32_t* offsets,
                             const uint16_t* h, float* y, uint32_t* err, hipStream_t stream) {
+  // the kernel the fused layer would use for this shape (down_small_preferred), without
+  // the combine, so that the stage calls reproduce the layer bit for bit
   return with_fmt(fmt, [&](auto F) {
-    if (down_combine_small_ok(T, k, E, I)) {   // the fused layer's kernel, without the combine
+    if (down_small_preferred(F(), T, k, E, I)) {
       const bool short_batch = down_short_batch(F(), T, k, I);
       with_pairs_per_expert(T, [&](auto NP) {
         if constexpr (NP() == 1) {
@@ -1348,9 +1664,134 @@ hipError_t launch_down_gemv(int fmt, const PoolView& down, const int32_t* slot_m
   });
 }
 
+bool decode_fused_ok(int T, int H, int E) { return route_fused_ok(T, H, E); }
+
+hipError_t launch_decode_fused(int fmt, const PoolView& gate, const PoolView& up,
+                               const PoolView& down, const int32_t* slot_map, int n_slots, int E,
+                               const uint16_t* x, int T, int k, int H, int I, const RouteIn& rin,
+                               uint16_t* h, float* y, float* out, int32_t* sync, uint32_t* err,
+                               hipStream_t stream) {
+  if (!decode_fused_ok(T, H, E) || rin.T != T || rin.ns != route_fused_split(H) ||
+      gate.q_slot != up.q_slot || gate.s_slot != up.s_slot || sync == nullptr)
+    return hipErrorInvalidValue;
+  RouteIn r = rin;
+  r.tickets = nullptr;   // the sync words were zeroed by the router kernel
+  r.n_tickets = 0;
+  int32_t* counters = sync + H / 16;
+  const FusedDown fd{down.q, down.s, down.q_slot, down.s_slot, y, out, counters,
+                     counters + kFuseMaxPairs * kHandoffSplit, sync, kSpinLimit};
+  const int nt = gemv_nt(fmt, T);
+  return with_fmt(fmt, [&](auto F) -> hipError_t {
+    constexpr int FMT = F();
+    // gate/up batch: as launch_gate_up_route chooses it
+    const int bpc = LaneMap<FMT>::kBlocksPerChunk;
+    const int need = ((H / 32 + bpc - 1) / bpc + kGWaves - 1) / kGWaves;
+    const int dflt = FMT == kQ4_K ? 6 : (FMT == kQ5_K || FMT == kQ6_K) ? 4 : kU;
+    auto slots = [](int nd, int ru) { return (nd + ru - 1) / ru * ru; };
+    int ru = dflt;
+    if (6 < dflt && slots(need, 6) < slots(need, ru)) ru = 6;
+    if (4 < dflt && slots(need, 4) < slots(need, ru)) ru = 4;
+    // down batch: 2, 6 or 8 (k-quants: 2, 6 / 2, 4), the fewest masked slots
+    const int needd = ((I / 32 + bpc - 1) / bpc + kGWaves - 1) / kGWaves;
+    const int rud_max = FMT == kQ4_K ? 6 : (FMT == kQ5_K || FMT == kQ6_K) ? 4 : 8;
+    int rud = rud_max;
+    if (6 < rud_max && slots(needd, 6) < slots(needd, rud)) rud = 6;
+    if (slots(needd, 2) < slots(needd, rud)) rud = 2;
+    auto go = [&](auto NTc, auto RUc) -> hipError_t {
+      constexpr int NT = decltype(NTc)::value, RU = decltype(RUc)::value;
+      if (rud == 2)
+        return launch_fused_t<FMT, NT, RU, 2>(gate, up, down, slot_map, n_slots, E, x, T, k, H, I,
+                                              r, h, fd, err, stream);
+      if constexpr (FMT == kQ5_K || FMT == kQ6_K) {
+        return launch_fused_t<FMT, NT, RU, 4>(gate, up, down, slot_map, n_slots, E, x, T, k, H, I,
+                                              r, h, fd, err, stream);
+      } else {
+        if (rud == 6 || FMT == kQ4_K)
+          return launch_fused_t<FMT, NT, RU, 6>(gate, up, down, slot_map, n_slots, E, x, T, k, H,
+                                                I, r, h, fd, err, stream);
+        if constexpr (FMT != kQ4_K)
+          return launch_fused_t<FMT, NT, RU, 8>(gate, up, down, slot_map, n_slots, E, x, T, k, H,
+                                                I, r, h, fd, err, stream);
+        return hipErrorInvalidValue;
+      }
+    };
+    using I1 = std::integral_constant<int, 1>;
+    constexpr int kDflt = FMT == kQ4_K ? 6 : (FMT == kQ5_K || FMT == kQ6_K) ? 4 : kU;
+    if (nt == 1) {   // only the batches that can differ from the default are instantiated
+      if constexpr (kDflt > 4)
+        if (ru == 4) return go(I1{}, std::integral_constant<int, 4>{});
+      if constexpr (kDflt > 6)
+        if (ru == 6) return go(I1{}, std::integral_constant<int, 6>{});
+      return go(I1{}, std::integral_constant<int, 0>{});
+    }
+    if (nt == 2) return go(std::integral_constant<int, 2>{}, std::integral_constant<int, 0>{});
+    return go(std::integral_constant<int, 4>{}, std::integral_constant<int, 0>{});
+  });
+}
+
+bool down_ticket_ok(int T, int k, int E) {
+  return T >= 1 && T <= kFuseMaxT && k >= 1 && k <= kMaxK && E >= 1;
+}
+
+hipError_t launch_down_ticket(int fmt, const PoolView& down, int n_slots, int E, int T, int k,
+                              int H, int I, const int32_t* act, const uint16_t* h,
+                              const int32_t* inv_perm, const float* topk_w, float* y,
+                              float* out, int32_t* tickets, uint32_t* err, hipStream_t stream) {
+  if (!down_ticket_ok(T, k, E) || tickets == nullptr) return hipErrorInvalidValue;
+  const DownTail tail{inv_perm, topk_w, out, tickets, T};
+  // one workgroup per (16-row group of out, active expert): at most min(E, T k) experts
+  dim3 grid(H / 16, min(E, T * k));
+  return with_fmt(fmt, [&](auto F) {
+    constexpr int FMT = F();
+    // chunks per wave per batch: of the sizes the format's registers allow, the one that
+    // leaves the fewest masked slots in the row's batches (the larger on a tie)
+    const int bpc = LaneMap<FMT>::kBlocksPerChunk;
+    const int need = ((I / 32 + bpc - 1) / bpc + kGWaves - 1) / kGWaves;
+    const int ru_max = FMT == kQ4_K ? 6 : (FMT == kQ5_K || FMT == kQ6_K) ? 4 : 8;
+    auto slots = [&](int ru) { return (need + ru - 1) / ru * ru; };
+    int ru = ru_max;
+    for (int c = ru_max - 2; c >= 2; c -= 2)
+      if (slots(c) < slots(ru)) ru = c;
+#define MOE_DT_CASE(N, R)                                                                     \
+  hipLaunchKernelGGL((k_gemv<FMT, false, kSrcAct, N, R, true>), grid, dim3(kGThreads), 0,     \
+                     stream, down.q, down.s, down.q_slot, down.s_slot, nullptr, nullptr,      \
+                     nullptr, n_slots, E, nullptr, nullptr, k, h, I, H, nullptr, y, err, act, \
+                     tail)
+    auto go = [&](auto NTc) {
+      constexpr int NT = decltype(NTc)::value;
+      if (ru == 2) MOE_DT_CASE(NT, 2);
+      else if (ru == 4) MOE_DT_CASE(NT, 4);
+      else if constexpr (FMT != kQ5_K && FMT != kQ6_K) {
+        if (ru == 6) MOE_DT_CASE(NT, 6);
+        else if constexpr (FMT != kQ4_K) MOE_DT_CASE(NT, 8);
+      }
+    };
+    if (T <= 1) go(std::integral_constant<int, 1>{});
+    else if (T <= 2) go(std::integral_constant<int, 2>{});
+    else go(std::integral_constant<int, 4>{});
+#undef MOE_DT_CASE
+    return hipGetLastError();
+  });
+}
+
 bool down_combine_small_ok(int T, int k, int E, int I) {
   const int np = T * k;
   return np >= 1 && np <= kDCMaxPairs && (int64_t)np * I <= kDCMaxH && min(E, np) <= kDCWaves;
+}
+
+// The small-batch down kernel gives each workgroup a 16-row group of every active expert;
+// where that is at most kDCPreferBytes of weights it beats one workgroup per (row group,
+// expert) with the ticket combine, whose tail of device-scope round trips (y stores, the
+// ticket, y loads) outweighs its finer split: measured, Qwen-A3B-shaped (52 KB per
+// workgroup) 55.5 K against 48.7 K tokens/s; GPT-OSS-shaped (98 KB) even; Mixtral-shaped
+// Q8_0 (487 KB) 13.5 K against 13.8 K, Q4_K (258 KB) 18.1 K against 19.0 K.
+constexpr int64_t kDCPreferBytes = 128 << 10;
+bool down_small_preferred(int fmt, int T, int k, int E, int I) {
+  if (!down_combine_small_ok(T, k, E, I)) return false;
+  const int64_t per_block = code_bytes_per_block(fmt) + scale_bytes_per_block(fmt) +
+                            hi_bytes_per_block(fmt);
+  const int64_t bytes = (int64_t)16 * min(E, T * k) * (I / 32) * per_block;
+  return bytes <= kDCPreferBytes;
 }
 
 hipError_t launch_down_combine_small(int fmt, const PoolView& down, int n_slots, int E, int T,

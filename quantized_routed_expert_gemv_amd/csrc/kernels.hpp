@@ -33,8 +33,11 @@ hipError_t launch_route_small(const uint16_t* x, const uint16_t* wr, const float
 // (launch_gate_up_route). For 1 <= T <= 4, T*E <= 256 and at least 2 slices.
 bool route_fused_ok(int T, int H, int E);
 int route_fused_split(int H);
+// sync (nullable): n_sync int32 that the launch zeroes (the fused decode layer's
+// synchronisation words).
 hipError_t launch_router_partials(const uint16_t* x, const uint16_t* wr, int T, int H, int E,
-                                  int ns, float* partial, hipStream_t stream);
+                                  int ns, float* partial, hipStream_t stream,
+                                  int32_t* sync = nullptr, int n_sync = 0);
 // The partials finished by one workgroup (same order as the fused gate/up kernel), with
 // or without the counting sort.
 hipError_t launch_router_finish(const float* partial, int ns, const float* bias, int T, int E,
@@ -65,10 +68,32 @@ hipError_t launch_gate_up_route(int fmt, const PoolView& gate, const PoolView& u
 // Down projection + combine in one launch for T*k <= 8 (down_combine_small_ok); needs the
 // small-batch router's active-expert list.
 bool down_combine_small_ok(int T, int k, int E, int I);
+// Whether the small-batch down kernel (rather than one workgroup per row group and expert)
+// serves this shape: both the fused layer's tail and the stage down call follow it.
+bool down_small_preferred(int fmt, int T, int k, int E, int I);
 hipError_t launch_down_combine_small(int fmt, const PoolView& down, int n_slots, int E, int T,
                                      int k, int H, int I, const int32_t* act, const uint16_t* h,
                                      const int32_t* inv_perm, const float* topk_w, float* y,
                                      float* out, uint32_t* err, hipStream_t stream);
+// Down projection + combine for the fused decode layer (1 <= T <= 4): one workgroup per
+// (16-row group, active expert) of the gate/up kernel's active list; the last workgroup
+// of each row group (by ticket) writes out. tickets: int32 [H/16], zeroed by the routed
+// gate/up kernel of the same call.
+// The fused decode layer (1 <= T <= 4, as route_fused_ok): after the router's partials,
+// one persistent kernel finishes the routing, computes gate/up + SwiGLU, the down projection
+// and the combine (k_gate_up_routed with a down phase). sync: sync_ints(H) int32, zeroed by
+// launch_router_partials of the same call.
+bool decode_fused_ok(int T, int H, int E);
+hipError_t launch_decode_fused(int fmt, const PoolView& gate, const PoolView& up,
+                               const PoolView& down, const int32_t* slot_map, int n_slots, int E,
+                               const uint16_t* x, int T, int k, int H, int I, const RouteIn& rin,
+                               uint16_t* h, float* y, float* out, int32_t* sync, uint32_t* err,
+                               hipStream_t stream);
+bool down_ticket_ok(int T, int k, int E);
+hipError_t launch_down_ticket(int fmt, const PoolView& down, int n_slots, int E, int T, int k,
+                              int H, int I, const int32_t* act, const uint16_t* h,
+                              const int32_t* inv_perm, const float* topk_w, float* y,
+                              float* out, int32_t* tickets, uint32_t* err, hipStream_t stream);
 hipError_t launch_gate_up_grouped(int fmt, const PoolView& gate, const PoolView& up,
                                   const int32_t* slot_map, int n_slots, int E, const uint16_t* x,
                                   int T, int k, int H, int I, const int32_t* offsets,

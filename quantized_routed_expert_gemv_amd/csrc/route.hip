@@ -158,7 +158,8 @@ __global__ __launch_bounds__(256) void k_router(const uint16_t* __restrict__ x,
 template <int NF>
 __global__ __launch_bounds__(kWave) void k_router_part(const uint16_t* __restrict__ x,
                                                        const uint16_t* __restrict__ wr, int T,
-                                                       int H, int E, float* __restrict__ partial) {
+                                                       int H, int E, float* __restrict__ partial,
+                                                       int32_t* __restrict__ sync, int n_sync) {
   // a slice of the fused decode split is at most 2 pairs of steps
   constexpr int RB = router_rb<NF>() < 4 ? router_rb<NF>() : 4;
   const int lane = threadIdx.x;
@@ -206,6 +207,9 @@ __global__ __launch_bounds__(kWave) void k_router_part(const uint16_t* __restric
       }
     }
   }
+  // the next kernel's synchronisation words start at zero
+  if (z == 0)
+    for (int i = lane; i < n_sync; i += kWave) sync[i] = 0;
   // lane holds D[token 4*(lane/16)+v][expert 16f + lane%16]
   float* dst = partial + (int64_t)z * T * E;
 #pragma unroll
@@ -344,12 +348,13 @@ bool route_fused_ok(int T, int H, int E) {
 }
 
 hipError_t launch_router_partials(const uint16_t* x, const uint16_t* wr, int T, int H, int E,
-                                  int ns, float* partial, hipStream_t stream) {
+                                  int ns, float* partial, hipStream_t stream, int32_t* sync,
+                                  int n_sync) {
   if (T < 1 || T > kRouteTok || ns < 2 || ns > kMaxSplit) return hipErrorInvalidValue;
 #define MOE_PART_CASE(N)                                                                     \
   case N:                                                                                   \
     hipLaunchKernelGGL(k_router_part<N>, dim3(ns), dim3(kWave), 0, stream, x, wr, T, H, E,  \
-                       partial);                                                            \
+                       partial, sync, sync != nullptr ? n_sync : 0);                        \
     break;
   switch ((E + 15) / 16) {
     MOE_PART_CASE(1) MOE_PART_CASE(2) MOE_PART_CASE(3) MOE_PART_CASE(4)

@@ -53,7 +53,8 @@ class Pool(ctypes.Structure):
 
 class Ws(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("total", "topk_ids", "topk_w", "counts", "offsets",
-                                               "perm", "inv_perm", "h", "y", "scratch", "act")]
+                                               "perm", "inv_perm", "h", "y", "scratch", "act",
+                                               "sync")]
 
 
 def _setup(lib):
@@ -174,7 +175,7 @@ def test_ffn_and_layer_argument_checks(lib):
     assert lib.moe_layer_workspace(3, 64, 32, 4, 2, ctypes.byref(ws)) == OK
     assert ws.total >= 3 * 2 * (32 * 2 + 64 * 4)
     for name in ("topk_ids", "topk_w", "counts", "offsets", "perm", "inv_perm", "h", "y", "scratch",
-                 "act"):
+                 "act", "sync"):
         assert getattr(ws, name) % 256 == 0
     # workspace too small
     assert g(ctypes.byref(p), FAKE, FAKE, None, FAKE, 3, 4, 2, FAKE, FAKE, ws.total - 1, None, 0,

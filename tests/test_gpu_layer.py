@@ -83,6 +83,43 @@ def test_layer_parity_small(name, path):
     run_layer(synth.CONFIGS[name], path)
 
 
+PERSISTENT = [("gptoss_decode_t1", None), ("gptoss_decode_t4", None), ("gptoss_decode_t4", 2),
+              ("gptoss_decode_t4", 3), ("qwen_a3b_decode", None), ("mixtral_q8_decode", None),
+              ("mixtral_q8_decode", 3), ("qwen_a3b_q4k_decode", None),
+              ("mixtral_q5k_decode", None), ("qwen_a3b_q6k_decode", None), ("tiny", 4)]
+
+
+@pytest.mark.parametrize("name,T", PERSISTENT)
+def test_layer_parity_persistent_decode(name, T):
+    """The persistent decode layer (routing, gate/up, down and combine in one kernel after
+    the router's partials) against the oracle."""
+    cfg = synth.config(name) if T is None else synth.config(name, T=T)
+    print(f"layer {name} T={cfg.T} persistent", flush=True)
+    run_layer(cfg, qm.PATH_PERSISTENT)
+
+
+def test_layer_persistent_invalid_slot_and_repeat():
+    """Persistent path: an out-of-range slot sets bit 0 (bit 1, a timed-out hand-off, must
+    stay clear), contributes nothing, and repeated runs on one workspace are bit-identical."""
+    cfg = synth.config("gptoss_decode_t4", T=2, H=256, I=512)
+    L = make_case(cfg)
+    ids, w, _ = omoe.route(L.x, L.wr, L.bias, cfg.k)
+    pool, x, wr, bias, sm = to_device(L)
+    sm_bad = sm.clone()
+    sm_bad[int(ids[0, 0])] = cfg.E + 5
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out, ws = qm.layer(pool, sm_bad, wr, bias, x, cfg.k, err_flags=err, path=qm.PATH_PERSISTENT)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 1
+    ref = out.clone()
+    for _ in range(3):
+        err.zero_()
+        o, _ = qm.layer(pool, sm_bad, wr, bias, x, cfg.k, workspace=ws, err_flags=err,
+                        path=qm.PATH_PERSISTENT)
+        torch.cuda.synchronize()
+        assert int(err.item()) == 1 and torch.equal(o, ref)
+
+
 @pytest.mark.parametrize("T", [2, 3])
 def test_layer_parity_decode_two_and_three_tokens(T):
     """Decode with fewer tokens than the 4-token kernel's rows (MXFP4 runs them on MFMA with
