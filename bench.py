@@ -59,6 +59,10 @@ def parse():
                     help="staged prefill: every third expert is resident, the others are "
                          "copied each step from a backing store into a window of pool slots "
                          "(plan + copy + mapping rewrite before the expert FFN); eager launches")
+    ap.add_argument("--stage-overlap", action="store_true",
+                    help="with --stage: each layer's plan and copy run on a second stream (default "
+                         "priority), one layer ahead, so they overlap the previous layer's "
+                         "expert FFN; the compute stream waits on an event before the gate/up")
     return ap.parse_args()
 
 
@@ -196,8 +200,12 @@ def run_workload(cfg, args, n_layers, steps, warmup, hip, qm, synth, np, torch, 
         if mode == "graph":
             print("[bench] --stage runs eager", file=sys.stderr, flush=True)
             mode = "eager"
-        timed_calls, copy_ev = staged_calls(qm, torch, layers, staged, outs, cfg, resident,
-                                            window, stream, hip, ev)
+        if args.stage_overlap:
+            timed_calls, copy_ev = staged_overlap_calls(qm, torch, layers, staged, outs, cfg,
+                                                        resident, window, stream, hip, ev)
+        else:
+            timed_calls, copy_ev = staged_calls(qm, torch, layers, staged, outs, cfg, resident,
+                                                window, stream, hip, ev)
         plain_calls = timed_calls
 
     copy_ms = []
@@ -318,7 +326,9 @@ def run_workload(cfg, args, n_layers, steps, warmup, hip, qm, synth, np, torch, 
                          for sc in (False, True))
         moved = 2.0 * window * per_expert
         copy_s = float(np.mean(copy_ms)) * 1e-3
-        res["config"]["staging"] = {"resident": len(resident), "window": window}
+        res["config"]["staging"] = {"resident": len(resident), "window": window,
+                                    "copy": ("second stream, one layer ahead" if args.stage_overlap
+                                             else "in series on the compute stream")}
         res["stage_copy"] = {
             "kernel": "k_stage_copy", "bound": "hbm", "bytes_per_launch": moved,
             "avg_launch_us": round(copy_s * 1e6, 3), "achieved": round(moved / copy_s / 1e9, 1),
@@ -389,6 +399,78 @@ def staged_calls(qm, torch, layers, staged, outs, cfg, resident, window, stream,
             hip.record(ev[li][1], stream.cuda_stream)
             qm.expert_down(pool, sm2, T, k, offsets, h, y=y, stream=stream)
             qm.combine(y, inv, w, out=outs[li], stream=stream)
+        calls.append(call)
+    return calls, copy_ev
+
+
+def staged_overlap_calls(qm, torch, layers, staged, outs, cfg, resident, window, stream, hip,
+                         ev):
+    """Staged prefill with the bulk copy of each layer on a second stream, issued one layer
+    ahead: while the compute stream runs layer l's expert FFN, the copy stream plans and
+    copies layer l+1's window. The plan is made from a count of one per expert (every expert
+    of a large prefill batch has pairs), so it needs no routing of its own and the copy can
+    start before the layer's router runs. Each layer has its own pool, window and rewritten
+    map, so the copy never writes slots a running GEMM reads. The compute stream waits on an
+    event recorded after the layer's copy. Returns one callable per layer (the first also
+    issues layer 0's copy) and the copy events."""
+    T, k, E, H, I = cfg.T, cfg.k, cfg.E, cfg.H, cfg.I
+    dev = outs[0].device
+    i32 = dict(dtype=torch.int32, device=dev)
+    copy_stream = torch.cuda.Stream(device=dev)   # default priority, as the compute stream
+    ids = torch.empty((T, k), **i32)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    counts, offsets = torch.empty(E, **i32), torch.empty(E + 1, **i32)
+    perm, inv = torch.empty(T * k, **i32), torch.empty(T * k, **i32)
+    rs = qm._scratch(qm.route_scratch_bytes(T, H, E), dev)
+    bs = qm._scratch(qm.bucket_scratch_bytes(T, k, E), dev)
+    every = torch.ones(E, **i32)
+    n = len(layers)
+    sm2 = [torch.empty(E, **i32) for _ in range(n)]
+    cl = [torch.empty(E, **i32) for _ in range(n)]
+    cnt = [torch.empty(2, **i32) for _ in range(n)]
+    ready = [hip.create() for _ in range(n)]      # layer's window copied
+    consumed = [hip.create() for _ in range(n)]   # layer's expert FFN done with its window
+    h = torch.empty((T * k, I), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((T * k, H), dtype=torch.float32, device=dev)
+    copy_ev = [(hip.create(), hip.create()) for _ in layers]
+    first = len(resident)
+    lib = hip.lib
+    lib.hipStreamWaitEvent.argtypes = [hip.ct.c_void_p, hip.ct.c_void_p, hip.ct.c_uint]
+
+    def wait(stream_, event):
+        st = lib.hipStreamWaitEvent(hip.ct.c_void_p(stream_.cuda_stream), hip.ct.c_void_p(event), 0)
+        if st != 0:
+            raise RuntimeError(f"hipStreamWaitEvent failed ({st})")
+
+    def issue_copy(li):
+        pool = layers[li][0]
+        backing, sm_res = staged[li]
+        # the previous step's expert FFN of this layer must be done with the window (an event
+        # not yet recorded, as on the first step, is no wait)
+        wait(copy_stream, consumed[li])
+        qm.stage_plan(every, sm_res, first, window, slot_map_out=sm2[li], copy_list=cl[li],
+                      counters=cnt[li], stream=copy_stream)
+        hip.record(copy_ev[li][0], copy_stream.cuda_stream)
+        qm.stage_copy(pool, backing, cl[li], cnt[li], first, window, stream=copy_stream)
+        hip.record(copy_ev[li][1], copy_stream.cuda_stream)
+        hip.record(ready[li], copy_stream.cuda_stream)
+
+    calls = []
+    for li, (pool, x, wr, bias, _) in enumerate(layers):
+        def call(pool=pool, x=x, wr=wr, bias=bias, li=li):
+            if li == 0:
+                issue_copy(0)
+            if li + 1 < n:
+                issue_copy(li + 1)
+            qm.route(x, wr, bias, k, ids=ids, w=w, scratch=rs, stream=stream)
+            qm.bucket(ids, E, counts, offsets, perm, inv, scratch=bs, stream=stream)
+            wait(stream, ready[li])
+            hip.record(ev[li][0], stream.cuda_stream)
+            qm.expert_gate_up(pool, sm2[li], x, k, offsets, perm, h=h, stream=stream)
+            hip.record(ev[li][1], stream.cuda_stream)
+            qm.expert_down(pool, sm2[li], T, k, offsets, h, y=y, stream=stream)
+            qm.combine(y, inv, w, out=outs[li], stream=stream)
+            hip.record(consumed[li], stream.cuda_stream)
         calls.append(call)
     return calls, copy_ev
 

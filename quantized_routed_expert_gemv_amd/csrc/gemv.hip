@@ -1783,8 +1783,8 @@ bool down_combine_small_ok(int T, int k, int E, int I) {
 // where that is at most kDCPreferBytes of weights it beats one workgroup per (row group,
 // expert) with the ticket combine, whose tail of device-scope round trips (y stores, the
 // ticket, y loads) outweighs its finer split: measured, Qwen-A3B-shaped (52 KB per
-// workgroup) 55.5 K against 48.7 K tokens/s; GPT-OSS-shaped (98 KB) even; Mixtral-shaped
-// Q8_0 (487 KB) 13.5 K against 13.8 K, Q4_K (258 KB) 18.1 K against 19.0 K.
+// workgroup) 53.7 K against 48.7 K tokens/s; GPT-OSS-shaped (98 KB) even; Mixtral-shaped
+// Q8_0 (487 KB) 13.5 K against 14.1 K, Q4_K (258 KB) 18.1 K against 19.2 K.
 constexpr int64_t kDCPreferBytes = 128 << 10;
 bool down_small_preferred(int fmt, int T, int k, int E, int I) {
   if (!down_combine_small_ok(T, k, E, I)) return false;

@@ -155,3 +155,64 @@ def test_copy_of_an_expert_outside_the_backing_store_sets_the_flag():
     assert int(err.item()) & 1
     for n, t in pool.planes.items():
         assert torch.equal(t, before[n])
+
+
+def test_staged_layers_with_the_copy_on_a_second_stream():
+    """Staging overlapped with compute: three layers, each with its own pool and window; each
+    layer's plan and copy run on a second stream (default priority) one layer ahead, planned
+    from a count of one per expert, and the compute stream waits on an event before the
+    layer's expert FFN. Every layer equals its all-resident layer bit for bit."""
+    cfg = synth.config("qwen_a3b_prefill", T=384, H=512)
+    E, k, T = cfg.E, cfg.k, cfg.T
+    resident = list(range(0, E, 3))
+    window = E - len(resident)
+    first = len(resident)
+    compute, copier = torch.cuda.Stream(), torch.cuda.Stream()
+    every = torch.ones(E, dtype=torch.int32, device="cuda")
+    layers = []
+    for l in range(3):
+        L, backing, pool, slot_map = _setup_layer(cfg, l, resident, window)
+        layers.append((L, backing, pool, _dev(slot_map)))
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    maps, ready, outs = [], [], []
+    with torch.cuda.stream(copier):
+        for L, backing, pool, smr in layers:
+            sm, cl, cnt = qm.stage_plan(every, smr, first, window, stream=copier)
+            qm.stage_copy(pool, backing, cl, cnt, first, window, err_flags=err, stream=copier)
+            ev = torch.cuda.Event()
+            ev.record(copier)
+            maps.append(sm)
+            ready.append(ev)
+    with torch.cuda.stream(compute):
+        for (L, backing, pool, smr), sm, ev in zip(layers, maps, ready):
+            x = torch.from_numpy(L.x.view(np.int16)).cuda().view(torch.bfloat16)
+            wr = torch.from_numpy(L.wr.view(np.int16)).cuda().view(torch.bfloat16)
+            bias = None if L.bias is None else torch.from_numpy(L.bias).cuda()
+            compute.wait_event(ev)
+            out, _ = qm.layer(pool, sm, wr, bias, x, k, err_flags=err, path=qm.PATH_GROUPED,
+                              stream=compute)
+            ident = torch.arange(E, dtype=torch.int32, device="cuda")
+            full, _ = qm.layer(backing, ident, wr, bias, x, k, path=qm.PATH_GROUPED,
+                               stream=compute)
+            outs.append((out, full))
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    for i, (out, full) in enumerate(outs):
+        assert torch.equal(out, full), f"layer {i}"
+
+
+def _setup_layer(cfg, layer, resident, window):
+    """_setup for another layer of the workload (its own experts, input and slot map)."""
+    L = synth.make_layer(cfg, layer)
+    from parity import margin_fixed_x
+    L.x, _ = margin_fixed_x(cfg, layer)
+    E = cfg.E
+    by_expert = {n: a[L.slot_map] for n, a in L.planes.items()}
+    backing = qm.Pool.from_canonical(cfg.fmt, cfg.H, cfg.I, by_expert)
+    S = len(resident) + window
+    filler = [resident[i] if i < len(resident) else (i * 7 + 3) % E for i in range(S)]
+    pool = qm.Pool.from_canonical(cfg.fmt, cfg.H, cfg.I,
+                                  {n: a[filler] for n, a in by_expert.items()})
+    slot_map = np.full(E, qm.SLOT_MISS, dtype=np.int32)
+    slot_map[resident] = np.arange(len(resident), dtype=np.int32)
+    return L, backing, pool, slot_map
