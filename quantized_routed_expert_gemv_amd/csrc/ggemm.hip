@@ -99,6 +99,7 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
   constexpr int NG = 4 * WN;                  // weight row groups per tile
   constexpr int RPT = BM / 16;                // A rows staged per thread
   static_assert(BM == 64 || BM == 128, "64 or 128 rows per tile");
+  static_assert(FMT != kMXFP4, "MXFP4 runs k_ggemm_mx");
   using BS = BStage<FMT, NG>;
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[BM * kLdsStride];
   // Q8_0 codes are staged already widened to bf16 (2 bytes per code): both waves that
@@ -365,42 +366,7 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
       load_a(c + 1);
       load_b(c + 1);
     }
-    if constexpr (FMT == kMXFP4) {
-      // lane's operand: unit `lane` of its row group's run = block 4c + lane/16 of row lane%16.
-      // FULL: all 4 of the wave's 16-row fragments hold a bucket row; otherwise only the
-      // first nmf do, and the others (past the expert's last pair) run no MFMA at all.
-      auto mx_step = [&](auto full) {
-        constexpr bool kFull = decltype(full)::value;
-        u32x4 bqv[4];
-        float bsc[4];
-#pragma unroll
-        for (int f = 0; f < 4; ++f) {
-          bqv[f] = *(const u32x4*)(lds_bq + fg[f] * BS::kRunQ + lane * 16);
-          // read unconditionally, mask arithmetically (a conditional read becomes a branch)
-          const uint32_t sb = lds_bs[fg[f] * BS::kRunS + lane];
-          const uint32_t keep = (fcol[f] && 4 * c + g4 < nb) ? 0xffffffffu : 0u;
-          bsc[f] = __uint_as_float((sb << 23) & keep);   // E8M0 -> 2^(b-127), or +0
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          bf16x8 bv[4];
-#pragma unroll
-          for (int f = 0; f < 4; ++f) bv[f] = fp4x8_to_bf16x8(bqv[f][i], bsc[f]);
-#pragma unroll
-          for (int mf = 0; mf < 4; ++mf) {
-            if (!kFull && mf >= nmf) continue;
-            const int row = 64 * wm + 16 * mf + mrow;
-            const bf16x8 av = __builtin_bit_cast(
-                bf16x8, *(const u32x4*)(lds_a + row * kLdsStride + (32 * g4 + 8 * i) * 2));
-#pragma unroll
-            for (int f = 0; f < 4; ++f)
-              acc[mf][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[f], acc[mf][f], 0, 0, 0);
-          }
-        }
-      };
-      if (nmf == 4) mx_step(std::true_type{});
-      else if (nmf > 0) mx_step(std::false_type{});
-    } else if constexpr (FMT == kQ6_K) {
+    if constexpr (FMT == kQ6_K) {
       // per block: lanes g = 0, 1 supply K 0..15 (half 0), g = 2, 3 K 16..31 (half 1). A
       // with the other half's lanes zeroed gives each half its own MFMAs: codes as low
       // nibbles plus 16 x the high part (two MFMAs into one sum), and the half's row sums
@@ -582,9 +548,228 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
   }
 }
 
-// MXFP4 tiles are 64 rows x 256 weight rows: its B is the smallest per weight, so a wider
-// tile cuts the A (activation) bytes that each CU pulls in per flop.
-constexpr int kMxfp4BM = 64;
+// Zeros that the MXFP4 kernel's LDS loads read for A pieces past K.
+__device__ __attribute__((aligned(16))) uint32_t g_zero16[4];
+
+// MXFP4 grouped GEMM with its tiles loaded straight into LDS (gfx950 global_load_lds_dwordx4:
+// 64 lanes x 16 bytes land contiguously at an LDS address the wave names), so no register
+// holds a staged operand and three workgroups fit on a CU; each waits for its own step's
+// loads, and the others' MFMAs run meanwhile. Tile 64 bucket rows x 256 weight rows (waves
+// 1 x 4), 128 K per step: MXFP4 B is the smallest per weight, so a wide tile cuts the A
+// (activation) bytes that each CU pulls in per flop.
+//   A: row r of the tile at r * 256 bytes, its 16-byte piece c (8 K) at position c ^ (r % 16):
+//      the XOR spreads the 16 rows an MFMA operand read touches over all banks. A lane's load
+//      picks the global piece whose position is its lane slot; pieces past K read zeros.
+//   B: the step's run of each of the 16 row groups (64 units of 16 bytes, 1 KiB) verbatim;
+//      scales: the runs' 64 bytes each, verbatim.
+template <bool GATED>
+__global__ __launch_bounds__(kTThreads, 3) void k_ggemm_mx(
+    const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as, int64_t qslot,
+    int64_t sslot, const uint8_t* __restrict__ bq, const uint8_t* __restrict__ bs,
+    const int32_t* __restrict__ slot_map, int n_slots, int E,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm, int k,
+    const uint16_t* __restrict__ src, int K, int N, int n_mtiles, int n_ntiles,
+    uint16_t* __restrict__ h_out, float* __restrict__ y_out, uint32_t* __restrict__ err_flags) {
+  constexpr int BM = 64, NG = 16;
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[BM * 256];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_bq[NG * 1024];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_bs[NG * 64];
+  __shared__ int tmp4[4];
+  __shared__ int sh[2];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wn = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // waves along the columns
+  // XCD-aware 2-D tile order, as k_ggemm
+  const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+  const int64_t i = (int64_t)(local >> 6) * 512 + xcd * 64 + (local & 63);
+  if (i >= (int64_t)n_mtiles * n_ntiles) return;
+  const int sr = (int)(i / (8LL * n_ntiles));
+  const int hh = min(8, n_mtiles - 8 * sr);
+  const int jj = (int)(i - 8LL * n_ntiles * sr);
+  const int gcol = jj / (8 * hh);
+  const int w = min(8, n_ntiles - 8 * gcol);
+  const int kk0 = jj - 8 * hh * gcol;
+  const int mt = 8 * sr + kk0 / w;
+  const int nt = 8 * gcol + kk0 % w;
+  int e, m0;
+  if (!map_row_tile(offsets, E, BM, mt, &e, &m0, tmp4, sh)) return;
+  const int mend = offsets[e + 1];
+  const int slot = slot_map[e];
+  const int n0 = GATED ? nt * 128 : nt * 256;
+  if (slot < 0 || slot >= n_slots) {
+    const int ncols = GATED ? 128 : 256;
+    for (int t = threadIdx.x; t < BM * ncols; t += kTThreads) {
+      const int pos = m0 + t / ncols, n = n0 + t % ncols;
+      if (pos < mend && n < N) {
+        if (GATED) h_out[(int64_t)pos * N + n] = 0;
+        else y_out[(int64_t)pos * N + n] = 0.f;
+      }
+    }
+    if (threadIdx.x == 0 && err_flags && slot != kSlotMiss) atomicOr(err_flags, 1u);
+    return;
+  }
+  const int nb = K / 32;
+  const int nsteps = (K + kBK - 1) / kBK;
+
+  // ---- A: wave wn loads rows 16 wn + 4 j + lane / 16 (j < 4), position lane % 16
+  const u32x4* src16 = (const u32x4*)src;
+  const uint32_t kp = (uint32_t)K / 8;     // 16-byte units per row
+  const int apos = lane & 15;
+  uint32_t arow[4];                        // unit index of each row's start
+  int aswz[4];                             // the global piece that lands at position apos
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 16 * wn + 4 * j + (lane >> 4);
+    const int pos = min(m0 + r, mend - 1);   // rows past the tile's end repeat its last row
+    const int row = GATED ? perm[pos] / k : pos;
+    arow[j] = (uint32_t)row * kp;
+    aswz[j] = apos ^ (r & 15);
+  }
+  // ---- B: wave wn copies the runs of local row groups 4 wn .. 4 wn + 3. GATED: groups
+  // g < 8 are gate rows n0/16 + g, g >= 8 up rows n0/16 + g - 8; a group past N reads
+  // group 0 (never stored).
+  const uint8_t* q0 = aq + (int64_t)slot * qslot;
+  const uint8_t* s0 = as + (int64_t)slot * sslot;
+  const uint8_t* q1 = GATED ? bq + (int64_t)slot * qslot : q0;
+  const uint8_t* s1 = GATED ? bs + (int64_t)slot * sslot : s0;
+  const uint8_t* brun[4];
+  const uint8_t* srun;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int g = 4 * wn + j;
+    const int rg = GATED ? n0 / 16 + (g & 7) : n0 / 16 + g;
+    const int rgc = rg * 16 < N ? rg : 0;
+    brun[j] = (GATED && g >= 8 ? q1 : q0) + (int64_t)rgc * nb * 16 * 16;
+  }
+  {
+    // scales: lane l copies dword l % 16 of run 4 wn + l / 16
+    const int g = 4 * wn + (lane >> 4);
+    const int rg = GATED ? n0 / 16 + (g & 7) : n0 / 16 + g;
+    const int rgc = rg * 16 < N ? rg : 0;
+    srun = (GATED && g >= 8 ? s1 : s0) + (int64_t)rgc * nb * 16 + (lane & 15) * 4;
+  }
+  const int ublk = lane >> 4;   // block (of the step's 4) of the lane's B unit
+  auto load_step = [&](int c) {
+    const int kk = c * kBK;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool ok = kk + aswz[j] * 8 < K;
+      const void* gp = ok ? (const void*)(src16 + arow[j] + (uint32_t)(kk / 8 + aswz[j]))
+                          : (const void*)g_zero16;
+      __builtin_amdgcn_global_load_lds(gp, (lds_ptr)(lds_a + (16 * wn + 4 * j) * 256), 16, 0, 0);
+    }
+    // B: blocks past the row re-read step 0 (their scales are masked when consumed)
+    const int cs = 4 * c + ublk < nb ? c : 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_global_load_lds(brun[j] + (int64_t)cs * 1024 + lane * 16,
+                                       (lds_ptr)(lds_bq + (4 * wn + j) * 1024), 16, 0, 0);
+    const int css = 4 * c + (lane & 15) / 4 < nb ? c : 0;
+    __builtin_amdgcn_global_load_lds(srun + (int64_t)css * 64, (lds_ptr)(lds_bs + 256 * wn), 4, 0, 0);
+  };
+
+  // ---- this wave's 4 n-fragments: local row group and column validity
+  int fg[4];
+  bool fcol[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    int col0;
+    if (GATED) {
+      col0 = n0 + 32 * wn + 16 * (f & 1);
+      fg[f] = (f < 2 ? 0 : NG / 2) + 2 * wn + (f & 1);
+    } else {
+      col0 = n0 + 64 * wn + 16 * f;
+      fg[f] = 4 * wn + f;
+    }
+    fcol[f] = col0 < N;
+  }
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int f = 0; f < 4; ++f) acc[a][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // 16-row fragments holding at least one bucket row (wave-uniform)
+  const int nmf = min(4, max(0, (mend - m0 + 15) >> 4));
+  const int g4 = lane >> 4;
+  const int mrow = lane & 15;
+  for (int c = 0; c < nsteps; ++c) {
+    __syncthreads();   // every wave is done reading the previous step
+    load_step(c);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();   // every wave's loads have landed
+    auto mx_step = [&](auto full) {
+      constexpr bool kFull = decltype(full)::value;
+      float bsc[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const uint32_t sb = lds_bs[fg[f] * 64 + lane];
+        const uint32_t keep = (fcol[f] && 4 * c + g4 < nb) ? 0xffffffffu : 0u;
+        bsc[f] = __uint_as_float((sb << 23) & keep);   // E8M0 -> 2^(b-127), or +0
+      }
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        // one dword of each fragment's unit per 32-K slice, widened just before its MFMAs
+        // (widening all four slices at once would hold 64 more registers)
+        bf16x8 bv[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+          bv[f] = fp4x8_to_bf16x8(*(const uint32_t*)(lds_bq + fg[f] * 1024 + lane * 16 + 4 * ii), bsc[f]);
+#pragma unroll
+        for (int mf = 0; mf < 4; ++mf) {
+          if (!kFull && mf >= nmf) continue;
+          const int row = 16 * mf + mrow;
+          const int piece = (4 * g4 + ii) ^ (row & 15);
+          const bf16x8 av = __builtin_bit_cast(bf16x8, *(const u32x4*)(lds_a + row * 256 + piece * 16));
+#pragma unroll
+          for (int f = 0; f < 4; ++f)
+            acc[mf][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[f], acc[mf][f], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // keep the next slice's reads after these MFMAs
+      }
+    };
+    if (nmf == 4) mx_step(std::true_type{});
+    else if (nmf > 0) mx_step(std::false_type{});
+  }
+  // ---- epilogue: lane holds D[row 4*(lane/16) + v][col lane%16] of each 16x16 tile
+#pragma unroll
+  for (int mf = 0; mf < 4; ++mf) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int pos = m0 + 16 * mf + 4 * g4 + v;
+      if (pos >= mend) continue;
+      if constexpr (GATED) {
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          const int n = n0 + 32 * wn + 16 * f + mrow;
+          if (n < N)
+            h_out[(int64_t)pos * N + n] = f32_to_bf16_rne(silu_mul(acc[mf][f][v], acc[mf][f + 2][v]));
+        }
+      } else {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          const int n = n0 + 64 * wn + 16 * f + mrow;
+          if (n < N) y_out[(int64_t)pos * N + n] = acc[mf][f][v];
+        }
+      }
+    }
+  }
+}
+
+template <bool GATED>
+hipError_t launch_ggemm_mx(const PoolView& a, const PoolView& b, const int32_t* slot_map,
+                           int n_slots, int E, const int32_t* offsets, const int32_t* perm,
+                           int T, int k, const uint16_t* src, int K, int N, uint16_t* h,
+                           float* y, uint32_t* err, hipStream_t stream) {
+  const int pairs = T * k;
+  const int max_mtiles = (pairs + 63) / 64 + min(E, pairs);
+  const int n_ntiles = (N + (GATED ? 127 : 255)) / (GATED ? 128 : 256);
+  const int64_t grid = ((int64_t)max_mtiles * n_ntiles + 511) / 512 * 512;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_ggemm_mx<GATED>), dim3((unsigned)grid), dim3(kTThreads), 0, stream, a.q,
+                     a.s, a.q_slot, a.s_slot, b.q, b.s, slot_map, n_slots, E, offsets, perm, k,
+                     src, K, N, max_mtiles, n_ntiles, h, y, err);
+  return hipGetLastError();
+}
 
 template <int FMT, bool GATED, int BM = 128>
 hipError_t launch_ggemm_t(const PoolView& a, const PoolView& b, const int32_t* slot_map,
@@ -612,8 +797,8 @@ hipError_t launch_gate_up_grouped(int fmt, const PoolView& gate, const PoolView&
                                   hipStream_t stream) {
   switch (fmt) {
     case kMXFP4:
-      return launch_ggemm_t<kMXFP4, true, kMxfp4BM>(gate, up, slot_map, n_slots, E, offsets, perm, T, k, x,
-                                          H, I, h, nullptr, err, stream);
+      return launch_ggemm_mx<true>(gate, up, slot_map, n_slots, E, offsets, perm, T, k, x, H, I,
+                                   h, nullptr, err, stream);
     case kQ8_0:
       return launch_ggemm_t<kQ8_0, true>(gate, up, slot_map, n_slots, E, offsets, perm, T, k, x,
                                          H, I, h, nullptr, err, stream);
@@ -636,8 +821,8 @@ hipError_t launch_down_grouped(int fmt, const PoolView& down, const int32_t* slo
                                uint32_t* err, hipStream_t stream) {
   switch (fmt) {
     case kMXFP4:
-      return launch_ggemm_t<kMXFP4, false, kMxfp4BM>(down, down, slot_map, n_slots, E, offsets, nullptr, T,
-                                           k, h, I, H, nullptr, y, err, stream);
+      return launch_ggemm_mx<false>(down, down, slot_map, n_slots, E, offsets, nullptr, T, k, h,
+                                    I, H, nullptr, y, err, stream);
     case kQ8_0:
       return launch_ggemm_t<kQ8_0, false>(down, down, slot_map, n_slots, E, offsets, nullptr, T,
                                           k, h, I, H, nullptr, y, err, stream);
