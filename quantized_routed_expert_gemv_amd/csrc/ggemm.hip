@@ -553,15 +553,16 @@ __device__ __attribute__((aligned(16))) uint32_t g_zero16[4];
 
 // MXFP4 grouped GEMM with its tiles loaded straight into LDS (gfx950 global_load_lds_dwordx4:
 // 64 lanes x 16 bytes land contiguously at an LDS address the wave names), so no register
-// holds a staged operand and three workgroups fit on a CU; each waits for its own step's
-// loads, and the others' MFMAs run meanwhile. Tile 64 bucket rows x 256 weight rows (waves
-// 1 x 4), 128 K per step: MXFP4 B is the smallest per weight, so a wide tile cuts the A
-// (activation) bytes that each CU pulls in per flop.
+// holds a staged operand; each workgroup waits for its own step's loads while the other
+// workgroups on the CU (three fit) run their MFMAs. Tile 64 bucket rows x 256 weight rows
+// (waves 1 x 4, each a 64 x 64 block), 128 K per step: MXFP4 B is the smallest operand per
+// weight, so a wide tile cuts the A (activation) bytes that each CU pulls in per flop.
 //   A: row r of the tile at r * 256 bytes, its 16-byte piece c (8 K) at position c ^ (r % 16):
 //      the XOR spreads the 16 rows an MFMA operand read touches over all banks. A lane's load
 //      picks the global piece whose position is its lane slot; pieces past K read zeros.
 //   B: the step's run of each of the 16 row groups (64 units of 16 bytes, 1 KiB) verbatim;
-//      scales: the runs' 64 bytes each, verbatim.
+//      scales: the runs' 64 bytes each, verbatim. A lane reads its whole unit at once
+//      (consecutive 16-byte reads: no bank conflicts) and widens one 32-K slice at a time.
 template <bool GATED>
 __global__ __launch_bounds__(kTThreads, 3) void k_ggemm_mx(
     const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as, int64_t qslot,
@@ -570,7 +571,7 @@ __global__ __launch_bounds__(kTThreads, 3) void k_ggemm_mx(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm, int k,
     const uint16_t* __restrict__ src, int K, int N, int n_mtiles, int n_ntiles,
     uint16_t* __restrict__ h_out, float* __restrict__ y_out, uint32_t* __restrict__ err_flags) {
-  constexpr int BM = 64, NG = 16;
+  constexpr int BM = 64, NG = 16, NF = 4;   // rows, B row groups, n-fragments per wave
   typedef __attribute__((address_space(3))) void* lds_ptr;
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[BM * 256];
   __shared__ __attribute__((aligned(16))) uint8_t lds_bq[NG * 1024];
@@ -668,28 +669,30 @@ __global__ __launch_bounds__(kTThreads, 3) void k_ggemm_mx(
     __builtin_amdgcn_global_load_lds(srun + (int64_t)css * 64, (lds_ptr)(lds_bs + 256 * wn), 4, 0, 0);
   };
 
-  // ---- this wave's 4 n-fragments: local row group and column validity
-  int fg[4];
-  bool fcol[4];
+  // ---- this wave's NF n-fragments: local row group and column validity. GATED: fragments
+  // f < NF/2 are gate columns n0 + 16 (NF/2) wn + 16 f, f >= NF/2 the same up columns.
+  // Every wave reads the whole A tile from LDS, so its 64-column share sets the LDS bytes
+  // per flop; a lane reads its B unit whole (no bank conflicts) and widens it per slice.
+  constexpr int NH = NF / 2;
+  int fg[NF];
+  bool fcol[NF];
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
+  for (int f = 0; f < NF; ++f) {
     int col0;
     if (GATED) {
-      col0 = n0 + 32 * wn + 16 * (f & 1);
-      fg[f] = (f < 2 ? 0 : NG / 2) + 2 * wn + (f & 1);
+      col0 = n0 + 16 * NH * wn + 16 * (f % NH);
+      fg[f] = (f < NH ? 0 : NG / 2) + NH * wn + f % NH;
     } else {
-      col0 = n0 + 64 * wn + 16 * f;
-      fg[f] = 4 * wn + f;
+      col0 = n0 + 16 * NF * wn + 16 * f;
+      fg[f] = NF * wn + f;
     }
     fcol[f] = col0 < N;
   }
-  f32x4 acc[4][4];
+  f32x4 acc[4][NF];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int f = 0; f < 4; ++f) acc[a][f] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // 16-row fragments holding at least one bucket row (wave-uniform)
-  const int nmf = min(4, max(0, (mend - m0 + 15) >> 4));
+    for (int f = 0; f < NF; ++f) acc[a][f] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int g4 = lane >> 4;
   const int mrow = lane & 15;
   for (int c = 0; c < nsteps; ++c) {
@@ -697,38 +700,36 @@ __global__ __launch_bounds__(kTThreads, 3) void k_ggemm_mx(
     load_step(c);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();   // every wave's loads have landed
-    auto mx_step = [&](auto full) {
-      constexpr bool kFull = decltype(full)::value;
-      float bsc[4];
+    // all 4 row fragments run: rows past the expert's last pair repeat it and are never stored
+    u32x4 bq4[NF];
+    float bsc[NF];
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        const uint32_t sb = lds_bs[fg[f] * 64 + lane];
-        const uint32_t keep = (fcol[f] && 4 * c + g4 < nb) ? 0xffffffffu : 0u;
-        bsc[f] = __uint_as_float((sb << 23) & keep);   // E8M0 -> 2^(b-127), or +0
+    for (int f = 0; f < NF; ++f) {
+      bq4[f] = *(const u32x4*)(lds_bq + fg[f] * 1024 + lane * 16);
+      const uint32_t sb = lds_bs[fg[f] * 64 + lane];
+      const uint32_t keep = (fcol[f] && 4 * c + g4 < nb) ? 0xffffffffu : 0u;
+      bsc[f] = __uint_as_float((sb << 23) & keep);   // E8M0 -> 2^(b-127), or +0
+    }
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      // one 32-K slice: the wave's 4 A fragments are read once; each B fragment is widened
+      // just before its 4 MFMAs, so a single widened fragment is live at a time
+      bf16x8 av[4];
+#pragma unroll
+      for (int mf = 0; mf < 4; ++mf) {
+        const int row = 16 * mf + mrow;
+        const int piece = (4 * g4 + ii) ^ mrow;   // row % 16 == mrow
+        av[mf] = __builtin_bit_cast(bf16x8, *(const u32x4*)(lds_a + row * 256 + piece * 16));
       }
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        // one dword of each fragment's unit per 32-K slice, widened just before its MFMAs
-        // (widening all four slices at once would hold 64 more registers)
-        bf16x8 bv[4];
+      for (int f = 0; f < NF; ++f) {
+        const bf16x8 bv = fp4x8_to_bf16x8(bq4[f][ii], bsc[f]);
 #pragma unroll
-        for (int f = 0; f < 4; ++f)
-          bv[f] = fp4x8_to_bf16x8(*(const uint32_t*)(lds_bq + fg[f] * 1024 + lane * 16 + 4 * ii), bsc[f]);
-#pragma unroll
-        for (int mf = 0; mf < 4; ++mf) {
-          if (!kFull && mf >= nmf) continue;
-          const int row = 16 * mf + mrow;
-          const int piece = (4 * g4 + ii) ^ (row & 15);
-          const bf16x8 av = __builtin_bit_cast(bf16x8, *(const u32x4*)(lds_a + row * 256 + piece * 16));
-#pragma unroll
-          for (int f = 0; f < 4; ++f)
-            acc[mf][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[f], acc[mf][f], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);   // keep the next slice's reads after these MFMAs
+        for (int mf = 0; mf < 4; ++mf)
+          acc[mf][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mf], bv, acc[mf][f], 0, 0, 0);
       }
-    };
-    if (nmf == 4) mx_step(std::true_type{});
-    else if (nmf > 0) mx_step(std::false_type{});
+      __builtin_amdgcn_sched_barrier(0);   // keep the next slice's reads after these MFMAs
+    }
   }
   // ---- epilogue: lane holds D[row 4*(lane/16) + v][col lane%16] of each 16x16 tile
 #pragma unroll
@@ -739,15 +740,15 @@ __global__ __launch_bounds__(kTThreads, 3) void k_ggemm_mx(
       if (pos >= mend) continue;
       if constexpr (GATED) {
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          const int n = n0 + 32 * wn + 16 * f + mrow;
+        for (int f = 0; f < NH; ++f) {
+          const int n = n0 + 16 * NH * wn + 16 * f + mrow;
           if (n < N)
-            h_out[(int64_t)pos * N + n] = f32_to_bf16_rne(silu_mul(acc[mf][f][v], acc[mf][f + 2][v]));
+            h_out[(int64_t)pos * N + n] = f32_to_bf16_rne(silu_mul(acc[mf][f][v], acc[mf][f + NH][v]));
         }
       } else {
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
-          const int n = n0 + 64 * wn + 16 * f + mrow;
+        for (int f = 0; f < NF; ++f) {
+          const int n = n0 + 16 * NF * wn + 16 * f + mrow;
           if (n < N) y_out[(int64_t)pos * N + n] = acc[mf][f][v];
         }
       }
@@ -760,14 +761,15 @@ hipError_t launch_ggemm_mx(const PoolView& a, const PoolView& b, const int32_t* 
                            int n_slots, int E, const int32_t* offsets, const int32_t* perm,
                            int T, int k, const uint16_t* src, int K, int N, uint16_t* h,
                            float* y, uint32_t* err, hipStream_t stream) {
+  constexpr int BM = 64;
   const int pairs = T * k;
-  const int max_mtiles = (pairs + 63) / 64 + min(E, pairs);
+  const int max_mtiles = (pairs + BM - 1) / BM + min(E, pairs);
   const int n_ntiles = (N + (GATED ? 127 : 255)) / (GATED ? 128 : 256);
   const int64_t grid = ((int64_t)max_mtiles * n_ntiles + 511) / 512 * 512;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_ggemm_mx<GATED>), dim3((unsigned)grid), dim3(kTThreads), 0, stream, a.q,
-                     a.s, a.q_slot, a.s_slot, b.q, b.s, slot_map, n_slots, E, offsets, perm, k,
-                     src, K, N, max_mtiles, n_ntiles, h, y, err);
+  hipLaunchKernelGGL((k_ggemm_mx<GATED>), dim3((unsigned)grid), dim3(kTThreads), 0, stream,
+                     a.q, a.s, a.q_slot, a.s_slot, b.q, b.s, slot_map, n_slots, E, offsets, perm,
+                     k, src, K, N, max_mtiles, n_ntiles, h, y, err);
   return hipGetLastError();
 }
 
