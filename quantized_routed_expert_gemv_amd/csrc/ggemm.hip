@@ -548,6 +548,16 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
   }
 }
 
+// XOR mask for the 16-byte pieces of LDS row m (0..15) of a 256-byte-row tile. Measured on
+// gfx950: a 64-lane ds_read_b128 is served in four passes of 16 lanes, two per half-wave,
+// split by the parity of lane bits 2, 3 and 4; a pass is conflict-free when its lanes touch
+// 16 different 16-byte bank groups (address / 16 mod 16) or the same address. An MFMA operand
+// read takes piece 4 g + i of row m in lane 16 g + m; with this mask (bits 0, 1 of m, then
+// bit 3, then bit 2 ^ bit 3) every pass sees 16 different positions, for every i.
+__device__ __forceinline__ int lds_row_swizzle(int m) {
+  return (m & 3) | (((m >> 3) & 1) << 2) | ((((m >> 2) ^ (m >> 3)) & 1) << 3);
+}
+
 // Zeros that the MXFP4 kernel's LDS loads read for A pieces past K.
 __device__ __attribute__((aligned(16))) uint32_t g_zero16[4];
 
@@ -557,9 +567,10 @@ __device__ __attribute__((aligned(16))) uint32_t g_zero16[4];
 // workgroups on the CU (three fit) run their MFMAs. Tile 64 bucket rows x 256 weight rows
 // (waves 1 x 4, each a 64 x 64 block), 128 K per step: MXFP4 B is the smallest operand per
 // weight, so a wide tile cuts the A (activation) bytes that each CU pulls in per flop.
-//   A: row r of the tile at r * 256 bytes, its 16-byte piece c (8 K) at position c ^ (r % 16):
-//      the XOR spreads the 16 rows an MFMA operand read touches over all banks. A lane's load
-//      picks the global piece whose position is its lane slot; pieces past K read zeros.
+//   A: row r of the tile at r * 256 bytes, its 16-byte piece c (8 K) at position
+//      c ^ lds_row_swizzle(r % 16), which keeps every 128-bit operand read free of bank
+//      conflicts. A lane's load picks the global piece whose position is its lane slot;
+//      pieces past K read zeros.
 //   B: the step's run of each of the 16 row groups (64 units of 16 bytes, 1 KiB) verbatim;
 //      scales: the runs' 64 bytes each, verbatim. A lane reads its whole unit at once
 //      (consecutive 16-byte reads: no bank conflicts) and widens one 32-K slice at a time.
@@ -624,7 +635,7 @@ __global__ __launch_bounds__(kTThreads, 3) void k_ggemm_mx(
     const int pos = min(m0 + r, mend - 1);   // rows past the tile's end repeat its last row
     const int row = GATED ? perm[pos] / k : pos;
     arow[j] = (uint32_t)row * kp;
-    aswz[j] = apos ^ (r & 15);
+    aswz[j] = apos ^ lds_row_swizzle(r & 15);
   }
   // ---- B: wave wn copies the runs of local row groups 4 wn .. 4 wn + 3. GATED: groups
   // g < 8 are gate rows n0/16 + g, g >= 8 up rows n0/16 + g - 8; a group past N reads
@@ -695,6 +706,7 @@ __global__ __launch_bounds__(kTThreads, 3) void k_ggemm_mx(
     for (int f = 0; f < NF; ++f) acc[a][f] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int g4 = lane >> 4;
   const int mrow = lane & 15;
+  const int rswz = lds_row_swizzle(mrow);   // rows 16 mf + mrow all have r % 16 == mrow
   for (int c = 0; c < nsteps; ++c) {
     __syncthreads();   // every wave is done reading the previous step
     load_step(c);
@@ -718,7 +730,7 @@ __global__ __launch_bounds__(kTThreads, 3) void k_ggemm_mx(
 #pragma unroll
       for (int mf = 0; mf < 4; ++mf) {
         const int row = 16 * mf + mrow;
-        const int piece = (4 * g4 + ii) ^ mrow;   // row % 16 == mrow
+        const int piece = (4 * g4 + ii) ^ rswz;
         av[mf] = __builtin_bit_cast(bf16x8, *(const u32x4*)(lds_a + row * 256 + piece * 16));
       }
 #pragma unroll
