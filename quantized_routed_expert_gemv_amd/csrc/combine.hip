@@ -28,7 +28,8 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
     }
     f32x4 v[kMaxK];
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) v[j] = *(const f32x4*)(y + (int64_t)pos[j] * H + c);
+    for (int j = 0; j < kMaxK; ++j)   // y is read once: nontemporal
+      v[j] = __builtin_nontemporal_load((const f32x4*)(y + (int64_t)pos[j] * H + c));
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j)

@@ -17,7 +17,9 @@
 //     exact for MXFP4. For Q8_0 each MFMA covers exactly one block, its int8 codes are exact
 //     in bf16, and the block scale d multiplies the fp32 MFMA result before accumulation;
 //   * gate and up tiles of the same columns live in the same wave, so SwiGLU is applied in
-//     registers and h is written once, rounded to bf16; the down projection writes fp32 y.
+//     registers and h is written once, rounded to bf16; the down projection writes fp32 y
+//     with nontemporal stores (y is read once, by the combine, and is far larger than the
+//     caches: the stores then do not evict the A and B tiles other workgroups still read).
 #include <type_traits>
 
 #include "common.hpp"
@@ -541,7 +543,7 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
           const int n = n0 + 64 * wn + 16 * f + mrow;
-          if (n < N) y_out[(int64_t)pos * N + n] = acc[mf][f][v];
+          if (n < N) __builtin_nontemporal_store(acc[mf][f][v], &y_out[(int64_t)pos * N + n]);
         }
       }
     }
@@ -761,7 +763,7 @@ __global__ __launch_bounds__(kTThreads, 3) void k_ggemm_mx(
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
           const int n = n0 + 16 * NF * wn + 16 * f + mrow;
-          if (n < N) y_out[(int64_t)pos * N + n] = acc[mf][f][v];
+          if (n < N) __builtin_nontemporal_store(acc[mf][f][v], &y_out[(int64_t)pos * N + n]);
         }
       }
     }
