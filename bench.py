@@ -30,6 +30,11 @@ import time
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+
+
+def ggemm_kernel(fmt: str) -> str:
+    """The grouped-GEMM kernel that runs a format's prefill expert FFN."""
+    return "k_ggemm_mx" if fmt == "mxfp4" else "k_ggemm"
 METRIC = "MoE-layer tokens/s; decode HBM GB/s and prefill MFMA % of peak"
 # bytes per weight of each format: MXFP4 16+1 and Q8_0 32+2 per 32; Q4_K 144, Q5_K 176 and
 # Q6_K 210 per 256 (the pool keeps 0.5 more per 32 for Q4_K / Q5_K, the 6-bit scale and min
@@ -286,7 +291,7 @@ def run_workload(cfg, args, n_layers, steps, warmup, hip, qm, synth, np, torch, 
         achieved = flops / kern_avg_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
-                "kernel": "gate/up grouped GEMM (k_ggemm)", "work_per_launch": flops}
+                "kernel": f"gate/up grouped GEMM ({ggemm_kernel(cfg.fmt)})", "work_per_launch": flops}
         c = counts_all[0]
         res["experts"] = {"tokens_per_expert": [int(v) for v in c],
                           "empty": int(np.sum(c == 0)),
@@ -359,7 +364,7 @@ def time_down_gemm(qm, torch, np, hip, layer, cfg, stream, reps):
     s = float(np.mean(ms)) * 1e-3
     return {"bound": "mfma", "achieved": round(flops / s / 1e12, 2), "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": round(flops / s / 1e12 / BF16_PEAK_TFLOPS, 4),
-            "kernel": "down grouped GEMM (k_ggemm)", "work_per_launch": flops,
+            "kernel": f"down grouped GEMM ({ggemm_kernel(cfg.fmt)})", "work_per_launch": flops,
             "avg_launch_us": round(s * 1e6, 3),
             "method": f"HIP events around {reps} stand-alone launches on the kernel's stream"}
 
