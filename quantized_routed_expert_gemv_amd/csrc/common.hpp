@@ -10,6 +10,7 @@ typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
 typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
+typedef int16_t i16x2 __attribute__((__vector_size__(2 * sizeof(int16_t))));
 
 constexpr int kWave = 64;
 constexpr int kBlock = 32;      // elements per quantization block (MXFP4 and Q8_0)

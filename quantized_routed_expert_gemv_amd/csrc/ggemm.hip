@@ -369,61 +369,69 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
       load_b(c + 1);
     }
     if constexpr (FMT == kQ6_K) {
-      // per block: lanes g = 0, 1 supply K 0..15 (half 0), g = 2, 3 K 16..31 (half 1). A
-      // with the other half's lanes zeroed gives each half its own MFMAs: codes as low
-      // nibbles plus 16 x the high part (two MFMAs into one sum), and the half's row sums
-      // against ones; the half adds d sc_h (P_h - 32 S_h).
-      const bf16x8 ones = __builtin_bit_cast(
-          bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
-      const bf16x8 zero = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-#pragma unroll 1
-      for (int j = 0; j < 4; ++j) {
-        bf16x8 bv[4], bvh[4];
-        float a0[4], a1[4];
+      // Weight = d * v with v = sc * (q - 32), sc the half block's int8 scale: an integer of
+      // at most 14 bits (|v| <= 4096). It splits exactly into two bf16 operands,
+      //   hi = (v with its low 7 bits cleared) - 128: a multiple of 128 within +-4224, at most
+      //        6 significant bits, and
+      //   lo = the bf16 of exponent 7 and mantissa v & 127, i.e. 128 + (v & 127),
+      // with hi + lo = v. One accumulator per fragment collects sum x v over the step's 4
+      // blocks, two MFMAs per block, and the step adds d t: no scaling per block, and no
+      // offset to take out. Lane g4 supplies elements 8 g4 .. 8 g4 + 7 of its block, all in
+      // half g4 / 2.
+      auto read_a = [&](int mf, int j) {
+        const int row = 64 * wm + 16 * mf + mrow;
+        return __builtin_bit_cast(bf16x8, *(const u32x4*)(lds_a + row * kLdsStride + (32 * j + 8 * g4) * 2));
+      };
+      const int sh = 4 * (g4 & 1);
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
+      for (int f = 0; f < 4; ++f) {
+        f32x4 t[4];
+#pragma unroll
+        for (int mf = 0; mf < 4; ++mf) t[mf] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
           const int unit = 16 * j + mrow;
-          const uint32_t q = *(const uint32_t*)(lds_bq + fg[f] * BS::kRunQ + unit * 16 + 4 * g4);
-          bv[f] = u4x8_split_to_bf16x8(q);
-          // high parts of the same 8 elements: dword g4 / 2 of the unit, planes at bit
-          // 4 (g4 % 2) and 4 (g4 % 2) + 2; bytes 0..3 -> E4M3 0..3 * 2^-9, x 2^13
+          // codes: low nibbles of elements 0..3 (bytes) and 4..7 (high nibbles), plus their
+          // 2-bit high parts from dword g4 / 2 of the unit's high plane
+          const uint32_t qd = *(const uint32_t*)(lds_bq + fg[f] * BS::kRunQ + unit * 16 + 4 * g4);
           const uint32_t hw = *(const uint32_t*)(lds_bh + fg[f] * BS::kRunH + unit * 8 + 4 * (g4 >> 1));
-          const int sh = 4 * (g4 & 1);
-          const uint32_t lo = (hw >> sh) & 0x03030303u, hi = (hw >> (sh + 2)) & 0x03030303u;
-          const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 8192.0f, false);
-          const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 8192.0f, true);
-          const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 8192.0f, false);
-          const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 8192.0f, true);
-          bvh[f] = bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-          const uint32_t keep = (fcol[f] && 4 * c + j < nb) ? 0xffffu : 0u;
-          const uint32_t rec = *(const uint16_t*)(lds_bs + fg[f] * BS::kRunS + unit * 2) & keep;
-          const float d = fp16_to_f32(*(const uint16_t*)(lds_bs2 + fg[f] * BS::kRunS2 + mrow * 4));
-          a0[f] = d * (float)(int8_t)(rec & 0xFFu);
-          a1[f] = d * (float)(int8_t)(rec >> 8);
-        }
+          const uint32_t rec = *(const uint16_t*)(lds_bs + fg[f] * BS::kRunS + unit * 2);
+          const uint32_t qa = (qd & 0x0F0F0F0Fu) | (((hw >> sh) & 0x03030303u) << 4);
+          const uint32_t qb = ((qd >> 4) & 0x0F0F0F0Fu) | (((hw >> (sh + 2)) & 0x03030303u) << 4);
+          const int sc = (4 * c + j < nb) ? (int)(int8_t)(rec >> (8 * (g4 >> 1))) : 0;
+          const uint32_t scp = ((uint32_t)sc & 0xFFFFu) * 0x00010001u;
+          const uint32_t cp = ((uint32_t)(-32 * sc) & 0xFFFFu) * 0x00010001u;
+          u32x4 hi, lo;
 #pragma unroll
-        for (int mf = 0; mf < 4; ++mf) {
-          const int row = 64 * wm + 16 * mf + mrow;
-          const bf16x8 av =
-              __builtin_bit_cast(bf16x8, *(const u32x4*)(lds_a + row * kLdsStride + (32 * j + 8 * g4) * 2));
-          const bf16x8 av0 = g4 < 2 ? av : zero, av1 = g4 < 2 ? zero : av;
-          const f32x4 z4 = f32x4{0.f, 0.f, 0.f, 0.f};
-          const f32x4 s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av0, ones, z4, 0, 0, 0);
-          const f32x4 s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av1, ones, z4, 0, 0, 0);
-#pragma unroll
-          for (int f = 0; f < 4; ++f) {
-            f32x4 t0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av0, bv[f], z4, 0, 0, 0);
-            t0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av0, bvh[f], t0, 0, 0, 0);
-            f32x4 t1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av1, bv[f], z4, 0, 0, 0);
-            t1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av1, bvh[f], t1, 0, 0, 0);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              acc[mf][f][v] = fmaf(a0[f], fmaf(-32.f, s0[v], t0[v]), acc[mf][f][v]);
-              acc[mf][f][v] = fmaf(a1[f], fmaf(-32.f, s1[v], t1[v]), acc[mf][f][v]);
-            }
+          for (int pr = 0; pr < 4; ++pr) {
+            // elements 2 pr, 2 pr + 1 as two 16-bit lanes, then v = sc q - 32 sc per lane
+            const uint32_t qs = pr < 2 ? qa : qb;
+            const uint32_t qq = __builtin_amdgcn_perm(0u, qs, (pr & 1) ? 0x0c030c02u : 0x0c010c00u);
+            const i16x2 vv = __builtin_bit_cast(i16x2, qq) * __builtin_bit_cast(i16x2, scp) +
+                             __builtin_bit_cast(i16x2, cp);
+            const uint32_t v = __builtin_bit_cast(uint32_t, vv);
+            lo[pr] = (v & 0x007F007Fu) | 0x43004300u;
+            const i16x2 hv = __builtin_bit_cast(i16x2, v & 0xFF80FF80u) - i16x2{128, 128};
+            const uint32_t h = __builtin_bit_cast(uint32_t, hv);
+            const float f0 = (float)(int16_t)(h & 0xFFFFu), f1 = (float)(int16_t)(h >> 16);
+            hi[pr] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
           }
-          __builtin_amdgcn_sched_barrier(0);
+          const bf16x8 bhi = __builtin_bit_cast(bf16x8, hi), blo = __builtin_bit_cast(bf16x8, lo);
+#pragma unroll
+          for (int mf = 0; mf < 4; ++mf) {
+            const bf16x8 av = read_a(mf, j);
+            t[mf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bhi, t[mf], 0, 0, 0);
+            t[mf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, blo, t[mf], 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);   // one block's operands live at a time
         }
+        const float d = fcol[f] ? fp16_to_f32(*(const uint16_t*)(lds_bs2 + fg[f] * BS::kRunS2 + mrow * 4)) : 0.f;
+#pragma unroll
+        for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            acc[mf][f][v] = fmaf(d, t[mf][v], acc[mf][f][v]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     } else if constexpr (kquant(FMT)) {
       // one MFMA per 32-wide block, as for Q8_0: lane supplies K = 32 j + 8 g .. + 7 of block
