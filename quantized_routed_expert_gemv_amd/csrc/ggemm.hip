@@ -101,7 +101,7 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
   constexpr int NG = 4 * WN;                  // weight row groups per tile
   constexpr int RPT = BM / 16;                // A rows staged per thread
   static_assert(BM == 64 || BM == 128, "64 or 128 rows per tile");
-  static_assert(FMT != kMXFP4, "MXFP4 runs k_ggemm_mx");
+  static_assert(FMT != kMXFP4 && FMT != kQ6_K, "MXFP4 and Q6_K run k_ggemm_mx");
   using BS = BStage<FMT, NG>;
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[BM * kLdsStride];
   // Q8_0 codes are staged already widened to bf16 (2 bytes per code): both waves that
@@ -368,72 +368,7 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
       load_a(c + 1);
       load_b(c + 1);
     }
-    if constexpr (FMT == kQ6_K) {
-      // Weight = d * v with v = sc * (q - 32), sc the half block's int8 scale: an integer of
-      // at most 14 bits (|v| <= 4096). It splits exactly into two bf16 operands,
-      //   hi = (v with its low 7 bits cleared) - 128: a multiple of 128 within +-4224, at most
-      //        6 significant bits, and
-      //   lo = the bf16 of exponent 7 and mantissa v & 127, i.e. 128 + (v & 127),
-      // with hi + lo = v. One accumulator per fragment collects sum x v over the step's 4
-      // blocks, two MFMAs per block, and the step adds d t: no scaling per block, and no
-      // offset to take out. Lane g4 supplies elements 8 g4 .. 8 g4 + 7 of its block, all in
-      // half g4 / 2.
-      auto read_a = [&](int mf, int j) {
-        const int row = 64 * wm + 16 * mf + mrow;
-        return __builtin_bit_cast(bf16x8, *(const u32x4*)(lds_a + row * kLdsStride + (32 * j + 8 * g4) * 2));
-      };
-      const int sh = 4 * (g4 & 1);
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        f32x4 t[4];
-#pragma unroll
-        for (int mf = 0; mf < 4; ++mf) t[mf] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int unit = 16 * j + mrow;
-          // codes: low nibbles of elements 0..3 (bytes) and 4..7 (high nibbles), plus their
-          // 2-bit high parts from dword g4 / 2 of the unit's high plane
-          const uint32_t qd = *(const uint32_t*)(lds_bq + fg[f] * BS::kRunQ + unit * 16 + 4 * g4);
-          const uint32_t hw = *(const uint32_t*)(lds_bh + fg[f] * BS::kRunH + unit * 8 + 4 * (g4 >> 1));
-          const uint32_t rec = *(const uint16_t*)(lds_bs + fg[f] * BS::kRunS + unit * 2);
-          const uint32_t qa = (qd & 0x0F0F0F0Fu) | (((hw >> sh) & 0x03030303u) << 4);
-          const uint32_t qb = ((qd >> 4) & 0x0F0F0F0Fu) | (((hw >> (sh + 2)) & 0x03030303u) << 4);
-          const int sc = (4 * c + j < nb) ? (int)(int8_t)(rec >> (8 * (g4 >> 1))) : 0;
-          const uint32_t scp = ((uint32_t)sc & 0xFFFFu) * 0x00010001u;
-          const uint32_t cp = ((uint32_t)(-32 * sc) & 0xFFFFu) * 0x00010001u;
-          u32x4 hi, lo;
-#pragma unroll
-          for (int pr = 0; pr < 4; ++pr) {
-            // elements 2 pr, 2 pr + 1 as two 16-bit lanes, then v = sc q - 32 sc per lane
-            const uint32_t qs = pr < 2 ? qa : qb;
-            const uint32_t qq = __builtin_amdgcn_perm(0u, qs, (pr & 1) ? 0x0c030c02u : 0x0c010c00u);
-            const i16x2 vv = __builtin_bit_cast(i16x2, qq) * __builtin_bit_cast(i16x2, scp) +
-                             __builtin_bit_cast(i16x2, cp);
-            const uint32_t v = __builtin_bit_cast(uint32_t, vv);
-            lo[pr] = (v & 0x007F007Fu) | 0x43004300u;
-            const i16x2 hv = __builtin_bit_cast(i16x2, v & 0xFF80FF80u) - i16x2{128, 128};
-            const uint32_t h = __builtin_bit_cast(uint32_t, hv);
-            const float f0 = (float)(int16_t)(h & 0xFFFFu), f1 = (float)(int16_t)(h >> 16);
-            hi[pr] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
-          }
-          const bf16x8 bhi = __builtin_bit_cast(bf16x8, hi), blo = __builtin_bit_cast(bf16x8, lo);
-#pragma unroll
-          for (int mf = 0; mf < 4; ++mf) {
-            const bf16x8 av = read_a(mf, j);
-            t[mf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bhi, t[mf], 0, 0, 0);
-            t[mf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, blo, t[mf], 0, 0, 0);
-          }
-          __builtin_amdgcn_sched_barrier(0);   // one block's operands live at a time
-        }
-        const float d = fcol[f] ? fp16_to_f32(*(const uint16_t*)(lds_bs2 + fg[f] * BS::kRunS2 + mrow * 4)) : 0.f;
-#pragma unroll
-        for (int mf = 0; mf < 4; ++mf)
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            acc[mf][f][v] = fmaf(d, t[mf][v], acc[mf][f][v]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    } else if constexpr (kquant(FMT)) {
+    if constexpr (kquant(FMT)) {
       // one MFMA per 32-wide block, as for Q8_0: lane supplies K = 32 j + 8 g .. + 7 of block
       // j, i.e. bytes 4 g .. 4 g + 3 of unit 16 j + lane%16, widened to bf16 q (exact). A
       // fifth MFMA against ones gives each row's block sum S, and the block adds a P - c S
@@ -558,6 +493,38 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
   }
 }
 
+// Q6_K: the two exact bf16 operands of 8 weights' integer parts v = sc * (q - 32), sc the
+// half block's int8 scale (|v| <= 4096, at most 14 bits):
+//   hi = (v with its low 7 bits cleared) - 128, a multiple of 128 within +-4224 (at most 6
+//        significant bits), and lo = the bf16 of exponent 7 and mantissa v & 127, i.e.
+//        128 + (v & 127),
+// so hi + lo = v exactly and two MFMAs against the same A give sum x v. qd: one code dword
+// (low nibbles of elements 0..3 in its bytes, high nibbles elements 4..7); hw >> sh and
+// hw >> (sh + 2): the elements' 2-bit high parts as bytes (the pool's high-part layout).
+__device__ __forceinline__ void q6k_parts(uint32_t qd, uint32_t hw, int sh, int sc, bf16x8& bhi,
+                                          bf16x8& blo) {
+  const uint32_t qa = (qd & 0x0F0F0F0Fu) | (((hw >> sh) & 0x03030303u) << 4);
+  const uint32_t qb = ((qd >> 4) & 0x0F0F0F0Fu) | (((hw >> (sh + 2)) & 0x03030303u) << 4);
+  const uint32_t scp = ((uint32_t)sc & 0xFFFFu) * 0x00010001u;
+  const uint32_t cp = ((uint32_t)(-32 * sc) & 0xFFFFu) * 0x00010001u;
+  u32x4 hi, lo;
+#pragma unroll
+  for (int pr = 0; pr < 4; ++pr) {
+    // elements 2 pr, 2 pr + 1 as two 16-bit lanes, then v = sc q - 32 sc per lane
+    const uint32_t qq = __builtin_amdgcn_perm(0u, pr < 2 ? qa : qb, (pr & 1) ? 0x0c030c02u : 0x0c010c00u);
+    const i16x2 vv = __builtin_bit_cast(i16x2, qq) * __builtin_bit_cast(i16x2, scp) +
+                     __builtin_bit_cast(i16x2, cp);
+    const uint32_t v = __builtin_bit_cast(uint32_t, vv);
+    lo[pr] = (v & 0x007F007Fu) | 0x43004300u;
+    const i16x2 hv = __builtin_bit_cast(i16x2, v & 0xFF80FF80u) - i16x2{128, 128};
+    const uint32_t h = __builtin_bit_cast(uint32_t, hv);
+    const float f0 = (float)(int16_t)(h & 0xFFFFu), f1 = (float)(int16_t)(h >> 16);
+    hi[pr] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+  }
+  bhi = __builtin_bit_cast(bf16x8, hi);
+  blo = __builtin_bit_cast(bf16x8, lo);
+}
+
 // XOR mask for the 16-byte pieces of LDS row m (0..15) of a 256-byte-row tile. Measured on
 // gfx950: a 64-lane ds_read_b128 is served in four passes of 16 lanes, two per half-wave,
 // split by the parity of lane bits 2, 3 and 4; a pass is conflict-free when its lanes touch
@@ -584,7 +551,7 @@ __device__ __attribute__((aligned(16))) uint32_t g_zero16[4];
 //   B: the step's run of each of the 16 row groups (64 units of 16 bytes, 1 KiB) verbatim;
 //      scales: the runs' 64 bytes each, verbatim. A lane reads its whole unit at once
 //      (consecutive 16-byte reads: no bank conflicts) and widens one 32-K slice at a time.
-template <bool GATED>
+template <int FMT, bool GATED>
 __global__ __launch_bounds__(kTThreads, 3) void k_ggemm_mx(
     const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as, int64_t qslot,
     int64_t sslot, const uint8_t* __restrict__ bq, const uint8_t* __restrict__ bs,
@@ -592,11 +559,18 @@ __global__ __launch_bounds__(kTThreads, 3) void k_ggemm_mx(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm, int k,
     const uint16_t* __restrict__ src, int K, int N, int n_mtiles, int n_ntiles,
     uint16_t* __restrict__ h_out, float* __restrict__ y_out, uint32_t* __restrict__ err_flags) {
+  static_assert(FMT == kMXFP4 || FMT == kQ6_K, "MXFP4 or Q6_K");
+  constexpr bool kQ6 = FMT == kQ6_K;
   constexpr int BM = 64, NG = 16, NF = 4;   // rows, B row groups, n-fragments per wave
   typedef __attribute__((address_space(3))) void* lds_ptr;
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[BM * 256];
   __shared__ __attribute__((aligned(16))) uint8_t lds_bq[NG * 1024];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_bs[NG * 64];
+  // per run: MXFP4's 64 E8M0 bytes; Q6_K's 64 records of two int8 half-block scales
+  __shared__ __attribute__((aligned(16))) uint8_t lds_bs[NG * (kQ6 ? 128 : 64)];
+  // Q6_K: the runs' 2-bit high parts (8 bytes per unit), and each group's 16 rows' d records
+  // of the step's super-block
+  __shared__ __attribute__((aligned(16))) uint8_t lds_bh[kQ6 ? NG * 512 : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_bd[kQ6 ? NG * 64 : 16];
   __shared__ int tmp4[4];
   __shared__ int sh[2];
   const int lane = threadIdx.x & (kWave - 1);
@@ -663,12 +637,33 @@ __global__ __launch_bounds__(kTThreads, 3) void k_ggemm_mx(
     const int rgc = rg * 16 < N ? rg : 0;
     brun[j] = (GATED && g >= 8 ? q1 : q0) + (int64_t)rgc * nb * 16 * 16;
   }
-  {
+  auto group_rgc = [&](int g) {
+    const int rg = GATED ? n0 / 16 + (g & 7) : n0 / 16 + g;
+    return rg * 16 < N ? rg : 0;
+  };
+  const uint8_t* hrun[2] = {nullptr, nullptr};   // Q6_K: high parts and scale records
+  const uint8_t* rrun[2] = {nullptr, nullptr};
+  const uint8_t* drun = nullptr;                 // Q6_K: d records
+  if constexpr (!kQ6) {
     // scales: lane l copies dword l % 16 of run 4 wn + l / 16
     const int g = 4 * wn + (lane >> 4);
-    const int rg = GATED ? n0 / 16 + (g & 7) : n0 / 16 + g;
-    const int rgc = rg * 16 < N ? rg : 0;
-    srun = (GATED && g >= 8 ? s1 : s0) + (int64_t)rgc * nb * 16 + (lane & 15) * 4;
+    srun = (GATED && g >= 8 ? s1 : s0) + (int64_t)group_rgc(g) * nb * 16 + (lane & 15) * 4;
+  } else {
+    srun = nullptr;
+    // high parts: load h copies the runs of groups 4 wn + 2 h (lanes 0..31) and 4 wn + 2 h + 1
+    // (lanes 32..63), 16 bytes a lane; scale records likewise, 4 bytes a lane; d records:
+    // lane l copies row l % 16 of group 4 wn + l / 16
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int g = 4 * wn + 2 * h + (lane >> 5);
+      const int64_t u0 = (int64_t)group_rgc(g) * nb * 16;   // first unit of the group
+      hrun[h] = (GATED && g >= 8 ? q1 : q0) + hi_region(N, K) + u0 * 8 + (lane & 31) * 16;
+      rrun[h] = (GATED && g >= 8 ? s1 : s0) + u0 * 2 + (lane & 31) * 4;
+    }
+    const int g = 4 * wn + (lane >> 4);
+    const int nsb = nb / kSuperBlocks;
+    drun = (GATED && g >= 8 ? s1 : s0) + super_region(N, K) +
+           ((int64_t)group_rgc(g) * nsb * kRowGroup + (lane & 15)) * kSuperBytes;
   }
   const int ublk = lane >> 4;   // block (of the step's 4) of the lane's B unit
   auto load_step = [&](int c) {
@@ -686,8 +681,21 @@ __global__ __launch_bounds__(kTThreads, 3) void k_ggemm_mx(
     for (int j = 0; j < 4; ++j)
       __builtin_amdgcn_global_load_lds(brun[j] + (int64_t)cs * 1024 + lane * 16,
                                        (lds_ptr)(lds_bq + (4 * wn + j) * 1024), 16, 0, 0);
-    const int css = 4 * c + (lane & 15) / 4 < nb ? c : 0;
-    __builtin_amdgcn_global_load_lds(srun + (int64_t)css * 64, (lds_ptr)(lds_bs + 256 * wn), 4, 0, 0);
+    if constexpr (!kQ6) {
+      const int css = 4 * c + (lane & 15) / 4 < nb ? c : 0;
+      __builtin_amdgcn_global_load_lds(srun + (int64_t)css * 64, (lds_ptr)(lds_bs + 256 * wn), 4, 0, 0);
+    } else {
+      // K is a whole number of 256-element super-blocks: every step is in range
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        __builtin_amdgcn_global_load_lds(hrun[h] + (int64_t)c * 512,
+                                         (lds_ptr)(lds_bh + (4 * wn + 2 * h) * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(rrun[h] + (int64_t)c * 128,
+                                         (lds_ptr)(lds_bs + (4 * wn + 2 * h) * 128), 4, 0, 0);
+      }
+      __builtin_amdgcn_global_load_lds(drun + (int64_t)(c >> 1) * kRowGroup * kSuperBytes,
+                                       (lds_ptr)(lds_bd + 4 * wn * 64), 4, 0, 0);
+    }
   };
 
   // ---- this wave's NF n-fragments: local row group and column validity. GATED: fragments
@@ -723,34 +731,70 @@ __global__ __launch_bounds__(kTThreads, 3) void k_ggemm_mx(
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();   // every wave's loads have landed
     // all 4 row fragments run: rows past the expert's last pair repeat it and are never stored
-    u32x4 bq4[NF];
-    float bsc[NF];
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      bq4[f] = *(const u32x4*)(lds_bq + fg[f] * 1024 + lane * 16);
-      const uint32_t sb = lds_bs[fg[f] * 64 + lane];
-      const uint32_t keep = (fcol[f] && 4 * c + g4 < nb) ? 0xffffffffu : 0u;
-      bsc[f] = __uint_as_float((sb << 23) & keep);   // E8M0 -> 2^(b-127), or +0
-    }
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      // one 32-K slice: the wave's 4 A fragments are read once; each B fragment is widened
-      // just before its 4 MFMAs, so a single widened fragment is live at a time
-      bf16x8 av[4];
-#pragma unroll
-      for (int mf = 0; mf < 4; ++mf) {
-        const int row = 16 * mf + mrow;
-        const int piece = (4 * g4 + ii) ^ rswz;
-        av[mf] = __builtin_bit_cast(bf16x8, *(const u32x4*)(lds_a + row * 256 + piece * 16));
-      }
+    auto read_a = [&](int mf, int ii) {
+      const int row = 16 * mf + mrow;
+      return __builtin_bit_cast(bf16x8, *(const u32x4*)(lds_a + row * 256 + ((4 * g4 + ii) ^ rswz) * 16));
+    };
+    if constexpr (!kQ6) {
+      u32x4 bq4[NF];
+      float bsc[NF];
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
-        const bf16x8 bv = fp4x8_to_bf16x8(bq4[f][ii], bsc[f]);
+        bq4[f] = *(const u32x4*)(lds_bq + fg[f] * 1024 + lane * 16);
+        const uint32_t sb = lds_bs[fg[f] * 64 + lane];
+        const uint32_t keep = (fcol[f] && 4 * c + g4 < nb) ? 0xffffffffu : 0u;
+        bsc[f] = __uint_as_float((sb << 23) & keep);   // E8M0 -> 2^(b-127), or +0
+      }
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        // one 32-K slice: the wave's 4 A fragments are read once; each B fragment is widened
+        // just before its 4 MFMAs, so a single widened fragment is live at a time
+        bf16x8 av[4];
+#pragma unroll
+        for (int mf = 0; mf < 4; ++mf) {
+          const int row = 16 * mf + mrow;
+          const int piece = (4 * g4 + ii) ^ rswz;
+          av[mf] = __builtin_bit_cast(bf16x8, *(const u32x4*)(lds_a + row * 256 + piece * 16));
+        }
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const bf16x8 bv = fp4x8_to_bf16x8(bq4[f][ii], bsc[f]);
+#pragma unroll
+          for (int mf = 0; mf < 4; ++mf)
+            acc[mf][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mf], bv, acc[mf][f], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // keep the next slice's reads after these MFMAs
+      }
+    } else {
+      // lane's unit: block 4 c + lane / 16 of row lane % 16; slice ii is its code dword ii
+      // (elements 8 ii .. 8 ii + 7, half ii / 2). Per fragment the step's 4 slices go into one
+      // accumulator, two MFMAs each, and the step adds d t (d is the super-block's).
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const u32x4 q4 = *(const u32x4*)(lds_bq + fg[f] * 1024 + lane * 16);
+        const u32x2 h2 = *(const u32x2*)(lds_bh + fg[f] * 512 + lane * 8);
+        const uint32_t rec = *(const uint16_t*)(lds_bs + fg[f] * 128 + lane * 2);
+        const float d = fcol[f] ? fp16_to_f32(*(const uint16_t*)(lds_bd + fg[f] * 64 + mrow * 4)) : 0.f;
+        f32x4 t[4];
+#pragma unroll
+        for (int mf = 0; mf < 4; ++mf) t[mf] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          bf16x8 bhi, blo;
+          q6k_parts(q4[ii], h2[ii >> 1], 4 * (ii & 1), (int)(int8_t)(rec >> (8 * (ii >> 1))), bhi, blo);
+#pragma unroll
+          for (int mf = 0; mf < 4; ++mf) {
+            const bf16x8 av = read_a(mf, ii);
+            t[mf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bhi, t[mf], 0, 0, 0);
+            t[mf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, blo, t[mf], 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);   // one slice's operands live at a time
+        }
 #pragma unroll
         for (int mf = 0; mf < 4; ++mf)
-          acc[mf][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mf], bv, acc[mf][f], 0, 0, 0);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[mf][f][v] = fmaf(d, t[mf][v], acc[mf][f][v]);
       }
-      __builtin_amdgcn_sched_barrier(0);   // keep the next slice's reads after these MFMAs
     }
   }
   // ---- epilogue: lane holds D[row 4*(lane/16) + v][col lane%16] of each 16x16 tile
@@ -778,7 +822,7 @@ __global__ __launch_bounds__(kTThreads, 3) void k_ggemm_mx(
   }
 }
 
-template <bool GATED>
+template <int FMT, bool GATED>
 hipError_t launch_ggemm_mx(const PoolView& a, const PoolView& b, const int32_t* slot_map,
                            int n_slots, int E, const int32_t* offsets, const int32_t* perm,
                            int T, int k, const uint16_t* src, int K, int N, uint16_t* h,
@@ -789,7 +833,7 @@ hipError_t launch_ggemm_mx(const PoolView& a, const PoolView& b, const int32_t* 
   const int n_ntiles = (N + (GATED ? 127 : 255)) / (GATED ? 128 : 256);
   const int64_t grid = ((int64_t)max_mtiles * n_ntiles + 511) / 512 * 512;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_ggemm_mx<GATED>), dim3((unsigned)grid), dim3(kTThreads), 0, stream,
+  hipLaunchKernelGGL((k_ggemm_mx<FMT, GATED>), dim3((unsigned)grid), dim3(kTThreads), 0, stream,
                      a.q, a.s, a.q_slot, a.s_slot, b.q, b.s, slot_map, n_slots, E, offsets, perm,
                      k, src, K, N, max_mtiles, n_ntiles, h, y, err);
   return hipGetLastError();
@@ -821,7 +865,7 @@ hipError_t launch_gate_up_grouped(int fmt, const PoolView& gate, const PoolView&
                                   hipStream_t stream) {
   switch (fmt) {
     case kMXFP4:
-      return launch_ggemm_mx<true>(gate, up, slot_map, n_slots, E, offsets, perm, T, k, x, H, I,
+      return launch_ggemm_mx<kMXFP4, true>(gate, up, slot_map, n_slots, E, offsets, perm, T, k, x, H, I,
                                    h, nullptr, err, stream);
     case kQ8_0:
       return launch_ggemm_t<kQ8_0, true>(gate, up, slot_map, n_slots, E, offsets, perm, T, k, x,
@@ -833,8 +877,8 @@ hipError_t launch_gate_up_grouped(int fmt, const PoolView& gate, const PoolView&
       return launch_ggemm_t<kQ5_K, true>(gate, up, slot_map, n_slots, E, offsets, perm, T, k, x,
                                          H, I, h, nullptr, err, stream);
     case kQ6_K:
-      return launch_ggemm_t<kQ6_K, true>(gate, up, slot_map, n_slots, E, offsets, perm, T, k, x,
-                                         H, I, h, nullptr, err, stream);
+      return launch_ggemm_mx<kQ6_K, true>(gate, up, slot_map, n_slots, E, offsets, perm, T, k, x,
+                                          H, I, h, nullptr, err, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -845,7 +889,7 @@ hipError_t launch_down_grouped(int fmt, const PoolView& down, const int32_t* slo
                                uint32_t* err, hipStream_t stream) {
   switch (fmt) {
     case kMXFP4:
-      return launch_ggemm_mx<false>(down, down, slot_map, n_slots, E, offsets, nullptr, T, k, h,
+      return launch_ggemm_mx<kMXFP4, false>(down, down, slot_map, n_slots, E, offsets, nullptr, T, k, h,
                                     I, H, nullptr, y, err, stream);
     case kQ8_0:
       return launch_ggemm_t<kQ8_0, false>(down, down, slot_map, n_slots, E, offsets, nullptr, T,
@@ -857,8 +901,8 @@ hipError_t launch_down_grouped(int fmt, const PoolView& down, const int32_t* slo
       return launch_ggemm_t<kQ5_K, false>(down, down, slot_map, n_slots, E, offsets, nullptr, T,
                                           k, h, I, H, nullptr, y, err, stream);
     case kQ6_K:
-      return launch_ggemm_t<kQ6_K, false>(down, down, slot_map, n_slots, E, offsets, nullptr, T,
-                                          k, h, I, H, nullptr, y, err, stream);
+      return launch_ggemm_mx<kQ6_K, false>(down, down, slot_map, n_slots, E, offsets, nullptr, T,
+                                           k, h, I, H, nullptr, y, err, stream);
     default: return hipErrorInvalidValue;
   }
 }
