@@ -494,10 +494,10 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
 }
 
 // Q6_K: the two exact bf16 operands of 8 weights' integer parts v = sc * (q - 32), sc the
-// half block's int8 scale (|v| <= 4096, at most 14 bits):
-//   hi = (v with its low 7 bits cleared) - 128, a multiple of 128 within +-4224 (at most 6
-//        significant bits), and lo = the bf16 of exponent 7 and mantissa v & 127, i.e.
-//        128 + (v & 127),
+// half block's int8 scale (|v| <= 4096, at most 14 bits). With w = v - 128:
+//   hi = w with its low 7 bits cleared: a multiple of 128 within [-4224, 3840], at most 6
+//        significant bits, and
+//   lo = the bf16 of exponent 7 and mantissa w & 127, i.e. 128 + (w & 127),
 // so hi + lo = v exactly and two MFMAs against the same A give sum x v. qd: one code dword
 // (low nibbles of elements 0..3 in its bytes, high nibbles elements 4..7); hw >> sh and
 // hw >> (sh + 2): the elements' 2-bit high parts as bytes (the pool's high-part layout).
@@ -506,19 +506,18 @@ __device__ __forceinline__ void q6k_parts(uint32_t qd, uint32_t hw, int sh, int 
   const uint32_t qa = (qd & 0x0F0F0F0Fu) | (((hw >> sh) & 0x03030303u) << 4);
   const uint32_t qb = ((qd >> 4) & 0x0F0F0F0Fu) | (((hw >> (sh + 2)) & 0x03030303u) << 4);
   const uint32_t scp = ((uint32_t)sc & 0xFFFFu) * 0x00010001u;
-  const uint32_t cp = ((uint32_t)(-32 * sc) & 0xFFFFu) * 0x00010001u;
+  const uint32_t cp = ((uint32_t)(-32 * sc - 128) & 0xFFFFu) * 0x00010001u;
   u32x4 hi, lo;
 #pragma unroll
   for (int pr = 0; pr < 4; ++pr) {
-    // elements 2 pr, 2 pr + 1 as two 16-bit lanes, then v = sc q - 32 sc per lane
+    // elements 2 pr, 2 pr + 1 as two 16-bit lanes, then w = sc q - 32 sc - 128 per lane
     const uint32_t qq = __builtin_amdgcn_perm(0u, pr < 2 ? qa : qb, (pr & 1) ? 0x0c030c02u : 0x0c010c00u);
-    const i16x2 vv = __builtin_bit_cast(i16x2, qq) * __builtin_bit_cast(i16x2, scp) +
+    const i16x2 wv = __builtin_bit_cast(i16x2, qq) * __builtin_bit_cast(i16x2, scp) +
                      __builtin_bit_cast(i16x2, cp);
-    const uint32_t v = __builtin_bit_cast(uint32_t, vv);
-    lo[pr] = (v & 0x007F007Fu) | 0x43004300u;
-    const i16x2 hv = __builtin_bit_cast(i16x2, v & 0xFF80FF80u) - i16x2{128, 128};
-    const uint32_t h = __builtin_bit_cast(uint32_t, hv);
-    const float f0 = (float)(int16_t)(h & 0xFFFFu), f1 = (float)(int16_t)(h >> 16);
+    const uint32_t w = __builtin_bit_cast(uint32_t, wv);
+    lo[pr] = (w & 0x007F007Fu) | 0x43004300u;
+    const i16x2 h = __builtin_bit_cast(i16x2, w & 0xFF80FF80u);
+    const float f0 = (float)h[0], f1 = (float)h[1];
     hi[pr] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
   }
   bhi = __builtin_bit_cast(bf16x8, hi);
@@ -535,24 +534,27 @@ __device__ __forceinline__ int lds_row_swizzle(int m) {
   return (m & 3) | (((m >> 3) & 1) << 2) | ((((m >> 2) ^ (m >> 3)) & 1) << 3);
 }
 
-// Zeros that the MXFP4 kernel's LDS loads read for A pieces past K.
+// Zeros that the direct-LDS kernel's loads read for A pieces past K.
 __device__ __attribute__((aligned(16))) uint32_t g_zero16[4];
 
-// MXFP4 grouped GEMM with its tiles loaded straight into LDS (gfx950 global_load_lds_dwordx4:
-// 64 lanes x 16 bytes land contiguously at an LDS address the wave names), so no register
-// holds a staged operand; each workgroup waits for its own step's loads while the other
-// workgroups on the CU (three fit) run their MFMAs. Tile 64 bucket rows x 256 weight rows
-// (waves 1 x 4, each a 64 x 64 block), 128 K per step: MXFP4 B is the smallest operand per
-// weight, so a wide tile cuts the A (activation) bytes that each CU pulls in per flop.
+// Grouped GEMM (MXFP4, Q6_K) with its tiles loaded straight into LDS (gfx950
+// global_load_lds_dwordx4: 64 lanes x 16 bytes land contiguously at an LDS address the wave
+// names), so no register holds a staged operand; each workgroup waits for its own step's
+// loads while the other workgroups on the CU run their MFMAs (three fit for MXFP4, two for
+// Q6_K, whose operand building needs more registers). Tile 64 bucket rows x 256 weight rows
+// (waves 1 x 4, each a 64 x 64 block), 128 K per step: 4-bit and 6-bit B are the smallest
+// operands per weight, so a wide tile cuts the A (activation) bytes each CU pulls in per flop.
 //   A: row r of the tile at r * 256 bytes, its 16-byte piece c (8 K) at position
 //      c ^ lds_row_swizzle(r % 16), which keeps every 128-bit operand read free of bank
 //      conflicts. A lane's load picks the global piece whose position is its lane slot;
 //      pieces past K read zeros.
-//   B: the step's run of each of the 16 row groups (64 units of 16 bytes, 1 KiB) verbatim;
-//      scales: the runs' 64 bytes each, verbatim. A lane reads its whole unit at once
-//      (consecutive 16-byte reads: no bank conflicts) and widens one 32-K slice at a time.
+//   B: the step's run of each of the 16 row groups (64 units of 16 bytes, 1 KiB) verbatim,
+//      and likewise the runs' scales (MXFP4: one byte a unit), or their 2-bit high parts,
+//      scale records and d records (Q6_K). A lane reads its whole unit at once (consecutive
+//      16-byte reads: no bank conflicts); MXFP4 widens one 32-K slice at a time, Q6_K builds
+//      the slice's two exact operands (q6k_parts).
 template <int FMT, bool GATED>
-__global__ __launch_bounds__(kTThreads, 3) void k_ggemm_mx(
+__global__ __launch_bounds__(kTThreads, FMT == kQ6_K ? 2 : 3) void k_ggemm_mx(
     const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as, int64_t qslot,
     int64_t sslot, const uint8_t* __restrict__ bq, const uint8_t* __restrict__ bs,
     const int32_t* __restrict__ slot_map, int n_slots, int E,
@@ -780,14 +782,19 @@ __global__ __launch_bounds__(kTThreads, 3) void k_ggemm_mx(
         for (int mf = 0; mf < 4; ++mf) t[mf] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
+          // the A reads first (their latency hides behind building the operands), then the
+          // hi MFMAs of all 4 row fragments and the lo ones: no MFMA waits on the one before
+          bf16x8 av[4];
+#pragma unroll
+          for (int mf = 0; mf < 4; ++mf) av[mf] = read_a(mf, ii);
           bf16x8 bhi, blo;
           q6k_parts(q4[ii], h2[ii >> 1], 4 * (ii & 1), (int)(int8_t)(rec >> (8 * (ii >> 1))), bhi, blo);
 #pragma unroll
-          for (int mf = 0; mf < 4; ++mf) {
-            const bf16x8 av = read_a(mf, ii);
-            t[mf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bhi, t[mf], 0, 0, 0);
-            t[mf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, blo, t[mf], 0, 0, 0);
-          }
+          for (int mf = 0; mf < 4; ++mf)
+            t[mf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mf], bhi, t[mf], 0, 0, 0);
+#pragma unroll
+          for (int mf = 0; mf < 4; ++mf)
+            t[mf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mf], blo, t[mf], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);   // one slice's operands live at a time
         }
 #pragma unroll
