@@ -7,19 +7,19 @@
 //   * the workgroup grid is sized for the worst case, sum_e ceil(n_e / BM) <= T*k/BM + E
 //     row tiles, times the column tiles; each workgroup finds its (expert, row tile) from
 //     the bucket offsets and exits if it has none, so the host never reads the counts;
-//   * A rows are gathered through perm on load (gate/up: x[perm[pos] / k]; down: h[pos]),
-//     staged in LDS one 128-wide K step at a time, and prefetched into registers one step
-//     ahead;
-//   * B comes straight from the tiled pool: a 64-lane 16-byte load is 16 weight rows x 4
-//     MXFP4 blocks, exactly the operand shape of four v_mfma_f32_16x16x32_bf16 (the 32-wide
-//     K of one MFMA is a fixed permutation of the step's 128 K indices, applied to A and B
-//     alike); codes are widened to bf16 in registers with the block scale folded in, which is
-//     exact for MXFP4. For Q8_0 each MFMA covers exactly one block, its int8 codes are exact
-//     in bf16, and the block scale d multiplies the fp32 MFMA result before accumulation;
+//   * A rows are gathered through perm on load (gate/up: x[perm[pos] / k]; down: h[pos]);
+//   * B comes straight from the tiled pool, whose 16-byte units hold one 32-element block
+//     of one weight row, 16 rows side by side;
+//   * the weights enter the MFMAs as exact bf16 values: MXFP4 codes widened with the
+//     power-of-two scale folded in, Q6_K as two exact bf16 parts of each sc * (q - 32) with
+//     d applied per K step, Q8_0 and Q4_K / Q5_K as their integer codes with the fp32 block
+//     scales (and mins) applied to each block's MFMA result;
 //   * gate and up tiles of the same columns live in the same wave, so SwiGLU is applied in
 //     registers and h is written once, rounded to bf16; the down projection writes fp32 y
 //     with nontemporal stores (y is read once, by the combine, and is far larger than the
 //     caches: the stores then do not evict the A and B tiles other workgroups still read).
+// Two kernels: k_ggemm_mx (MXFP4, Q6_K) loads its tiles straight into LDS; k_ggemm (Q8_0,
+// Q4_K, Q5_K) stages them through registers one K step ahead.
 #include <type_traits>
 
 #include "common.hpp"
@@ -86,10 +86,9 @@ struct BStage {
   static constexpr int kHDwords = NG * kRunH / 4 / kTThreads;  // high-part dwords per thread
 };
 
-// BM: bucket rows per tile, 128 (waves 2 x 2) or 64 (waves 1 x 4). Each wave computes a
-// 64 x 64 block of the tile (gate/up: 32 gate + the same 32 up columns, twice), so a tile
-// spans 64 * 4 / (BM / 64) columns of weight rows: fewer A bytes per flop at BM = 64.
-template <int FMT, bool GATED, int BM>
+// Q8_0, Q4_K and Q5_K: tiles of 128 bucket rows x 128 weight rows (waves 2 x 2). Each wave
+// computes a 64 x 64 block of the tile (gate/up: 32 gate + the same 32 up columns, twice).
+template <int FMT, bool GATED>
 __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
     const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as, int64_t qslot,
     int64_t sslot, const uint8_t* __restrict__ bq, const uint8_t* __restrict__ bs,
@@ -97,10 +96,10 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm, int k,
     const uint16_t* __restrict__ src, int K, int N, int n_mtiles, int n_ntiles,
     uint16_t* __restrict__ h_out, float* __restrict__ y_out, uint32_t* __restrict__ err_flags) {
+  constexpr int BM = 128;                     // bucket rows per tile
   constexpr int WM = BM / 64, WN = 4 / WM;   // waves along rows / columns
   constexpr int NG = 4 * WN;                  // weight row groups per tile
   constexpr int RPT = BM / 16;                // A rows staged per thread
-  static_assert(BM == 64 || BM == 128, "64 or 128 rows per tile");
   static_assert(FMT != kMXFP4 && FMT != kQ6_K, "MXFP4 and Q6_K run k_ggemm_mx");
   using BS = BStage<FMT, NG>;
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[BM * kLdsStride];
@@ -846,18 +845,19 @@ hipError_t launch_ggemm_mx(const PoolView& a, const PoolView& b, const int32_t* 
   return hipGetLastError();
 }
 
-template <int FMT, bool GATED, int BM = 128>
+template <int FMT, bool GATED>
 hipError_t launch_ggemm_t(const PoolView& a, const PoolView& b, const int32_t* slot_map,
                           int n_slots, int E, const int32_t* offsets, const int32_t* perm,
                           int T, int k, const uint16_t* src, int K, int N, uint16_t* h,
                           float* y, uint32_t* err, hipStream_t stream) {
+  constexpr int BM = 128;
   const int pairs = T * k;
   const int max_mtiles = (pairs + BM - 1) / BM + min(E, pairs);
-  constexpr int kCols = GATED ? 32 * (256 / BM) : 64 * (256 / BM);   // columns per tile
+  constexpr int kCols = GATED ? 64 : 128;   // columns per tile (gate/up: of each matrix)
   const int n_ntiles = (N + kCols - 1) / kCols;
   const int64_t grid = ((int64_t)max_mtiles * n_ntiles + 511) / 512 * 512;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_ggemm<FMT, GATED, BM>), dim3((unsigned)grid), dim3(kTThreads), 0, stream,
+  hipLaunchKernelGGL((k_ggemm<FMT, GATED>), dim3((unsigned)grid), dim3(kTThreads), 0, stream,
                      a.q, a.s, a.q_slot, a.s_slot, b.q, b.s, slot_map, n_slots, E, offsets, perm,
                      k, src, K, N, max_mtiles, n_ntiles, h, y, err);
   return hipGetLastError();
