@@ -494,7 +494,7 @@ __global__ __launch_bounds__(kTThreads, 2) void k_ggemm(
 
 // Q6_K: the two exact bf16 operands of 8 weights' integer parts v = sc * (q - 32), sc the
 // half block's int8 scale (|v| <= 4096, at most 14 bits). With w = v - 128:
-//   hi = w with its low 7 bits cleared: a multiple of 128 within [-4224, 3840], at most 6
+//   hi = w with its low 7 bits cleared: a multiple of 128 within [-4224, 3968], at most 6
 //        significant bits, and
 //   lo = the bf16 of exponent 7 and mantissa w & 127, i.e. 128 + (w & 127),
 // so hi + lo = v exactly and two MFMAs against the same A give sum x v. qd: one code dword

@@ -36,5 +36,5 @@ def test_q6k_two_part_split_is_exact(sc_range):
     # lo's bf16 bits are 0x4300 | rem: exponent field 134 (2^7), mantissa rem
     lo_bits = (lo.astype(np.float32).view(np.uint32) >> 16).astype(np.int64)
     assert np.array_equal(lo_bits, 0x4300 | rem)
-    # hi spans multiples of 128 within [-4224, 3840]: at most 6 significant bits
-    assert hi.min() >= -4224 and hi.max() <= 3840 and (hi % 128 == 0).all()
+    # hi spans multiples of 128 within [-4224, 3968]: at most 6 significant bits
+    assert hi.min() >= -4224 and hi.max() <= 3968 and (hi % 128 == 0).all()
