@@ -150,11 +150,13 @@ __global__ __launch_bounds__(256) void k_router(const uint16_t* __restrict__ x,
 }
 
 // Partial logits of the split router for a small batch (T <= 16): one wave per slice z of
-// the reduction dimension (the slices of router_tile, whole pairs of 32-wide steps), its
-// steps accumulated in increasing order in one MFMA chain and stored from registers as
-// partial[z][t][e]. A slice holds at most a few steps, so the wave issues the loads of RB
-// steps before the MFMAs that consume them; rows past T or E are loaded from a valid row
-// and zeroed when consumed.
+// the reduction dimension (the slices of router_tile, whole pairs of 32-wide steps) and
+// group blockIdx.y of NF 16-expert tiles, its steps accumulated in increasing order in one
+// MFMA chain and stored from registers as partial[z][t][e]. A slice holds at most a few
+// steps, so the wave issues the loads of RB steps before the MFMAs that consume them; rows
+// past T or E are loaded from a valid row and zeroed when consumed. Splitting the experts
+// over workgroups as well keeps each wave's share of the router weights to a few KB, so
+// the read is spread over many CUs.
 template <int NF>
 __global__ __launch_bounds__(kWave) void k_router_part(const uint16_t* __restrict__ x,
                                                        const uint16_t* __restrict__ wr, int T,
@@ -171,13 +173,14 @@ __global__ __launch_bounds__(kWave) void k_router_part(const uint16_t* __restric
   const int row = lane & 15;        // token (A) / expert (B) within the 16-tile
   const int kq = (lane >> 4) * 8;   // this lane's 8-element slice of the 32-step
   const bool tok_ok = row < T;
+  const int e0 = (int)blockIdx.y * NF * 16;   // first expert of this workgroup's tiles
   const uint16_t* xr = x + (int64_t)(tok_ok ? row : 0) * H + kq;
   const uint16_t* wrow[NF];
   bool e_ok[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
-    e_ok[f] = f * 16 + row < E;
-    wrow[f] = wr + (int64_t)(e_ok[f] ? f * 16 + row : 0) * H + kq;
+    e_ok[f] = e0 + f * 16 + row < E;
+    wrow[f] = wr + (int64_t)(e_ok[f] ? e0 + f * 16 + row : 0) * H + kq;
   }
   f32x4 acc[NF];
 #pragma unroll
@@ -208,13 +211,13 @@ __global__ __launch_bounds__(kWave) void k_router_part(const uint16_t* __restric
     }
   }
   // the next kernel's synchronisation words start at zero
-  if (z == 0)
+  if (z == 0 && blockIdx.y == 0)
     for (int i = lane; i < n_sync; i += kWave) sync[i] = 0;
-  // lane holds D[token 4*(lane/16)+v][expert 16f + lane%16]
+  // lane holds D[token 4*(lane/16)+v][expert e0 + 16f + lane%16]
   float* dst = partial + (int64_t)z * T * E;
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
-    const int e = f * 16 + row;
+    const int e = e0 + f * 16 + row;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int t = 4 * (lane >> 4) + v;
@@ -351,19 +354,11 @@ hipError_t launch_router_partials(const uint16_t* x, const uint16_t* wr, int T, 
                                   int ns, float* partial, hipStream_t stream, int32_t* sync,
                                   int n_sync) {
   if (T < 1 || T > kRouteTok || ns < 2 || ns > kMaxSplit) return hipErrorInvalidValue;
-#define MOE_PART_CASE(N)                                                                     \
-  case N:                                                                                   \
-    hipLaunchKernelGGL(k_router_part<N>, dim3(ns), dim3(kWave), 0, stream, x, wr, T, H, E,  \
-                       partial, sync, sync != nullptr ? n_sync : 0);                        \
-    break;
-  switch ((E + 15) / 16) {
-    MOE_PART_CASE(1) MOE_PART_CASE(2) MOE_PART_CASE(3) MOE_PART_CASE(4)
-    MOE_PART_CASE(5) MOE_PART_CASE(6) MOE_PART_CASE(7) MOE_PART_CASE(8)
-    MOE_PART_CASE(9) MOE_PART_CASE(10) MOE_PART_CASE(11) MOE_PART_CASE(12)
-    MOE_PART_CASE(13) MOE_PART_CASE(14) MOE_PART_CASE(15) MOE_PART_CASE(16)
-    default: return hipErrorInvalidValue;
-  }
-#undef MOE_PART_CASE
+  const int ntiles = (E + 15) / 16;
+  if (E < 1 || ntiles > 16) return hipErrorInvalidValue;
+  // one 16-expert tile per workgroup: ns x ntiles single-wave workgroups
+  hipLaunchKernelGGL(k_router_part<1>, dim3(ns, ntiles), dim3(kWave), 0, stream, x, wr, T, H, E,
+                     partial, sync, sync != nullptr ? n_sync : 0);
   return hipGetLastError();
 }
 
