@@ -540,19 +540,21 @@ __device__ __attribute__((aligned(16))) uint32_t g_zero16[4];
 // global_load_lds_dwordx4: 64 lanes x 16 bytes land contiguously at an LDS address the wave
 // names), so no register holds a staged operand; each workgroup waits for its own step's
 // loads while the other workgroups on the CU run their MFMAs (three fit for MXFP4, two for
-// Q6_K, whose operand building needs more registers). Tile 64 bucket rows x 256 weight rows
-// (waves 1 x 4, each a 64 x 64 block), 128 K per step: 4-bit and 6-bit B are the smallest
-// operands per weight, so a wide tile cuts the A (activation) bytes each CU pulls in per flop.
+// Q6_K, whose operand building needs more registers). MXFP4: BM = 64 bucket rows x 256
+// weight rows (waves 1 x 4, each a 64 x 64 block, NF = 4 n-fragments), 128 K per step: 4-bit
+// B is the smallest operand per weight, so a wide tile cuts the A (activation) bytes each
+// CU pulls in per flop. Q6_K: BM = 128 x 128 (each wave 128 x 32, NF = 2), so each pair of
+// exact operands it builds (about 40 VALU per fragment and slice) feeds 16 MFMAs.
 //   A: row r of the tile at r * 256 bytes, its 16-byte piece c (8 K) at position
 //      c ^ lds_row_swizzle(r % 16), which keeps every 128-bit operand read free of bank
 //      conflicts. A lane's load picks the global piece whose position is its lane slot;
 //      pieces past K read zeros.
-//   B: the step's run of each of the 16 row groups (64 units of 16 bytes, 1 KiB) verbatim,
+//   B: the step's run of each of the 4 NF row groups (64 units of 16 bytes, 1 KiB) verbatim,
 //      and likewise the runs' scales (MXFP4: one byte a unit), or their 2-bit high parts,
 //      scale records and d records (Q6_K). A lane reads its whole unit at once (consecutive
 //      16-byte reads: no bank conflicts); MXFP4 widens one 32-K slice at a time, Q6_K builds
 //      the slice's two exact operands (q6k_parts).
-template <int FMT, bool GATED>
+template <int FMT, bool GATED, int BM, int NF>
 __global__ __launch_bounds__(kTThreads, FMT == kQ6_K ? 2 : 3) void k_ggemm_mx(
     const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as, int64_t qslot,
     int64_t sslot, const uint8_t* __restrict__ bq, const uint8_t* __restrict__ bs,
@@ -561,17 +563,23 @@ __global__ __launch_bounds__(kTThreads, FMT == kQ6_K ? 2 : 3) void k_ggemm_mx(
     const uint16_t* __restrict__ src, int K, int N, int n_mtiles, int n_ntiles,
     uint16_t* __restrict__ h_out, float* __restrict__ y_out, uint32_t* __restrict__ err_flags) {
   static_assert(FMT == kMXFP4 || FMT == kQ6_K, "MXFP4 or Q6_K");
+  static_assert(BM == 64 || BM == 128, "64 or 128 bucket rows");
+  static_assert(NF == 4 || (NF == 2 && FMT == kQ6_K), "n-fragments per wave");
   constexpr bool kQ6 = FMT == kQ6_K;
-  constexpr int BM = 64, NG = 16, NF = 4;   // rows, B row groups, n-fragments per wave
+  constexpr int NG = 4 * NF;       // B row groups per tile: each wave loads NF of them
+  constexpr int TN = GATED ? NG / 2 * 16 : NG * 16;   // tile columns (gate/up: of each matrix)
+  constexpr int MF = BM / 16;      // row fragments per wave (every wave covers all BM rows)
+  constexpr int RW = BM / 4;       // tile rows each wave loads, 4 per load
+  constexpr int NA = RW / 4;       // A loads per wave per step
   typedef __attribute__((address_space(3))) void* lds_ptr;
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[BM * 256];
   __shared__ __attribute__((aligned(16))) uint8_t lds_bq[NG * 1024];
   // per run: MXFP4's 64 E8M0 bytes; Q6_K's 64 records of two int8 half-block scales
   __shared__ __attribute__((aligned(16))) uint8_t lds_bs[NG * (kQ6 ? 128 : 64)];
   // Q6_K: the runs' 2-bit high parts (8 bytes per unit), and each group's 16 rows' d records
-  // of the step's super-block
+  // of the step's super-block (a 256-byte region per loading wave, NF groups of 64 bytes used)
   __shared__ __attribute__((aligned(16))) uint8_t lds_bh[kQ6 ? NG * 512 : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_bd[kQ6 ? NG * 64 : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_bd[kQ6 ? 4 * 256 : 16];
   __shared__ int tmp4[4];
   __shared__ int sh[2];
   const int lane = threadIdx.x & (kWave - 1);
@@ -592,9 +600,9 @@ __global__ __launch_bounds__(kTThreads, FMT == kQ6_K ? 2 : 3) void k_ggemm_mx(
   if (!map_row_tile(offsets, E, BM, mt, &e, &m0, tmp4, sh)) return;
   const int mend = offsets[e + 1];
   const int slot = slot_map[e];
-  const int n0 = GATED ? nt * 128 : nt * 256;
+  const int n0 = nt * TN;
   if (slot < 0 || slot >= n_slots) {
-    const int ncols = GATED ? 128 : 256;
+    const int ncols = TN;
     for (int t = threadIdx.x; t < BM * ncols; t += kTThreads) {
       const int pos = m0 + t / ncols, n = n0 + t % ncols;
       if (pos < mend && n < N) {
@@ -608,94 +616,96 @@ __global__ __launch_bounds__(kTThreads, FMT == kQ6_K ? 2 : 3) void k_ggemm_mx(
   const int nb = K / 32;
   const int nsteps = (K + kBK - 1) / kBK;
 
-  // ---- A: wave wn loads rows 16 wn + 4 j + lane / 16 (j < 4), position lane % 16
+  // ---- A: wave wn loads rows RW wn + 4 j + lane / 16 (j < NA), position lane % 16
   const u32x4* src16 = (const u32x4*)src;
   const uint32_t kp = (uint32_t)K / 8;     // 16-byte units per row
   const int apos = lane & 15;
-  uint32_t arow[4];                        // unit index of each row's start
-  int aswz[4];                             // the global piece that lands at position apos
+  uint32_t arow[NA];                       // unit index of each row's start
+  int aswz[NA];                            // the global piece that lands at position apos
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = 16 * wn + 4 * j + (lane >> 4);
+  for (int j = 0; j < NA; ++j) {
+    const int r = RW * wn + 4 * j + (lane >> 4);
     const int pos = min(m0 + r, mend - 1);   // rows past the tile's end repeat its last row
     const int row = GATED ? perm[pos] / k : pos;
     arow[j] = (uint32_t)row * kp;
     aswz[j] = apos ^ lds_row_swizzle(r & 15);
   }
-  // ---- B: wave wn copies the runs of local row groups 4 wn .. 4 wn + 3. GATED: groups
-  // g < 8 are gate rows n0/16 + g, g >= 8 up rows n0/16 + g - 8; a group past N reads
-  // group 0 (never stored).
+  // ---- B: wave wn copies the runs of local row groups NF wn .. NF wn + NF - 1. GATED:
+  // groups g < NG/2 are gate rows n0/16 + g, g >= NG/2 up rows n0/16 + g - NG/2; a group
+  // past N reads group 0 (never stored).
+  constexpr int NGH = NG / 2;
   const uint8_t* q0 = aq + (int64_t)slot * qslot;
   const uint8_t* s0 = as + (int64_t)slot * sslot;
   const uint8_t* q1 = GATED ? bq + (int64_t)slot * qslot : q0;
   const uint8_t* s1 = GATED ? bs + (int64_t)slot * sslot : s0;
-  const uint8_t* brun[4];
+  auto group_rgc = [&](int g) {
+    const int rg = GATED ? n0 / 16 + g % NGH : n0 / 16 + g;
+    return rg * 16 < N ? rg : 0;
+  };
+  // fixed-size arrays: when load_step captured arrays sized by NF, hipcc's host pass
+  // silently dropped the kernel's launch stub
+  const uint8_t* brun[4];   // the first NF are used
   const uint8_t* srun;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int g = 4 * wn + j;
-    const int rg = GATED ? n0 / 16 + (g & 7) : n0 / 16 + g;
-    const int rgc = rg * 16 < N ? rg : 0;
-    brun[j] = (GATED && g >= 8 ? q1 : q0) + (int64_t)rgc * nb * 16 * 16;
+    const int g = NF * wn + (j < NF ? j : 0);
+    brun[j] = (GATED && g >= NGH ? q1 : q0) + (int64_t)group_rgc(g) * nb * 16 * 16;
   }
-  auto group_rgc = [&](int g) {
-    const int rg = GATED ? n0 / 16 + (g & 7) : n0 / 16 + g;
-    return rg * 16 < N ? rg : 0;
-  };
-  const uint8_t* hrun[2] = {nullptr, nullptr};   // Q6_K: high parts and scale records
-  const uint8_t* rrun[2] = {nullptr, nullptr};
-  const uint8_t* drun = nullptr;                 // Q6_K: d records
+  const uint8_t* hrun[2] = {nullptr, nullptr};   // Q6_K: high parts and scale records (the
+  const uint8_t* rrun[2] = {nullptr, nullptr};   // first NF / 2 are used)
+  const uint8_t* drun = nullptr;   // Q6_K: d records
   if constexpr (!kQ6) {
-    // scales: lane l copies dword l % 16 of run 4 wn + l / 16
-    const int g = 4 * wn + (lane >> 4);
-    srun = (GATED && g >= 8 ? s1 : s0) + (int64_t)group_rgc(g) * nb * 16 + (lane & 15) * 4;
+    // scales: lane l copies dword l % 16 of run NF wn + l / 16 (NF = 4)
+    const int g = NF * wn + (lane >> 4);
+    srun = (GATED && g >= NGH ? s1 : s0) + (int64_t)group_rgc(g) * nb * 16 + (lane & 15) * 4;
   } else {
     srun = nullptr;
-    // high parts: load h copies the runs of groups 4 wn + 2 h (lanes 0..31) and 4 wn + 2 h + 1
-    // (lanes 32..63), 16 bytes a lane; scale records likewise, 4 bytes a lane; d records:
-    // lane l copies row l % 16 of group 4 wn + l / 16
+    // high parts: load h copies the runs of groups NF wn + 2 h (lanes 0..31) and
+    // NF wn + 2 h + 1 (lanes 32..63), 16 bytes a lane; scale records likewise, 4 bytes a
+    // lane; d records: lane l copies row l % 16 of group NF wn + min(l / 16, NF - 1) into
+    // the wave's 256-byte region (lanes past the wave's groups fill its spare bytes)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int g = 4 * wn + 2 * h + (lane >> 5);
+    for (int h = 0; h < NF / 2; ++h) {
+      const int g = NF * wn + 2 * h + (lane >> 5);
       const int64_t u0 = (int64_t)group_rgc(g) * nb * 16;   // first unit of the group
-      hrun[h] = (GATED && g >= 8 ? q1 : q0) + hi_region(N, K) + u0 * 8 + (lane & 31) * 16;
-      rrun[h] = (GATED && g >= 8 ? s1 : s0) + u0 * 2 + (lane & 31) * 4;
+      hrun[h] = (GATED && g >= NGH ? q1 : q0) + hi_region(N, K) + u0 * 8 + (lane & 31) * 16;
+      rrun[h] = (GATED && g >= NGH ? s1 : s0) + u0 * 2 + (lane & 31) * 4;
     }
-    const int g = 4 * wn + (lane >> 4);
+    const int g = NF * wn + min(lane >> 4, NF - 1);
     const int nsb = nb / kSuperBlocks;
-    drun = (GATED && g >= 8 ? s1 : s0) + super_region(N, K) +
+    drun = (GATED && g >= NGH ? s1 : s0) + super_region(N, K) +
            ((int64_t)group_rgc(g) * nsb * kRowGroup + (lane & 15)) * kSuperBytes;
   }
   const int ublk = lane >> 4;   // block (of the step's 4) of the lane's B unit
   auto load_step = [&](int c) {
     const int kk = c * kBK;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NA; ++j) {
       const bool ok = kk + aswz[j] * 8 < K;
       const void* gp = ok ? (const void*)(src16 + arow[j] + (uint32_t)(kk / 8 + aswz[j]))
                           : (const void*)g_zero16;
-      __builtin_amdgcn_global_load_lds(gp, (lds_ptr)(lds_a + (16 * wn + 4 * j) * 256), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(gp, (lds_ptr)(lds_a + (RW * wn + 4 * j) * 256), 16, 0, 0);
     }
     // B: blocks past the row re-read step 0 (their scales are masked when consumed)
     const int cs = 4 * c + ublk < nb ? c : 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NF; ++j)
       __builtin_amdgcn_global_load_lds(brun[j] + (int64_t)cs * 1024 + lane * 16,
-                                       (lds_ptr)(lds_bq + (4 * wn + j) * 1024), 16, 0, 0);
+                                       (lds_ptr)(lds_bq + (NF * wn + j) * 1024), 16, 0, 0);
     if constexpr (!kQ6) {
       const int css = 4 * c + (lane & 15) / 4 < nb ? c : 0;
       __builtin_amdgcn_global_load_lds(srun + (int64_t)css * 64, (lds_ptr)(lds_bs + 256 * wn), 4, 0, 0);
     } else {
       // K is a whole number of 256-element super-blocks: every step is in range
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < NF / 2; ++h) {
         __builtin_amdgcn_global_load_lds(hrun[h] + (int64_t)c * 512,
-                                         (lds_ptr)(lds_bh + (4 * wn + 2 * h) * 512), 16, 0, 0);
+                                         (lds_ptr)(lds_bh + (NF * wn + 2 * h) * 512), 16, 0, 0);
         __builtin_amdgcn_global_load_lds(rrun[h] + (int64_t)c * 128,
-                                         (lds_ptr)(lds_bs + (4 * wn + 2 * h) * 128), 4, 0, 0);
+                                         (lds_ptr)(lds_bs + (NF * wn + 2 * h) * 128), 4, 0, 0);
       }
       __builtin_amdgcn_global_load_lds(drun + (int64_t)(c >> 1) * kRowGroup * kSuperBytes,
-                                       (lds_ptr)(lds_bd + 4 * wn * 64), 4, 0, 0);
+                                       (lds_ptr)(lds_bd + 256 * wn), 4, 0, 0);
     }
   };
 
@@ -718,9 +728,9 @@ __global__ __launch_bounds__(kTThreads, FMT == kQ6_K ? 2 : 3) void k_ggemm_mx(
     }
     fcol[f] = col0 < N;
   }
-  f32x4 acc[4][NF];
+  f32x4 acc[MF][NF];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < MF; ++a)
 #pragma unroll
     for (int f = 0; f < NF; ++f) acc[a][f] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int g4 = lane >> 4;
@@ -731,7 +741,7 @@ __global__ __launch_bounds__(kTThreads, FMT == kQ6_K ? 2 : 3) void k_ggemm_mx(
     load_step(c);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();   // every wave's loads have landed
-    // all 4 row fragments run: rows past the expert's last pair repeat it and are never stored
+    // all MF row fragments run: rows past the expert's last pair repeat it and are never stored
     auto read_a = [&](int mf, int ii) {
       const int row = 16 * mf + mrow;
       return __builtin_bit_cast(bf16x8, *(const u32x4*)(lds_a + row * 256 + ((4 * g4 + ii) ^ rswz) * 16));
@@ -748,11 +758,11 @@ __global__ __launch_bounds__(kTThreads, FMT == kQ6_K ? 2 : 3) void k_ggemm_mx(
       }
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        // one 32-K slice: the wave's 4 A fragments are read once; each B fragment is widened
-        // just before its 4 MFMAs, so a single widened fragment is live at a time
-        bf16x8 av[4];
+        // one 32-K slice: the wave's MF A fragments are read once; each B fragment is
+        // widened just before its MF MFMAs, so a single widened fragment is live at a time
+        bf16x8 av[MF];
 #pragma unroll
-        for (int mf = 0; mf < 4; ++mf) {
+        for (int mf = 0; mf < MF; ++mf) {
           const int row = 16 * mf + mrow;
           const int piece = (4 * g4 + ii) ^ rswz;
           av[mf] = __builtin_bit_cast(bf16x8, *(const u32x4*)(lds_a + row * 256 + piece * 16));
@@ -761,7 +771,7 @@ __global__ __launch_bounds__(kTThreads, FMT == kQ6_K ? 2 : 3) void k_ggemm_mx(
         for (int f = 0; f < NF; ++f) {
           const bf16x8 bv = fp4x8_to_bf16x8(bq4[f][ii], bsc[f]);
 #pragma unroll
-          for (int mf = 0; mf < 4; ++mf)
+          for (int mf = 0; mf < MF; ++mf)
             acc[mf][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mf], bv, acc[mf][f], 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);   // keep the next slice's reads after these MFMAs
@@ -775,29 +785,36 @@ __global__ __launch_bounds__(kTThreads, FMT == kQ6_K ? 2 : 3) void k_ggemm_mx(
         const u32x4 q4 = *(const u32x4*)(lds_bq + fg[f] * 1024 + lane * 16);
         const u32x2 h2 = *(const u32x2*)(lds_bh + fg[f] * 512 + lane * 8);
         const uint32_t rec = *(const uint16_t*)(lds_bs + fg[f] * 128 + lane * 2);
-        const float d = fcol[f] ? fp16_to_f32(*(const uint16_t*)(lds_bd + fg[f] * 64 + mrow * 4)) : 0.f;
-        f32x4 t[4];
+        const uint8_t* drec = lds_bd + (fg[f] / NF) * 256 + (fg[f] % NF) * 64 + mrow * 4;
+        const float d = fcol[f] ? fp16_to_f32(*(const uint16_t*)drec) : 0.f;
+        f32x4 t[MF];
 #pragma unroll
-        for (int mf = 0; mf < 4; ++mf) t[mf] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int mf = 0; mf < MF; ++mf) t[mf] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-          // the A reads first (their latency hides behind building the operands), then the
-          // hi MFMAs of all 4 row fragments and the lo ones: no MFMA waits on the one before
-          bf16x8 av[4];
-#pragma unroll
-          for (int mf = 0; mf < 4; ++mf) av[mf] = read_a(mf, ii);
+          // per group of 4 row fragments: the A reads first (the first group's latency hides
+          // behind building the operands), then their hi MFMAs and their lo ones, so no MFMA
+          // waits on the one before and only 4 A fragments are live
           bf16x8 bhi, blo;
-          q6k_parts(q4[ii], h2[ii >> 1], 4 * (ii & 1), (int)(int8_t)(rec >> (8 * (ii >> 1))), bhi, blo);
 #pragma unroll
-          for (int mf = 0; mf < 4; ++mf)
-            t[mf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mf], bhi, t[mf], 0, 0, 0);
+          for (int mg = 0; mg < MF; mg += 4) {
+            bf16x8 av[4];
 #pragma unroll
-          for (int mf = 0; mf < 4; ++mf)
-            t[mf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mf], blo, t[mf], 0, 0, 0);
+            for (int mf = 0; mf < 4; ++mf) av[mf] = read_a(mg + mf, ii);
+            if (mg == 0)
+              q6k_parts(q4[ii], h2[ii >> 1], 4 * (ii & 1), (int)(int8_t)(rec >> (8 * (ii >> 1))),
+                        bhi, blo);
+#pragma unroll
+            for (int mf = 0; mf < 4; ++mf)
+              t[mg + mf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mf], bhi, t[mg + mf], 0, 0, 0);
+#pragma unroll
+            for (int mf = 0; mf < 4; ++mf)
+              t[mg + mf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mf], blo, t[mg + mf], 0, 0, 0);
+          }
           __builtin_amdgcn_sched_barrier(0);   // one slice's operands live at a time
         }
 #pragma unroll
-        for (int mf = 0; mf < 4; ++mf)
+        for (int mf = 0; mf < MF; ++mf)
 #pragma unroll
           for (int v = 0; v < 4; ++v) acc[mf][f][v] = fmaf(d, t[mf][v], acc[mf][f][v]);
       }
@@ -805,7 +822,7 @@ __global__ __launch_bounds__(kTThreads, FMT == kQ6_K ? 2 : 3) void k_ggemm_mx(
   }
   // ---- epilogue: lane holds D[row 4*(lane/16) + v][col lane%16] of each 16x16 tile
 #pragma unroll
-  for (int mf = 0; mf < 4; ++mf) {
+  for (int mf = 0; mf < MF; ++mf) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int pos = m0 + 16 * mf + 4 * g4 + v;
@@ -828,20 +845,33 @@ __global__ __launch_bounds__(kTThreads, FMT == kQ6_K ? 2 : 3) void k_ggemm_mx(
   }
 }
 
+// MXFP4: 64 rows x 256 weight rows; Q6_K: 128 x 128, so each operand it builds feeds
+// twice the MFMAs
+constexpr int mx_rows(int fmt) { return fmt == kQ6_K ? 128 : 64; }
+constexpr int mx_nfrag(int fmt) { return fmt == kQ6_K ? 2 : 4; }
+
 template <int FMT, bool GATED>
 hipError_t launch_ggemm_mx(const PoolView& a, const PoolView& b, const int32_t* slot_map,
                            int n_slots, int E, const int32_t* offsets, const int32_t* perm,
                            int T, int k, const uint16_t* src, int K, int N, uint16_t* h,
                            float* y, uint32_t* err, hipStream_t stream) {
-  constexpr int BM = 64;
+  constexpr int BM = mx_rows(FMT);
+  constexpr int TN = GATED ? 2 * mx_nfrag(FMT) * 16 : 4 * mx_nfrag(FMT) * 16;   // tile columns
   const int pairs = T * k;
   const int max_mtiles = (pairs + BM - 1) / BM + min(E, pairs);
-  const int n_ntiles = (N + (GATED ? 127 : 255)) / (GATED ? 128 : 256);
+  const int n_ntiles = (N + TN - 1) / TN;
   const int64_t grid = ((int64_t)max_mtiles * n_ntiles + 511) / 512 * 512;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_ggemm_mx<FMT, GATED>), dim3((unsigned)grid), dim3(kTThreads), 0, stream,
-                     a.q, a.s, a.q_slot, a.s_slot, b.q, b.s, slot_map, n_slots, E, offsets, perm,
-                     k, src, K, N, max_mtiles, n_ntiles, h, y, err);
+  if constexpr (FMT == kQ6_K)
+    hipLaunchKernelGGL((k_ggemm_mx<FMT, GATED, 128, 2>), dim3((unsigned)grid), dim3(kTThreads), 0,
+                       stream,
+                       a.q, a.s, a.q_slot, a.s_slot, b.q, b.s, slot_map, n_slots, E, offsets, perm,
+                       k, src, K, N, max_mtiles, n_ntiles, h, y, err);
+  else
+    hipLaunchKernelGGL((k_ggemm_mx<FMT, GATED, 64, 4>), dim3((unsigned)grid), dim3(kTThreads), 0,
+                       stream,
+                       a.q, a.s, a.q_slot, a.s_slot, b.q, b.s, slot_map, n_slots, E, offsets, perm,
+                       k, src, K, N, max_mtiles, n_ntiles, h, y, err);
   return hipGetLastError();
 }
 
