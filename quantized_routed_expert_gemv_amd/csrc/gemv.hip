@@ -1745,13 +1745,16 @@ hipError_t launch_down_ticket(int fmt, const PoolView& down, int n_slots, int E,
     constexpr int FMT = F();
     // chunks per wave per batch: of the sizes the format's registers allow, the one that
     // leaves the fewest masked slots in the row's batches (the larger on a tie)
+    // (MXFP4 and Q8_0 also 14 or 16 for long rows: a wave's batches are sequential round
+    // trips, so fewer, larger batches keep more bytes in flight)
     const int bpc = LaneMap<FMT>::kBlocksPerChunk;
     const int need = ((I / 32 + bpc - 1) / bpc + kGWaves - 1) / kGWaves;
-    const int ru_max = FMT == kQ4_K ? 6 : (FMT == kQ5_K || FMT == kQ6_K) ? 4 : 8;
+    constexpr bool kLong = FMT == kMXFP4 || FMT == kQ8_0;
+    const int ru_max = FMT == kQ4_K ? 6 : (FMT == kQ5_K || FMT == kQ6_K) ? 4 : kLong && need > 8 ? 16 : 8;
     auto slots = [&](int ru) { return (need + ru - 1) / ru * ru; };
     int ru = ru_max;
     for (int c = ru_max - 2; c >= 2; c -= 2)
-      if (slots(c) < slots(ru)) ru = c;
+      if ((c <= 8 || c == 14) && slots(c) < slots(ru)) ru = c;
 #define MOE_DT_CASE(N, R)                                                                     \
   hipLaunchKernelGGL((k_gemv<FMT, false, kSrcAct, N, R, true>), grid, dim3(kGThreads), 0,     \
                      stream, down.q, down.s, down.q_slot, down.s_slot, nullptr, nullptr,      \
@@ -1763,7 +1766,11 @@ hipError_t launch_down_ticket(int fmt, const PoolView& down, int n_slots, int E,
       else if (ru == 4) MOE_DT_CASE(NT, 4);
       else if constexpr (FMT != kQ5_K && FMT != kQ6_K) {
         if (ru == 6) MOE_DT_CASE(NT, 6);
-        else if constexpr (FMT != kQ4_K) MOE_DT_CASE(NT, 8);
+        else if constexpr (FMT != kQ4_K) {
+          if (ru == 8) MOE_DT_CASE(NT, 8);
+          else if (ru == 14) MOE_DT_CASE(NT, 14);
+          else MOE_DT_CASE(NT, 16);
+        }
       }
     };
     if (T <= 1) go(std::integral_constant<int, 1>{});
