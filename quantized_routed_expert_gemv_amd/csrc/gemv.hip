@@ -1526,6 +1526,8 @@ hipError_t launch_gate_up_gemv(int fmt, const PoolView& gate, const PoolView& up
 }
 
 
+hipError_t coresident_wgs(const void* kern, hipStream_t stream, int* out);
+
 hipError_t launch_gate_up_route(int fmt, const PoolView& gate, const PoolView& up,
                                 const int32_t* slot_map, int n_slots, int E, const uint16_t* x,
                                 int T, int k, int H, int I, const RouteIn& rin, uint16_t* h,
@@ -1534,13 +1536,20 @@ hipError_t launch_gate_up_route(int fmt, const PoolView& gate, const PoolView& u
       gate.q_slot != up.q_slot || gate.s_slot != up.s_slot)
     return hipErrorInvalidValue;
   const int n_units = (I / 16) * min(E, T * k);
-  dim3 grid(min(n_units, kRoutedMaxWG));
   const int nt = gemv_nt(fmt, T);
   return with_fmt(fmt, [&](auto F) {
+    // at most kRoutedMaxWG workgroups, and no more than fit on the device at once: a
+    // workgroup that waited for a slot would pay the routing late and lengthen the tail
 #define MOE_ROUTED_CASE(N, R)                                                                 \
-  hipLaunchKernelGGL((k_gate_up_routed<F(), N, R>), grid, dim3(kGThreads), 0, stream, gate.q, \
-                     gate.s, up.q, up.s, gate.q_slot, gate.s_slot, slot_map, n_slots, E, k, x, \
-                     H, I, h, err, rin, FusedDown{})
+  do {                                                                                        \
+    const void* kern = (const void*)k_gate_up_routed<F(), N, R>;                              \
+    int fit = kRoutedMaxWG;                                                                   \
+    if (coresident_wgs(kern, stream, &fit) != hipSuccess || fit < 1) fit = kRoutedMaxWG;      \
+    const dim3 grid(min(n_units, min(fit, kRoutedMaxWG)));                                     \
+    hipLaunchKernelGGL((k_gate_up_routed<F(), N, R>), grid, dim3(kGThreads), 0, stream,       \
+                       gate.q, gate.s, up.q, up.s, gate.q_slot, gate.s_slot, slot_map,        \
+                       n_slots, E, k, x, H, I, h, err, rin, FusedDown{});                     \
+  } while (0)
     // one token: a batch of chunks per wave (4 waves share a row) that wastes fewer slots
     // on masked chunks than the format's default (8 chunks; Q4_K 6; Q5_K, Q6_K 4)
     const int bpc = LaneMap<F()>::kBlocksPerChunk;
