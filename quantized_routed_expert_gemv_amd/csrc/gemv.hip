@@ -983,37 +983,51 @@ __global__ __launch_bounds__(kGThreads, 3) void k_gate_up_routed(
       if (lane == 0) nact_l = nact;
     }
   };
-  // 2'. one token, by wave 0 alone in registers: k rounds of a wave-wide maximum over the
-  //     unique keys of wave_topk_softmax (each round takes the largest remaining key, which
-  //     is the key of rank r: the same choices in the same order), then the softmax of the
-  //     chosen logits exactly as wave_softmax_chosen computes it.
+  // 2'. one token, by wave 0 alone in registers: k rounds, each taking the largest
+  //     remaining logit (its order_key, a 32-bit wave maximum) and, among equal ones, the
+  //     lowest expert index (ballots of the slots in expert order, the first set lane): the
+  //     largest remaining key of wave_topk_softmax, i.e. the key of rank r, so the same
+  //     choices in the same order; then the softmax of the chosen logits exactly as
+  //     wave_softmax_chosen computes it.
   // 3'. the k pairs of the one token (distinct experts): pair j goes to position
   //     #{j' : e_j' < e_j}, and is its expert's only pair.
   auto route_one_token = [&](auto slots) {
     constexpr int SLOTS = decltype(slots)::value;
     if (wave != 0) return;
-    uint64_t key[SLOTS];
+    // order_key of expert s * 64 + lane's logit (every real key is at least order_key(-inf),
+    // which is not 0); 0 for experts past E and for experts already taken
+    uint32_t key[SLOTS];
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) {
       const int e = s * kWave + lane;
       float x = e < E ? lg_l[e] : -INFINITY;
       x = (x != x) ? -INFINITY : x;
-      key[s] = e < E ? topk_key(x, e) : 0ull;
+      key[s] = e < E ? order_key(x) : 0u;
     }
-    uint64_t mine = 0ull;   // lane r < k: the key chosen in round r
+    uint32_t mkey = 0u;   // lane r < k: the order_key and expert chosen in round r
+    int ej = 0x7fffffff;
     for (int r = 0; r < k; ++r) {
-      uint64_t m = key[0];
+      uint32_t m = key[0];
 #pragma unroll
-      for (int s = 1; s < SLOTS; ++s) m = umax64(m, key[s]);
-      m = wave_max_u64(m);
-      mine = lane == r ? m : mine;
+      for (int s = 1; s < SLOTS; ++s) m = max(m, key[s]);
+      m = wave_max_u32(m);
+      int sel = -1;   // wave-uniform: the lowest expert whose key is m
 #pragma unroll
-      for (int s = 0; s < SLOTS; ++s) key[s] = key[s] == m ? 0ull : key[s];
+      for (int s = 0; s < SLOTS; ++s) {
+        const uint64_t b = __builtin_amdgcn_ballot_w64(key[s] == m);
+        if (sel < 0 && b != 0ull) sel = s * kWave + (int)__builtin_ctzll(b);
+      }
+#pragma unroll
+      for (int s = 0; s < SLOTS; ++s) key[s] = s * kWave + lane == sel ? 0u : key[s];
+      if (lane == r) {
+        mkey = m;
+        ej = sel;
+      }
     }
-    const int ej = lane < k ? key_index(mine) : 0x7fffffff;
+    if (lane >= k) ej = 0x7fffffff;
     // the value the key orders by: the logit itself, except that -0 comes back as +0,
     // which gives the same differences below
-    const float val = lane < k ? key_value(mine) : 0.f;
+    const float val = lane < k ? key_value(mkey) : 0.f;
     const float l0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(val), 0));
     const float z = lane < k ? expf(val - l0) : 0.f;
     float sum = 0.f;

@@ -37,38 +37,24 @@ __device__ __forceinline__ uint64_t topk_key(float x, int e) {
   return ((uint64_t)order_key(x) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
 }
 
-// A 64-bit value moved across lanes by one DPP control (both halves); lanes without a
-// source, or outside the row mask, receive 0.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROW_MASK, 0xf, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, ROW_MASK, 0xf, false);
-  return ((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo;
-}
-__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-
-// Largest 64-bit value of the wave, in every lane: running maxima within each 16-lane row
-// (row_shr 1, 2, 4, 8), then across rows (row_bcast 15 into rows 1 and 3, row_bcast 31
-// into rows 2 and 3), so that lane 63 holds the maximum, read back as a scalar.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  v = umax64(v, dpp_u64<0x111, 0xf>(v));
-  v = umax64(v, dpp_u64<0x112, 0xf>(v));
-  v = umax64(v, dpp_u64<0x114, 0xf>(v));
-  v = umax64(v, dpp_u64<0x118, 0xf>(v));
-  v = umax64(v, dpp_u64<0x142, 0xa>(v));
-  v = umax64(v, dpp_u64<0x143, 0xc>(v));
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
-  return ((uint64_t)hi << 32) | lo;
+// Largest 32-bit value of the wave, in every lane: running maxima within each 16-lane row
+// (row_shr 1, 2, 4, 8), then across rows (row_bcast 15 into rows 1 and 3, row_bcast 31 into
+// rows 2 and 3), so that lane 63 holds the maximum, read back as a scalar.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// The float a topk_key was made from (-0 comes back as +0, NaN as -inf: the values the key
+// The float an order_key was made from (-0 comes back as +0, NaN as -inf: the values the key
 // orders by).
-__device__ __forceinline__ float key_value(uint64_t key) {
-  const uint32_t u = (uint32_t)(key >> 32);
-  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+__device__ __forceinline__ float key_value(uint32_t okey) {
+  return __uint_as_float((okey & 0x80000000u) ? (okey & 0x7fffffffu) : ~okey);
 }
-__device__ __forceinline__ int key_index(uint64_t key) { return (int)(0xffffffffu - (uint32_t)key); }
 
 template <int SLOTS>
 __device__ void wave_topk_softmax_impl(const float* logit, int E, int k, int32_t* ids_out,
