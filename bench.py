@@ -34,7 +34,7 @@ BF16_PEAK_TFLOPS = 2500.0
 
 def ggemm_kernel(fmt: str) -> str:
     """The grouped-GEMM kernel that runs a format's prefill expert FFN."""
-    return "k_ggemm_mx" if fmt == "mxfp4" else "k_ggemm"
+    return "k_ggemm_mx" if fmt in ("mxfp4", "q6_k") else "k_ggemm"
 METRIC = "MoE-layer tokens/s; decode HBM GB/s and prefill MFMA % of peak"
 # bytes per weight of each format: MXFP4 16+1 and Q8_0 32+2 per 32; Q4_K 144, Q5_K 176 and
 # Q6_K 210 per 256 (the pool keeps 0.5 more per 32 for Q4_K / Q5_K, the 6-bit scale and min
