@@ -174,6 +174,10 @@ def test_layer_dense_and_full_mixture_special_cases():
     synth.Config("h7168_t2_q6k", 2, 7168, 512, 64, 6, "q6_k", None, "perm", 37, 1),
     # one Q8_0 token at the gpt-oss shape: 45 chunks per row, two batches of 6 per wave
     synth.Config("gptoss_q8_t1", 1, 2880, 2880, 32, 4, "q8_0", None, "perm", 40, 1),
+    # long MXFP4 down rows on the ticket-combining down kernel: 64 chunks per row, one batch
+    # of 16 per wave (one token), and 56 chunks, four batches of 14 (four tokens)
+    synth.Config("i8192_t1", 1, 256, 8192, 8, 2, "mxfp4", None, "perm", 41, 1),
+    synth.Config("i7168_t4", 4, 256, 7168, 8, 2, "mxfp4", None, "perm", 42, 1),
 ])
 def test_layer_decode_routing_edge_cases(cfg):
     """Shapes at the edges of the decode path that finishes the routing in the gate/up
